@@ -1,0 +1,233 @@
+"""Benchmark of one MuonH optimizer step on one MI355X.
+
+Default workload: the GPT-2-small matrix set (12 layers x {768x2304 qkv,
+768x768 attn-out, 768x3072 fc, 3072x768 proj} = 48 matrices), bf16 gradients
+and momentum, fp32 master weights, K = 5 quintic Newton-Schulz iterations on
+the full matrices, Hyperball with rho = ||W0||_F.  Gradients are Gaussian
+(sigma = 1e-3) plus a rank-4 spike of 10x entrywise magnitude, drawn on the
+device from a fixed seed; several gradient sets are pre-generated and used in
+turn, so the timed region only runs optimizer steps on HBM-resident data.
+
+One step = momentum, Newton-Schulz, Hyperball for all 48 matrices (the whole
+hot path).  Timing: W untimed steps, then exactly K timed steps between two
+device synchronizations.  A second pass of the same K steps records a HIP
+event pair around every kernel launch (on the stream it runs on) to get the
+per-kernel average durations behind the roofline figures; the headline value
+comes from the first, event-free pass.
+
+    python bench.py [--steps K] [--warmup W] [--workload gpt2|qwen1p2b|dense8b|single256]
+                    [--tile T] [--ns-precision x32|fold] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MuonH optimizer steps/sec + NS TFLOP/s (% bf16 MFMA peak), HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+NS_CLASSES = ("ns_gram_G1", "ns_poly_G2", "ns_update_G3")
+STREAM_CLASSES = ("momentum_prep", "hook_reduce", "hook_write")
+
+
+def workload_shapes(name):
+    from synth import gen
+    if name == "gpt2":
+        return gen.gpt2_small_shapes(), "gpt2-small matrix set: 12 x {768x2304, 768x768, 768x3072, 3072x768}"
+    if name == "qwen1p2b":
+        return gen.qwen3_1p2b_shapes(), "qwen3-style 1.2B matrix set: 28 x {2048x2048 q, 2048x1024 k, 2048x1024 v, 2048x2048 o, 2048x6144 gate, 2048x6144 up, 6144x2048 down}"
+    if name == "dense8b":
+        return gen.dense_8b_shapes(), "8B-shaped dense matrix set: 32 x {4096x4096 q, 4096x1024 k, 4096x1024 v, 4096x4096 o, 4096x14336 gate, 4096x14336 up, 14336x4096 down}"
+    if name == "single256":
+        return [(256, 256)], "single 256x256 matrix"
+    raise SystemExit(f"unknown workload {name}")
+
+
+def make_device_inputs(shapes, nsets, seed, torch):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    Ws, Ms, Gsets = [], [], []
+    for H, W in shapes:
+        Ws.append((torch.randn(H, W, generator=g, device="cuda") * 0.02).contiguous())
+        Ms.append(torch.zeros(H, W, device="cuda", dtype=torch.bfloat16))
+    sigma, rank, mag = 1e-3, 4, 10.0
+    for _ in range(nsets):
+        gs = []
+        for H, W in shapes:
+            Z = torch.randn(H, W, generator=g, device="cuda")
+            A = torch.randn(H, rank, generator=g, device="cuda")
+            B = torch.randn(W, rank, generator=g, device="cuda")
+            G = sigma * Z + (mag * sigma / math.sqrt(rank)) * (A @ B.t())
+            gs.append(G.to(torch.bfloat16).contiguous())
+        Gsets.append(gs)
+    rho = [float(torch.linalg.vector_norm(w.double())) for w in Ws]
+    return Ws, Ms, Gsets, rho
+
+
+def cpu_baseline(shapes, layer_size, budget_s=12.0):
+    """The fp64 numpy oracle, as it stands, on a bounded sample: whole layers
+    (layer_size consecutive matrices) of the same workload until ~budget_s of
+    CPU time, extrapolated to the full matrix set."""
+    import numpy as np
+    from oracle import muonh_oracle as orc
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    nlayers_total = max(1, len(shapes) // layer_size)
+    t_layers = []
+    done = 0
+    t_all = time.perf_counter()
+    while done < nlayers_total and (time.perf_counter() - t_all) < budget_s:
+        sub = shapes[done * layer_size:(done + 1) * layer_size]
+        Ws, Gs, Ms = gen.model_set(sub, 2, 1)
+        rho = [float(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+        t0 = time.perf_counter()
+        orc.muonh_step(Ws, Gs, Ms, 0.02, 0.95, 5, rho, state_bf16=True)
+        t_layers.append(time.perf_counter() - t0)
+        done += 1
+    per_layer = sum(t_layers) / len(t_layers)
+    step_s = per_layer * nlayers_total
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {nlayers_total} layers ({done * layer_size} of {len(shapes)} matrices) "
+                      f"timed with the fp64 numpy oracle, {sum(t_layers):.1f} s; value extrapolated to the "
+                      f"full set ({step_s:.1f} s/step)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2")
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--ns-precision", default="x32", choices=["x32", "fold"])
+    ap.add_argument("--K", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--grad-sets", type=int, default=4)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the step: this build runs on a single GPU "
+              "(no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import matrix_orthogonalizing_optimizer_momentum_amd as mm
+    if not os.path.exists(mm.LIB_PATH):
+        from matrix_orthogonalizing_optimizer_momentum_amd import build as b
+        b.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    shapes, wdesc = workload_shapes(args.workload)
+    K = args.K
+    Ws, Ms, Gsets, rho = make_device_inputs(shapes, args.grad_sets, 1234, torch)
+    q = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision)
+    torch.cuda.synchronize()
+
+    def step(i):
+        mm.muonh_step(Ws, Gsets[i % len(Gsets)], Ms, eta=0.02, beta=0.95, K=K, rho=rho, tile_T=args.tile,
+                      ns_precision=args.ns_precision)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # pass A: headline, no events
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # pass B: same steps with per-launch HIP events
+    mm.profile_begin()
+    tb0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    tb1 = time.perf_counter()
+    prof = mm.profile_read()
+    ms_b = (tb1 - tb0) * 1e3 / args.steps
+
+    ns_ms = sum(prof[c]["total_ms"] for c in NS_CLASSES if c in prof) / args.steps
+    st_ms = sum(prof[c]["total_ms"] for c in STREAM_CLASSES if c in prof) / args.steps
+    st_bytes = sum(prof[c]["bytes"] for c in STREAM_CLASSES if c in prof) / args.steps
+    ns_tflops = q["ns_flops"] / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
+    stream_gbs = st_bytes / (st_ms * 1e-3) / 1e9 if st_ms > 0 else None
+
+    dom = max(prof, key=lambda c: prof[c]["total_ms"])
+    d = prof[dom]
+    if dom in NS_CLASSES:
+        per_launch = d["flops"] / d["launches"]
+        achieved = per_launch / (d["avg_ms"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": per_launch, "avg_launch_ms": d["avg_ms"]}
+    else:
+        per_launch = d["bytes"] / d["launches"]
+        achieved = per_launch / (d["avg_ms"] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "bytes_per_launch": per_launch, "avg_launch_ms": d["avg_ms"]}
+
+    kernels = {c: {"launches_per_step": v["launches"] / args.steps, "avg_ms": round(v["avg_ms"], 5),
+                   "ms_per_step": round(v["total_ms"] / args.steps, 5)} for c, v in prof.items()}
+    for c in NS_CLASSES:
+        if c in prof and prof[c]["total_ms"] > 0:
+            kernels[c]["tflops"] = round(prof[c]["flops"] / (prof[c]["total_ms"] * 1e-3) / 1e12, 2)
+    for c in STREAM_CLASSES:
+        if c in prof and prof[c]["total_ms"] > 0:
+            kernels[c]["gbps"] = round(prof[c]["bytes"] / (prof[c]["total_ms"] * 1e-3) / 1e9, 1)
+
+    out = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_per_step, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded device RNG: W0 ~ N(0, 0.02^2); grads N(0, 1e-3^2) + rank-4 10x spike)",
+        "config": {"workload": f"{wdesc}; MuonH step, K={K} quintic NS "
+                               f"{'tiled T=' + str(args.tile) if args.tile else 'full-matrix'}, "
+                               f"bf16 grads/momentum, fp32 master weights, Hyperball rho=||W0||_F",
+                   "matrices": len(shapes), "K": K, "tile_T": args.tile, "ns_precision": args.ns_precision,
+                   "elements": sum(h * w for h, w in shapes)},
+        "ns_tflops": round(ns_tflops, 2) if ns_tflops else None,
+        "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
+        "ns_ms_per_step": round(ns_ms, 4),
+        "stream_gbps": round(stream_gbs, 1) if stream_gbs else None,
+        "stream_frac_hbm": round(stream_gbs / PEAK_HBM_GBS, 4) if stream_gbs else None,
+        "stream_ms_per_step": round(st_ms, 4),
+        "ms_per_step_with_events": round(ms_b, 4),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        layer = {"gpt2": 4, "qwen1p2b": 7, "dense8b": 7, "single256": 1}[args.workload]
+        out["cpu_baseline"] = cpu_baseline(shapes, layer)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * muonh.h -- C ABI of libmuonh, the MuonH / Hierarchical-Muon optimizer step
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One step over a list of weight matrices W_i (H_i x W_i, row-major, fp32
+ * master copies), with gradients G_i and momentum buffers M_i:
+ *
+ *   1. momentum          M <- beta * M + G
+ *        ("Muon: The Orthogonalized Optimizer Explained Through Equations,
+ *         Intuition, Code and Results", momentum recap note / Equation 1,
+ *         plain-sum form);
+ *   2. orthogonalize     O = NS_K(M): divide by ||M||_F + eps, then K times
+ *                        A = X X^T, B = b A + c A A, X = a X + B X on the
+ *                        wide side of the matrix
+ *        (same page, Newton-Schulz section, Equation 6 and the code section);
+ *        with tile_T > 0 the same map runs independently on every zero-padded
+ *        tile_T x tile_T tile
+ *        ("Hierarchical Muon: Tiled Newton-Schulz Updates for Efficient Muon
+ *         Optimization", core claim and abstract);
+ *   3. Hyperball         U_hat = O / ||O||_F, W <- rho * Pi(W - eta * U_hat),
+ *                        Pi(x) = x / ||x||_F
+ *        ("Fantastic Pretraining Optimizers and Where to Find Them II:
+ *         Hyperball Optimization", §2 eq. 1 / Algorithm 1 and Method), where a
+ *        numerically zero W - eta*U_hat restores the radius along the
+ *        pre-update W instead of leaving zero ("Refactor of pre/post weight
+ *        update hook functions", review comments on zero-norm handling);
+ *      or RadialBrake    W' = W - eta * max(1, H/W)^0.5 * O, then
+ *                        ||W_new|| = ||W|| + s (||W'|| - ||W||), s = outward
+ *                        if the norm grew else inward
+ *        (same hook page, PR description).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers to caller-owned, contiguous,
+ *     row-major buffers on the current HIP device.  The library never frees
+ *     or retains them beyond the call.  Arrays of pointers, shapes, rho and
+ *     coefficient tables are HOST memory, read during the call only.
+ *   - Every argument is validated before any GPU work is queued; a call that
+ *     returns an error has changed nothing.
+ *   - Work is queued asynchronously on opts->stream (NULL: the null stream).
+ *     No entry point synchronizes the host except muonh_get_flags and
+ *     muonh_profile_read.  GPU-side faults surface at the caller's next sync.
+ *   - Zero norms are not errors: they follow the rules above and bump the
+ *     device flag counters (muonh_get_flags).
+ *   - Thread-compatible: calls from several host threads must not overlap.
+ *     The library owns one workspace (grown on demand up to
+ *     opts->workspace_limit, freed by muonh_release) and calls that share it
+ *     are serialized on their streams by the caller.
+ *   - Return value: MUONH_OK (0) or a negative MUONH_E* code; never throws.
+ */
+#ifndef MUONH_H
+#define MUONH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MUONH_OK = 0,
+  MUONH_EINVAL = -1,   /* invalid argument (null pointer, bad size, bad scalar, bad dtype) */
+  MUONH_ENOMEM = -2,   /* workspace for one matrix exceeds workspace_limit, or allocation failed */
+  MUONH_EHIP = -3,     /* a HIP runtime call or kernel launch failed */
+  MUONH_ENOTIMPL = -4  /* valid request this build does not implement */
+};
+
+/* element types */
+enum { MUONH_F32 = 0, MUONH_BF16 = 1 };
+
+/* How bf16 Newton-Schulz keeps X between iterations (MFMA operands are bf16
+ * and accumulation is fp32 in both):
+ *   MUONH_NS_X32  -- an fp32 master copy of X carries the a*X term, a bf16
+ *                    shadow feeds the matrix cores (default);
+ *   MUONH_NS_FOLD -- X itself is stored in bf16.
+ * Both fold the 1/(||M||+eps) pre-scale into the first iteration instead of
+ * rounding the pre-scaled X0 to bf16.  Ignored when ns_dtype is MUONH_F32. */
+enum { MUONH_NS_X32 = 0, MUONH_NS_FOLD = 1 };
+
+/* weight-update hook */
+enum { MUONH_HOOK_HYPERBALL = 0, MUONH_HOOK_RADIAL_BRAKE = 1 };
+
+typedef struct muonh_opts {
+  void*        stream;          /* hipStream_t to queue on; NULL = null stream */
+  int          state_dtype;     /* dtype of grads, momentum, ns_orthogonalize in/out and
+                                   frob_project's U: MUONH_BF16 (default) or MUONH_F32 */
+  int          ns_dtype;        /* Newton-Schulz operand dtype: MUONH_BF16 (default) or MUONH_F32 */
+  int          ns_precision;    /* MUONH_NS_X32 (default) or MUONH_NS_FOLD */
+  const float* coeffs;          /* host, 3*K floats: (a,b,c) for iteration k at [3k..3k+2];
+                                   NULL = (3.4445, -4.7750, 2.0315) every iteration */
+  float        ns_eps;          /* added to ||M||_F before dividing; default 1e-7 */
+  float        zero_rel_eps;    /* Hyperball: ||W - eta*U_hat|| < zero_rel_eps*rho counts as
+                                   zero and restores the radius; default 1e-6 */
+  int          hook;            /* MUONH_HOOK_HYPERBALL (default) or MUONH_HOOK_RADIAL_BRAKE */
+  float        outward;         /* RadialBrake factor when the norm grows, in [0,1]; default 0.5 */
+  float        inward;          /* RadialBrake factor otherwise, in [0,1]; default 1.0 */
+  float        rb_eps;          /* RadialBrake: post-update norm <= rb_eps leaves W'; default 1e-15 */
+  size_t       workspace_limit; /* bytes the library may hold as workspace; 0 = 3/4 of free HBM.
+                                   Matrices are processed in chunks that fit it. */
+} muonh_opts;
+
+/* Fill *o with the defaults listed above. */
+void muonh_default_opts(muonh_opts* o);
+
+/*
+ * muonh_step -- one full optimizer step (momentum -> NS -> hook) for n matrices.
+ *
+ *   params[i]  device, fp32, shapes[2i] x shapes[2i+1], updated in place (W)
+ *   grads[i]   device, state_dtype, same shape, read only (G)
+ *   moms[i]    device, state_dtype, same shape, updated in place (M)
+ *   shapes     host, 2*n int64: rows, cols of matrix i (each >= 1)
+ *   n          number of matrices (>= 1)
+ *   eta        learning rate / Hyperball angular step (finite, >= 0)
+ *   beta       momentum coefficient, in [0, 1)
+ *   K          Newton-Schulz iterations, 0..64 (0: O = M / (||M|| + eps))
+ *   rho        host, n floats: Hyperball radius per matrix (finite, > 0);
+ *              ignored (may be NULL) for RadialBrake
+ *   tile_T     0 = full-matrix NS; > 0 = Hierarchical Muon with tile side tile_T
+ *              (1..128, or a multiple of 64 up to 8192); the hook always acts on
+ *              the full matrix
+ *   opts       NULL = defaults
+ * Buffers of different matrices must not overlap; grads may not alias moms.
+ */
+int muonh_step(void* const params[], const void* const grads[], void* const moms[],
+               const int64_t shapes[], int n, float eta, float beta, int K,
+               const float rho[], int tile_T, const muonh_opts* opts);
+
+/*
+ * ns_orthogonalize -- out[i] = NS_K(in[i]) (tile_T > 0: tiled), no momentum,
+ * no hook.  in/out are device buffers of opts->state_dtype; out[i] may alias
+ * in[i].  Same shape, K and tile_T rules as muonh_step.
+ */
+int ns_orthogonalize(const void* const in[], void* const out[], const int64_t shapes[],
+                     int n, int K, int tile_T, const muonh_opts* opts);
+
+/*
+ * frob_project -- the Hyperball projection on its own:
+ *   W[i] <- rho[i] * Pi(W[i] - eta * U[i] / ||U[i]||)
+ * with the same zero rules as muonh_step.  W: device fp32, in place.
+ * U: NULL (plain projection W <- rho * W / ||W||) or an array of n device
+ * buffers of opts->state_dtype (a NULL entry is treated as a zero update).
+ */
+int frob_project(void* const W[], const void* const U[], const int64_t shapes[], int n,
+                 float eta, const float rho[], const muonh_opts* opts);
+
+/*
+ * Device flag counters, accumulated since the last reset:
+ *   out[0] matrices whose orthogonalized update had zero norm,
+ *   out[1] Hyperball radius restores (numerically zero post-update weight),
+ *   out[2] restores impossible because W was zero too (W left unchanged),
+ *   out[3] matrices with a non-finite norm.
+ * Synchronizes the device.  Returns MUONH_OK or MUONH_EHIP.
+ */
+int muonh_get_flags(uint64_t out[4]);
+int muonh_reset_flags(void);
+
+/* Static message for an error code. */
+const char* muonh_strerror(int code);
+
+/* Free the workspace and cached plans (synchronizes the device first). */
+void muonh_release(void);
+
+/*
+ * Host-only planning query (no GPU call): how a muonh_step with these
+ * arguments would be split.  out[0] = chunks, out[1] = workspace bytes of the
+ * largest chunk, out[2] = Newton-Schulz units (matrices or tiles),
+ * out[3] = dense NS flops per step (sum of K (4 r^2 s + 2 r^3) over units,
+ * with r, s the true (unpadded) sides), out[4] = GEMM tile jobs per NS
+ * iteration, out[5] = streaming bytes per step (momentum 3 passes + hook
+ * 2 passes, algorithmic).  Returns MUONH_OK, MUONH_EINVAL or MUONH_ENOMEM
+ * exactly as muonh_step's validation would.
+ */
+int muonh_plan_query(const int64_t shapes[], int n, int K, int tile_T,
+                     const muonh_opts* opts, size_t workspace_limit, int64_t out[6]);
+
+/*
+ * Per-kernel timing for measurement.  muonh_profile_begin() makes every later
+ * launch record a pair of HIP events on the stream it is queued on;
+ * muonh_profile_read() synchronizes, and fills up to max entries with the
+ * accumulated launch count, total milliseconds and algorithmic work of each
+ * kernel class since begin (flops for Newton-Schulz kernels, bytes for
+ * streaming kernels), then stops recording.  *n_out receives the entry count.
+ */
+typedef struct muonh_kernel_stat {
+  char     name[40];
+  uint64_t launches;
+  double   total_ms;
+  double   flops;   /* algorithmic flops over all recorded launches */
+  double   bytes;   /* algorithmic HBM bytes over all recorded launches */
+} muonh_kernel_stat;
+
+int muonh_profile_begin(void);
+int muonh_profile_read(muonh_kernel_stat* out, int max, int* n_out);
+
+/* Library version string. */
+const char* muonh_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUONH_H */

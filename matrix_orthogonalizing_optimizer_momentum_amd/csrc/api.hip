@@ -1,0 +1,681 @@
+// libmuonh C ABI: validation, workspace, cached descriptor tables, launch
+// sequencing and measurement hooks.  The per-step sequence for one chunk of
+// matrices is
+//   k_momentum_prep                      (momentum, ||M||^2, X0 layouts)
+//   K x { G1 gram, G2 poly, G3 update }  (Newton-Schulz, grouped MFMA GEMMs)
+//   k_hook_reduce, k_hook_write          (Hyperball or RadialBrake)
+// all queued on the caller's stream with no host synchronization.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <list>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/muonh.h"
+#include "desc.h"
+#include "planner.h"
+
+namespace muonh {
+
+// launchers (kernels_*.hip)
+hipError_t launch_momentum_prep(int state_dt, int op_dt, const MomMat* mats, const MomBlock* blocks,
+                                int nblocks, const NsUnit* units, const SlotTable& st, float beta,
+                                hipStream_t s);
+hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
+                              const SlotTable& st, float eta, hipStream_t s);
+hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
+                             const SlotTable& st, float eta, float zero_rel_eps, float outward,
+                             float inward, float rb_eps, Flags* flags, hipStream_t s);
+hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
+                        hipStream_t s);
+hipError_t launch_ns_gemm(int op_dt, int phase, const NsUnit* units, const GemmJob* jobs, int njobs,
+                          float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
+                          const SlotTable& st, hipStream_t s);
+int gemm_tile_m();
+int gemm_tile_n();
+
+namespace {
+
+constexpr int kMaxK = 64;
+
+// ------------------------------------------------------------------ state
+struct DevTables {  // one chunk's tables on the device
+  char* mem = nullptr;
+  NsUnit* units = nullptr;
+  GemmJob* g12 = nullptr;
+  GemmJob* g3 = nullptr;
+  MomMat* mom_mats = nullptr;
+  MomBlock* mom_blocks = nullptr;
+  HookMat* hook_mats = nullptr;
+  HookBlock* hook_blocks = nullptr;
+  int32_t* nparts = nullptr;
+  int64_t* part_base = nullptr;
+  int n_g12 = 0, n_g3 = 0, n_mom = 0, n_hook = 0;
+  int64_t parts_total = 0;
+  int nslots = 0;
+  double flops_g1 = 0, flops_g2 = 0, flops_g3 = 0;
+  double bytes_mom = 0, bytes_hook1 = 0, bytes_hook2 = 0, bytes_sumsq = 0;
+};
+
+struct CachedPlan {
+  std::vector<uint64_t> key;
+  std::vector<DevTables> chunks;
+  int64_t max_parts = 0;
+  int max_slots = 0;
+};
+
+struct ProfRec {
+  int cls;
+  hipEvent_t e0, e1;
+  double flops, bytes;
+};
+
+struct State {
+  std::mutex mu;
+  int device = -1;
+  char* ws = nullptr;          // data workspace
+  int64_t ws_bytes = 0;
+  double* partials = nullptr;  // meta
+  int64_t partials_cap = 0;
+  unsigned* counters = nullptr;
+  double* sums = nullptr;
+  int slots_cap = 0;
+  Flags* flags = nullptr;
+  std::list<CachedPlan> plans;  // most recent first
+  bool profiling = false;
+  std::vector<ProfRec> prof;
+};
+
+State& S() {
+  static State s;
+  return s;
+}
+
+const char* kClassNames[] = {"momentum_prep", "ns_gram_G1", "ns_poly_G2", "ns_update_G3",
+                             "hook_reduce",   "hook_write", "sumsq"};
+enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_N };
+
+// ------------------------------------------------------------------ helpers
+void free_plan(CachedPlan& p) {
+  for (auto& c : p.chunks)
+    if (c.mem) (void)hipFree(c.mem);
+  p.chunks.clear();
+}
+
+void clear_plans(State& st) {
+  for (auto& p : st.plans) free_plan(p);
+  st.plans.clear();
+}
+
+int ensure_meta(State& st, int64_t parts, int slots) {
+  if (!st.flags) {
+    if (hipMalloc(&st.flags, sizeof(Flags)) != hipSuccess) return MUONH_ENOMEM;
+    if (hipMemset(st.flags, 0, sizeof(Flags)) != hipSuccess) return MUONH_EHIP;
+  }
+  if (parts > st.partials_cap) {
+    if (st.partials) (void)hipFree(st.partials);
+    st.partials = nullptr;
+    const int64_t cap = std::max<int64_t>(parts, 4096);
+    if (hipMalloc(&st.partials, cap * 2 * sizeof(double)) != hipSuccess) {
+      st.partials_cap = 0;
+      return MUONH_ENOMEM;
+    }
+    st.partials_cap = cap;
+  }
+  if (slots > st.slots_cap) {
+    if (st.counters) (void)hipFree(st.counters);
+    if (st.sums) (void)hipFree(st.sums);
+    st.counters = nullptr;
+    st.sums = nullptr;
+    const int cap = std::max(slots, 1024);
+    if (hipMalloc(&st.counters, cap * sizeof(unsigned)) != hipSuccess) return MUONH_ENOMEM;
+    if (hipMalloc(&st.sums, cap * 2 * sizeof(double)) != hipSuccess) return MUONH_ENOMEM;
+    if (hipMemset(st.counters, 0, cap * sizeof(unsigned)) != hipSuccess) return MUONH_EHIP;
+    st.slots_cap = cap;
+  }
+  return MUONH_OK;
+}
+
+int ensure_ws(State& st, int64_t bytes) {
+  if (bytes <= st.ws_bytes) return MUONH_OK;
+  // Growing invalidates every cached table (they hold workspace addresses);
+  // hipFree waits for in-flight work that may still use the old buffer.
+  clear_plans(st);
+  if (st.ws) (void)hipFree(st.ws);
+  st.ws = nullptr;
+  st.ws_bytes = 0;
+  if (hipMalloc(&st.ws, bytes) != hipSuccess) return MUONH_ENOMEM;
+  st.ws_bytes = bytes;
+  return MUONH_OK;
+}
+
+bool finite_f(float v) { return std::isfinite(v); }
+
+struct Resolved {
+  muonh_opts o;
+  float coeffs[3 * kMaxK];
+};
+
+int resolve(const muonh_opts* in, int K, Resolved& r) {
+  muonh_default_opts(&r.o);
+  if (in) r.o = *in;
+  const muonh_opts& o = r.o;
+  if (o.state_dtype != MUONH_BF16 && o.state_dtype != MUONH_F32) return MUONH_EINVAL;
+  if (o.ns_dtype != MUONH_BF16 && o.ns_dtype != MUONH_F32) return MUONH_EINVAL;
+  if (o.ns_precision != MUONH_NS_X32 && o.ns_precision != MUONH_NS_FOLD) return MUONH_EINVAL;
+  if (o.hook != MUONH_HOOK_HYPERBALL && o.hook != MUONH_HOOK_RADIAL_BRAKE) return MUONH_EINVAL;
+  if (!finite_f(o.ns_eps) || o.ns_eps < 0.f) return MUONH_EINVAL;
+  if (!finite_f(o.zero_rel_eps) || o.zero_rel_eps < 0.f) return MUONH_EINVAL;
+  if (!finite_f(o.rb_eps) || o.rb_eps < 0.f) return MUONH_EINVAL;
+  // RadialBrake factors may damp but never amplify a radial change.
+  if (!(o.outward >= 0.f && o.outward <= 1.f) || !(o.inward >= 0.f && o.inward <= 1.f)) return MUONH_EINVAL;
+  for (int k = 0; k < K; ++k) {
+    for (int j = 0; j < 3; ++j) {
+      const float v = o.coeffs ? o.coeffs[3 * k + j] : (j == 0 ? 3.4445f : j == 1 ? -4.7750f : 2.0315f);
+      if (!finite_f(v)) return MUONH_EINVAL;
+      r.coeffs[3 * k + j] = v;
+    }
+  }
+  return MUONH_OK;
+}
+
+int check_tile(int tile_T) {
+  if (tile_T < 0) return MUONH_EINVAL;
+  if (tile_T == 0) return MUONH_OK;
+  if (tile_T > 8192) return MUONH_EINVAL;
+  if (tile_T % 64 == 0) return MUONH_OK;
+  if (tile_T <= 128) return MUONH_ENOTIMPL;  // resident small-tile kernel not in this build
+  return MUONH_EINVAL;
+}
+
+// 3/4 of the HBM free at the first call (fixed afterwards, so that chunking
+// does not change as the library's own workspace grows).
+size_t default_limit() {
+  static size_t lim = 0;
+  if (lim == 0) {
+    size_t fr = 0, tot = 0;
+    lim = hipMemGetInfo(&fr, &tot) == hipSuccess ? fr / 4 * 3 : (size_t)8 << 30;
+  }
+  return lim;
+}
+
+Cfg make_cfg(int kind, int n, int K, int tile_T, const Resolved& r, size_t limit) {
+  Cfg c{};
+  c.kind = kind;
+  c.n = n;
+  c.K = K;
+  c.tile_T = tile_T;
+  c.state_dt = r.o.state_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
+  c.op_dt = r.o.ns_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
+  c.x32 = (c.op_dt == DT_BF16 && r.o.ns_precision == MUONH_NS_X32) ? 1 : 0;
+  c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB : kModeHB;
+  c.gemm_bm = gemm_tile_m();
+  c.gemm_bn = gemm_tile_n();
+  c.ws_limit = limit;
+  return c;
+}
+
+template <typename T>
+void put(std::vector<char>& blob, const std::vector<T>& v, size_t& off) {
+  off = (blob.size() + 255) / 256 * 256;
+  blob.resize(off + v.size() * sizeof(T));
+  if (!v.empty()) memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
+}
+
+int upload_chunk(const ChunkTables& t, DevTables& d) {
+  std::vector<char> blob;
+  size_t o_units, o_g12, o_g3, o_mm, o_mb, o_hm, o_hb, o_np, o_pb;
+  put(blob, t.units, o_units);
+  put(blob, t.g12_jobs, o_g12);
+  put(blob, t.g3_jobs, o_g3);
+  put(blob, t.mom_mats, o_mm);
+  put(blob, t.mom_blocks, o_mb);
+  put(blob, t.hook_mats, o_hm);
+  put(blob, t.hook_blocks, o_hb);
+  put(blob, t.nparts, o_np);
+  put(blob, t.part_base, o_pb);
+  if (blob.empty()) blob.resize(256);
+  if (hipMalloc(&d.mem, blob.size()) != hipSuccess) return MUONH_ENOMEM;
+  // Synchronous copy: runs once per new (buffers, shapes, options) set.
+  if (hipMemcpy(d.mem, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess) return MUONH_EHIP;
+  d.units = reinterpret_cast<NsUnit*>(d.mem + o_units);
+  d.g12 = reinterpret_cast<GemmJob*>(d.mem + o_g12);
+  d.g3 = reinterpret_cast<GemmJob*>(d.mem + o_g3);
+  d.mom_mats = reinterpret_cast<MomMat*>(d.mem + o_mm);
+  d.mom_blocks = reinterpret_cast<MomBlock*>(d.mem + o_mb);
+  d.hook_mats = reinterpret_cast<HookMat*>(d.mem + o_hm);
+  d.hook_blocks = reinterpret_cast<HookBlock*>(d.mem + o_hb);
+  d.nparts = reinterpret_cast<int32_t*>(d.mem + o_np);
+  d.part_base = reinterpret_cast<int64_t*>(d.mem + o_pb);
+  d.n_g12 = (int)t.g12_jobs.size();
+  d.n_g3 = (int)t.g3_jobs.size();
+  d.n_mom = (int)t.mom_blocks.size();
+  d.n_hook = (int)t.hook_blocks.size();
+  d.parts_total = t.parts_total;
+  d.nslots = (int)t.nparts.size();
+  d.flops_g1 = t.flops_g1;
+  d.flops_g2 = t.flops_g2;
+  d.flops_g3 = t.flops_g3;
+  d.bytes_mom = t.bytes_mom;
+  d.bytes_hook1 = t.bytes_hook1;
+  d.bytes_hook2 = t.bytes_hook2;
+  d.bytes_sumsq = t.bytes_sumsq;
+  return MUONH_OK;
+}
+
+void key_push_ptrs(std::vector<uint64_t>& k, const void* const* a, int n) {
+  for (int i = 0; i < n; ++i) k.push_back(a ? (uint64_t)(uintptr_t)a[i] : 0);
+}
+
+// Looks up or builds the device tables for this call.
+int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, const int64_t* shapes,
+             CachedPlan*& out) {
+  std::vector<uint64_t> key;
+  key.push_back((uint64_t)cfg.kind);
+  key.push_back((uint64_t)cfg.n);
+  key.push_back((uint64_t)cfg.tile_T);
+  key.push_back((uint64_t)cfg.state_dt);
+  key.push_back((uint64_t)cfg.op_dt);
+  key.push_back((uint64_t)cfg.x32);
+  key.push_back((uint64_t)cfg.hook);
+  key.push_back((uint64_t)plan.chunks.size());
+  for (const auto& c : plan.chunks) key.push_back((uint64_t)c.m1);
+  key.push_back((uint64_t)(uintptr_t)st.ws);
+  uint32_t eb;
+  memcpy(&eb, &p.eta, 4);
+  key.push_back(cfg.hook == kModeRB ? eb : 0);  // RadialBrake tables hold eta * shape scale
+  for (int i = 0; i < 2 * cfg.n; ++i) key.push_back((uint64_t)shapes[i]);
+  key_push_ptrs(key, p.params, cfg.kind == CALL_NS ? 0 : cfg.n);
+  key_push_ptrs(key, p.grads, cfg.n);
+  key_push_ptrs(key, p.moms, cfg.kind == CALL_STEP ? cfg.n : 0);
+  key_push_ptrs(key, p.outs, cfg.kind == CALL_NS ? cfg.n : 0);
+  if (p.rho && cfg.kind != CALL_NS) {
+    for (int i = 0; i < cfg.n; ++i) {
+      uint32_t b;
+      memcpy(&b, &p.rho[i], 4);
+      key.push_back(b);
+    }
+  }
+  for (auto it = st.plans.begin(); it != st.plans.end(); ++it) {
+    if (it->key == key) {
+      st.plans.splice(st.plans.begin(), st.plans, it);
+      out = &st.plans.front();
+      return MUONH_OK;
+    }
+  }
+  CachedPlan cp;
+  cp.key = std::move(key);
+  for (size_t c = 0; c < plan.chunks.size(); ++c) {
+    ChunkTables t;
+    fill_chunk(plan, (int)c, cfg, p, st.ws, t);
+    DevTables d;
+    const int rc = upload_chunk(t, d);
+    if (rc != MUONH_OK) {
+      if (d.mem) (void)hipFree(d.mem);
+      free_plan(cp);
+      return rc;
+    }
+    cp.max_parts = std::max(cp.max_parts, d.parts_total);
+    cp.max_slots = std::max(cp.max_slots, d.nslots);
+    cp.chunks.push_back(d);
+  }
+  const int rc = ensure_meta(st, cp.max_parts, cp.max_slots);
+  if (rc != MUONH_OK) {
+    free_plan(cp);
+    return rc;
+  }
+  st.plans.push_front(std::move(cp));
+  while (st.plans.size() > 8) {  // bounded cache; hipFree waits for in-flight users
+    free_plan(st.plans.back());
+    st.plans.pop_back();
+  }
+  out = &st.plans.front();
+  return MUONH_OK;
+}
+
+// ------------------------------------------------------------------ profiling
+struct Prof {
+  State& st;
+  hipStream_t s;
+  int cls;
+  double flops, bytes;
+  hipEvent_t e0{}, e1{};
+  bool on;
+  Prof(State& st_, hipStream_t s_, int cls_, double f, double b)
+      : st(st_), s(s_), cls(cls_), flops(f), bytes(b), on(st_.profiling) {
+    if (on) {
+      (void)hipEventCreate(&e0);
+      (void)hipEventCreate(&e1);
+      (void)hipEventRecord(e0, s);
+    }
+  }
+  ~Prof() {
+    if (on) {
+      (void)hipEventRecord(e1, s);
+      st.prof.push_back({cls, e0, e1, flops, bytes});
+    }
+  }
+};
+
+SlotTable slot_table(State& st, const DevTables& d) {
+  SlotTable t;
+  t.partials = st.partials;
+  t.counters = st.counters;
+  t.nparts = d.nparts;
+  t.part_base = d.part_base;
+  t.sums = st.sums;
+  return t;
+}
+
+#define MUONH_TRY_HIP(x)              \
+  do {                                \
+    if ((x) != hipSuccess) return MUONH_EHIP; \
+  } while (0)
+
+int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, const SlotTable& sl,
+           hipStream_t s) {
+  const float eps = r.o.ns_eps;
+  if (cfg.K == 0) {
+    Prof pf(st, s, PC_G3, 0, 0);
+    MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, d.units, d.g3, d.n_g3, 1.f, 0.f, 0.f, eps, 1, 1, 0, 1, sl, s));
+    return MUONH_OK;
+  }
+  for (int k = 0; k < cfg.K; ++k) {
+    const float a = r.coeffs[3 * k], b = r.coeffs[3 * k + 1], c = r.coeffs[3 * k + 2];
+    const int first = k == 0, last = k == cfg.K - 1, cur = k & 1;
+    {
+      Prof pf(st, s, PC_G1, d.flops_g1, 0);
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 0, d.units, d.g12, d.n_g12, a, b, c, eps, first, 0, cur, 0, sl, s));
+    }
+    {
+      Prof pf(st, s, PC_G2, d.flops_g2, 0);
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 1, d.units, d.g12, d.n_g12, a, b, c, eps, first, 0, cur, 0, sl, s));
+    }
+    {
+      Prof pf(st, s, PC_G3, d.flops_g3, 0);
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, d.units, d.g3, d.n_g3, a, b, c, eps, first, last, cur, 0, sl, s));
+    }
+  }
+  return MUONH_OK;
+}
+
+int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Resolved& r,
+             const CallPtrs& p, float beta) {
+  State& st = S();
+  std::lock_guard<std::mutex> lk(st.mu);
+  int dev = 0;
+  MUONH_TRY_HIP(hipGetDevice(&dev));
+  if (st.device != -1 && st.device != dev) return MUONH_EINVAL;  // one device per process
+  st.device = dev;
+  const size_t limit = r.o.workspace_limit ? r.o.workspace_limit : default_limit();
+  Cfg cfg = make_cfg(kind, n, K, tile_T, r, limit);
+  Plan plan;
+  int rc = make_plan(shapes, cfg, plan);
+  if (rc != MUONH_OK) return rc;
+  rc = ensure_ws(st, std::max<int64_t>(plan.ws_bytes, 256));
+  if (rc != MUONH_OK) return rc;
+  CachedPlan* cp = nullptr;
+  rc = get_plan(st, plan, cfg, p, shapes, cp);
+  if (rc != MUONH_OK) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(r.o.stream);
+  for (const DevTables& d : cp->chunks) {
+    const SlotTable sl = slot_table(st, d);
+    if (kind != CALL_PROJ) {
+      {
+        Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
+        MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
+                                           sl, kind == CALL_STEP ? beta : 0.f, s));
+      }
+      rc = run_ns(st, cfg, d, r, sl, s);
+      if (rc != MUONH_OK) return rc;
+    }
+    if (kind == CALL_PROJ && p.grads) {
+      Prof pf(st, s, PC_SQ, 0, d.bytes_sumsq);
+      MUONH_TRY_HIP(launch_sumsq(d.hook_mats, d.hook_blocks, d.n_hook, sl, s));
+    }
+    if (kind != CALL_NS) {
+      {
+        Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
+        MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta, s));
+      }
+      {
+        Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
+        MUONH_TRY_HIP(launch_hook_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta,
+                                        r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, st.flags, s));
+      }
+    }
+  }
+  return MUONH_OK;
+}
+
+bool bad_ptrs(const void* const* a, int n) {
+  if (!a) return true;
+  for (int i = 0; i < n; ++i)
+    if (!a[i]) return true;
+  return false;
+}
+
+int validate_common(const int64_t* shapes, int n, int K, int tile_T) {
+  if (!shapes || n <= 0) return MUONH_EINVAL;
+  if (K < 0 || K > kMaxK) return MUONH_EINVAL;
+  for (int i = 0; i < 2 * n; ++i)
+    if (shapes[i] < 1) return MUONH_EINVAL;
+  return check_tile(tile_T);
+}
+
+}  // namespace
+}  // namespace muonh
+
+using namespace muonh;
+
+extern "C" {
+
+void muonh_default_opts(muonh_opts* o) {
+  if (!o) return;
+  memset(o, 0, sizeof(*o));
+  o->stream = nullptr;
+  o->state_dtype = MUONH_BF16;
+  o->ns_dtype = MUONH_BF16;
+  o->ns_precision = MUONH_NS_X32;
+  o->coeffs = nullptr;
+  o->ns_eps = 1e-7f;
+  o->zero_rel_eps = 1e-6f;
+  o->hook = MUONH_HOOK_HYPERBALL;
+  o->outward = 0.5f;
+  o->inward = 1.0f;
+  o->rb_eps = 1e-15f;
+  o->workspace_limit = 0;
+}
+
+int muonh_step(void* const params[], const void* const grads[], void* const moms[], const int64_t shapes[],
+               int n, float eta, float beta, int K, const float rho[], int tile_T, const muonh_opts* opts) {
+  int rc = validate_common(shapes, n, K, tile_T);
+  if (rc != MUONH_OK) return rc;
+  if (bad_ptrs(params, n) || bad_ptrs(grads, n) || bad_ptrs((const void* const*)moms, n)) return MUONH_EINVAL;
+  if (!std::isfinite(eta) || eta < 0.f) return MUONH_EINVAL;
+  if (!std::isfinite(beta) || beta < 0.f || beta >= 1.f) return MUONH_EINVAL;
+  Resolved r;
+  rc = resolve(opts, K, r);
+  if (rc != MUONH_OK) return rc;
+  if (r.o.hook == MUONH_HOOK_HYPERBALL) {
+    if (!rho) return MUONH_EINVAL;
+    for (int i = 0; i < n; ++i)
+      if (!std::isfinite(rho[i]) || rho[i] <= 0.f) return MUONH_EINVAL;
+  }
+  for (int i = 0; i < n; ++i)
+    if (grads[i] == moms[i]) return MUONH_EINVAL;
+  CallPtrs p{params, grads, moms, nullptr, r.o.hook == MUONH_HOOK_HYPERBALL ? rho : nullptr, eta};
+  return run_call(CALL_STEP, shapes, n, K, tile_T, r, p, beta);
+}
+
+int ns_orthogonalize(const void* const in[], void* const out[], const int64_t shapes[], int n, int K,
+                     int tile_T, const muonh_opts* opts) {
+  int rc = validate_common(shapes, n, K, tile_T);
+  if (rc != MUONH_OK) return rc;
+  if (bad_ptrs(in, n) || bad_ptrs((const void* const*)out, n)) return MUONH_EINVAL;
+  Resolved r;
+  rc = resolve(opts, K, r);
+  if (rc != MUONH_OK) return rc;
+  CallPtrs p{nullptr, in, nullptr, out, nullptr, 0.f};
+  return run_call(CALL_NS, shapes, n, K, tile_T, r, p, 0.f);
+}
+
+int frob_project(void* const W[], const void* const U[], const int64_t shapes[], int n, float eta,
+                 const float rho[], const muonh_opts* opts) {
+  if (!shapes || n <= 0) return MUONH_EINVAL;
+  for (int i = 0; i < 2 * n; ++i)
+    if (shapes[i] < 1) return MUONH_EINVAL;
+  if (bad_ptrs((const void* const*)W, n) || !rho) return MUONH_EINVAL;
+  if (!std::isfinite(eta) || eta < 0.f) return MUONH_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (!std::isfinite(rho[i]) || rho[i] <= 0.f) return MUONH_EINVAL;
+  Resolved r;
+  int rc = resolve(opts, 0, r);
+  if (rc != MUONH_OK) return rc;
+  r.o.hook = MUONH_HOOK_HYPERBALL;
+  // A NULL U array is the plain projection; NULL entries are zero updates.
+  std::vector<const void*> us;
+  const void* const* up = nullptr;
+  if (U) {
+    bool any = false;
+    for (int i = 0; i < n; ++i) any = any || U[i];
+    if (any) up = U;
+  }
+  CallPtrs p{W, up, nullptr, nullptr, rho, eta};
+  return run_call(CALL_PROJ, shapes, n, 0, 0, r, p, 0.f);
+}
+
+int muonh_get_flags(uint64_t out[4]) {
+  if (!out) return MUONH_EINVAL;
+  State& st = S();
+  std::lock_guard<std::mutex> lk(st.mu);
+  if (!st.flags) {
+    out[0] = out[1] = out[2] = out[3] = 0;
+    return MUONH_OK;
+  }
+  Flags f;
+  if (hipDeviceSynchronize() != hipSuccess) return MUONH_EHIP;
+  if (hipMemcpy(&f, st.flags, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return MUONH_EHIP;
+  out[0] = f.zero_update;
+  out[1] = f.restored;
+  out[2] = f.unrestorable;
+  out[3] = f.nonfinite;
+  return MUONH_OK;
+}
+
+int muonh_reset_flags(void) {
+  State& st = S();
+  std::lock_guard<std::mutex> lk(st.mu);
+  if (!st.flags) return MUONH_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return MUONH_EHIP;
+  if (hipMemset(st.flags, 0, sizeof(Flags)) != hipSuccess) return MUONH_EHIP;
+  return MUONH_OK;
+}
+
+const char* muonh_strerror(int code) {
+  switch (code) {
+    case MUONH_OK: return "success";
+    case MUONH_EINVAL: return "invalid argument";
+    case MUONH_ENOMEM: return "workspace limit exceeded or device allocation failed";
+    case MUONH_EHIP: return "HIP runtime or kernel launch error";
+    case MUONH_ENOTIMPL: return "not implemented in this build";
+    default: return "unknown error";
+  }
+}
+
+void muonh_release(void) {
+  State& st = S();
+  std::lock_guard<std::mutex> lk(st.mu);
+  if (st.device < 0) return;
+  (void)hipDeviceSynchronize();
+  clear_plans(st);
+  if (st.ws) (void)hipFree(st.ws);
+  if (st.partials) (void)hipFree(st.partials);
+  if (st.counters) (void)hipFree(st.counters);
+  if (st.sums) (void)hipFree(st.sums);
+  if (st.flags) (void)hipFree(st.flags);
+  for (auto& r : st.prof) {
+    (void)hipEventDestroy(r.e0);
+    (void)hipEventDestroy(r.e1);
+  }
+  st.prof.clear();
+  st.profiling = false;
+  st.ws = nullptr;
+  st.ws_bytes = 0;
+  st.partials = nullptr;
+  st.partials_cap = 0;
+  st.counters = nullptr;
+  st.sums = nullptr;
+  st.slots_cap = 0;
+  st.flags = nullptr;
+  st.device = -1;
+}
+
+int muonh_plan_query(const int64_t shapes[], int n, int K, int tile_T, const muonh_opts* opts,
+                     size_t workspace_limit, int64_t out[6]) {
+  if (!out) return MUONH_EINVAL;
+  int rc = validate_common(shapes, n, K, tile_T);
+  if (rc != MUONH_OK) return rc;
+  Resolved r;
+  rc = resolve(opts, K, r);
+  if (rc != MUONH_OK) return rc;
+  if (workspace_limit == 0) workspace_limit = (size_t)1 << 62;
+  Cfg cfg = make_cfg(CALL_STEP, n, K, tile_T, r, workspace_limit);
+  Plan plan;
+  rc = make_plan(shapes, cfg, plan);
+  if (rc != MUONH_OK) return rc;
+  out[0] = (int64_t)plan.chunks.size();
+  out[1] = plan.ws_bytes;
+  out[2] = plan.units;
+  out[3] = (int64_t)plan.ns_flops;
+  out[4] = plan.jobs_per_iter;
+  out[5] = (int64_t)plan.stream_bytes;
+  return MUONH_OK;
+}
+
+int muonh_profile_begin(void) {
+  State& st = S();
+  std::lock_guard<std::mutex> lk(st.mu);
+  for (auto& r : st.prof) {
+    (void)hipEventDestroy(r.e0);
+    (void)hipEventDestroy(r.e1);
+  }
+  st.prof.clear();
+  st.profiling = true;
+  return MUONH_OK;
+}
+
+int muonh_profile_read(muonh_kernel_stat* out, int max, int* n_out) {
+  State& st = S();
+  std::lock_guard<std::mutex> lk(st.mu);
+  st.profiling = false;
+  muonh_kernel_stat acc[PC_N];
+  memset(acc, 0, sizeof(acc));
+  for (int c = 0; c < PC_N; ++c) strncpy(acc[c].name, kClassNames[c], sizeof(acc[c].name) - 1);
+  int rc = MUONH_OK;
+  for (auto& r : st.prof) {
+    if (hipEventSynchronize(r.e1) != hipSuccess) rc = MUONH_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) rc = MUONH_EHIP;
+    acc[r.cls].launches += 1;
+    acc[r.cls].total_ms += ms;
+    acc[r.cls].flops += r.flops;
+    acc[r.cls].bytes += r.bytes;
+    (void)hipEventDestroy(r.e0);
+    (void)hipEventDestroy(r.e1);
+  }
+  st.prof.clear();
+  int k = 0;
+  for (int c = 0; c < PC_N && k < max; ++c)
+    if (acc[c].launches) out[k++] = acc[c];
+  if (n_out) *n_out = k;
+  return rc;
+}
+
+const char* muonh_version(void) { return "libmuonh 0.1 (gfx950)"; }
+
+}  // extern "C"

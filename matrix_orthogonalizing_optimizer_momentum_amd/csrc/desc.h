@@ -1,0 +1,114 @@
+// Plain-old-data descriptors shared by the host planner and the HIP kernels.
+// No HIP headers here: the planner builds these tables on the host, copies
+// them to the device once per step, and the kernels decode them.
+#pragma once
+#include <stdint.h>
+
+namespace muonh {
+
+enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+
+// Padding granule of every workspace leading dimension (elements).  Producers
+// write zeros into [valid, padded) so GEMM loaders can read whole vectors.
+constexpr int kPad = 64;
+
+inline int64_t pad_up(int64_t v, int64_t g) { return (v + g - 1) / g * g; }
+
+// Reduction slots: each slot owns nparts double2 partials starting at
+// part_base; the last block to commit a slot sums its partials in a fixed
+// order (deterministic) into sums[slot] and re-arms the counter.
+struct SlotTable {
+  double* partials;        // 2 doubles per partial
+  unsigned* counters;      // one per slot, zero between uses
+  const int32_t* nparts;   // per slot
+  const int64_t* part_base;// per slot, index of the first partial
+  double* sums;            // 2 doubles per slot
+};
+
+// One Newton-Schulz unit: a whole matrix, or one HiMuon tile handled as a
+// T x T matrix.  Logical X is r x s with r <= s.
+//   X layout : r rows, leading dim ld_s = pad(s)
+//   XT layout: s rows, leading dim ld_r = pad(r)
+struct NsUnit {
+  int32_t r, s;
+  int32_t ld_s, ld_r;
+  int32_t norm_slot;    // slot holding ||M||^2 for the pre-scale
+  int32_t onorm_slot;   // slot collecting ||O||^2 (per full matrix)
+  int32_t onorm_part0;  // first partial of this unit inside onorm_slot
+  int32_t o_trans;      // 1: X(i, n) is out[n * o_ld + i]; 0: out[i * o_ld + n]
+  int32_t o_rows;       // valid rows of X written to out (i < o_rows)
+  int32_t o_cols;       // valid cols of X written to out (n < o_cols)
+  int32_t o_dtype;      // DType of out
+  int32_t g3_cols;      // number of G3 column tiles of this unit (for partial numbering)
+  int64_t o_ld;
+  void* o_ptr;          // output base, already offset to the unit's origin
+  void* x;              // op-dtype X (X layout)
+  void* xt[2];          // op-dtype X^T ping-pong (XT layout)
+  float* x32;           // fp32 master X (X layout) or nullptr
+  void* a;              // op-dtype A = X X^T (r rows, ld_r)
+  void* b;              // op-dtype B = b A + c A A (r rows, ld_r)
+};
+
+// One output macro-tile of a grouped GEMM launch.
+struct GemmJob {
+  int32_t unit;
+  int32_t tm, tn;       // macro-tile row / column
+  int32_t kchunks;      // K extent in BK steps (for scheduling only)
+};
+
+// Momentum / prep: one source matrix.
+struct MomMat {
+  const void* g;        // gradient (or the NS input for ns_orthogonalize)
+  void* m;              // momentum, updated in place; nullptr = prep only (m = g)
+  int64_t H, W;         // M layout rows, cols (ld = W)
+  int32_t trans;        // full mode: X = M^T (H > W)
+  int32_t tile_T;       // 0: full matrix; > 0: per-tile units (multiple of 64)
+  int32_t unit0;        // first NsUnit of this matrix
+  int32_t ntc;          // tiles per row (tile mode)
+  int32_t nbc;          // 64-wide column blocks over the padded extent
+  int32_t write_x;      // 1: write X0 / X0^T into the units' workspace
+};
+
+// One 64 x 64 block of a momentum / prep launch.
+struct MomBlock {
+  int32_t mat;
+  int32_t br, bc;       // block row / column in the padded M grid
+  int32_t slot;         // norm slot this block contributes to (-1: none)
+  int32_t part;         // partial index inside the slot
+  int32_t pad_;
+};
+
+// Hook / projection / norm passes: one full matrix, streamed flat.
+struct HookMat {
+  float* w;             // fp32 weights (M layout), updated in pass 2
+  const void* o;        // update direction (o_dtype), nullptr = zero update
+  int64_t numel;
+  int32_t o_dtype;
+  int32_t onorm_slot;   // slot of ||O||^2 (Hyperball); -1: none (zero update)
+  int32_t slot;         // slot for this matrix's pass-1 sums
+  int32_t nblocks;      // blocks of this matrix in a pass
+  float rho;            // Hyperball radius
+  float oscale;         // RadialBrake: eta * max(1, H/W)^0.5
+};
+
+struct HookBlock {
+  int32_t mat;
+  int32_t blk;          // block index within the matrix
+};
+
+// Hook modes.
+constexpr int kModeHB = 0;  // Hyperball
+constexpr int kModeRB = 1;  // RadialBrake
+
+// Elements per block of the flat hook / norm passes (256 threads x 32).
+constexpr int kHookBlockElems = 8192;
+
+// Device-side flag counters (see muonh_get_flags).
+struct Flags {
+  unsigned long long zero_update;
+  unsigned long long restored;
+  unsigned long long unrestorable;
+  unsigned long long nonfinite;
+};
+
+}  // namespace muonh

@@ -1,0 +1,339 @@
+// HBM-streaming kernels of the MuonH step (gfx950):
+//   k_momentum_prep  M <- beta*M + G (Muon explainer, momentum recap /
+//                    Equation 1), the Frobenius sum of squares of the stored M
+//                    per Newton-Schulz unit, and X0 = M written in both
+//                    Newton-Schulz layouts (the wide-side orientation of the
+//                    Muon explainer's code section is a layout choice here,
+//                    never a copy of its own);
+//   k_hook_reduce    pass 1 of the Hyperball / RadialBrake hook: per-matrix
+//                    sums of ||W'||^2 and ||W||^2 in fp64;
+//   k_hook_write     pass 2: re-projection / brake (Hyperball show notes,
+//                    Algorithm 1 and Method; hook PR, PR description and the
+//                    zero-norm review comments);
+//   k_sumsq          per-matrix ||U||^2 for the stand-alone projection.
+// All of them are bandwidth-bound: 16-byte vector accesses, 64x64 blocks
+// with an LDS transpose where a layout flips, one deterministic fp64
+// reduction commit per block.
+#include "common.h"
+
+namespace muonh {
+
+constexpr int kMomThreads = 256;
+constexpr int kHookThreads = 256;
+constexpr int kHookPerThread = 32;  // elements per thread per block (4 x 8)
+static_assert(kHookBlockElems == kHookThreads * kHookPerThread, "hook block size");
+
+// ---------------------------------------------------------------------------
+// momentum + norm + X0 layouts
+// ---------------------------------------------------------------------------
+template <typename ST, typename OT>
+__global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
+    const MomMat* __restrict__ mats, const MomBlock* __restrict__ blocks,
+    const NsUnit* __restrict__ units, SlotTable st, float beta) {
+  __shared__ float tile[64][65];
+  const MomBlock blk = blocks[blockIdx.x];
+  const MomMat mm = mats[blk.mat];
+  const int t = threadIdx.x;
+  const int cc = t & 7;   // 8-element column chunk
+  const int rr = t >> 3;  // 0..31
+  const int64_t H = mm.H, W = mm.W;
+  const bool vec = (W % 8) == 0;
+  const ST* __restrict__ g = reinterpret_cast<const ST*>(mm.g);
+  ST* __restrict__ m = reinterpret_cast<ST*>(mm.m);
+
+  float sq = 0.f;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int lr = rr + 32 * p;
+    const int64_t row = (int64_t)blk.br * 64 + lr;
+    const int64_t col0 = (int64_t)blk.bc * 64 + cc * 8;
+    float v[8];
+    if (row < H && vec && col0 + 8 <= W) {
+      const int64_t idx = row * W + col0;
+      float gv[8];
+      load8(g, idx, gv);
+      if (m != nullptr) {
+        float mv[8];
+        load8(m, idx, mv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = St<ST>::round(fmaf(beta, mv[k], gv[k]));
+        store8(m, idx, v);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = gv[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t col = col0 + k;
+        float x = 0.f;
+        if (row < H && col < W) {
+          const int64_t idx = row * W + col;
+          float gg = St<ST>::ld(g, idx);
+          if (m != nullptr) {
+            x = St<ST>::round(fmaf(beta, St<ST>::ld(m, idx), gg));
+            St<ST>::st(m, idx, x);
+          } else {
+            x = gg;
+          }
+        }
+        v[k] = x;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sq = fmaf(v[k], v[k], sq);
+      tile[lr][cc * 8 + k] = v[k];
+    }
+  }
+
+  if (mm.write_x) {
+    // Destination unit and in-unit coordinates of this block's origin.
+    int unit_id = mm.unit0;
+    int64_t r0 = (int64_t)blk.br * 64, c0 = (int64_t)blk.bc * 64;  // M coordinates
+    if (mm.tile_T > 0) {
+      const int T = mm.tile_T;
+      unit_id += (int)(r0 / T) * mm.ntc + (int)(c0 / T);
+      r0 %= T;
+      c0 %= T;
+    }
+    const NsUnit u = units[unit_id];
+    // "direct" buffer keeps M's orientation, "flipped" buffer is its transpose.
+    OT* dir;
+    OT* flp;
+    int64_t ld_dir, ld_flp;
+    if (mm.trans) {  // X = M^T: X^T layout == M layout
+      dir = reinterpret_cast<OT*>(u.xt[0]); ld_dir = u.ld_r;
+      flp = reinterpret_cast<OT*>(u.x);     ld_flp = u.ld_s;
+    } else {
+      dir = reinterpret_cast<OT*>(u.x);     ld_dir = u.ld_s;
+      flp = reinterpret_cast<OT*>(u.xt[0]); ld_flp = u.ld_r;
+    }
+    // Valid rows of the two buffers (in-unit coordinates).
+    const int64_t dir_rows = mm.tile_T > 0 ? mm.tile_T : H;
+    const int64_t flp_rows = mm.tile_T > 0 ? mm.tile_T : W;
+    // Direct write: same element positions as loaded.
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int lr = rr + 32 * p;
+      const int64_t row = r0 + lr;
+      const int64_t col = c0 + cc * 8;
+      if (row < dir_rows && col + 8 <= ld_dir) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = tile[lr][cc * 8 + k];
+        store8(dir, row * ld_dir + col, v);
+      }
+    }
+    __syncthreads();
+    // Flipped write: row = M column, 16 consecutive M rows per thread.
+    {
+      const int lc = t >> 2;          // column of the block -> flipped row
+      const int seg = (t & 3) * 16;   // 16 M rows
+      const int64_t frow = c0 + lc;
+      const int64_t fcol = r0 + seg;
+      if (frow < flp_rows) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (fcol + 8 * h + 8 <= ld_flp) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = tile[seg + 8 * h + k][lc];
+            store8(flp, frow * ld_flp + fcol + 8 * h, v);
+          }
+        }
+      }
+    }
+  }
+  if (blk.slot >= 0) commit_partial2<kMomThreads>((double)sq, 0.0, st, blk.slot, blk.part);
+}
+
+// ---------------------------------------------------------------------------
+// hook passes
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load8_dyn(const void* p, int64_t i, int dtype, float (&v)[8]) {
+  if (dtype == DT_BF16) load8(reinterpret_cast<const bf16_t*>(p), i, v);
+  else load8(reinterpret_cast<const float*>(p), i, v);
+}
+
+// Coefficient applied to O in W' = W - coef * O.
+__device__ __forceinline__ float hook_coef(const HookMat& hm, const SlotTable& st, float eta, int mode) {
+  if (mode == kModeRB) return hm.oscale;
+  if (hm.o == nullptr || hm.onorm_slot < 0) return 0.f;
+  const double n2 = st.sums[2 * hm.onorm_slot];
+  if (!(n2 > 0.0)) return 0.f;
+  return (float)((double)eta / sqrt(n2));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kHookThreads) void k_hook_reduce(
+    const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st, float eta) {
+  const HookBlock hb = blocks[blockIdx.x];
+  const HookMat hm = mats[hb.mat];
+  const float coef = hook_coef(hm, st, eta, MODE);
+  double s0 = 0.0, s1 = 0.0;
+  const int64_t base = (int64_t)hb.blk * kHookBlockElems;
+#pragma unroll
+  for (int it = 0; it < kHookPerThread / 8; ++it) {
+    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
+    if (i >= hm.numel) break;
+    float w[8], o[8];
+    if (i + 8 <= hm.numel) {
+      load8(hm.w, i, w);
+      if (hm.o) load8_dyn(hm.o, i, hm.o_dtype, o);
+      else for (int k = 0; k < 8; ++k) o[k] = 0.f;
+    } else {
+      for (int k = 0; k < 8; ++k) {
+        const bool ok = i + k < hm.numel;
+        w[k] = ok ? hm.w[i + k] : 0.f;
+        o[k] = (ok && hm.o) ? load_dyn(hm.o, i + k, hm.o_dtype) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float wp = fmaf(-coef, o[k], w[k]);
+      s0 = fma((double)wp, (double)wp, s0);
+      s1 = fma((double)w[k], (double)w[k], s1);
+    }
+  }
+  commit_partial2<kHookThreads>(s0, s1, st, hm.slot, hb.blk);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kHookThreads) void k_hook_write(
+    const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st, float eta,
+    float zero_rel_eps, float outward, float inward, float rb_eps, Flags* flags) {
+  const HookBlock hb = blocks[blockIdx.x];
+  const HookMat hm = mats[hb.mat];
+  const float coef = hook_coef(hm, st, eta, MODE);
+  const double v0 = st.sums[2 * hm.slot];      // ||W'||^2
+  const double v1 = st.sums[2 * hm.slot + 1];  // ||W||^2
+  const double nwp = sqrt(v0), nw = sqrt(v1);
+  // Per-matrix decision, identical in every block of the matrix.
+  int branch;          // 0: scale W', 1: scale W (restore), 2: leave W
+  double scale;
+  if (MODE == kModeRB) {
+    const double s = (nwp > nw) ? (double)outward : (double)inward;
+    if (nwp > (double)rb_eps) { branch = 0; scale = (nw + s * (nwp - nw)) / nwp; }
+    else { branch = 0; scale = 1.0; }
+  } else {
+    const double rho = (double)hm.rho;
+    if (nwp >= (double)zero_rel_eps * rho) { branch = 0; scale = rho / nwp; }
+    else if (nw > 0.0) { branch = 1; scale = rho / nw; }
+    else { branch = 2; scale = 1.0; }
+  }
+  if (hb.blk == 0 && threadIdx.x == 0 && flags != nullptr) {
+    if (MODE == kModeHB) {
+      if (coef == 0.f && hm.o != nullptr) atomicAdd(&flags->zero_update, 1ull);
+      if (branch == 1) atomicAdd(&flags->restored, 1ull);
+      if (branch == 2) atomicAdd(&flags->unrestorable, 1ull);
+    }
+    if (!isfinite(v0) || !isfinite(v1)) atomicAdd(&flags->nonfinite, 1ull);
+  }
+  if (branch == 2) return;
+  const int64_t base = (int64_t)hb.blk * kHookBlockElems;
+#pragma unroll
+  for (int it = 0; it < kHookPerThread / 8; ++it) {
+    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
+    if (i >= hm.numel) break;
+    float w[8], o[8];
+    const bool full = i + 8 <= hm.numel;
+    if (full) {
+      load8(hm.w, i, w);
+      if (hm.o && branch == 0) load8_dyn(hm.o, i, hm.o_dtype, o);
+      else for (int k = 0; k < 8; ++k) o[k] = 0.f;
+    } else {
+      for (int k = 0; k < 8; ++k) {
+        const bool ok = i + k < hm.numel;
+        w[k] = ok ? hm.w[i + k] : 0.f;
+        o[k] = (ok && hm.o && branch == 0) ? load_dyn(hm.o, i + k, hm.o_dtype) : 0.f;
+      }
+    }
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float base_v = (branch == 0) ? fmaf(-coef, o[k], w[k]) : w[k];
+      r[k] = (float)((double)base_v * scale);
+    }
+    if (full) {
+      store8(hm.w, i, r);
+    } else {
+      for (int k = 0; k < 8; ++k)
+        if (i + k < hm.numel) hm.w[i + k] = r[k];
+    }
+  }
+}
+
+// ||U||^2 per matrix (HookMat.o is U; the result lands in slot onorm_slot).
+__global__ __launch_bounds__(kHookThreads) void k_sumsq(
+    const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st) {
+  const HookBlock hb = blocks[blockIdx.x];
+  const HookMat hm = mats[hb.mat];
+  if (hm.o == nullptr || hm.onorm_slot < 0) return;  // zero update: no norm needed (uniform per block)
+  double s0 = 0.0;
+  const int64_t base = (int64_t)hb.blk * kHookBlockElems;
+  for (int it = 0; it < kHookPerThread / 8; ++it) {
+    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
+    if (i >= hm.numel) break;
+    float o[8];
+    if (i + 8 <= hm.numel) {
+      load8_dyn(hm.o, i, hm.o_dtype, o);
+    } else {
+      for (int k = 0; k < 8; ++k) o[k] = (i + k < hm.numel) ? load_dyn(hm.o, i + k, hm.o_dtype) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s0 = fma((double)o[k], (double)o[k], s0);
+  }
+  commit_partial2<kHookThreads>(s0, 0.0, st, hm.onorm_slot, hb.blk);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_momentum_prep(int state_dt, int op_dt, const MomMat* mats, const MomBlock* blocks,
+                                int nblocks, const NsUnit* units, const SlotTable& st, float beta,
+                                hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  dim3 grid(nblocks), block(kMomThreads);
+  if (state_dt == DT_BF16 && op_dt == DT_BF16)
+    hipLaunchKernelGGL((k_momentum_prep<bf16_t, bf16_t>), grid, block, 0, s, mats, blocks, units, st, beta);
+  else if (state_dt == DT_BF16 && op_dt == DT_F32)
+    hipLaunchKernelGGL((k_momentum_prep<bf16_t, float>), grid, block, 0, s, mats, blocks, units, st, beta);
+  else if (state_dt == DT_F32 && op_dt == DT_BF16)
+    hipLaunchKernelGGL((k_momentum_prep<float, bf16_t>), grid, block, 0, s, mats, blocks, units, st, beta);
+  else
+    hipLaunchKernelGGL((k_momentum_prep<float, float>), grid, block, 0, s, mats, blocks, units, st, beta);
+  return hipGetLastError();
+}
+
+hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
+                              const SlotTable& st, float eta, hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  if (mode == kModeRB)
+    hipLaunchKernelGGL((k_hook_reduce<kModeRB>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, eta);
+  else
+    hipLaunchKernelGGL((k_hook_reduce<kModeHB>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, eta);
+  return hipGetLastError();
+}
+
+hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
+                             const SlotTable& st, float eta, float zero_rel_eps, float outward,
+                             float inward, float rb_eps, Flags* flags, hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  if (mode == kModeRB)
+    hipLaunchKernelGGL((k_hook_write<kModeRB>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st,
+                       eta, zero_rel_eps, outward, inward, rb_eps, flags);
+  else
+    hipLaunchKernelGGL((k_hook_write<kModeHB>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st,
+                       eta, zero_rel_eps, outward, inward, rb_eps, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
+                        hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sumsq, dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st);
+  return hipGetLastError();
+}
+
+}  // namespace muonh

@@ -1,0 +1,310 @@
+// Host-side planner of libmuonh (no HIP runtime calls).
+//
+// Units.  Full-matrix Newton-Schulz works on the wide side of each matrix
+// (Muon explainer, code section: a tall matrix is transposed so that X X^T is
+// the small Gram); here that is only a layout flag.  Hierarchical Muon
+// ("Hierarchical Muon: Tiled Newton-Schulz Updates for Efficient Muon
+// Optimization", core claim) cuts each matrix into T x T tiles from (0, 0);
+// every tile becomes its own zero-padded T x T unit.
+//
+// Chunks.  Matrices are taken in order and packed into chunks whose
+// workspace fits the limit (the memory-bounded chunking that page lists
+// among the tiled scheme's implementation options); each chunk runs the whole
+// step before the next one reuses the workspace.
+#include "planner.h"
+
+#include <algorithm>
+#include <cmath>
+
+#include "../../include/muonh.h"
+
+namespace muonh {
+
+UnitBytes unit_bytes(int r, int s, int op_dt, int x32) {
+  const int64_t es = esize(op_dt);
+  const int64_t ld_s = pad_up(s, kPad), ld_r = pad_up(r, kPad);
+  UnitBytes u;
+  u.x = align256((int64_t)r * ld_s * es);
+  u.xt = align256((int64_t)s * ld_r * es);
+  u.x32 = (x32 && op_dt == DT_BF16) ? align256((int64_t)r * ld_s * 4) : 0;
+  u.a = align256((int64_t)r * ld_r * es);
+  u.b = u.a;
+  return u;
+}
+
+static double ns_flops_true(int64_t h, int64_t w, int K) {
+  const double r = (double)std::min(h, w), s = (double)std::max(h, w);
+  return (double)K * (4.0 * r * r * s + 2.0 * r * r * r);
+}
+
+int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
+  plan = Plan();
+  const int n = cfg.n;
+  plan.mats.resize(n);
+  const int T = cfg.tile_T;
+  const int BM = cfg.gemm_bm, BN = cfg.gemm_bn;
+  for (int i = 0; i < n; ++i) {
+    MatPlan& m = plan.mats[i];
+    m.H = shapes[2 * i];
+    m.W = shapes[2 * i + 1];
+    if (m.H < 1 || m.W < 1 || m.H > (int64_t)1 << 30 || m.W > (int64_t)1 << 30) return MUONH_EINVAL;
+    if (m.H * m.W > ((int64_t)1 << 40)) return MUONH_EINVAL;
+    m.ws_bytes = 0;
+    const int64_t numel = m.H * m.W;
+    if (cfg.kind == CALL_PROJ) {
+      m.r = (int)std::min(m.H, m.W);
+      m.s = (int)std::max(m.H, m.W);
+      m.trans = m.H > m.W;
+      m.nunits = 0;
+      m.ntr = m.ntc = 0;
+      const double ob = cfg.state_dt == DT_F32 ? 4 : 2;
+      plan.stream_bytes += (double)numel * (ob + (4 + ob) + (4 + ob + 4));
+      continue;
+    }
+    if (T > 0) {
+      m.r = m.s = T;
+      m.trans = 0;
+      m.ntr = (int)((m.H + T - 1) / T);
+      m.ntc = (int)((m.W + T - 1) / T);
+      m.nunits = m.ntr * m.ntc;
+      const UnitBytes ub = unit_bytes(T, T, cfg.op_dt, cfg.x32);
+      m.ws_bytes += (int64_t)m.nunits * ub.total();
+      for (int a = 0; a < m.ntr; ++a)
+        for (int b = 0; b < m.ntc; ++b) {
+          const int64_t h = std::min<int64_t>(T, m.H - (int64_t)a * T);
+          const int64_t w = std::min<int64_t>(T, m.W - (int64_t)b * T);
+          plan.ns_flops += ns_flops_true(h, w, cfg.K);
+        }
+      const int64_t ld = pad_up(T, kPad);
+      plan.jobs_per_iter += (int64_t)m.nunits * (2 * ((ld + BM - 1) / BM) * ((T + BN - 1) / BN) +
+                                                 ((ld + BM - 1) / BM) * ((ld + BN - 1) / BN));
+    } else {
+      m.r = (int)std::min(m.H, m.W);
+      m.s = (int)std::max(m.H, m.W);
+      m.trans = m.H > m.W ? 1 : 0;
+      m.nunits = 1;
+      m.ntr = m.ntc = 1;
+      const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32);
+      m.ws_bytes += ub.total();
+      plan.ns_flops += ns_flops_true(m.H, m.W, cfg.K);
+      const int64_t ldr = pad_up(m.r, kPad), lds = pad_up(m.s, kPad);
+      plan.jobs_per_iter += 2 * ((ldr + BM - 1) / BM) * ((m.r + BN - 1) / BN) +
+                            ((ldr + BM - 1) / BM) * ((lds + BN - 1) / BN);
+    }
+    if (cfg.kind == CALL_STEP) m.ws_bytes += align256(numel * esize(cfg.op_dt));  // O
+    plan.units += m.nunits;
+    const double sb = cfg.state_dt == DT_F32 ? 4 : 2;
+    const double ob = esize(cfg.op_dt);
+    if (cfg.kind == CALL_STEP) plan.stream_bytes += (double)numel * (3 * sb + (4 + ob) + (4 + ob + 4));
+    else plan.stream_bytes += (double)numel * (sb + sb);  // NS: read input, write output
+  }
+  // chunks
+  const int64_t limit = (int64_t)cfg.ws_limit;
+  int m0 = 0;
+  int64_t acc = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t b = plan.mats[i].ws_bytes;
+    if (b > limit) return MUONH_ENOMEM;
+    if (acc + b > limit && i > m0) {
+      plan.chunks.push_back({m0, i, acc});
+      m0 = i;
+      acc = 0;
+    }
+    acc += b;
+  }
+  plan.chunks.push_back({m0, n, acc});
+  for (auto& c : plan.chunks) plan.ws_bytes = std::max(plan.ws_bytes, c.ws_bytes);
+  return MUONH_OK;
+}
+
+void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char* ws, ChunkTables& t) {
+  t = ChunkTables();
+  const ChunkPlan& ch = plan.chunks[c];
+  const int BM = cfg.gemm_bm, BN = cfg.gemm_bn;
+  const int T = cfg.tile_T;
+  const int nm = ch.m1 - ch.m0;
+  const int es_op = esize(cfg.op_dt);
+
+  // --- units and workspace carve
+  int64_t off = 0;
+  auto carve = [&](int64_t bytes) -> char* {
+    char* q = ws + off;
+    off += bytes;
+    return q;
+  };
+  std::vector<int> unit0(nm);
+  std::vector<char*> obuf(nm, nullptr);
+  for (int mi = 0; mi < nm; ++mi) {
+    const MatPlan& m = plan.mats[ch.m0 + mi];
+    unit0[mi] = (int)t.units.size();
+    if (cfg.kind == CALL_PROJ) continue;
+    const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32);
+    for (int k = 0; k < m.nunits; ++k) {
+      NsUnit u{};
+      u.r = m.r;
+      u.s = m.s;
+      u.ld_s = (int32_t)pad_up(m.s, kPad);
+      u.ld_r = (int32_t)pad_up(m.r, kPad);
+      u.x = carve(ub.x);
+      u.xt[0] = carve(ub.xt);
+      u.xt[1] = carve(ub.xt);
+      u.x32 = ub.x32 ? reinterpret_cast<float*>(carve(ub.x32)) : nullptr;
+      u.a = carve(ub.a);
+      u.b = carve(ub.b);
+      t.units.push_back(u);
+    }
+    if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
+  }
+  const int nunits = (int)t.units.size();
+
+  // --- slots: [unit norms][matrix O norms][matrix hook sums]
+  const int s_norm0 = 0, s_onorm0 = nunits, s_hook0 = nunits + nm;
+  const int nslots = nunits + 2 * nm;
+  t.nparts.assign(nslots, 0);
+
+  // --- output placement, O-norm partial numbering, GEMM jobs, flops
+  for (int mi = 0; mi < nm; ++mi) {
+    const int gi = ch.m0 + mi;
+    const MatPlan& m = plan.mats[gi];
+    if (cfg.kind == CALL_PROJ) continue;
+    void* out = cfg.kind == CALL_STEP ? (void*)obuf[mi] : p.outs[gi];
+    const int out_dt = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
+    const int oes = esize(out_dt);
+    int part = 0;
+    for (int k = 0; k < m.nunits; ++k) {
+      NsUnit& u = t.units[unit0[mi] + k];
+      u.norm_slot = s_norm0 + unit0[mi] + k;
+      u.onorm_slot = s_onorm0 + mi;
+      u.onorm_part0 = part;
+      u.o_dtype = out_dt;
+      u.o_ld = m.W;
+      int64_t h, w;
+      if (T > 0) {
+        const int a = k / m.ntc, b = k % m.ntc;
+        h = std::min<int64_t>(T, m.H - (int64_t)a * T);
+        w = std::min<int64_t>(T, m.W - (int64_t)b * T);
+        u.o_trans = 0;
+        u.o_rows = (int32_t)h;
+        u.o_cols = (int32_t)w;
+        u.o_ptr = static_cast<char*>(out) + ((int64_t)a * T * m.W + (int64_t)b * T) * oes;
+      } else {
+        h = m.H;
+        w = m.W;
+        u.o_trans = m.trans;
+        u.o_rows = m.r;
+        u.o_cols = m.s;
+        u.o_ptr = out;
+      }
+      const int g3r = (u.ld_r + BM - 1) / BM, g3c = (u.ld_s + BN - 1) / BN;
+      const int g12c = (u.r + BN - 1) / BN;
+      u.g3_cols = g3c;
+      part += g3r * g3c;
+      const int uid = unit0[mi] + k;
+      for (int tm = 0; tm < g3r; ++tm)
+        for (int tn = 0; tn < g12c; ++tn) t.g12_jobs.push_back({uid, tm, tn, u.ld_r / 64});
+      for (int tn = 0; tn < g3c; ++tn)
+        for (int tm = 0; tm < g3r; ++tm) t.g3_jobs.push_back({uid, tm, tn, u.ld_r / 64});
+      const double r = (double)std::min(h, w), s = (double)std::max(h, w);
+      t.flops_g1 += 2.0 * r * r * s;
+      t.flops_g2 += 2.0 * r * r * r;
+      t.flops_g3 += 2.0 * r * r * s;
+    }
+    t.nparts[s_onorm0 + mi] = part;
+  }
+
+  // --- momentum / prep blocks
+  if (cfg.kind != CALL_PROJ) {
+    for (int mi = 0; mi < nm; ++mi) {
+      const int gi = ch.m0 + mi;
+      const MatPlan& m = plan.mats[gi];
+      MomMat mm{};
+      mm.g = p.grads[gi];
+      mm.m = cfg.kind == CALL_STEP ? p.moms[gi] : nullptr;
+      mm.H = m.H;
+      mm.W = m.W;
+      mm.trans = T > 0 ? 0 : m.trans;
+      mm.tile_T = T;
+      mm.unit0 = unit0[mi];
+      mm.ntc = m.ntc;
+      mm.write_x = 1;
+      int64_t rows_p, cols_p;
+      if (T > 0) {
+        rows_p = (int64_t)m.ntr * T;
+        cols_p = (int64_t)m.ntc * T;
+      } else {
+        rows_p = pad_up(m.H, 64);
+        cols_p = pad_up(m.W, 64);
+      }
+      const int nbr = (int)(rows_p / 64), nbc = (int)(cols_p / 64);
+      mm.nbc = nbc;
+      const int mat_idx = (int)t.mom_mats.size();
+      t.mom_mats.push_back(mm);
+      for (int br = 0; br < nbr; ++br)
+        for (int bc = 0; bc < nbc; ++bc) {
+          MomBlock b{};
+          b.mat = mat_idx;
+          b.br = br;
+          b.bc = bc;
+          if (T > 0) {
+            const int tr = (int)((int64_t)br * 64 / T), tc = (int)((int64_t)bc * 64 / T);
+            const int per = T / 64;
+            b.slot = s_norm0 + unit0[mi] + tr * m.ntc + tc;
+            b.part = ((br * 64 % T) / 64) * per + (bc * 64 % T) / 64;
+          } else {
+            b.slot = s_norm0 + unit0[mi];
+            b.part = br * nbc + bc;
+          }
+          t.mom_blocks.push_back(b);
+        }
+      const int per_slot = T > 0 ? (T / 64) * (T / 64) : nbr * nbc;
+      for (int k = 0; k < m.nunits; ++k) t.nparts[s_norm0 + unit0[mi] + k] = per_slot;
+      const double sb = esize(cfg.state_dt);
+      t.bytes_mom += (double)m.H * m.W * (cfg.kind == CALL_STEP ? 3 * sb : sb);
+    }
+  }
+
+  // --- hook / projection blocks
+  if (cfg.kind != CALL_NS) {
+    for (int mi = 0; mi < nm; ++mi) {
+      const int gi = ch.m0 + mi;
+      const MatPlan& m = plan.mats[gi];
+      HookMat hm{};
+      hm.w = static_cast<float*>(p.params[gi]);
+      hm.numel = m.H * m.W;
+      hm.nblocks = (int)((hm.numel + kHookBlockElems - 1) / kHookBlockElems);
+      hm.slot = s_hook0 + mi;
+      hm.rho = p.rho ? p.rho[gi] : 1.0f;
+      hm.oscale = (float)((double)p.eta * std::sqrt(std::max(1.0, (double)m.H / (double)m.W)));
+      if (cfg.kind == CALL_STEP) {
+        hm.o = obuf[mi];
+        hm.o_dtype = cfg.op_dt;
+        hm.onorm_slot = s_onorm0 + mi;
+      } else {
+        const void* U = p.grads ? p.grads[gi] : nullptr;
+        hm.o = U;
+        hm.o_dtype = cfg.state_dt;
+        hm.onorm_slot = U ? s_onorm0 + mi : -1;
+        if (U) t.nparts[s_onorm0 + mi] = hm.nblocks;
+      }
+      t.nparts[s_hook0 + mi] = hm.nblocks;
+      const int idx = (int)t.hook_mats.size();
+      t.hook_mats.push_back(hm);
+      for (int b = 0; b < hm.nblocks; ++b) t.hook_blocks.push_back({idx, b});
+      const double ob = hm.o ? esize(hm.o_dtype) : 0;
+      t.bytes_hook1 += (double)hm.numel * (4 + ob);
+      t.bytes_hook2 += (double)hm.numel * (4 + ob + 4);
+      if (cfg.kind == CALL_PROJ && hm.o) t.bytes_sumsq += (double)hm.numel * ob;
+    }
+  }
+
+  // --- partial bases
+  t.part_base.assign(nslots, 0);
+  int64_t acc = 0;
+  for (int s = 0; s < nslots; ++s) {
+    t.part_base[s] = acc;
+    acc += t.nparts[s];
+  }
+  t.parts_total = acc;
+}
+
+}  // namespace muonh

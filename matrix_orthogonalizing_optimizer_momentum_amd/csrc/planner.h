@@ -1,0 +1,95 @@
+// Host-side planning for libmuonh: validation, Newton-Schulz units, memory-
+// bounded chunks, GEMM job lists, momentum / hook block lists and reduction
+// slots.  Pure host C++ (no HIP runtime calls), so it can be exercised on a
+// machine without a GPU through muonh_plan_query.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "desc.h"
+
+namespace muonh {
+
+enum CallKind { CALL_STEP = 0, CALL_NS = 1, CALL_PROJ = 2 };
+
+struct Cfg {
+  int kind;
+  int n;
+  int K;
+  int tile_T;
+  int state_dt, op_dt;
+  int x32;        // fp32 master X (bf16 operands only)
+  int hook;       // kModeHB / kModeRB
+  int gemm_bm, gemm_bn;
+  size_t ws_limit;
+};
+
+// Per source matrix.
+struct MatPlan {
+  int64_t H, W;
+  int r, s;        // full mode: oriented sides; tile mode: T, T
+  int trans;       // full mode: H > W
+  int nunits;      // 1, or tiles
+  int ntr, ntc;    // tile grid (tile mode)
+  int64_t ws_bytes;
+};
+
+struct ChunkPlan {
+  int m0, m1;      // matrices [m0, m1)
+  int64_t ws_bytes;
+};
+
+struct Plan {
+  std::vector<MatPlan> mats;
+  std::vector<ChunkPlan> chunks;
+  int64_t ws_bytes = 0;     // max over chunks
+  int64_t units = 0;
+  double ns_flops = 0;      // dense, true sides
+  int64_t jobs_per_iter = 0;
+  double stream_bytes = 0;  // algorithmic
+};
+
+// Byte sizes of one unit's workspace pieces (each rounded to 256 B).
+struct UnitBytes {
+  int64_t x, xt, x32, a, b;
+  int64_t total() const { return x + 2 * xt + x32 + a + b; }
+};
+UnitBytes unit_bytes(int r, int s, int op_dt, int x32);
+
+inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+inline int esize(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+// Builds mats / chunks; returns MUONH_OK, MUONH_EINVAL or MUONH_ENOMEM.
+int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan);
+
+// Host tables of one chunk (everything a launch sequence needs).
+struct ChunkTables {
+  std::vector<NsUnit> units;
+  std::vector<GemmJob> g12_jobs, g3_jobs;
+  std::vector<MomMat> mom_mats;
+  std::vector<MomBlock> mom_blocks;
+  std::vector<HookMat> hook_mats;
+  std::vector<HookBlock> hook_blocks;
+  std::vector<int32_t> nparts;
+  std::vector<int64_t> part_base;
+  int64_t parts_total = 0;
+  double flops_g1 = 0, flops_g2 = 0, flops_g3 = 0;
+  double bytes_mom = 0, bytes_hook1 = 0, bytes_hook2 = 0, bytes_sumsq = 0;
+};
+
+struct CallPtrs {
+  void* const* params;        // STEP, PROJ
+  const void* const* grads;   // STEP: grads; NS: inputs; PROJ: U (may be null)
+  void* const* moms;          // STEP
+  void* const* outs;          // NS
+  const float* rho;           // STEP (HB), PROJ
+  float eta;
+};
+
+// Fill the tables of chunk c; ws is the data workspace base (device).
+void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char* ws, ChunkTables& t);
+
+}  // namespace muonh

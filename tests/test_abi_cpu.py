@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute call):
+the library loads, exports every function the header declares, rejects bad
+arguments before touching the GPU, and the host planner's accounting matches
+the closed-form work counts."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import matrix_orthogonalizing_optimizer_momentum_amd as mm
+from synth import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muonh.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mm.LIB_PATH), reason="libmuonh.so not built")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_ \*]*?\b([a-z_][a-z0-9_]*)\s*\(", txt, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("muonh_step", "ns_orthogonalize", "frob_project", "muonh_strerror", "muonh_get_flags",
+              "muonh_release", "muonh_plan_query"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mm.LIB_PATH)
+    for n in header_functions():
+        assert hasattr(lib, n), n
+    assert set(header_functions()) == set(mm.EXPORTED)
+
+
+def test_strerror_and_version():
+    assert mm.strerror(mm.MUONH_OK) == "success"
+    assert "invalid" in mm.strerror(mm.MUONH_EINVAL)
+    assert mm.strerror(-99) == "unknown error"
+    assert "gfx950" in mm.version()
+
+
+def _opts():
+    o = mm.Opts()
+    mm.load().muonh_default_opts(ctypes.byref(o))
+    return o
+
+
+def _step(n=1, shapes=(4, 4), eta=0.02, beta=0.95, K=5, rho=1.0, tile=0, ptr=0x1000, opts=None, null_rho=False):
+    lib = mm.load()
+    P = ctypes.c_void_p * max(n, 1)
+    ps = P(*[ptr + 0x100 * i for i in range(max(n, 1))])
+    gs = P(*[ptr + 0x10000 + 0x100 * i for i in range(max(n, 1))])
+    ms = P(*[ptr + 0x20000 + 0x100 * i for i in range(max(n, 1))])
+    sh = (ctypes.c_int64 * (2 * max(n, 1)))(*(list(shapes) * max(n, 1)))
+    rh = None if null_rho else (ctypes.c_float * max(n, 1))(*([rho] * max(n, 1)))
+    o = opts or _opts()
+    return lib.muonh_step(ps, gs, ms, sh, n, eta, beta, K, rh, tile, ctypes.byref(o))
+
+
+# Each of these is rejected by host validation, before any HIP call.
+@pytest.mark.parametrize("kw", [
+    dict(n=0), dict(K=-1), dict(K=65), dict(beta=1.0), dict(beta=-0.1), dict(eta=-1.0),
+    dict(eta=float("nan")), dict(rho=0.0), dict(rho=float("inf")), dict(null_rho=True),
+    dict(shapes=(0, 4)), dict(shapes=(4, -2)), dict(tile=-1), dict(tile=8256), dict(tile=200),
+])
+def test_step_validation_rejects(kw):
+    assert _step(**kw) == mm.MUONH_EINVAL
+
+
+def test_step_rejects_bad_options():
+    for field, val in [("state_dtype", 7), ("ns_dtype", 3), ("ns_precision", 9), ("hook", 5),
+                       ("outward", 1.5), ("inward", -0.1), ("ns_eps", float("nan"))]:
+        o = _opts()
+        setattr(o, field, val)
+        assert _step(opts=o) == mm.MUONH_EINVAL, field
+
+
+def test_step_rejects_null_pointers_and_aliasing():
+    lib = mm.load()
+    o = _opts()
+    P = ctypes.c_void_p * 1
+    sh = (ctypes.c_int64 * 2)(4, 4)
+    rh = (ctypes.c_float * 1)(1.0)
+    assert lib.muonh_step(P(None), P(0x1000), P(0x2000), sh, 1, 0.1, 0.9, 5, rh, 0, ctypes.byref(o)) == mm.MUONH_EINVAL
+    assert lib.muonh_step(P(0x1000), P(0x2000), P(0x2000), sh, 1, 0.1, 0.9, 5, rh, 0, ctypes.byref(o)) == mm.MUONH_EINVAL
+    assert lib.muonh_step(None, P(0x2000), P(0x3000), sh, 1, 0.1, 0.9, 5, rh, 0, ctypes.byref(o)) == mm.MUONH_EINVAL
+
+
+def test_coefficient_table_must_be_finite():
+    o = _opts()
+    arr = (ctypes.c_float * 15)(*([3.4445, -4.775, 2.0315] * 4 + [float("nan"), 0, 0]))
+    o.coeffs = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    assert _step(opts=o, K=5) == mm.MUONH_EINVAL
+
+
+def test_ns_and_projection_validation():
+    lib = mm.load()
+    o = _opts()
+    P = ctypes.c_void_p * 1
+    sh = (ctypes.c_int64 * 2)(4, 4)
+    assert lib.ns_orthogonalize(P(None), P(0x1000), sh, 1, 5, 0, ctypes.byref(o)) == mm.MUONH_EINVAL
+    assert lib.ns_orthogonalize(P(0x1000), P(0x2000), sh, 1, 99, 0, ctypes.byref(o)) == mm.MUONH_EINVAL
+    rh = (ctypes.c_float * 1)(-1.0)
+    assert lib.frob_project(P(0x1000), None, sh, 1, 0.1, rh, ctypes.byref(o)) == mm.MUONH_EINVAL
+    rh = (ctypes.c_float * 1)(1.0)
+    assert lib.frob_project(P(0x1000), None, sh, 1, float("inf"), rh, ctypes.byref(o)) == mm.MUONH_EINVAL
+
+
+def _dense_flops(shapes, K):
+    tot = 0
+    for H, W in shapes:
+        r, s = min(H, W), max(H, W)
+        tot += K * (4 * r * r * s + 2 * r ** 3)
+    return tot
+
+
+def test_plan_query_gpt2_accounting():
+    shapes = gen.gpt2_small_shapes()
+    q = mm.plan_query(shapes, K=5)
+    assert q["chunks"] == 1 and q["units"] == 48
+    assert q["ns_flops"] == _dense_flops(shapes, 5)
+    elems = sum(H * W for H, W in shapes)
+    # bf16 state, bf16 operands: momentum 6 B + hook pass 1 (4 + 2) + pass 2 (4 + 2 + 4) = 22 B/elem
+    assert q["stream_bytes"] == 22 * elems
+
+
+def test_plan_query_tiled_units_and_flops():
+    shapes = [(300, 700), (768, 2304)]
+    q = mm.plan_query(shapes, K=5, tile_T=128)
+    assert q["units"] == 3 * 6 + 6 * 18
+    tot = 0
+    for H, W in shapes:
+        for r0 in range(0, H, 128):
+            for c0 in range(0, W, 128):
+                h, w = min(128, H - r0), min(128, W - c0)
+                a, b = min(h, w), max(h, w)
+                tot += 5 * (4 * a * a * b + 2 * a ** 3)
+    assert q["ns_flops"] == tot
+
+
+def test_plan_query_chunking_under_a_budget():
+    shapes = gen.gpt2_small_shapes()
+    one = mm.plan_query(shapes[:1], K=5)["ws_bytes"]
+    q = mm.plan_query(shapes, K=5, workspace_limit=3 * one)
+    assert q["chunks"] > 1 and q["ws_bytes"] <= 3 * one
+    with pytest.raises(mm.MuonhError) as e:
+        mm.plan_query([(3072, 768)], K=5, workspace_limit=1024)
+    assert e.value.code == mm.MUONH_ENOMEM
+
+
+def test_x32_needs_more_workspace_than_fold():
+    s = [(768, 3072)]
+    assert mm.plan_query(s, ns_precision="x32")["ws_bytes"] > mm.plan_query(s, ns_precision="fold")["ws_bytes"]

@@ -1,0 +1,381 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Tolerances:
+* Newton-Schulz output, relative Frobenius error: <= 1e-4 with fp32 operands,
+  <= 2e-2 with bf16 operands (fp32 accumulation in both);
+* Hyperball radius: |‖W‖_F / rho - 1| <= 1e-5 with fp32 master weights;
+* the weight step ΔW = W_new - W_old inherits the NS tolerance (relative);
+* momentum: one bf16 (fp32) rounding of beta*M + G, elementwise.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import muonh_oracle as orc
+from synth import gen
+
+torch = pytest.importorskip("torch")
+import matrix_orthogonalizing_optimizer_momentum_amd as mm  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def dev(a, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32))).to(DEV).to(dtype).contiguous()
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+SMALL_SHAPES = [(1, 1), (5, 7), (7, 5), (33, 17), (64, 128), (128, 64), (256, 256), (300, 700), (700, 300),
+                (129, 257), (1, 200)]
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_ns_fp32_small(shape):
+    H, W = shape
+    banner(f"ns fp32 {H}x{W}")
+    X = gen.gaussian((H, W), 1.0, 7 + H * 3 + W)
+    out = mm.ns_orthogonalize([dev(X)], K=5, ns_dtype="f32")[0]
+    torch.cuda.synchronize()
+    assert rel(host(out), orc.newton_schulz(X, 5)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("prec", ["x32", "fold"])
+@pytest.mark.parametrize("shape", [(768, 768), (768, 3072), (3072, 768), (768, 2304), (300, 700)],
+                         ids=lambda s: f"{s[0]}x{s[1]}" if isinstance(s, tuple) else s)
+def test_ns_bf16_spiked(shape, prec):
+    H, W = shape
+    banner(f"ns bf16 {prec} {H}x{W}")
+    G = gen.store(gen.spiked_grad(H, W, 1e-3, seed=11 + H + W), "bf16")
+    out = mm.ns_orthogonalize([dev(G, torch.bfloat16)], K=5, ns_dtype="bf16", ns_precision=prec)[0]
+    torch.cuda.synchronize()
+    err = rel(host(out), orc.newton_schulz(G, 5))
+    print(f"  rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("K", [0, 1, 2, 7])
+def test_ns_iteration_counts(K):
+    banner(f"ns K={K}")
+    X = gen.gaussian((96, 160), 1.0, 3)
+    out = mm.ns_orthogonalize([dev(X)], K=K, ns_dtype="f32")[0]
+    torch.cuda.synchronize()
+    assert rel(host(out), orc.newton_schulz(X, K)) <= TOL["f32"]
+
+
+def test_ns_coefficient_table_two_stage():
+    banner("ns two-stage coefficients")
+    table = [(3.4445, -4.7750, 2.0315)] * 8 + [(2.0, -1.5, 0.5)] * 2
+    X = gen.gaussian((64, 192), 1.0, 5)
+    out = mm.ns_orthogonalize([dev(X)], K=10, ns_dtype="f32", coeffs=table)[0]
+    torch.cuda.synchronize()
+    assert rel(host(out), orc.newton_schulz(X, 10, coeffs=table)) <= TOL["f32"]
+
+
+def test_ns_many_shapes_one_launch():
+    banner("ns grouped launch, mixed shapes")
+    shapes = [(64, 128), (128, 64), (200, 72), (33, 300), (256, 256)]
+    Xs = [gen.gaussian(s, 1.0, 40 + i) for i, s in enumerate(shapes)]
+    outs = mm.ns_orthogonalize([dev(x) for x in Xs], K=5, ns_dtype="f32")
+    torch.cuda.synchronize()
+    for x, o in zip(Xs, outs):
+        assert rel(host(o), orc.newton_schulz(x, 5)) <= TOL["f32"]
+
+
+def test_ns_in_place_alias():
+    banner("ns out aliases in")
+    X = gen.gaussian((48, 80), 1.0, 9)
+    t = dev(X)
+    mm.ns_orthogonalize([t], [t], K=5, ns_dtype="f32")
+    torch.cuda.synchronize()
+    assert rel(host(t), orc.newton_schulz(X, 5)) <= TOL["f32"]
+
+
+def test_ns_zero_input_is_zero():
+    banner("ns zero input")
+    out = mm.ns_orthogonalize([torch.zeros(64, 96, device=DEV)], K=5, ns_dtype="f32")[0]
+    torch.cuda.synchronize()
+    assert not torch.any(out != 0)
+
+
+def test_ns_closed_form_spectrum_bf16_768():
+    # Muon explainer, code section closing check: 768x768 with singular values
+    # 0.9, 0.3, 0.1, 0.01, 0.001 and 763 near 0.011 lands within 0.005 of the
+    # scalar polynomial in bf16.
+    banner("ns bf16 768 spectrum example")
+    n = 768
+    s = np.array([0.9, 0.3, 0.1, 0.01, 0.001] + [0.011] * 763)
+    X = gen.with_singular_values(n, n, s, 77)
+    Xb = gen.store(X, "bf16")
+    out = host(mm.ns_orthogonalize([dev(Xb, torch.bfloat16)], K=5, ns_dtype="bf16")[0])
+    got = np.sort(np.linalg.svd(out, compute_uv=False))[::-1]
+    sb = np.sort(np.linalg.svd(Xb, compute_uv=False))[::-1]
+    x = sb / (np.linalg.norm(sb) + 1e-7)
+    for _ in range(5):
+        x = 3.4445 * x - 4.7750 * x ** 3 + 2.0315 * x ** 5
+    # compare the sorted spectra
+    assert np.max(np.abs(got - np.sort(x)[::-1])) <= 0.005
+
+
+def test_ns_random_3072x768_band_bf16():
+    banner("ns bf16 random 3072x768 band")
+    X = gen.store(gen.gaussian((3072, 768), 1.0, 3), "bf16")
+    out = host(mm.ns_orthogonalize([dev(X, torch.bfloat16)], K=5, ns_dtype="bf16")[0])
+    sv = np.linalg.svd(out, compute_uv=False)
+    assert round(sv.min(), 2) >= 0.68 and round(sv.max(), 2) <= 1.15
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical Muon
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [64, 128, 256])
+@pytest.mark.parametrize("shape", [(300, 700), (768, 768), (256, 130)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_tiled_ns_fp32(shape, T):
+    H, W = shape
+    banner(f"tiled ns fp32 T={T} {H}x{W}")
+    X = gen.gaussian((H, W), 1.0, 21 + T)
+    out = mm.ns_orthogonalize([dev(X)], K=5, tile_T=T, ns_dtype="f32")[0]
+    torch.cuda.synchronize()
+    assert rel(host(out), orc.tiled_newton_schulz(X, T, 5)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("T", [64, 128, 256])
+def test_tiled_ns_bf16_gpt2_shape(T):
+    banner(f"tiled ns bf16 T={T} 768x2304")
+    G = gen.store(gen.spiked_grad(768, 2304, 1e-3, seed=5), "bf16")
+    out = mm.ns_orthogonalize([dev(G, torch.bfloat16)], K=5, tile_T=T)[0]
+    torch.cuda.synchronize()
+    err = rel(host(out), orc.tiled_newton_schulz(G, T, 5))
+    print(f"  rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# full step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(256, 256), (64, 128)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+def test_step_single_matrix_fp32_trajectory(shape, ns):
+    # 10 steps with fresh Gaussian gradients; the oracle runs its own
+    # trajectory from the same W0, M0 and gradients.
+    H, W = shape
+    banner(f"step fp32 state, ns={ns}, {H}x{W}, 10 steps")
+    W0, Gs, M0 = gen.single_matrix_case(H, W, steps=10)
+    rho = np.float32(np.linalg.norm(W0.astype(np.float64)))
+    w, m = dev(W0), dev(M0)
+    Wo, Mo = [W0.astype(np.float64)], [M0.astype(np.float64)]
+    g_prev, o_prev = W0.astype(np.float64), W0.astype(np.float64)
+    for G in Gs:
+        mm.muonh_step([w], [dev(G)], [m], eta=0.02, beta=0.95, K=5, rho=[rho], ns_dtype=ns)
+        torch.cuda.synchronize()
+        Wo, Mo, _, _ = orc.muonh_step(Wo, [G], Mo, 0.02, np.float32(0.95), 5, [rho])
+        wg = host(w)
+        assert abs(np.linalg.norm(wg) / rho - 1) <= 1e-5
+        assert rel(wg - g_prev, Wo[0] - o_prev) <= TOL[ns]
+        assert np.allclose(host(m), Mo[0], rtol=1e-6, atol=1e-12)
+        g_prev, o_prev = wg, Wo[0]
+    assert rel(g_prev - W0, Wo[0] - W0) <= TOL[ns]
+
+
+@pytest.mark.parametrize("shape", [(64, 64), (64, 128)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+def test_step_exact_cancel_restores_radius(shape, ns):
+    H, W = shape
+    banner(f"exact cancel {H}x{W} ns={ns}")
+    W0, G, M0, rho, eta = gen.exact_cancel_case(H, W)
+    mm.reset_flags()
+    w = dev(W0)
+    mm.muonh_step([w], [dev(G)], [dev(M0)], eta=eta, beta=0.95, K=5, rho=[rho], ns_dtype=ns)
+    torch.cuda.synchronize()
+    flags = mm.get_flags()
+    W0d = W0.astype(np.float64)
+    expect = rho * W0d / np.linalg.norm(W0d)
+    assert flags[1] == 1 and flags[2] == 0
+    assert np.abs(host(w) - expect).max() <= 1e-6 * np.abs(expect).max()
+    assert abs(np.linalg.norm(host(w)) / rho - 1) <= 1e-5
+
+
+def _gpt2_like(shapes, cfg=2, step=1):
+    Ws, Gs, Ms = gen.model_set(shapes, cfg, step)
+    return Ws, Gs, Ms
+
+
+@pytest.mark.parametrize("prec", ["x32", "fold"])
+def test_step_gpt2_full_set_bf16(prec):
+    # The full 48-matrix GPT-2-small set in one call (the benchmarked launch
+    # configuration); parity on one matrix of each shape, invariants on all.
+    banner(f"gpt2 full set step bf16 {prec}")
+    shapes = gen.gpt2_small_shapes()
+    Ws, Gs, Ms = _gpt2_like(shapes)
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    w_t = [dev(w) for w in Ws]
+    g_t = [dev(g, torch.bfloat16) for g in Gs]
+    m_t = [dev(m, torch.bfloat16) for m in Ms]
+    mm.muonh_step(w_t, g_t, m_t, eta=0.02, beta=0.95, K=5, rho=rhos, ns_precision=prec)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert abs(np.linalg.norm(host(w_t[i])) / rhos[i] - 1) <= 1e-5
+    for i in (0, 1, 2, 3):  # qkv, attn-out, fc, proj
+        Wn, Mn, _, _ = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.02, np.float32(0.95), 5, [rhos[i]],
+                                      state_bf16=True)
+        assert np.array_equal(host(m_t[i]), Mn[0])
+        err = rel(host(w_t[i]) - Ws[i], Wn[0] - Ws[i])
+        print(f"  matrix {i} {shapes[i]} step rel err {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [64, 256])
+def test_step_himuon_bf16(T):
+    banner(f"himuon step T={T}")
+    shapes = [(768, 2304), (3072, 768), (300, 700)]
+    Ws, Gs, Ms = _gpt2_like(shapes, cfg=4)
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    w_t = [dev(w) for w in Ws]
+    mm.muonh_step(w_t, [dev(g, torch.bfloat16) for g in Gs], [dev(m, torch.bfloat16) for m in Ms],
+                  eta=0.02, beta=0.95, K=5, rho=rhos, tile_T=T)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        Wn, _, _, _ = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.02, np.float32(0.95), 5, [rhos[i]], tile_T=T,
+                                     state_bf16=True)
+        assert abs(np.linalg.norm(host(w_t[i])) / rhos[i] - 1) <= 1e-5
+        assert rel(host(w_t[i]) - Ws[i], Wn[0] - Ws[i]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+def test_step_radial_brake(ns):
+    banner(f"radial brake ns={ns}")
+    shapes = [(128, 64), (64, 192), (96, 96)]
+    Ws, Gs, Ms = [], [], []
+    for i, (H, W) in enumerate(shapes):
+        Ws.append(gen.gaussian((H, W), 0.02, 300 + i))
+        Gs.append(gen.gaussian((H, W), 0.02, 400 + i))
+        Ms.append(gen.gaussian((H, W), 0.02, 500 + i))
+    w_t = [dev(w) for w in Ws]
+    mm.muonh_step(w_t, [dev(g) for g in Gs], [dev(m) for m in Ms], eta=0.02, beta=0.95, K=5,
+                  hook="radial_brake", outward=0.5, inward=1.0, ns_dtype=ns)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        Wn, _, _, _ = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.02, np.float32(0.95), 5, None,
+                                     hook="radial_brake", outward=0.5, inward=1.0)
+        assert rel(host(w_t[i]) - Ws[i], Wn[0] - Ws[i]) <= TOL[ns]
+
+
+def test_radial_brake_tiny_matrix():
+    # A 3x4 weight along a 3-4-5 direction with a gradient against it.
+    banner("radial brake 3x4")
+    H, W = 3, 4
+    d = np.zeros((H, W), np.float32)
+    d[0, 0] = 3
+    d[1, 1] = 4
+    G = -d
+    w_t = [dev(d)]
+    mm.muonh_step(w_t, [dev(G)], [torch.zeros(H, W, device=DEV)], eta=0.5, beta=0.9, K=5,
+                  hook="radial_brake", outward=0.5, inward=1.0, ns_dtype="f32")
+    torch.cuda.synchronize()
+    Wn, _, _, _ = orc.muonh_step([d], [G], [np.zeros((H, W))], 0.5, np.float32(0.9), 5, None,
+                                 hook="radial_brake", outward=0.5, inward=1.0)
+    assert np.abs(host(w_t[0]) - Wn[0]).max() <= 1e-5 * np.abs(Wn[0]).max()
+
+
+# ---------------------------------------------------------------------------
+# projection, chunking, determinism, zero cases
+# ---------------------------------------------------------------------------
+
+def test_frob_project_plain_and_with_update():
+    banner("frob_project")
+    Ws = [gen.gaussian((50, 70), 1.0, 1), gen.gaussian((128, 32), 1.0, 2)]
+    Us = [gen.gaussian((50, 70), 1.0, 3), gen.gaussian((128, 32), 1.0, 4)]
+    rho = [2.5, 0.75]
+    wt = [dev(w) for w in Ws]
+    mm.frob_project(wt, None, 0.3, rho)
+    torch.cuda.synchronize()
+    for w, g, r in zip(Ws, wt, rho):
+        assert np.allclose(host(g), orc.frob_project(w, None, 0.3, r)[0], rtol=1e-6, atol=1e-7)
+    wt = [dev(w) for w in Ws]
+    mm.frob_project(wt, [dev(u) for u in Us], 0.3, rho)
+    torch.cuda.synchronize()
+    for w, u, g, r in zip(Ws, Us, wt, rho):
+        assert np.allclose(host(g), orc.frob_project(w, u, 0.3, r)[0], rtol=1e-5, atol=1e-6)
+
+
+def test_chunked_equals_unchunked_bitwise():
+    banner("chunking")
+    shapes = [(256, 512), (512, 256), (128, 128), (384, 640)]
+    Ws, Gs, Ms = _gpt2_like(shapes, cfg=9)
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    outs = []
+    for limit in (0, mm.plan_query(shapes[:1])["ws_bytes"] + 1):
+        w_t = [dev(w) for w in Ws]
+        m_t = [dev(m, torch.bfloat16) for m in Ms]
+        mm.muonh_step(w_t, [dev(g, torch.bfloat16) for g in Gs], m_t, eta=0.02, beta=0.95, K=5, rho=rhos,
+                      workspace_limit=limit)
+        torch.cuda.synchronize()
+        outs.append([host(w) for w in w_t])
+    q = mm.plan_query(shapes, workspace_limit=mm.plan_query(shapes[:1])["ws_bytes"] + 1)
+    assert q["chunks"] > 1
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_rerun_is_bitwise_deterministic():
+    banner("determinism")
+    shapes = [(768, 768), (768, 3072)]
+    Ws, Gs, Ms = _gpt2_like(shapes, cfg=8)
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    res = []
+    for _ in range(2):
+        w_t = [dev(w) for w in Ws]
+        mm.muonh_step(w_t, [dev(g, torch.bfloat16) for g in Gs], [dev(m, torch.bfloat16) for m in Ms],
+                      eta=0.02, beta=0.95, K=5, rho=rhos)
+        torch.cuda.synchronize()
+        res.append([host(w) for w in w_t])
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
+def test_zero_grad_and_momentum_only_projects():
+    banner("zero update")
+    W0 = gen.gaussian((64, 96), 0.02, 1)
+    mm.reset_flags()
+    w = dev(W0)
+    mm.muonh_step([w], [torch.zeros(64, 96, device=DEV, dtype=torch.bfloat16)],
+                  [torch.zeros(64, 96, device=DEV, dtype=torch.bfloat16)], eta=0.02, beta=0.95, K=5, rho=[3.0])
+    torch.cuda.synchronize()
+    assert mm.get_flags()[0] == 1
+    expect = 3.0 * W0.astype(np.float64) / np.linalg.norm(W0.astype(np.float64))
+    assert np.allclose(host(w), expect, rtol=1e-6, atol=1e-7)
+
+
+def test_zero_weight_fixed_radius():
+    banner("zero weight")
+    G = gen.gaussian((32, 48), 1.0, 2)
+    w = torch.zeros(32, 48, device=DEV)
+    mm.muonh_step([w], [dev(G)], [torch.zeros(32, 48, device=DEV)], eta=0.1, beta=0.9, K=5, rho=[2.0],
+                  ns_dtype="f32")
+    torch.cuda.synchronize()
+    Wn, _, _, flags = orc.muonh_step([np.zeros((32, 48))], [G], [np.zeros((32, 48))], 0.1, np.float32(0.9), 5,
+                                     [2.0])
+    assert flags[0] == orc.FLAG_PROJECTED
+    assert np.allclose(host(w), Wn[0], rtol=1e-4, atol=1e-6)
