@@ -32,6 +32,7 @@ hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blo
                              float inward, float rb_eps, Flags* flags, hipStream_t s);
 hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
                         hipStream_t s);
+hipError_t launch_finalize(const SlotTable& st, int slot0, int nslots, hipStream_t s);
 hipError_t launch_ns_gemm(int op_dt, int phase, const NsUnit* units, const GemmJob* jobs, int njobs,
                           float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
                           const SlotTable& st, hipStream_t s);
@@ -57,6 +58,7 @@ struct DevTables {  // one chunk's tables on the device
   int n_g12 = 0, n_g3 = 0, n_mom = 0, n_hook = 0;
   int64_t parts_total = 0;
   int nslots = 0;
+  int nunits = 0, nmats = 0;  // slot ranges: [0,nunits) norms, then nmats O norms, then nmats hook sums
   double flops_g1 = 0, flops_g2 = 0, flops_g3 = 0;
   double bytes_mom = 0, bytes_hook1 = 0, bytes_hook2 = 0, bytes_sumsq = 0;
 };
@@ -81,7 +83,6 @@ struct State {
   int64_t ws_bytes = 0;
   double* partials = nullptr;  // meta
   int64_t partials_cap = 0;
-  unsigned* counters = nullptr;
   double* sums = nullptr;
   int slots_cap = 0;
   Flags* flags = nullptr;
@@ -96,8 +97,8 @@ State& S() {
 }
 
 const char* kClassNames[] = {"momentum_prep", "ns_gram_G1", "ns_poly_G2", "ns_update_G3",
-                             "hook_reduce",   "hook_write", "sumsq"};
-enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_N };
+                             "hook_reduce",   "hook_write", "sumsq",      "finalize"};
+enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_FIN, PC_N };
 
 // ------------------------------------------------------------------ helpers
 void free_plan(CachedPlan& p) {
@@ -127,14 +128,10 @@ int ensure_meta(State& st, int64_t parts, int slots) {
     st.partials_cap = cap;
   }
   if (slots > st.slots_cap) {
-    if (st.counters) (void)hipFree(st.counters);
     if (st.sums) (void)hipFree(st.sums);
-    st.counters = nullptr;
     st.sums = nullptr;
     const int cap = std::max(slots, 1024);
-    if (hipMalloc(&st.counters, cap * sizeof(unsigned)) != hipSuccess) return MUONH_ENOMEM;
     if (hipMalloc(&st.sums, cap * 2 * sizeof(double)) != hipSuccess) return MUONH_ENOMEM;
-    if (hipMemset(st.counters, 0, cap * sizeof(unsigned)) != hipSuccess) return MUONH_EHIP;
     st.slots_cap = cap;
   }
   return MUONH_OK;
@@ -257,6 +254,8 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   d.n_hook = (int)t.hook_blocks.size();
   d.parts_total = t.parts_total;
   d.nslots = (int)t.nparts.size();
+  d.nunits = (int)t.units.size();
+  d.nmats = (int)((t.nparts.size() - t.units.size()) / 2);
   d.flops_g1 = t.flops_g1;
   d.flops_g2 = t.flops_g2;
   d.flops_g3 = t.flops_g3;
@@ -364,7 +363,6 @@ struct Prof {
 SlotTable slot_table(State& st, const DevTables& d) {
   SlotTable t;
   t.partials = st.partials;
-  t.counters = st.counters;
   t.nparts = d.nparts;
   t.part_base = d.part_base;
   t.sums = st.sums;
@@ -380,8 +378,12 @@ int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, con
            hipStream_t s) {
   const float eps = r.o.ns_eps;
   if (cfg.K == 0) {
-    Prof pf(st, s, PC_G3, 0, 0);
-    MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, d.units, d.g3, d.n_g3, 1.f, 0.f, 0.f, eps, 1, 1, 0, 1, sl, s));
+    {
+      Prof pf(st, s, PC_G3, 0, 0);
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, d.units, d.g3, d.n_g3, 1.f, 0.f, 0.f, eps, 1, 1, 0, 1, sl, s));
+    }
+    Prof pf(st, s, PC_FIN, 0, 0);
+    MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));
     return MUONH_OK;
   }
   for (int k = 0; k < cfg.K; ++k) {
@@ -400,6 +402,8 @@ int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, con
       MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, d.units, d.g3, d.n_g3, a, b, c, eps, first, last, cur, 0, sl, s));
     }
   }
+  Prof pf(st, s, PC_FIN, 0, 0);
+  MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
   return MUONH_OK;
 }
 
@@ -430,17 +434,26 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
         MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
                                            sl, kind == CALL_STEP ? beta : 0.f, s));
       }
+      {
+        Prof pf(st, s, PC_FIN, 0, 0);
+        MUONH_TRY_HIP(launch_finalize(sl, 0, d.nunits, s));  // ||M||^2 per unit
+      }
       rc = run_ns(st, cfg, d, r, sl, s);
       if (rc != MUONH_OK) return rc;
     }
     if (kind == CALL_PROJ && p.grads) {
       Prof pf(st, s, PC_SQ, 0, d.bytes_sumsq);
       MUONH_TRY_HIP(launch_sumsq(d.hook_mats, d.hook_blocks, d.n_hook, sl, s));
+      MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||U||^2 per matrix
     }
     if (kind != CALL_NS) {
       {
         Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
         MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta, s));
+      }
+      {
+        Prof pf(st, s, PC_FIN, 0, 0);
+        MUONH_TRY_HIP(launch_finalize(sl, d.nunits + d.nmats, d.nmats, s));  // hook sums per matrix
       }
       {
         Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
@@ -595,7 +608,6 @@ void muonh_release(void) {
   clear_plans(st);
   if (st.ws) (void)hipFree(st.ws);
   if (st.partials) (void)hipFree(st.partials);
-  if (st.counters) (void)hipFree(st.counters);
   if (st.sums) (void)hipFree(st.sums);
   if (st.flags) (void)hipFree(st.flags);
   for (auto& r : st.prof) {
@@ -608,7 +620,6 @@ void muonh_release(void) {
   st.ws_bytes = 0;
   st.partials = nullptr;
   st.partials_cap = 0;
-  st.counters = nullptr;
   st.sums = nullptr;
   st.slots_cap = 0;
   st.flags = nullptr;

@@ -83,22 +83,15 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-__device__ __forceinline__ double coherent_load(const double* p) {
-  unsigned long long u = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __longlong_as_double((long long)u);
-}
-
-// Block-wide sum of (v0, v1) followed by a deterministic slot commit: the
-// block total goes to its partial; the last block of the slot (by an atomic
-// ticket) sums all partials of the slot in a fixed order into sums[slot] and
-// re-arms the slot counter.  Must be called by every thread of the block.
+// Block-wide sum of (v0, v1); thread 0 stores the block total as partial
+// `part` of reduction slot `slot`.  No fence: a later finalize kernel (a
+// kernel boundary later) sums the slot's partials in a fixed order, so the
+// result is bitwise reproducible.  Must be called by every thread.
 template <int NT>
-__device__ void commit_partial2(double v0, double v1, const SlotTable& st, int slot, int part) {
+__device__ void block_partial2(double v0, double v1, const SlotTable& st, int slot, int part) {
   static_assert(NT % 64 == 0, "block must be whole waves");
   constexpr int NW = NT / 64;
   __shared__ double red[2][NW];
-  __shared__ int is_last;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   v0 = wave_sum(v0);
   v1 = wave_sum(v1);
@@ -111,34 +104,6 @@ __device__ void commit_partial2(double v0, double v1, const SlotTable& st, int s
     const int64_t p = st.part_base[slot] + part;
     st.partials[2 * p] = t0;
     st.partials[2 * p + 1] = t1;
-    __threadfence();
-    unsigned prev = atomicAdd(&st.counters[slot], 1u);
-    is_last = (prev == (unsigned)st.nparts[slot] - 1u) ? 1 : 0;
-  }
-  __syncthreads();
-  if (is_last) {
-    __threadfence();
-    const int n = st.nparts[slot];
-    const int64_t base = st.part_base[slot];
-    double t0 = 0.0, t1 = 0.0;
-    for (int i = threadIdx.x; i < n; i += NT) {
-      t0 += coherent_load(st.partials + 2 * (base + i));
-      t1 += coherent_load(st.partials + 2 * (base + i) + 1);
-    }
-    t0 = wave_sum(t0);
-    t1 = wave_sum(t1);
-    __syncthreads();
-    if (l == 0) { red[0][w] = t0; red[1][w] = t1; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double s0 = 0.0, s1 = 0.0;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) { s0 += red[0][i]; s1 += red[1][i]; }
-      st.sums[2 * slot] = s0;
-      st.sums[2 * slot + 1] = s1;
-      atomicExch(&st.counters[slot], 0u);
-      __threadfence();
-    }
   }
 }
 

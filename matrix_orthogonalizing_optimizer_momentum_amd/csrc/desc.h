@@ -15,11 +15,10 @@ constexpr int kPad = 64;
 inline int64_t pad_up(int64_t v, int64_t g) { return (v + g - 1) / g * g; }
 
 // Reduction slots: each slot owns nparts double2 partials starting at
-// part_base; the last block to commit a slot sums its partials in a fixed
-// order (deterministic) into sums[slot] and re-arms the counter.
+// part_base; producers store one partial per block, a finalize launch sums
+// each slot's partials in a fixed order (deterministic) into sums[slot].
 struct SlotTable {
   double* partials;        // 2 doubles per partial
-  unsigned* counters;      // one per slot, zero between uses
   const int32_t* nparts;   // per slot
   const int64_t* part_base;// per slot, index of the first partial
   double* sums;            // 2 doubles per slot

@@ -81,8 +81,15 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
   constexpr int Q_LOADS = BN * CPR / kThreads;
   static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "tile/thread mismatch");
 
-  __shared__ __attribute__((aligned(16))) T sP[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) T sQ[2][BN * LDK];
+  // Main loop: P and Q stages (double buffered).  Epilogue: the fp32 output
+  // tile, pitch BN + 1 floats (conflict-free column reads).
+  constexpr int kStageBytes = 2 * (BM + BN) * LDK * (int)sizeof(T);
+  constexpr int CP = BN + 1;
+  constexpr int kTileBytes = BM * CP * 4;
+  constexpr int kSmem = kStageBytes > kTileBytes ? kStageBytes : kTileBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  T (*sP)[BM * LDK] = reinterpret_cast<T (*)[BM * LDK]>(smem);
+  T (*sQ)[BN * LDK] = reinterpret_cast<T (*)[BN * LDK]>(smem + 2 * BM * LDK * sizeof(T));
 
   // XCD-aware job order: hardware deals blocks round-robin over 8 XCDs; give
   // each XCD a contiguous run of the job list.
@@ -182,98 +189,148 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
   }
 
   // ----------------------------------------------------------------- epilogue
-  // acc[i][j][v] holds D(row, col) with
-  //   row = row0 + wm*WM + i*32 + 8*(v/4) + 4*(lane/32) + v%4
-  //   col = col0 + wn*WN + j*32 + lane%32
+  // Stage the fp32 tile in LDS, then write every output with 16-byte,
+  // row-contiguous accesses: a row pass (X, x32, A, B, O in X orientation) and,
+  // for G3, a column pass (X^T, or O when the caller's layout is transposed).
+  __syncthreads();
+  float* Ct = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int cl = wn * WN + j * 32 + (lane & 31);
+        Ct[rl * CP + cl] = acc[i][j][v];
+      }
+  __syncthreads();
+
   double sig = 1.0;
   if (args.first) {
     const double n2 = args.st.sums[2 * u.norm_slot];
     sig = 1.0 / (sqrt(n2) + (double)args.eps);
   }
-  float osq = 0.f;
   const int r = u.r;
+  float osq = 0.f;
+  constexpr int CPR_OUT = BN / 8;            // 8-element chunks per tile row
+  constexpr int ROWS_PER_IT = kThreads / CPR_OUT;
+  const int chunk = tid % CPR_OUT, rsub = tid / CPR_OUT;
+  const bool o_vec = (u.o_dtype == DT_BF16) ? ((u.o_ld % 8) == 0 && ((uintptr_t)u.o_ptr % 16) == 0)
+                                            : ((u.o_ld % 4) == 0 && ((uintptr_t)u.o_ptr % 16) == 0);
+
+  // ---- row pass
+#pragma unroll 1
+  for (int it = 0; it < BM / ROWS_PER_IT; ++it) {
+    const int rl = it * ROWS_PER_IT + rsub;
+    const int grow = row0 + rl;
+    const int cl = chunk * 8;
+    const int gcol = col0 + cl;
+    float v[8];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+    for (int e = 0; e < 8; ++e) v[e] = Ct[rl * CP + cl + e];
+    if (PHASE == kG1 || PHASE == kG2) {
+      if (grow < r && gcol < u.ld_r) {
+        T* out = reinterpret_cast<T*>(PHASE == kG1 ? u.a : u.b);
+        const int64_t oi = (int64_t)grow * u.ld_r + gcol;
+        if (PHASE == kG1) {
+          const float sc = (float)(sig * sig);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int col = col0 + wn * WN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rowb = row0 + wm * WM + i * 32 + 8 * g + 4 * (lane >> 5);
-        if (PHASE == kG1 || PHASE == kG2) {
-          // Output is symmetric (bit-exact: same products, same k order), so
-          // tile (row, col) is stored as its transpose: 4 consecutive entries.
-          if (col < r && rowb < u.ld_r) {
-            T* out = reinterpret_cast<T*>(PHASE == kG1 ? u.a : u.b);
-            float vals[4];
-            if (PHASE == kG1) {
-              const float sc = (float)(sig * sig);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) vals[e] = (rowb + e < r) ? acc[i][j][4 * g + e] * sc : 0.f;
-            } else {
-              const T* A = reinterpret_cast<const T*>(u.a);
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                vals[e] = (rowb + e < r)
-                              ? fmaf(args.c, acc[i][j][4 * g + e], args.b * St<T>::ld(A, (int64_t)col * u.ld_r + rowb + e))
-                              : 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) St<T>::st(out, (int64_t)col * u.ld_r + rowb + e, vals[e]);
-          }
+          for (int e = 0; e < 8; ++e) v[e] = (gcol + e < r) ? v[e] * sc : 0.f;
         } else {
-          // G3: X(row, col) <- a X(row, col) + acc, col indexes s.
-          const int s = u.s;
-          float vals[4];
+          float a8[8];
+          load8(reinterpret_cast<const T*>(u.a), oi, a8);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = rowb + e;
-            float v = 0.f;
-            if (row < r && col < s) {
-              const int64_t xi = (int64_t)row * u.ld_s + col;
-              float prev;
-              if (!args.first && u.x32 != nullptr) prev = u.x32[xi];
-              else prev = St<T>::ld(reinterpret_cast<const T*>(u.x), xi);
-              const float a = args.no_mma ? 1.f : args.a;
-              v = fmaf(a, prev, acc[i][j][4 * g + e]);
-              if (args.first) v = (float)((double)v * sig);
+          for (int e = 0; e < 8; ++e) v[e] = (gcol + e < r) ? fmaf(args.c, v[e], args.b * a8[e]) : 0.f;
+        }
+        store8(out, oi, v);
+      }
+    } else {
+      // G3: X(row, col) <- a X(row, col) + acc (times sig on the first iteration)
+      if (grow < r && gcol < u.ld_s) {
+        const int64_t xi = (int64_t)grow * u.ld_s + gcol;
+        float prev[8];
+        if (!args.first && u.x32 != nullptr) load8(u.x32, xi, prev);
+        else load8(reinterpret_cast<const T*>(u.x), xi, prev);
+        const float a = args.no_mma ? 1.f : args.a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float t = fmaf(a, prev[e], v[e]);
+          if (args.first) t = (float)((double)t * sig);
+          v[e] = (gcol + e < u.s) ? t : 0.f;
+        }
+        if (!args.last) {
+          store8(reinterpret_cast<T*>(u.x), xi, v);
+          if (u.x32 != nullptr) store8(u.x32, xi, v);
+        } else if (!u.o_trans && grow < u.o_rows) {
+          const int nv = min(8, u.o_cols - gcol);
+          if (nv > 0) {
+            const int64_t oi = (int64_t)grow * u.o_ld + gcol;
+            if (o_vec && nv == 8) {
+              float rv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) rv[e] = (u.o_dtype == DT_BF16) ? St<bf16_t>::round(v[e]) : v[e];
+              if (u.o_dtype == DT_BF16) store8(reinterpret_cast<bf16_t*>(u.o_ptr), oi, rv);
+              else store8(reinterpret_cast<float*>(u.o_ptr), oi, rv);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) osq = fmaf(rv[e], rv[e], osq);
+            } else {
+              for (int e = 0; e < nv; ++e) {
+                const float sv = store_dyn(u.o_ptr, oi + e, v[e], u.o_dtype);
+                osq = fmaf(sv, sv, osq);
+              }
             }
-            vals[e] = v;
           }
-          if (args.last) {
+        }
+      } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int row = rowb + e;
-              if (row < u.o_rows && col < u.o_cols) {
-                const int64_t oi = u.o_trans ? (int64_t)col * u.o_ld + row : (int64_t)row * u.o_ld + col;
-                const float stv = store_dyn(u.o_ptr, oi, vals[e], u.o_dtype);
-                osq = fmaf(stv, stv, osq);
-              }
-            }
-          } else {
-            T* X = reinterpret_cast<T*>(u.x);
-            T* XT = reinterpret_cast<T*>(u.xt[args.cur ^ 1]);
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;  // rows >= r: zero padding of X^T
+      }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int row = rowb + e;
-              if (row < r && col < u.ld_s) {
-                const int64_t xi = (int64_t)row * u.ld_s + col;
-                St<T>::st(X, xi, vals[e]);
-                if (u.x32 != nullptr) u.x32[xi] = vals[e];
-              }
-            }
-            if (col < s && rowb < u.ld_r) {
+      for (int e = 0; e < 8; ++e) Ct[rl * CP + cl + e] = v[e];
+    }
+  }
+
+  if (PHASE == kG3 && (!args.last || u.o_trans)) {
+    __syncthreads();
+    // ---- column pass: tile column cl -> X^T row (col0 + cl), 8 rows per chunk
+    T* XT = reinterpret_cast<T*>(u.xt[args.cur ^ 1]);
+    constexpr int CPC = BM / 8;                 // 8-row chunks per tile column
+    constexpr int COLS_PER_IT = kThreads / CPC;
+    const int q = tid % CPC, csub = tid / CPC;
+#pragma unroll 1
+    for (int it = 0; it < BN / COLS_PER_IT; ++it) {
+      const int cl = it * COLS_PER_IT + csub;
+      const int gn = col0 + cl;
+      const int gi = row0 + q * 8;
+      float v[8];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) St<T>::st(XT, (int64_t)col * u.ld_r + rowb + e, vals[e]);
-            }
+      for (int e = 0; e < 8; ++e) v[e] = Ct[(q * 8 + e) * CP + cl];
+      if (!args.last) {
+        if (gn < u.s && gi < u.ld_r) store8(XT, (int64_t)gn * u.ld_r + gi, v);
+      } else if (gn < u.o_cols && gi < u.o_rows) {
+        const int nv = min(8, u.o_rows - gi);
+        const int64_t oi = (int64_t)gn * u.o_ld + gi;
+        if (o_vec && nv == 8) {
+          float rv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rv[e] = (u.o_dtype == DT_BF16) ? St<bf16_t>::round(v[e]) : v[e];
+          if (u.o_dtype == DT_BF16) store8(reinterpret_cast<bf16_t*>(u.o_ptr), oi, rv);
+          else store8(reinterpret_cast<float*>(u.o_ptr), oi, rv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) osq = fmaf(rv[e], rv[e], osq);
+        } else {
+          for (int e = 0; e < nv; ++e) {
+            const float sv = store_dyn(u.o_ptr, oi + e, v[e], u.o_dtype);
+            osq = fmaf(sv, sv, osq);
           }
         }
       }
     }
   }
   if (PHASE == kG3 && args.last) {
-    commit_partial2<kThreads>((double)osq, 0.0, args.st, u.onorm_slot,
-                              u.onorm_part0 + job.tm * u.g3_cols + job.tn);
+    block_partial2<kThreads>((double)osq, 0.0, args.st, u.onorm_slot,
+                             u.onorm_part0 + job.tm * u.g3_cols + job.tn);
   }
 }
 

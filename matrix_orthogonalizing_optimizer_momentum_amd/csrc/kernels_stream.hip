@@ -41,6 +41,19 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
   const ST* __restrict__ g = reinterpret_cast<const ST*>(mm.g);
   ST* __restrict__ m = reinterpret_cast<ST*>(mm.m);
 
+  // Issue both rows' loads before any store (m is read and written).
+  float gv[2][8], mv[2][8];
+  bool fast[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int64_t row = (int64_t)blk.br * 64 + rr + 32 * p;
+    const int64_t col0 = (int64_t)blk.bc * 64 + cc * 8;
+    fast[p] = row < H && vec && col0 + 8 <= W;
+    if (fast[p]) {
+      load8(g, row * W + col0, gv[p]);
+      if (m != nullptr) load8(m, row * W + col0, mv[p]);
+    }
+  }
   float sq = 0.f;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -48,19 +61,14 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
     const int64_t row = (int64_t)blk.br * 64 + lr;
     const int64_t col0 = (int64_t)blk.bc * 64 + cc * 8;
     float v[8];
-    if (row < H && vec && col0 + 8 <= W) {
-      const int64_t idx = row * W + col0;
-      float gv[8];
-      load8(g, idx, gv);
+    if (fast[p]) {
       if (m != nullptr) {
-        float mv[8];
-        load8(m, idx, mv);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = St<ST>::round(fmaf(beta, mv[k], gv[k]));
-        store8(m, idx, v);
+        for (int k = 0; k < 8; ++k) v[k] = St<ST>::round(fmaf(beta, mv[p][k], gv[p][k]));
+        store8(m, row * W + col0, v);
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = gv[k];
+        for (int k = 0; k < 8; ++k) v[k] = gv[p][k];
       }
     } else {
 #pragma unroll
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
       }
     }
   }
-  if (blk.slot >= 0) commit_partial2<kMomThreads>((double)sq, 0.0, st, blk.slot, blk.part);
+  if (blk.slot >= 0) block_partial2<kMomThreads>((double)sq, 0.0, st, blk.slot, blk.part);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_reduce(
       s1 = fma((double)w[k], (double)w[k], s1);
     }
   }
-  commit_partial2<kHookThreads>(s0, s1, st, hm.slot, hb.blk);
+  block_partial2<kHookThreads>(s0, s1, st, hm.slot, hb.blk);
 }
 
 template <int MODE>
@@ -284,7 +292,29 @@ __global__ __launch_bounds__(kHookThreads) void k_sumsq(
 #pragma unroll
     for (int k = 0; k < 8; ++k) s0 = fma((double)o[k], (double)o[k], s0);
   }
-  commit_partial2<kHookThreads>(s0, 0.0, st, hm.onorm_slot, hb.blk);
+  block_partial2<kHookThreads>(s0, 0.0, st, hm.onorm_slot, hb.blk);
+}
+
+// Sum each slot's partials in a fixed order: slots [slot0, slot0 + gridDim.x).
+__global__ __launch_bounds__(256) void k_finalize(SlotTable st, int slot0) {
+  const int slot = slot0 + blockIdx.x;
+  const int n = st.nparts[slot];
+  const int64_t base = st.part_base[slot];
+  double t0 = 0.0, t1 = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    t0 += st.partials[2 * (base + i)];
+    t1 += st.partials[2 * (base + i) + 1];
+  }
+  __shared__ double red[2][4];
+  t0 = wave_sum(t0);
+  t1 = wave_sum(t1);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = t0; red[1][w] = t1; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st.sums[2 * slot] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+    st.sums[2 * slot + 1] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -333,6 +363,12 @@ hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblock
                         hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_sumsq, dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const SlotTable& st, int slot0, int nslots, hipStream_t s) {
+  if (nslots <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_finalize, dim3(nslots), dim3(256), 0, s, st, slot0);
   return hipGetLastError();
 }
 
