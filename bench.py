@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--K", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-sets", type=int, default=4)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run a plain device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -135,6 +137,14 @@ def main():
     K = args.K
     Ws, Ms, Gsets, rho = make_device_inputs(shapes, args.grad_sets, 1234, torch)
     q = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision)
+    if args.copy_calib_mib:
+        # a plain copy kernel of known size: reads and writes copy_calib_mib MiB each
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     def step(i):

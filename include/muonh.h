@@ -195,6 +195,10 @@ int muonh_profile_read(muonh_kernel_stat* out, int max, int* n_out);
 /* Library version string. */
 const char* muonh_version(void);
 
+/* Text of the last HIP failure behind a MUONH_EHIP return on this host
+ * thread: the failing call and HIP's error string ("" if none). */
+const char* muonh_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE = 0, 1
 EXPORTED = (
     "muonh_default_opts", "muonh_step", "ns_orthogonalize", "frob_project", "muonh_get_flags",
     "muonh_reset_flags", "muonh_strerror", "muonh_release", "muonh_plan_query",
-    "muonh_profile_begin", "muonh_profile_read", "muonh_version",
+    "muonh_profile_begin", "muonh_profile_read", "muonh_version", "muonh_last_error",
 )
 
 
@@ -47,7 +47,10 @@ class MuonhUnavailable(RuntimeError):
 class MuonhError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__(f"{where}: {strerror(code) if _LIB else code} (code {code})")
+        msg = f"{where}: {strerror(code) if _LIB else code} (code {code})"
+        if code == MUONH_EHIP and _LIB is not None:
+            msg += f" [{_LIB.muonh_last_error().decode()}]"
+        super().__init__(msg)
 
 
 class Opts(ctypes.Structure):
@@ -88,6 +91,13 @@ def load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise MuonhUnavailable(
             f"{path} is not built; run `python -m matrix_orthogonalizing_optimizer_momentum_amd.build`")
+    # The library must share PyTorch's HIP runtime (device pointers and
+    # streams come from it): load torch first so that its libamdhip64 is the
+    # one the dynamic linker binds, instead of a second runtime instance.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - torch is only needed for tensors
+        pass
     try:
         lib = ctypes.CDLL(path)
     except OSError as e:  # pragma: no cover
@@ -119,6 +129,8 @@ def load(path: str = LIB_PATH):
     lib.muonh_profile_read.restype = c_int
     lib.muonh_version.argtypes = []
     lib.muonh_version.restype = ctypes.c_char_p
+    lib.muonh_last_error.argtypes = []
+    lib.muonh_last_error.restype = ctypes.c_char_p
     _LIB = lib
     return lib
 

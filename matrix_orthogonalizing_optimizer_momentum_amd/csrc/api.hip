@@ -6,6 +6,7 @@
 //   k_hook_reduce, k_hook_write          (Hyperball or RadialBrake)
 // all queued on the caller's stream with no host synchronization.
 #include <hip/hip_runtime.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
@@ -15,7 +16,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/muonh.h"
+#include "muonh.h"
 #include "desc.h"
 #include "planner.h"
 
@@ -33,11 +34,9 @@ hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blo
 hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
                         hipStream_t s);
 hipError_t launch_finalize(const SlotTable& st, int slot0, int nslots, hipStream_t s);
-hipError_t launch_ns_gemm(int op_dt, int phase, const NsUnit* units, const GemmJob* jobs, int njobs,
+hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs, int njobs,
                           float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
                           const SlotTable& st, hipStream_t s);
-int gemm_tile_m();
-int gemm_tile_n();
 
 namespace {
 
@@ -47,19 +46,20 @@ constexpr int kMaxK = 64;
 struct DevTables {  // one chunk's tables on the device
   char* mem = nullptr;
   NsUnit* units = nullptr;
-  GemmJob* g12 = nullptr;
-  GemmJob* g3 = nullptr;
+  GemmJob* g12[kGemmCfgs] = {};
+  GemmJob* g3[kGemmCfgs] = {};
   MomMat* mom_mats = nullptr;
   MomBlock* mom_blocks = nullptr;
   HookMat* hook_mats = nullptr;
   HookBlock* hook_blocks = nullptr;
   int32_t* nparts = nullptr;
   int64_t* part_base = nullptr;
-  int n_g12 = 0, n_g3 = 0, n_mom = 0, n_hook = 0;
+  int n_g12[kGemmCfgs] = {}, n_g3[kGemmCfgs] = {};
+  int n_mom = 0, n_hook = 0;
   int64_t parts_total = 0;
   int nslots = 0;
   int nunits = 0, nmats = 0;  // slot ranges: [0,nunits) norms, then nmats O norms, then nmats hook sums
-  double flops_g1 = 0, flops_g2 = 0, flops_g3 = 0;
+  double flops_g1[kGemmCfgs] = {}, flops_g2[kGemmCfgs] = {}, flops_g3[kGemmCfgs] = {};
   double bytes_mom = 0, bytes_hook1 = 0, bytes_hook2 = 0, bytes_sumsq = 0;
 };
 
@@ -210,8 +210,6 @@ Cfg make_cfg(int kind, int n, int K, int tile_T, const Resolved& r, size_t limit
   c.op_dt = r.o.ns_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.x32 = (c.op_dt == DT_BF16 && r.o.ns_precision == MUONH_NS_X32) ? 1 : 0;
   c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB : kModeHB;
-  c.gemm_bm = gemm_tile_m();
-  c.gemm_bn = gemm_tile_n();
   c.ws_limit = limit;
   return c;
 }
@@ -225,10 +223,12 @@ void put(std::vector<char>& blob, const std::vector<T>& v, size_t& off) {
 
 int upload_chunk(const ChunkTables& t, DevTables& d) {
   std::vector<char> blob;
-  size_t o_units, o_g12, o_g3, o_mm, o_mb, o_hm, o_hb, o_np, o_pb;
+  size_t o_units, o_g12[kGemmCfgs], o_g3[kGemmCfgs], o_mm, o_mb, o_hm, o_hb, o_np, o_pb;
   put(blob, t.units, o_units);
-  put(blob, t.g12_jobs, o_g12);
-  put(blob, t.g3_jobs, o_g3);
+  for (int g = 0; g < kGemmCfgs; ++g) {
+    put(blob, t.g12_jobs[g], o_g12[g]);
+    put(blob, t.g3_jobs[g], o_g3[g]);
+  }
   put(blob, t.mom_mats, o_mm);
   put(blob, t.mom_blocks, o_mb);
   put(blob, t.hook_mats, o_hm);
@@ -240,25 +240,27 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   // Synchronous copy: runs once per new (buffers, shapes, options) set.
   if (hipMemcpy(d.mem, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess) return MUONH_EHIP;
   d.units = reinterpret_cast<NsUnit*>(d.mem + o_units);
-  d.g12 = reinterpret_cast<GemmJob*>(d.mem + o_g12);
-  d.g3 = reinterpret_cast<GemmJob*>(d.mem + o_g3);
+  for (int g = 0; g < kGemmCfgs; ++g) {
+    d.g12[g] = reinterpret_cast<GemmJob*>(d.mem + o_g12[g]);
+    d.g3[g] = reinterpret_cast<GemmJob*>(d.mem + o_g3[g]);
+    d.n_g12[g] = (int)t.g12_jobs[g].size();
+    d.n_g3[g] = (int)t.g3_jobs[g].size();
+    d.flops_g1[g] = t.flops_g1[g];
+    d.flops_g2[g] = t.flops_g2[g];
+    d.flops_g3[g] = t.flops_g3[g];
+  }
   d.mom_mats = reinterpret_cast<MomMat*>(d.mem + o_mm);
   d.mom_blocks = reinterpret_cast<MomBlock*>(d.mem + o_mb);
   d.hook_mats = reinterpret_cast<HookMat*>(d.mem + o_hm);
   d.hook_blocks = reinterpret_cast<HookBlock*>(d.mem + o_hb);
   d.nparts = reinterpret_cast<int32_t*>(d.mem + o_np);
   d.part_base = reinterpret_cast<int64_t*>(d.mem + o_pb);
-  d.n_g12 = (int)t.g12_jobs.size();
-  d.n_g3 = (int)t.g3_jobs.size();
   d.n_mom = (int)t.mom_blocks.size();
   d.n_hook = (int)t.hook_blocks.size();
   d.parts_total = t.parts_total;
   d.nslots = (int)t.nparts.size();
   d.nunits = (int)t.units.size();
   d.nmats = (int)((t.nparts.size() - t.units.size()) / 2);
-  d.flops_g1 = t.flops_g1;
-  d.flops_g2 = t.flops_g2;
-  d.flops_g3 = t.flops_g3;
   d.bytes_mom = t.bytes_mom;
   d.bytes_hook1 = t.bytes_hook1;
   d.bytes_hook2 = t.bytes_hook2;
@@ -369,37 +371,50 @@ SlotTable slot_table(State& st, const DevTables& d) {
   return t;
 }
 
-#define MUONH_TRY_HIP(x)              \
-  do {                                \
-    if ((x) != hipSuccess) return MUONH_EHIP; \
+// Last HIP failure, for muonh_last_error().
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char* what) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return MUONH_EHIP;
+}
+
+#define MUONH_TRY_HIP(x)                                  \
+  do {                                                    \
+    const hipError_t e_ = (x);                            \
+    if (e_ != hipSuccess) return hip_fail(e_, #x);        \
   } while (0)
 
 int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, const SlotTable& sl,
            hipStream_t s) {
   const float eps = r.o.ns_eps;
   if (cfg.K == 0) {
-    {
+    for (int g = 0; g < kGemmCfgs; ++g) {
       Prof pf(st, s, PC_G3, 0, 0);
-      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, d.units, d.g3, d.n_g3, 1.f, 0.f, 0.f, eps, 1, 1, 0, 1, sl, s));
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], 1.f, 0.f, 0.f, eps, 1, 1, 0, 1,
+                                   sl, s));
     }
-    Prof pf(st, s, PC_FIN, 0, 0);
-    MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));
-    return MUONH_OK;
   }
   for (int k = 0; k < cfg.K; ++k) {
     const float a = r.coeffs[3 * k], b = r.coeffs[3 * k + 1], c = r.coeffs[3 * k + 2];
     const int first = k == 0, last = k == cfg.K - 1, cur = k & 1;
-    {
-      Prof pf(st, s, PC_G1, d.flops_g1, 0);
-      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 0, d.units, d.g12, d.n_g12, a, b, c, eps, first, 0, cur, 0, sl, s));
+    for (int g = 0; g < kGemmCfgs; ++g) {
+      if (!d.n_g12[g]) continue;
+      Prof pf(st, s, PC_G1, d.flops_g1[g], 0);
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 0, g, d.units, d.g12[g], d.n_g12[g], a, b, c, eps, first, 0, cur, 0,
+                                   sl, s));
     }
-    {
-      Prof pf(st, s, PC_G2, d.flops_g2, 0);
-      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 1, d.units, d.g12, d.n_g12, a, b, c, eps, first, 0, cur, 0, sl, s));
+    for (int g = 0; g < kGemmCfgs; ++g) {
+      if (!d.n_g12[g]) continue;
+      Prof pf(st, s, PC_G2, d.flops_g2[g], 0);
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 1, g, d.units, d.g12[g], d.n_g12[g], a, b, c, eps, first, 0, cur, 0,
+                                   sl, s));
     }
-    {
-      Prof pf(st, s, PC_G3, d.flops_g3, 0);
-      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, d.units, d.g3, d.n_g3, a, b, c, eps, first, last, cur, 0, sl, s));
+    for (int g = 0; g < kGemmCfgs; ++g) {
+      if (!d.n_g3[g]) continue;
+      Prof pf(st, s, PC_G3, d.flops_g3[g], 0);
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], a, b, c, eps, first, last, cur, 0,
+                                   sl, s));
     }
   }
   Prof pf(st, s, PC_FIN, 0, 0);
@@ -688,5 +703,7 @@ int muonh_profile_read(muonh_kernel_stat* out, int max, int* n_out) {
 }
 
 const char* muonh_version(void) { return "libmuonh 0.1 (gfx950)"; }
+
+const char* muonh_last_error(void) { return g_last_error; }
 
 }  // extern "C"

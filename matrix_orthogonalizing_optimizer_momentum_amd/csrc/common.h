@@ -9,6 +9,16 @@ namespace muonh {
 
 typedef uint16_t bf16_t;  // bfloat16 storage
 
+// Pointers taken from descriptor tables are generic; accesses through them
+// compile to flat loads/stores, which count against both the vector-memory
+// and the LDS wait counters.  Everything the kernels touch in HBM goes
+// through these global (address space 1) views instead.
+#define MUONH_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ MUONH_GLOBAL T* gmem(T* p) { return (MUONH_GLOBAL T*)p; }
+template <typename T>
+__device__ __forceinline__ const MUONH_GLOBAL T* gmem(const T* p) { return (const MUONH_GLOBAL T*)p; }
+
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // float -> bfloat16, round to nearest even (NaN stays NaN).
@@ -22,59 +32,65 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 // Storage traits: load / store one element of a storage type as float.
 template <typename T> struct St;
 template <> struct St<float> {
-  static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
-  static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
+  static __device__ __forceinline__ float ld(const float* p, int64_t i) { return gmem(p)[i]; }
+  static __device__ __forceinline__ void st(float* p, int64_t i, float v) { gmem(p)[i] = v; }
   static __device__ __forceinline__ float round(float v) { return v; }
   static constexpr int dt = DT_F32;
 };
 template <> struct St<bf16_t> {
-  static __device__ __forceinline__ float ld(const bf16_t* p, int64_t i) { return bf2f(p[i]); }
-  static __device__ __forceinline__ void st(bf16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+  static __device__ __forceinline__ float ld(const bf16_t* p, int64_t i) { return bf2f(gmem(p)[i]); }
+  static __device__ __forceinline__ void st(bf16_t* p, int64_t i, float v) { gmem(p)[i] = f2bf(v); }
   static __device__ __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
   static constexpr int dt = DT_BF16;
 };
 
-// Load 8 consecutive elements [i, i+8) as float.  vec: the caller knows the
-// 8 elements are in range and 16-byte (bf16) / 32-byte (f32) aligned.
+// Native vector types for 16 / 8-byte global accesses (HIP's uint4 / float4
+// classes cannot bind address-space-1 references).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Load 8 consecutive elements [i, i+8) as float.  The caller knows the 8
+// elements are in range and 16-byte (bf16) / 32-byte (f32) aligned.
 __device__ __forceinline__ void load8(const bf16_t* p, int64_t i, float (&v)[8]) {
-  uint4 q = *reinterpret_cast<const uint4*>(p + i);
-  uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  const u32x4_t q = *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(p + i));
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    v[2 * k] = __uint_as_float(w[k] << 16);
-    v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    v[2 * k] = __uint_as_float(q[k] << 16);
+    v[2 * k + 1] = __uint_as_float(q[k] & 0xffff0000u);
   }
 }
 __device__ __forceinline__ void load8(const float* p, int64_t i, float (&v)[8]) {
-  float4 a = *reinterpret_cast<const float4*>(p + i);
-  float4 b = *reinterpret_cast<const float4*>(p + i + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  const f32x4_t a = *reinterpret_cast<const MUONH_GLOBAL f32x4_t*>(gmem(p + i));
+  const f32x4_t b = *reinterpret_cast<const MUONH_GLOBAL f32x4_t*>(gmem(p + i + 4));
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
 }
 __device__ __forceinline__ void store8(bf16_t* p, int64_t i, const float (&v)[8]) {
-  uint32_t w[4];
+  u32x4_t w;
 #pragma unroll
   for (int k = 0; k < 4; ++k) w[k] = (uint32_t)f2bf(v[2 * k]) | ((uint32_t)f2bf(v[2 * k + 1]) << 16);
-  *reinterpret_cast<uint4*>(p + i) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(p + i)) = w;
 }
 __device__ __forceinline__ void store8(float* p, int64_t i, const float (&v)[8]) {
-  *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  const f32x4_t a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+  *reinterpret_cast<MUONH_GLOBAL f32x4_t*>(gmem(p + i)) = a;
+  *reinterpret_cast<MUONH_GLOBAL f32x4_t*>(gmem(p + i + 4)) = b;
 }
 
 // Store one element of run-time dtype.
 __device__ __forceinline__ float store_dyn(void* p, int64_t i, float v, int dtype) {
   if (dtype == DT_BF16) {
     uint16_t h = f2bf(v);
-    reinterpret_cast<bf16_t*>(p)[i] = h;
+    gmem(reinterpret_cast<bf16_t*>(p))[i] = h;
     return bf2f(h);
   }
-  reinterpret_cast<float*>(p)[i] = v;
+  gmem(reinterpret_cast<float*>(p))[i] = v;
   return v;
 }
 __device__ __forceinline__ float load_dyn(const void* p, int64_t i, int dtype) {
-  if (dtype == DT_BF16) return bf2f(reinterpret_cast<const bf16_t*>(p)[i]);
-  return reinterpret_cast<const float*>(p)[i];
+  if (dtype == DT_BF16) return bf2f(gmem(reinterpret_cast<const bf16_t*>(p))[i]);
+  return gmem(reinterpret_cast<const float*>(p))[i];
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
@@ -102,8 +118,8 @@ __device__ void block_partial2(double v0, double v1, const SlotTable& st, int sl
 #pragma unroll
     for (int i = 0; i < NW; ++i) { t0 += red[0][i]; t1 += red[1][i]; }
     const int64_t p = st.part_base[slot] + part;
-    st.partials[2 * p] = t0;
-    st.partials[2 * p + 1] = t1;
+    gmem(st.partials)[2 * p] = t0;
+    gmem(st.partials)[2 * p + 1] = t1;
   }
 }
 

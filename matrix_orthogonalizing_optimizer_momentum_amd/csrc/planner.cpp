@@ -15,8 +15,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 
-#include "../../include/muonh.h"
+#include "muonh.h"
 
 namespace muonh {
 
@@ -32,6 +33,31 @@ UnitBytes unit_bytes(int r, int s, int op_dt, int x32) {
   return u;
 }
 
+// Tile configuration of a unit.  MUONH_GEMM_CFG (0/1/2) forces one for
+// tuning runs; fp32 operands always use configuration 0's 128 x 128 tile.
+static int forced_cfg() {
+  static int v = -2;
+  if (v == -2) {
+    const char* e = std::getenv("MUONH_GEMM_CFG");
+    v = (e && *e) ? std::atoi(e) : -1;
+    if (v < 0 || v >= kGemmCfgs) v = -1;
+  }
+  return v;
+}
+
+int unit_gemm_cfg(int r, int op_dt) {
+  if (op_dt != DT_BF16) return 0;
+  const int f = forced_cfg();
+  if (f >= 0) return f;
+  return 0;
+}
+
+static int64_t jobs_per_iter(int r, int s, int op_dt) {
+  const int B = gemm_tile_side(unit_gemm_cfg(r, op_dt));
+  const int64_t nr = (pad_up(r, kPad) + B - 1) / B, ns = (pad_up(s, kPad) + B - 1) / B;
+  return 2 * (nr * (nr + 1) / 2) + nr * ns;  // symmetric G1, G2 + G3
+}
+
 static double ns_flops_true(int64_t h, int64_t w, int K) {
   const double r = (double)std::min(h, w), s = (double)std::max(h, w);
   return (double)K * (4.0 * r * r * s + 2.0 * r * r * r);
@@ -42,7 +68,6 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
   const int n = cfg.n;
   plan.mats.resize(n);
   const int T = cfg.tile_T;
-  const int BM = cfg.gemm_bm, BN = cfg.gemm_bn;
   for (int i = 0; i < n; ++i) {
     MatPlan& m = plan.mats[i];
     m.H = shapes[2 * i];
@@ -75,9 +100,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
           const int64_t w = std::min<int64_t>(T, m.W - (int64_t)b * T);
           plan.ns_flops += ns_flops_true(h, w, cfg.K);
         }
-      const int64_t ld = pad_up(T, kPad);
-      plan.jobs_per_iter += (int64_t)m.nunits * (2 * ((ld + BM - 1) / BM) * ((T + BN - 1) / BN) +
-                                                 ((ld + BM - 1) / BM) * ((ld + BN - 1) / BN));
+      plan.jobs_per_iter += (int64_t)m.nunits * jobs_per_iter(T, T, cfg.op_dt);
     } else {
       m.r = (int)std::min(m.H, m.W);
       m.s = (int)std::max(m.H, m.W);
@@ -87,9 +110,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
       const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32);
       m.ws_bytes += ub.total();
       plan.ns_flops += ns_flops_true(m.H, m.W, cfg.K);
-      const int64_t ldr = pad_up(m.r, kPad), lds = pad_up(m.s, kPad);
-      plan.jobs_per_iter += 2 * ((ldr + BM - 1) / BM) * ((m.r + BN - 1) / BN) +
-                            ((ldr + BM - 1) / BM) * ((lds + BN - 1) / BN);
+      plan.jobs_per_iter += jobs_per_iter(m.r, m.s, cfg.op_dt);
     }
     if (cfg.kind == CALL_STEP) m.ws_bytes += align256(numel * esize(cfg.op_dt));  // O
     plan.units += m.nunits;
@@ -120,7 +141,6 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
 void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char* ws, ChunkTables& t) {
   t = ChunkTables();
   const ChunkPlan& ch = plan.chunks[c];
-  const int BM = cfg.gemm_bm, BN = cfg.gemm_bn;
   const int T = cfg.tile_T;
   const int nm = ch.m1 - ch.m0;
   const int es_op = esize(cfg.op_dt);
@@ -195,19 +215,22 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
         u.o_cols = m.s;
         u.o_ptr = out;
       }
-      const int g3r = (u.ld_r + BM - 1) / BM, g3c = (u.ld_s + BN - 1) / BN;
-      const int g12c = (u.r + BN - 1) / BN;
+      const int gc = unit_gemm_cfg(u.r, cfg.op_dt);
+      const int B = gemm_tile_side(gc);
+      const int g3r = (u.ld_r + B - 1) / B, g3c = (u.ld_s + B - 1) / B;
       u.g3_cols = g3c;
       part += g3r * g3c;
       const int uid = unit0[mi] + k;
+      // A and B are symmetric: only tiles on or above the diagonal, the
+      // epilogue mirrors the off-diagonal ones.
       for (int tm = 0; tm < g3r; ++tm)
-        for (int tn = 0; tn < g12c; ++tn) t.g12_jobs.push_back({uid, tm, tn, u.ld_r / 64});
+        for (int tn = tm; tn < g3r; ++tn) t.g12_jobs[gc].push_back({uid, tm, tn, u.ld_r / 64});
       for (int tn = 0; tn < g3c; ++tn)
-        for (int tm = 0; tm < g3r; ++tm) t.g3_jobs.push_back({uid, tm, tn, u.ld_r / 64});
+        for (int tm = 0; tm < g3r; ++tm) t.g3_jobs[gc].push_back({uid, tm, tn, u.ld_r / 64});
       const double r = (double)std::min(h, w), s = (double)std::max(h, w);
-      t.flops_g1 += 2.0 * r * r * s;
-      t.flops_g2 += 2.0 * r * r * r;
-      t.flops_g3 += 2.0 * r * r * s;
+      t.flops_g1[gc] += 2.0 * r * r * s;
+      t.flops_g2[gc] += 2.0 * r * r * r;
+      t.flops_g3[gc] += 2.0 * r * r * s;
     }
     t.nparts[s_onorm0 + mi] = part;
   }

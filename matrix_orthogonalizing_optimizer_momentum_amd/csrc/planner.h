@@ -23,7 +23,6 @@ struct Cfg {
   int state_dt, op_dt;
   int x32;        // fp32 master X (bf16 operands only)
   int hook;       // kModeHB / kModeRB
-  int gemm_bm, gemm_bn;
   size_t ws_limit;
 };
 
@@ -66,9 +65,15 @@ inline int esize(int dt) { return dt == DT_F32 ? 4 : 2; }
 int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan);
 
 // Host tables of one chunk (everything a launch sequence needs).
+// GEMM tile configurations: 0 = 128 x 128 (BK 64), 1 = 256 x 256 (BK 64,
+// bf16 operands), 2 = 128 x 128 (BK 32, bf16 operands).
+constexpr int kGemmCfgs = 3;
+inline int gemm_tile_side(int cfg) { return cfg == 1 ? 256 : 128; }
+int unit_gemm_cfg(int r, int op_dt);
+
 struct ChunkTables {
   std::vector<NsUnit> units;
-  std::vector<GemmJob> g12_jobs, g3_jobs;
+  std::vector<GemmJob> g12_jobs[kGemmCfgs], g3_jobs[kGemmCfgs];
   std::vector<MomMat> mom_mats;
   std::vector<MomBlock> mom_blocks;
   std::vector<HookMat> hook_mats;
@@ -76,7 +81,7 @@ struct ChunkTables {
   std::vector<int32_t> nparts;
   std::vector<int64_t> part_base;
   int64_t parts_total = 0;
-  double flops_g1 = 0, flops_g2 = 0, flops_g3 = 0;
+  double flops_g1[kGemmCfgs] = {}, flops_g2[kGemmCfgs] = {}, flops_g3[kGemmCfgs] = {};
   double bytes_mom = 0, bytes_hook1 = 0, bytes_hook2 = 0, bytes_sumsq = 0;
 };
 

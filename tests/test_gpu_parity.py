@@ -61,7 +61,8 @@ def test_ns_fp32_small(shape):
 
 
 @pytest.mark.parametrize("prec", ["x32", "fold"])
-@pytest.mark.parametrize("shape", [(768, 768), (768, 3072), (3072, 768), (768, 2304), (300, 700)],
+@pytest.mark.parametrize("shape", [(768, 768), (768, 3072), (3072, 768), (768, 2304), (300, 700), (500, 1300),
+                                   (1300, 500), (256, 256), (1024, 2048)],
                          ids=lambda s: f"{s[0]}x{s[1]}" if isinstance(s, tuple) else s)
 def test_ns_bf16_spiked(shape, prec):
     H, W = shape
