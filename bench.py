@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
-NS_CLASSES = ("ns_gram_G1", "ns_poly_G2", "ns_update_G3")
+NS_CLASSES = ("ns_gram_G1", "ns_poly_G2", "ns_update_G3", "ns_tile_resident")
 STREAM_CLASSES = ("momentum_prep", "hook_reduce", "hook_write")
 
 

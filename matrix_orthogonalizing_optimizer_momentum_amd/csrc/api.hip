@@ -37,10 +37,13 @@ hipError_t launch_finalize(const SlotTable& st, int slot0, int nslots, hipStream
 hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs, int njobs,
                           float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
                           const SlotTable& st, hipStream_t s);
+hipError_t launch_tile_ns(int state_dt, int op_dt, const TileMat* mats, const TileJob* jobs, int njobs,
+                          const TileArgs& args, hipStream_t s);
 
 namespace {
 
 constexpr int kMaxK = 64;
+static_assert(kMaxK == kTileMaxK, "iteration tables");
 
 // ------------------------------------------------------------------ state
 struct DevTables {  // one chunk's tables on the device
@@ -52,6 +55,10 @@ struct DevTables {  // one chunk's tables on the device
   MomBlock* mom_blocks = nullptr;
   HookMat* hook_mats = nullptr;
   HookBlock* hook_blocks = nullptr;
+  TileMat* tile_mats = nullptr;
+  TileJob* tile_jobs = nullptr;
+  int n_tile = 0;
+  double flops_tile = 0, bytes_tile = 0;
   int32_t* nparts = nullptr;
   int64_t* part_base = nullptr;
   int n_g12[kGemmCfgs] = {}, n_g3[kGemmCfgs] = {};
@@ -96,9 +103,9 @@ State& S() {
   return s;
 }
 
-const char* kClassNames[] = {"momentum_prep", "ns_gram_G1", "ns_poly_G2", "ns_update_G3",
-                             "hook_reduce",   "hook_write", "sumsq",      "finalize"};
-enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_FIN, PC_N };
+const char* kClassNames[] = {"momentum_prep", "ns_gram_G1", "ns_poly_G2", "ns_update_G3", "hook_reduce",
+                             "hook_write",    "sumsq",      "finalize",   "ns_tile_resident"};
+enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_FIN, PC_TILE, PC_N };
 
 // ------------------------------------------------------------------ helpers
 void free_plan(CachedPlan& p) {
@@ -184,8 +191,8 @@ int check_tile(int tile_T) {
   if (tile_T < 0) return MUONH_EINVAL;
   if (tile_T == 0) return MUONH_OK;
   if (tile_T > 8192) return MUONH_EINVAL;
-  if (tile_T % 64 == 0) return MUONH_OK;
-  if (tile_T <= 128) return MUONH_ENOTIMPL;  // resident small-tile kernel not in this build
+  if (tile_T <= kTileResidentMax) return MUONH_OK;  // resident-tile kernel
+  if (tile_T % 64 == 0) return MUONH_OK;             // GEMM engine
   return MUONH_EINVAL;
 }
 
@@ -223,7 +230,7 @@ void put(std::vector<char>& blob, const std::vector<T>& v, size_t& off) {
 
 int upload_chunk(const ChunkTables& t, DevTables& d) {
   std::vector<char> blob;
-  size_t o_units, o_g12[kGemmCfgs], o_g3[kGemmCfgs], o_mm, o_mb, o_hm, o_hb, o_np, o_pb;
+  size_t o_units, o_g12[kGemmCfgs], o_g3[kGemmCfgs], o_mm, o_mb, o_hm, o_hb, o_tm, o_tj, o_np, o_pb;
   put(blob, t.units, o_units);
   for (int g = 0; g < kGemmCfgs; ++g) {
     put(blob, t.g12_jobs[g], o_g12[g]);
@@ -233,6 +240,8 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   put(blob, t.mom_blocks, o_mb);
   put(blob, t.hook_mats, o_hm);
   put(blob, t.hook_blocks, o_hb);
+  put(blob, t.tile_mats, o_tm);
+  put(blob, t.tile_jobs, o_tj);
   put(blob, t.nparts, o_np);
   put(blob, t.part_base, o_pb);
   if (blob.empty()) blob.resize(256);
@@ -253,6 +262,11 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   d.mom_blocks = reinterpret_cast<MomBlock*>(d.mem + o_mb);
   d.hook_mats = reinterpret_cast<HookMat*>(d.mem + o_hm);
   d.hook_blocks = reinterpret_cast<HookBlock*>(d.mem + o_hb);
+  d.tile_mats = reinterpret_cast<TileMat*>(d.mem + o_tm);
+  d.tile_jobs = reinterpret_cast<TileJob*>(d.mem + o_tj);
+  d.n_tile = (int)t.tile_jobs.size();
+  d.flops_tile = t.flops_tile;
+  d.bytes_tile = t.bytes_tile;
   d.nparts = reinterpret_cast<int32_t*>(d.mem + o_np);
   d.part_base = reinterpret_cast<int64_t*>(d.mem + o_pb);
   d.n_mom = (int)t.mom_blocks.size();
@@ -443,7 +457,25 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
   hipStream_t s = reinterpret_cast<hipStream_t>(r.o.stream);
   for (const DevTables& d : cp->chunks) {
     const SlotTable sl = slot_table(st, d);
-    if (kind != CALL_PROJ) {
+    if (kind != CALL_PROJ && d.n_tile > 0) {
+      // Hierarchical Muon, resident tiles: momentum, norms and every
+      // Newton-Schulz iteration in one launch.
+      TileArgs ta{};
+      for (int k = 0; k < cfg.K; ++k)
+        for (int j = 0; j < 3; ++j) ta.abc[k][j] = r.coeffs[3 * k + j];
+      ta.T = cfg.tile_T;
+      ta.K = cfg.K;
+      ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
+      ta.beta = beta;
+      ta.eps = r.o.ns_eps;
+      ta.st = sl;
+      {
+        Prof pf(st, s, PC_TILE, d.flops_tile, d.bytes_tile);
+        MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs, d.n_tile, ta, s));
+      }
+      Prof pf(st, s, PC_FIN, 0, 0);
+      MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
+    } else if (kind != CALL_PROJ) {
       {
         Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
         MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,

@@ -95,6 +95,36 @@ struct HookBlock {
   int32_t blk;          // block index within the matrix
 };
 
+// Resident-tile Newton-Schulz (Hierarchical Muon with T <= kTileResidentMax):
+// one workgroup runs the whole step of one tile.
+constexpr int kTileResidentMax = 128;
+constexpr int kTileMaxK = 64;
+
+struct TileMat {
+  const void* g;        // gradient; nullptr: m is the Newton-Schulz input itself
+  void* m;              // momentum (updated in place when g is set) or NS input
+  void* out;            // orthogonalized output (H x W, ld = W)
+  int64_t H, W;
+  int32_t out_dtype;
+  int32_t onorm_slot;   // slot collecting this matrix's ||O||^2
+};
+
+struct TileJob {
+  int32_t mat;
+  int32_t ti, tj;       // tile row / column
+  int32_t part;         // partial index inside the matrix's O-norm slot
+};
+
+struct TileArgs {
+  float abc[kTileMaxK][3];  // (a, b, c) per iteration
+  int T;                    // tile side
+  int K;                    // iterations
+  int fold;                 // 1: round the master X to bf16 after every iteration
+  float beta;               // momentum coefficient (used when TileMat::g is set)
+  float eps;                // pre-scale eps
+  SlotTable st;
+};
+
 // Hook modes.
 constexpr int kModeHB = 0;  // Hyperball
 constexpr int kModeRB = 1;  // RadialBrake

@@ -92,15 +92,19 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
       m.ntr = (int)((m.H + T - 1) / T);
       m.ntc = (int)((m.W + T - 1) / T);
       m.nunits = m.ntr * m.ntc;
-      const UnitBytes ub = unit_bytes(T, T, cfg.op_dt, cfg.x32);
-      m.ws_bytes += (int64_t)m.nunits * ub.total();
       for (int a = 0; a < m.ntr; ++a)
         for (int b = 0; b < m.ntc; ++b) {
           const int64_t h = std::min<int64_t>(T, m.H - (int64_t)a * T);
           const int64_t w = std::min<int64_t>(T, m.W - (int64_t)b * T);
           plan.ns_flops += ns_flops_true(h, w, cfg.K);
         }
-      plan.jobs_per_iter += (int64_t)m.nunits * jobs_per_iter(T, T, cfg.op_dt);
+      if (resident_tiles(cfg)) {
+        plan.jobs_per_iter += m.nunits;  // one workgroup per tile runs every iteration
+      } else {
+        const UnitBytes ub = unit_bytes(T, T, cfg.op_dt, cfg.x32);
+        m.ws_bytes += (int64_t)m.nunits * ub.total();
+        plan.jobs_per_iter += (int64_t)m.nunits * jobs_per_iter(T, T, cfg.op_dt);
+      }
     } else {
       m.r = (int)std::min(m.H, m.W);
       m.s = (int)std::max(m.H, m.W);
@@ -158,6 +162,10 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
     const MatPlan& m = plan.mats[ch.m0 + mi];
     unit0[mi] = (int)t.units.size();
     if (cfg.kind == CALL_PROJ) continue;
+    if (resident_tiles(cfg)) {
+      if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
+      continue;
+    }
     const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32);
     for (int k = 0; k < m.nunits; ++k) {
       NsUnit u{};
@@ -176,17 +184,48 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
     if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
   }
   const int nunits = (int)t.units.size();
+  const bool resident = resident_tiles(cfg) && cfg.kind != CALL_PROJ;
 
-  // --- slots: [unit norms][matrix O norms][matrix hook sums]
+  // --- slots: [unit norms][matrix O norms][matrix hook sums]; the
+  // resident-tile kernel forms its tile norms itself, so it has no unit slots.
   const int s_norm0 = 0, s_onorm0 = nunits, s_hook0 = nunits + nm;
   const int nslots = nunits + 2 * nm;
   t.nparts.assign(nslots, 0);
+
+  // --- resident tiles: one job per tile, momentum fused
+  if (resident) {
+    const double sb = esize(cfg.state_dt);
+    for (int mi = 0; mi < nm; ++mi) {
+      const int gi = ch.m0 + mi;
+      const MatPlan& m = plan.mats[gi];
+      TileMat tm{};
+      tm.g = cfg.kind == CALL_STEP ? p.grads[gi] : nullptr;
+      tm.m = cfg.kind == CALL_STEP ? p.moms[gi] : const_cast<void*>(p.grads[gi]);
+      tm.out = cfg.kind == CALL_STEP ? (void*)obuf[mi] : p.outs[gi];
+      tm.H = m.H;
+      tm.W = m.W;
+      tm.out_dtype = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
+      tm.onorm_slot = s_onorm0 + mi;
+      const int idx = (int)t.tile_mats.size();
+      t.tile_mats.push_back(tm);
+      for (int a = 0; a < m.ntr; ++a)
+        for (int b = 0; b < m.ntc; ++b) {
+          t.tile_jobs.push_back({idx, a, b, a * m.ntc + b});
+          const int64_t h = std::min<int64_t>(T, m.H - (int64_t)a * T);
+          const int64_t w = std::min<int64_t>(T, m.W - (int64_t)b * T);
+          t.flops_tile += ns_flops_true(h, w, cfg.K);
+        }
+      t.nparts[s_onorm0 + mi] = m.nunits;
+      const double numel = (double)m.H * m.W;
+      t.bytes_tile += cfg.kind == CALL_STEP ? numel * (3 * sb + es_op) : numel * 2 * sb;
+    }
+  }
 
   // --- output placement, O-norm partial numbering, GEMM jobs, flops
   for (int mi = 0; mi < nm; ++mi) {
     const int gi = ch.m0 + mi;
     const MatPlan& m = plan.mats[gi];
-    if (cfg.kind == CALL_PROJ) continue;
+    if (cfg.kind == CALL_PROJ || resident) continue;
     void* out = cfg.kind == CALL_STEP ? (void*)obuf[mi] : p.outs[gi];
     const int out_dt = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
     const int oes = esize(out_dt);
@@ -236,7 +275,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   }
 
   // --- momentum / prep blocks
-  if (cfg.kind != CALL_PROJ) {
+  if (cfg.kind != CALL_PROJ && !resident) {
     for (int mi = 0; mi < nm; ++mi) {
       const int gi = ch.m0 + mi;
       const MatPlan& m = plan.mats[gi];

@@ -71,6 +71,11 @@ constexpr int kGemmCfgs = 3;
 inline int gemm_tile_side(int cfg) { return cfg == 1 ? 256 : 128; }
 int unit_gemm_cfg(int r, int op_dt);
 
+// Hierarchical Muon with T <= kTileResidentMax runs on the resident-tile
+// kernel (one workgroup per tile for the whole step, momentum fused, no
+// workspace but the step's O buffer); larger tiles go through the GEMM engine.
+inline bool resident_tiles(const Cfg& c) { return c.tile_T > 0 && c.tile_T <= kTileResidentMax; }
+
 struct ChunkTables {
   std::vector<NsUnit> units;
   std::vector<GemmJob> g12_jobs[kGemmCfgs], g3_jobs[kGemmCfgs];
@@ -78,11 +83,14 @@ struct ChunkTables {
   std::vector<MomBlock> mom_blocks;
   std::vector<HookMat> hook_mats;
   std::vector<HookBlock> hook_blocks;
+  std::vector<TileMat> tile_mats;
+  std::vector<TileJob> tile_jobs;
   std::vector<int32_t> nparts;
   std::vector<int64_t> part_base;
   int64_t parts_total = 0;
   double flops_g1[kGemmCfgs] = {}, flops_g2[kGemmCfgs] = {}, flops_g3[kGemmCfgs] = {};
   double bytes_mom = 0, bytes_hook1 = 0, bytes_hook2 = 0, bytes_sumsq = 0;
+  double flops_tile = 0, bytes_tile = 0;
 };
 
 struct CallPtrs {

@@ -144,6 +144,24 @@ def test_plan_query_tiled_units_and_flops():
     assert q["ns_flops"] == tot
 
 
+@pytest.mark.parametrize("T", [1, 37, 64, 96, 128])
+def test_plan_query_resident_tiles(T):
+    # T <= 128: one workgroup per tile for the whole step; the only workspace
+    # is the step's orthogonalized-update buffer (bf16, 256-byte aligned).
+    shapes = [(300, 700), (768, 2304)]
+    q = mm.plan_query(shapes, K=5, tile_T=T)
+    tiles = sum(-(-H // T) * -(-W // T) for H, W in shapes)
+    assert q["units"] == tiles and q["jobs_per_iter"] == tiles
+    assert q["ws_bytes"] == sum(-(-H * W * 2 // 256) * 256 for H, W in shapes)
+    assert q["chunks"] == 1
+
+
+def test_plan_query_gemm_engine_tiles_need_workspace():
+    # T > 128 (multiples of 64) runs through the GEMM engine with per-tile workspace.
+    shapes = [(768, 2304)]
+    assert mm.plan_query(shapes, K=5, tile_T=256)["ws_bytes"] > mm.plan_query(shapes, K=5, tile_T=128)["ws_bytes"]
+
+
 def test_plan_query_chunking_under_a_budget():
     shapes = gen.gpt2_small_shapes()
     one = mm.plan_query(shapes[:1], K=5)["ws_bytes"]

@@ -199,6 +199,74 @@ def test_tiled_ns_bf16_gpt2_shape(T):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T", [1, 17, 32, 96, 100])
+@pytest.mark.parametrize("shape", [(300, 700), (129, 65)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_tiled_ns_fp32_ragged_tile_sides(shape, T):
+    # Tile sides that are not multiples of the 64-element padding granule
+    # (resident-tile kernel, zero-padded to 64 or 128 inside LDS).
+    H, W = shape
+    banner(f"tiled ns fp32 T={T} {H}x{W}")
+    X = gen.gaussian((H, W), 1.0, 31 + T)
+    out = mm.ns_orthogonalize([dev(X)], K=5, tile_T=T, ns_dtype="f32")[0]
+    torch.cuda.synchronize()
+    assert rel(host(out), orc.tiled_newton_schulz(X, T, 5)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("T", [48, 96])
+@pytest.mark.parametrize("prec", ["x32", "fold"])
+def test_tiled_ns_bf16_ragged(T, prec):
+    banner(f"tiled ns bf16 T={T} {prec} 500x1300")
+    G = gen.store(gen.spiked_grad(500, 1300, 1e-3, seed=8), "bf16")
+    out = mm.ns_orthogonalize([dev(G, torch.bfloat16)], K=5, tile_T=T, ns_precision=prec)[0]
+    torch.cuda.synchronize()
+    err = rel(host(out), orc.tiled_newton_schulz(G, T, 5))
+    print(f"  rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [64, 128])
+def test_tiled_ns_f32_state_bf16_operands(T):
+    # fp32 input, bf16 operands: the fp32 master keeps the unrounded input.
+    banner(f"tiled ns f32 state / bf16 operands T={T}")
+    X = gen.gaussian((384, 640), 1.0, 41)
+    out = mm.ns_orthogonalize([dev(X)], K=5, tile_T=T, ns_dtype="bf16")[0]
+    torch.cuda.synchronize()
+    assert rel(host(out), orc.tiled_newton_schulz(X, T, 5)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("K", [0, 1, 3])
+@pytest.mark.parametrize("T", [64, 96])
+def test_tiled_ns_iteration_counts(K, T):
+    banner(f"tiled ns K={K} T={T}")
+    X = gen.gaussian((200, 300), 1.0, 51)
+    out = mm.ns_orthogonalize([dev(X)], K=K, tile_T=T, ns_dtype="f32")[0]
+    torch.cuda.synchronize()
+    assert rel(host(out), orc.tiled_newton_schulz(X, T, K)) <= TOL["f32"]
+
+
+def test_tiled_ns_coefficient_table_and_cubic():
+    # per-iteration coefficients, including c = 0 (B = b A with no A A product)
+    banner("tiled ns coefficient table with a cubic stage")
+    X = gen.gaussian((256, 384), 1.0, 61)
+    coeffs = [(3.4445, -4.7750, 2.0315)] * 3 + [(1.5, -0.5, 0.0)] * 2
+    out = mm.ns_orthogonalize([dev(X)], K=5, tile_T=128, ns_dtype="f32", coeffs=coeffs)[0]
+    torch.cuda.synchronize()
+    assert rel(host(out), orc.tiled_newton_schulz(X, 128, 5, coeffs=coeffs)) <= TOL["f32"]
+
+
+def test_tiled_ns_in_place_and_zero_tile():
+    # out aliases in; one 64 x 64 tile is exactly zero and must stay zero.
+    banner("tiled ns in place, zero tile")
+    X = gen.gaussian((192, 256), 1.0, 71)
+    X[64:128, 128:192] = 0.0
+    t = dev(X)
+    mm.ns_orthogonalize([t], [t], K=5, tile_T=64, ns_dtype="f32")
+    torch.cuda.synchronize()
+    got = host(t)
+    assert np.all(got[64:128, 128:192] == 0.0)
+    assert rel(got, orc.tiled_newton_schulz(X, 64, 5)) <= TOL["f32"]
+
+
 # ---------------------------------------------------------------------------
 # full step
 # ---------------------------------------------------------------------------
@@ -275,21 +343,49 @@ def test_step_gpt2_full_set_bf16(prec):
         assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("T", [64, 256])
+@pytest.mark.parametrize("T", [64, 96, 128, 256])
 def test_step_himuon_bf16(T):
+    # T <= 128: resident-tile kernel with the momentum update fused in;
+    # T = 256: GEMM engine.  Momentum must match the oracle's bf16 rounding
+    # exactly either way.
     banner(f"himuon step T={T}")
     shapes = [(768, 2304), (3072, 768), (300, 700)]
     Ws, Gs, Ms = _gpt2_like(shapes, cfg=4)
     rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
     w_t = [dev(w) for w in Ws]
-    mm.muonh_step(w_t, [dev(g, torch.bfloat16) for g in Gs], [dev(m, torch.bfloat16) for m in Ms],
+    m_t = [dev(m, torch.bfloat16) for m in Ms]
+    mm.muonh_step(w_t, [dev(g, torch.bfloat16) for g in Gs], m_t,
                   eta=0.02, beta=0.95, K=5, rho=rhos, tile_T=T)
     torch.cuda.synchronize()
     for i in range(len(shapes)):
-        Wn, _, _, _ = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.02, np.float32(0.95), 5, [rhos[i]], tile_T=T,
-                                     state_bf16=True)
+        Wn, Mn, _, _ = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.02, np.float32(0.95), 5, [rhos[i]], tile_T=T,
+                                      state_bf16=True)
+        assert np.array_equal(host(m_t[i]), Mn[0])
         assert abs(np.linalg.norm(host(w_t[i])) / rhos[i] - 1) <= 1e-5
-        assert rel(host(w_t[i]) - Ws[i], Wn[0] - Ws[i]) <= TOL["bf16"]
+        err = rel(host(w_t[i]) - Ws[i], Wn[0] - Ws[i])
+        print(f"  matrix {i} {shapes[i]} step rel err {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [32, 128])
+def test_step_himuon_fp32_trajectory(T):
+    # fp32 state and operands, 5 steps; the oracle runs its own trajectory.
+    banner(f"himuon fp32 trajectory T={T}")
+    H, W = 200, 330
+    W0, Gs, M0 = gen.single_matrix_case(H, W, steps=5)
+    rho = np.float32(np.linalg.norm(W0.astype(np.float64)))
+    w, m = dev(W0), dev(M0)
+    Wo, Mo = [W0.astype(np.float64)], [M0.astype(np.float64)]
+    g_prev, o_prev = W0.astype(np.float64), W0.astype(np.float64)
+    for G in Gs:
+        mm.muonh_step([w], [dev(G)], [m], eta=0.02, beta=0.95, K=5, rho=[rho], tile_T=T, ns_dtype="f32")
+        torch.cuda.synchronize()
+        Wo, Mo, _, _ = orc.muonh_step(Wo, [G], Mo, 0.02, np.float32(0.95), 5, [rho], tile_T=T)
+        wg = host(w)
+        assert abs(np.linalg.norm(wg) / rho - 1) <= 1e-5
+        assert rel(wg - g_prev, Wo[0] - o_prev) <= TOL["f32"]
+        assert np.abs(host(m) - Mo[0]).max() <= 1e-6 * np.abs(Mo[0]).max()
+        g_prev, o_prev = wg, Wo[0]
 
 
 @pytest.mark.parametrize("ns", ["f32", "bf16"])
