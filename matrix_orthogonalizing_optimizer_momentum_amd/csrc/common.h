@@ -21,12 +21,14 @@ __device__ __forceinline__ const MUONH_GLOBAL T* gmem(const T* p) { return (cons
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// float -> bfloat16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float -> bfloat16, round to nearest even (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32 under the default round-to-nearest-even mode.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two floats -> packed bf16 pair (lo in bits 0..15), one conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Storage traits: load / store one element of a storage type as float.
@@ -69,7 +71,7 @@ __device__ __forceinline__ void load8(const float* p, int64_t i, float (&v)[8]) 
 __device__ __forceinline__ void store8(bf16_t* p, int64_t i, const float (&v)[8]) {
   u32x4_t w;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = (uint32_t)f2bf(v[2 * k]) | ((uint32_t)f2bf(v[2 * k + 1]) << 16);
+  for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
   *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(p + i)) = w;
 }
 __device__ __forceinline__ void store8(float* p, int64_t i, const float (&v)[8]) {

@@ -107,6 +107,8 @@ struct TileMat {
   int64_t H, W;
   int32_t out_dtype;
   int32_t onorm_slot;   // slot collecting this matrix's ||O||^2
+  int32_t vec;          // 1: rows and tile origins allow 16-byte accesses
+  int32_t pad_;
 };
 
 struct TileJob {

@@ -80,8 +80,7 @@ __device__ __forceinline__ void load4(const float* p, int64_t i, float (&v)[4]) 
   v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
 }
 __device__ __forceinline__ void store4(bf16_t* p, int64_t i, const float (&v)[4]) {
-  const u32x2_t w = {(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
-                     (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
+  const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   *reinterpret_cast<MUONH_GLOBAL u32x2_t*>(gmem(p + i)) = w;
 }
 __device__ __forceinline__ void store4(float* p, int64_t i, const float (&v)[4]) {

@@ -23,6 +23,8 @@
 // and B are symmetric, so they are stored through the transposed (packed)
 // path.  fp32 operands read X column-wise instead of keeping X^T, so A and B
 // take a buffer of their own.
+#include <type_traits>
+
 #include "common.h"
 
 namespace muonh {
@@ -38,12 +40,15 @@ template <typename T> struct TileOp;
 template <> struct TileOp<bf16_t> {
   static constexpr int KSTEP = 16;
   static constexpr int PAD = 8;  // 16 bytes: conflict-free 16-byte fragment reads
-  static __device__ __forceinline__ void put(bf16_t* p, float v) { *p = f2bf(v); }
+  // p[0] = v0, p[ld] = v1 (two rows of one column, one conversion)
+  static __device__ __forceinline__ void put2col(bf16_t* p, int ld, float v0, float v1) {
+    const uint32_t w = pack_bf16x2(v0, v1);
+    p[0] = (bf16_t)w;
+    p[ld] = (bf16_t)(w >> 16);
+  }
   // p[0..3] = v0..v3; p is 8-byte aligned
   static __device__ __forceinline__ void put4(bf16_t* p, float v0, float v1, float v2, float v3) {
-    u32x2_t w;
-    w[0] = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
-    w[1] = (uint32_t)f2bf(v2) | ((uint32_t)f2bf(v3) << 16);
+    const u32x2_t w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
     *reinterpret_cast<u32x2_t*>(p) = w;
   }
   static __device__ __forceinline__ void get4(const bf16_t* p, float (&v)[4]) {
@@ -57,7 +62,10 @@ template <> struct TileOp<bf16_t> {
 template <> struct TileOp<float> {
   static constexpr int KSTEP = 2;
   static constexpr int PAD = 2;
-  static __device__ __forceinline__ void put(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ void put2col(float* p, int ld, float v0, float v1) {
+    p[0] = v0;
+    p[ld] = v1;
+  }
   static __device__ __forceinline__ void put4(float* p, float v0, float v1, float v2, float v3) {
     u32x2_t a, b;  // 8-byte aligned (even pitch, rows in fours)
     a[0] = __float_as_uint(v0); a[1] = __float_as_uint(v1);
@@ -86,10 +94,17 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int WT = TP / 2;                 // wave tile side (2 x 2 waves)
   constexpr int MI = WT / 32;                // 32 x 32 accumulator blocks per wave side
   constexpr bool kXT = sizeof(OT) == 2;      // bf16: keep X^T for B X
-  __shared__ __attribute__((aligned(16))) OT sX[TP * LD];
-  __shared__ __attribute__((aligned(16))) OT sT[TP * LD];  // bf16: X^T; fp32: A, then B
+  // One LDS block: sX, sT (bf16: X^T; fp32: A, then B) and, aliasing both,
+  // an fp32 staging tile for the coalesced load and store phases.
+  constexpr int XB = TP * LD * (int)sizeof(OT);
+  constexpr int SP = TP + 4;                 // staging pitch (floats)
+  constexpr int kSmem = 2 * XB > TP * SP * 4 ? 2 * XB : TP * SP * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   __shared__ double sred[4];
   __shared__ float ssig;
+  OT* const sX = reinterpret_cast<OT*>(smem);
+  OT* const sT = reinterpret_cast<OT*>(smem + XB);
+  float* const stg = reinterpret_cast<float*>(smem);
   OT* const sAB = kXT ? sX : sT;
 
   const TileJob job = jobs[blockIdx.x];
@@ -100,44 +115,85 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int lc = lane & 31;
   const int64_t r0 = (int64_t)job.ti * T, c0 = (int64_t)job.tj * T;
   const int h = (int)min<int64_t>(T, mt.H - r0), w = (int)min<int64_t>(T, mt.W - c0);
-  const ST* __restrict__ gp = reinterpret_cast<const ST*>(mt.g);
-  ST* __restrict__ mp = reinterpret_cast<ST*>(mt.m);
+  const int64_t ldm = mt.W;
+  const ST* tg = mt.g ? reinterpret_cast<const ST*>(mt.g) + r0 * ldm + c0 : nullptr;
+  ST* tm = reinterpret_cast<ST*>(mt.m) + r0 * ldm + c0;
 
-  // ---- tile load (+ momentum), in the accumulator layout: every thread owns
-  // the same elements from here to the final store.
-  float x32[MI][MI][16];
+  // ---- load phase: the tile in 8-element row chunks (thread t takes chunks
+  // t, t + 256, ...: consecutive threads read consecutive 16-byte pieces),
+  // momentum, M stored back, fp32 values staged row-major in LDS.
+  constexpr int CPR = TP / 8;                // chunks per row
+  constexpr int NCH = TP * CPR / kTileThreads;  // chunks per thread
+  static_assert(NCH * kTileThreads == TP * CPR, "whole chunks per thread");
   float sq = 0.f;
-  const ST* tg = gp ? gp + r0 * mt.W + c0 : nullptr;
-  ST* tm = mp + r0 * mt.W + c0;
+  if (mt.vec) {
+    // Whole chunks are either inside the matrix or outside it (8-aligned
+    // sides and origins); outside ones load the tile origin's chunk instead
+    // (always valid) and are zeroed.
+    float mv[NCH][8], gv[NCH][8];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    float mv[MI][16], gv[MI][16];
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * kTileThreads, row = ch / CPR, col = (ch % CPR) * 8;
+      const int64_t off = (row < h && col < w) ? (int64_t)row * ldm + col : 0;
+      load8(tm, off, mv[c]);
+      if (tg) load8(tg, off, gv[c]);
+    }
 #pragma unroll
-    for (int j = 0; j < MI; ++j)
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * kTileThreads, row = ch / CPR, col = (ch % CPR) * 8;
+      const bool ok = row < h && col < w;
+      float x[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wr + i * 32 + acc_row(v, lane), col = wc + j * 32 + lc;
-        // clamped to the tile origin outside the matrix: always in bounds
-        const int64_t o = (row < h && col < w) ? (int64_t)row * mt.W + col : 0;
-        mv[j][v] = St<ST>::ld(tm, o);
-        gv[j][v] = tg ? St<ST>::ld(tg, o) : 0.f;
+      for (int e = 0; e < 8; ++e) x[e] = tg ? St<ST>::round(fmaf(args.beta, mv[c][e], gv[c][e])) : mv[c][e];
+      if (tg && ok) store8(tm, (int64_t)row * ldm + col, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = ok ? x[e] : 0.f;
+        sq = fmaf(x[e], x[e], sq);
       }
+      f32x4_t* d = reinterpret_cast<f32x4_t*>(stg + row * SP + col);
+      d[0] = f32x4_t{x[0], x[1], x[2], x[3]};
+      d[1] = f32x4_t{x[4], x[5], x[6], x[7]};
+    }
+  } else {
+#pragma unroll 1
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * kTileThreads, row = ch / CPR, col = (ch % CPR) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = 0.f;
+        if (row < h && col + e < w) {
+          const int64_t o = (int64_t)row * ldm + col + e;
+          x = St<ST>::ld(tm, o);
+          if (tg) {
+            x = St<ST>::round(fmaf(args.beta, x, St<ST>::ld(tg, o)));
+            St<ST>::st(tm, o, x);
+          }
+        }
+        sq = fmaf(x, x, sq);
+        stg[row * SP + col + e] = x;
+      }
+    }
+  }
+  {
+    const double d = wave_sum((double)sq);
+    if (lane == 0) sred[wave] = d;
+  }
+  __syncthreads();
+  if (tid == 0) ssig = (float)(1.0 / (sqrt(((sred[0] + sred[1]) + sred[2]) + sred[3]) + (double)args.eps));
+  // Every thread takes its elements in the accumulator layout, which it owns
+  // from here to the final store.
+  float x32[MI][MI][16];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < MI; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = wr + i * 32 + acc_row(v, lane), col = wc + j * 32 + lc;
-        const bool ok = row < h && col < w;
-        float x = mv[j][v];
-        if (tg) {
-          x = St<ST>::round(fmaf(args.beta, x, gv[j][v]));
-          if (ok) St<ST>::st(tm, (int64_t)row * mt.W + col, x);
-        }
-        x = ok ? x : 0.f;
-        sq = fmaf(x, x, sq);
+        const float x = stg[(wr + i * 32 + acc_row(v, lane)) * SP + wc + j * 32 + lc];
         x32[i][j][v] = args.fold ? bf2f(f2bf(x)) : x;  // fold: X itself is kept in bf16
       }
-  }
+  __syncthreads();  // staging is overwritten by the operand copies below
   // X0 into LDS (unscaled): sX row-major, and sT = X^T for bf16 operands.
   auto store_x = [&]() {
 #pragma unroll
@@ -147,53 +203,67 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = wr + i * 32 + acc_row(4 * q, lane), col = wc + j * 32 + lc;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Op::put(&sX[(row + e) * LD + col], x32[i][j][4 * q + e]);
+          Op::put2col(&sX[row * LD + col], LD, x32[i][j][4 * q], x32[i][j][4 * q + 1]);
+          Op::put2col(&sX[(row + 2) * LD + col], LD, x32[i][j][4 * q + 2], x32[i][j][4 * q + 3]);
           if (kXT)
             Op::put4(&sT[col * LD + row], x32[i][j][4 * q], x32[i][j][4 * q + 1], x32[i][j][4 * q + 2],
                      x32[i][j][4 * q + 3]);
         }
   };
   store_x();
-  {
-    const double d = wave_sum((double)sq);
-    if (lane == 0) sred[wave] = d;
-    __syncthreads();
-    if (tid == 0) ssig = (float)(1.0 / (sqrt(((sred[0] + sred[1]) + sred[2]) + sred[3]) + (double)args.eps));
-    __syncthreads();
-  }
+  __syncthreads();
   const double sig = (double)ssig;
 
   f32x16_t acc[MI][MI];
   // acc += P Q^T over k in [0, TP): P rows from sp (row-major, k contiguous);
   // Q rows from sq (k contiguous) or, with q_kn, Q(n, k) = sq[k][n].
+  // Fragments of k-step ks are loaded one step ahead of the MFMAs that use
+  // them (register double buffer); scheduling barriers keep the compiler from
+  // sinking the loads next to their uses.
+  constexpr int NK = TP / Op::KSTEP;
+  static_assert(NK % 2 == 0, "k-steps come in pairs");
+  using Frag = typename std::conditional<sizeof(OT) == 2, bf16x8_t, float>::type;
   auto product = [&](const OT* sp, const OT* sq_, bool q_kn) {
-#pragma unroll 2
-    for (int k = 0; k < TP; k += Op::KSTEP) {
-      const int kk = k + (lane >> 5) * (Op::KSTEP / 2);
-      if constexpr (sizeof(OT) == 2) {
-        bf16x8_t fa[MI], fb[MI];
+    const int kl = (lane >> 5) * (Op::KSTEP / 2);
+    const OT* pa = sp + (wr + lc) * LD + kl;
+    const OT* pb = sq_ + (wc + lc) * LD + kl;
+    const OT* pt = sq_ + kl * LD + wc + lc;  // q_kn (fp32 only)
+    Frag fa[2][MI], fb[2][MI];
+    auto load = [&](int buf, int ks) {
+      const int k = ks * Op::KSTEP;
 #pragma unroll
-        for (int i = 0; i < MI; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(sp + (wr + i * 32 + lc) * LD + kk);
-#pragma unroll
-        for (int j = 0; j < MI; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(sq_ + (wc + j * 32 + lc) * LD + kk);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < MI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      } else {
-        float fa[MI], fb[MI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) fa[i] = sp[(wr + i * 32 + lc) * LD + kk];
-#pragma unroll
-        for (int j = 0; j < MI; ++j)
-          fb[j] = q_kn ? sq_[kk * LD + wc + j * 32 + lc] : sq_[(wc + j * 32 + lc) * LD + kk];
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < MI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < MI; ++i) {
+        if constexpr (sizeof(OT) == 2) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * LD + k);
+        else fa[buf][i] = pa[i * 32 * LD + k];
       }
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        if constexpr (sizeof(OT) == 2) fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * LD + k);
+        else fb[buf][j] = q_kn ? pt[k * LD + j * 32] : pb[j * 32 * LD + k];
+      }
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < MI; ++j) {
+          if constexpr (sizeof(OT) == 2)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        }
+    };
+    load(0, 0);
+#pragma unroll(sizeof(OT) == 2 ? NK / 2 : 4)
+    for (int ks = 0; ks < NK; ks += 2) {
+      load(1, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(0, min(ks + 2, NK - 1));  // the last one re-reads a valid step, unused
+      __builtin_amdgcn_sched_barrier(0);
+      mma(1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Symmetric result (A or B) = acc * sc into sAB through the packed
@@ -281,20 +351,44 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2)
         for (int v = 0; v < 16; ++v) x32[i][j][v] = (float)((double)x32[i][j][v] * sig);
   }
 
-  // ---- cropped tile out, sum of squares of the stored values
-  float osq = 0.f;
+  // ---- store phase: the result staged row-major in LDS (the last update's
+  // operand reads are behind a barrier), then written as 8-element chunks,
+  // cropped to the matrix; sum of squares of the stored values.
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < MI; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wr + i * 32 + acc_row(v, lane), col = wc + j * 32 + lc;
-        if (row < h && col < w) {
-          const float s = store_dyn(mt.out, (r0 + row) * mt.W + c0 + col, x32[i][j][v], mt.out_dtype);
-          osq = fmaf(s, s, osq);
+      for (int v = 0; v < 16; ++v) stg[(wr + i * 32 + acc_row(v, lane)) * SP + wc + j * 32 + lc] = x32[i][j][v];
+  __syncthreads();
+  float osq = 0.f;
+  const int64_t obase = r0 * ldm + c0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = tid + c * kTileThreads, row = ch / CPR, col = (ch % CPR) * 8;
+    if (row >= h || col >= w) continue;
+    const f32x4_t* sp = reinterpret_cast<const f32x4_t*>(stg + row * SP + col);
+    const f32x4_t lo = sp[0], hi = sp[1];
+    float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const int64_t o = obase + (int64_t)row * ldm + col;
+    if (mt.out_dtype == DT_BF16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf2f(f2bf(x[e]));
+    }
+    if (mt.vec) {
+      if (mt.out_dtype == DT_BF16) store8(reinterpret_cast<bf16_t*>(mt.out), o, x);
+      else store8(reinterpret_cast<float*>(mt.out), o, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) osq = fmaf(x[e], x[e], osq);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < w) {
+          store_dyn(mt.out, o + e, x[e], mt.out_dtype);
+          osq = fmaf(x[e], x[e], osq);
         }
-      }
+    }
+  }
   block_partial2<kTileThreads>((double)osq, 0.0, args.st, mt.onorm_slot, job.part);
 }
 

@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstdlib>
 
 #include "muonh.h"
@@ -206,6 +207,10 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       tm.W = m.W;
       tm.out_dtype = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
       tm.onorm_slot = s_onorm0 + mi;
+      // 8-element (16 / 32-byte) chunks need 8-aligned rows and tile origins
+      // and 16-byte aligned buffers.
+      auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+      tm.vec = (m.W % 8 == 0 && T % 8 == 0 && a16(tm.g) && a16(tm.m) && a16(tm.out)) ? 1 : 0;
       const int idx = (int)t.tile_mats.size();
       t.tile_mats.push_back(tm);
       for (int a = 0; a < m.ntr; ++a)
