@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--K", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-sets", type=int, default=4)
+    ap.add_argument("--ws-limit-mib", type=int, default=0,
+                    help="workspace limit (MiB): matrices run in chunks that fit it; 0 = library default")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -136,7 +138,8 @@ def main():
     shapes, wdesc = workload_shapes(args.workload)
     K = args.K
     Ws, Ms, Gsets, rho = make_device_inputs(shapes, args.grad_sets, 1234, torch)
-    q = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision)
+    ws_limit = args.ws_limit_mib << 20
+    q = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision, workspace_limit=ws_limit)
     if args.copy_calib_mib:
         # a plain copy kernel of known size: reads and writes copy_calib_mib MiB each
         n = args.copy_calib_mib * (1 << 20) // 4
@@ -149,7 +152,7 @@ def main():
 
     def step(i):
         mm.muonh_step(Ws, Gsets[i % len(Gsets)], Ms, eta=0.02, beta=0.95, K=K, rho=rho, tile_T=args.tile,
-                      ns_precision=args.ns_precision)
+                      ns_precision=args.ns_precision, workspace_limit=ws_limit)
 
     for i in range(args.warmup):
         step(i)
@@ -220,7 +223,7 @@ def main():
                                f"{'tiled T=' + str(args.tile) if args.tile else 'full-matrix'}, "
                                f"bf16 grads/momentum, fp32 master weights, Hyperball rho=||W0||_F",
                    "matrices": len(shapes), "K": K, "tile_T": args.tile, "ns_precision": args.ns_precision,
-                   "elements": sum(h * w for h, w in shapes)},
+                   "elements": sum(h * w for h, w in shapes), "chunks": q["chunks"]},
         "ns_tflops": round(ns_tflops, 2) if ns_tflops else None,
         "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
         "ns_ms_per_step": round(ns_ms, 4),

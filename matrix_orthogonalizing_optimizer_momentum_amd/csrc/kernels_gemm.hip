@@ -183,15 +183,59 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
+  // Accumulator seed.  G3 starts from a X (the a X term of the update; 1 * X0
+  // for K = 0) and G2 from (b / c) A, so B = c (A A + (b / c) A) (c = 0: B =
+  // b A with no product); G1 starts from zero.  The seed is read in the
+  // accumulator layout (32 lanes cover 32 consecutive columns) before the
+  // first operand stage, so its latency hides behind the operand loads and
+  // the epilogue issues no global reads.
+  const float g2_seed = args.c != 0.f ? args.b / args.c : args.b;
+  const float g2_mul = args.c != 0.f ? args.c : 1.f;
   f32x16_t acc[MI][NI];
+  {
+    const int rbase = row0 + wm * WM + 4 * (lane >> 5), cbase = col0 + wn * WN + (lane & 31);
+    if (PHASE == kG1) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+        for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    } else if (PHASE == kG3 && !args.first && u.x32 != nullptr) {
+      const MUONH_GLOBAL float* src = gmem(u.x32);
+      const float coef = args.no_mma ? 1.f : args.a;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = rbase + i * 32 + 8 * (v >> 2) + (v & 3), col = cbase + j * 32;
+            const bool ok = row < u.r && col < u.ld_s;
+            const float x = src[ok ? (int64_t)row * u.ld_s + col : 0];  // clamped: always in bounds
+            acc[i][j][v] = ok ? coef * x : 0.f;
+          }
+    } else {
+      // G2: A (r x ld_r); G3: X in operand precision (first iteration, or no
+      // fp32 master)
+      const T* src = reinterpret_cast<const T*>(PHASE == kG2 ? u.a : u.x);
+      const int64_t ld = PHASE == kG2 ? u.ld_r : u.ld_s;
+      const float coef = PHASE == kG2 ? g2_seed : (args.no_mma ? 1.f : args.a);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = rbase + i * 32 + 8 * (v >> 2) + (v & 3), col = cbase + j * 32;
+            const bool ok = row < u.r && col < ld;
+            const float x = St<T>::ld(src, ok ? (int64_t)row * ld + col : 0);
+            acc[i][j][v] = ok ? coef * x : 0.f;
+          }
+    }
+  }
 
-  const int nstage = args.no_mma ? 0 : K / BK;
+  const int nstage = (args.no_mma || (PHASE == kG2 && args.c == 0.f)) ? 0 : K / BK;
   // Global prefetch ring: stage ks+NPF's loads are issued when stage ks
   // starts, so each load has NPF-1 stages of MFMA work to arrive before its
   // LDS store; LDS itself is double buffered.  The ring is indexed only by
@@ -328,27 +372,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
   const bool o_vec = (u.o_dtype == DT_BF16) ? ((u.o_ld % 8) == 0 && ((uintptr_t)u.o_ptr % 16) == 0)
                                             : ((u.o_ld % 4) == 0 && ((uintptr_t)u.o_ptr % 16) == 0);
   T* const out12 = reinterpret_cast<T*>(PHASE == kG1 ? u.a : u.b);
-  const float a_coef = args.no_mma ? 1.f : args.a;
 
 #pragma unroll 1
   for (int sl = 0; sl < BM / SLAB; ++sl) {
-    // This slab's global reads first (the a*X term of G3, the b*A term of
-    // G2): one memory round trip per slab, overlapped with the staging.
-    float pv[RB][4];
-    if (PHASE != kG1) {
-#pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const int grow = row0 + sl * SLAB + b * ROWS_PER_IT + rsub;
-        const int gcol = col0 + gran * 4;
-        if (PHASE == kG2) {
-          if (grow < r && gcol < u.ld_r) load4(reinterpret_cast<const T*>(u.a), (int64_t)grow * u.ld_r + gcol, pv[b]);
-        } else if (grow < r && gcol < u.ld_s) {
-          const int64_t xi = (int64_t)grow * u.ld_s + gcol;
-          if (!args.first && u.x32 != nullptr) load4(u.x32, xi, pv[b]);
-          else load4(reinterpret_cast<const T*>(u.x), xi, pv[b]);
-        }
-      }
-    }
     __syncthreads();  // LDS free (main loop or previous slab done)
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -386,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
             for (int e = 0; e < 4; ++e) v[e] = (gcol + e < r) ? v[e] * sc : 0.f;
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (gcol + e < r) ? fmaf(args.c, v[e], args.b * pv[b][e]) : 0.f;
+            for (int e = 0; e < 4; ++e) v[e] = (gcol + e < r) ? g2_mul * v[e] : 0.f;
           }
           store4(out12, (int64_t)grow * u.ld_r + gcol, v);
         } else {
@@ -394,12 +420,12 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
           for (int e = 0; e < 4; ++e) v[e] = 0.f;
         }
       } else {
-        // G3: X(row, col) <- a X(row, col) + acc (times sig on the first iteration)
+        // G3: X(row, col) <- acc = a X + B X (times sig on the first iteration)
         if (grow < r && gcol < u.ld_s) {
           const int64_t xi = (int64_t)grow * u.ld_s + gcol;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float t = fmaf(a_coef, pv[b][e], v[e]);
+            float t = v[e];
             if (args.first) t = (float)((double)t * sig);
             v[e] = (gcol + e < u.s) ? t : 0.f;
           }

@@ -85,10 +85,12 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 }  // namespace
 
 // TP: padded tile side (64 or 128).  ST: momentum / input storage type,
-// OT: Newton-Schulz operand type.
+// OT: Newton-Schulz operand type.  With bf16 operands two workgroups fit one
+// CU's LDS, so registers are capped for two waves per SIMD; a 128-side fp32
+// tile takes most of the LDS on its own.
 template <typename ST, typename OT, int TP>
-__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_tile_ns(const TileMat* __restrict__ mats,
-                                                          const TileJob* __restrict__ jobs, TileArgs args) {
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(sizeof(OT) == 2 ? 2 : 1)))
+void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ jobs, TileArgs args) {
   using Op = TileOp<OT>;
   constexpr int LD = TP + Op::PAD;           // LDS pitch (elements)
   constexpr int WT = TP / 2;                 // wave tile side (2 x 2 waves)
@@ -254,7 +256,8 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2)
         }
     };
     load(0, 0);
-#pragma unroll(sizeof(OT) == 2 ? NK / 2 : 4)
+    constexpr int kUnroll = sizeof(OT) == 2 ? NK / 2 : 4;
+#pragma unroll kUnroll
     for (int ks = 0; ks < NK; ks += 2) {
       load(1, ks + 1);
       __builtin_amdgcn_sched_barrier(0);
