@@ -25,9 +25,9 @@ struct SlotTable {
 };
 
 // One Newton-Schulz unit: a whole matrix, or one HiMuon tile handled as a
-// T x T matrix.  Logical X is r x s with r <= s.
-//   X layout : r rows, leading dim ld_s = pad(s)
-//   XT layout: s rows, leading dim ld_r = pad(r)
+// T x T matrix.  Logical X is r x s with r <= s; it is kept only as X^T:
+//   XT layout: ld_s = pad(s) rows of ld_r = pad(r) elements, the padding
+//   (rows >= s, columns >= r) zero.
 struct NsUnit {
   int32_t r, s;
   int32_t ld_s, ld_r;
@@ -41,9 +41,8 @@ struct NsUnit {
   int32_t g3_cols;      // number of G3 column tiles of this unit (for partial numbering)
   int64_t o_ld;
   void* o_ptr;          // output base, already offset to the unit's origin
-  void* x;              // op-dtype X (X layout)
   void* xt[2];          // op-dtype X^T ping-pong (XT layout)
-  float* x32;           // fp32 master X (X layout) or nullptr
+  float* x32;           // fp32 master X^T (XT layout) or nullptr
   void* a;              // op-dtype A = X X^T (r rows, ld_r)
   void* b;              // op-dtype B = b A + c A A (r rows, ld_r)
 };
@@ -65,7 +64,7 @@ struct MomMat {
   int32_t unit0;        // first NsUnit of this matrix
   int32_t ntc;          // tiles per row (tile mode)
   int32_t nbc;          // 64-wide column blocks over the padded extent
-  int32_t write_x;      // 1: write X0 / X0^T into the units' workspace
+  int32_t write_x;      // 1: write X0^T into the units' workspace
 };
 
 // One 64 x 64 block of a momentum / prep launch.

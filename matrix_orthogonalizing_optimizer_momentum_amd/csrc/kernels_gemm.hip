@@ -10,24 +10,32 @@
 //                                       iteration; the last iteration writes O
 //                                       in the caller's layout and its sum of
 //                                       squares)
-// Every product here is D[i][j] = sum_k P[i][k] Q[j][k] with both operands
-// stored K-contiguous: G1 reads X twice, G2 reads A twice (A = A^T), G3 reads
-// B and X^T.  X^T is kept as a second copy that G3's epilogue writes, so no
-// operand is ever transposed on load.  A and B are symmetric, so G1 and G2
-// only compute tiles on or above the diagonal and mirror the rest.
+// X lives only as X^T (s rows of r, both sides zero-padded to 64), in operand
+// precision, plus an fp32 master copy in the same layout when requested.
+// Every product is D[i][j] = sum_k P[i][k] Q[j][k]:
+//   G2 reads A twice and G3 reads B and X^T with K-contiguous rows;
+//   G1 reads X^T tiles [k][m] and forms K-contiguous MFMA fragments with
+//   gfx950's transposing LDS read (ds_read_b64_tr_b16) for bf16, or plain
+//   column reads for fp32.
+// G3's accumulator is seeded with a X read from X^T (4 consecutive rows of X
+// per lane are contiguous in X^T), and the new X^T (and fp32 master) is
+// stored straight from the accumulator layout with packed 8 / 16-byte stores.
+// A and B are symmetric: G1 and G2 compute tiles on or above the diagonal and
+// mirror the rest.
 //
 // A launch covers every unit (matrix or HiMuon tile) of a chunk through a job
 // list of BM x BN output tiles; job order is remapped so that the jobs one XCD
 // runs are contiguous in the list (operand panels shared in its L2).
 // Operands are bf16 (v_mfma_f32_32x32x16_bf16) or fp32
 // (v_mfma_f32_32x32x2_f32), accumulation is fp32, LDS stages are double
-// buffered with a register prefetch of the next stage, and MFMA fragments are
-// double buffered in registers.
+// buffered with a register prefetch ring of the next stages, and MFMA
+// fragments are double buffered in registers.
 #include "common.h"
 
 namespace muonh {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 template <typename T> struct Mf;
@@ -59,7 +67,7 @@ struct NsIterArgs {
   float eps;          // pre-scale eps
   int first;          // iteration 0: fold the pre-scale
   int last;           // final iteration: write O and its norm
-  int cur;            // X^T ping-pong index read by G3
+  int cur;            // X^T ping-pong index read this iteration (G3 writes the other)
   int no_mma;         // K == 0: O = X0 / (||X0|| + eps) through the G3 epilogue
   int njobs;
   SlotTable st;
@@ -128,24 +136,46 @@ __device__ __forceinline__ float store_out8(void* p, int64_t i, const float (&v)
   return sq;
 }
 
-// Block tile BM x BN, 4 waves in 2 x 2, each wave (BM/2) x (BN/2) built from
-// 32 x 32 MFMA tiles; BK elements of K per LDS stage.
+// Two transposing LDS reads (gfx950 ds_read_b64_tr_b16) form one bf16 MFMA
+// fragment: within each 16-lane group, lane j addresses row j / 4, elements
+// 4 (j % 4) .. + 3 of a [k][m] tile, and lane i receives element i of rows
+// 0..3 (4 consecutive k for one m); p1 covers the next 4 rows.
+__device__ __forceinline__ bf16x8_t ld_tr8(const bf16_t* p0, const bf16_t* p1) {
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p0);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p1);
+  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Block tile BM x BN (BM == BN), 4 waves in 2 x 2, each wave (BM/2) x (BN/2)
+// built from 32 x 32 MFMA tiles; BK elements of K per LDS stage.
 template <typename T, int PHASE, int BM, int BN, int BK>
 __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__ units,
                                                      const GemmJob* __restrict__ jobs, NsIterArgs args) {
   using M = Mf<T>;
-  constexpr int VEC = M::VEC, KSTEP = M::KSTEP, LDK = BK + M::PAD;
+  constexpr bool TR = PHASE == kG1;  // operands are X^T tiles stored [k][m]
+  constexpr int VEC = M::VEC, KSTEP = M::KSTEP;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int CPR = BK / VEC;                          // 16-byte chunks per row
-  constexpr int P_LOADS = BM * CPR / kThreads;           // per thread per stage
-  constexpr int Q_LOADS = BN * CPR / kThreads;
-  static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "tile/thread mismatch");
+  // LDS operand tiles: K-contiguous rows [m][k] with pitch LDK, or (TR)
+  // [k][m] rows of BM elements, row k rotated by ROT * (k % RN) elements so
+  // that the rows one fragment read touches land in different banks.
+  constexpr int LDK = BK + M::PAD;
+  constexpr int RN = sizeof(T) == 2 ? 4 : 2, ROT = 32;
+  constexpr int PSZ = TR ? BK * BM : BM * LDK;  // elements per operand stage
+  constexpr int QSZ = TR ? BK * BN : BN * LDK;
+  constexpr int CPR = TR ? BM / VEC : BK / VEC;  // 16-byte chunks per LDS row
+  constexpr int P_LOADS = BM * BK / VEC / kThreads;
+  constexpr int Q_LOADS = BN * BK / VEC / kThreads;
+  static_assert(BM == BN, "square block tiles");
+  static_assert(BM * BK % (VEC * kThreads) == 0, "tile/thread mismatch");
   static_assert(BK % KSTEP == 0 && kPad % BK == 0, "K stage must divide the padding granule");
+  static_assert(!TR || (BM % (ROT * RN) == 0 && BK % (RN * KSTEP / 2) == 0), "rotation layout");
 
   // Main loop: P and Q stages (double buffered).  The epilogue reuses the
   // same LDS for its fp32 slabs.
-  constexpr int kStage = 2 * (BM + BN) * LDK * (int)sizeof(T);
+  constexpr int kStage = 2 * (PSZ + QSZ) * (int)sizeof(T);
   // Slab rows: fit the stage buffers, and keep the batched row-pass reads of
   // a slab (SLAB * BN / kThreads values per thread) within 64 registers.
   constexpr int SLAB_LDS = (BM * BN * 4 <= kStage) ? BM : ((BM / 2) * BN * 4 <= kStage ? BM / 2 : BM / 4);
@@ -153,8 +183,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
   constexpr int SLAB = SLAB_LDS < SLAB_REG ? SLAB_LDS : SLAB_REG;
   constexpr int kSmem = kStage > SLAB * BN * 4 ? kStage : SLAB * BN * 4;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
-  T (*sP)[BM * LDK] = reinterpret_cast<T (*)[BM * LDK]>(smem);
-  T (*sQ)[BN * LDK] = reinterpret_cast<T (*)[BN * LDK]>(smem + 2 * BM * LDK * sizeof(T));
+  T* const sP = reinterpret_cast<T*>(smem);  // [2][PSZ]
+  T* const sQ = sP + 2 * PSZ;                // [2][QSZ]
 
   // XCD-aware job order: hardware deals blocks round-robin over 8 XCDs; give
   // each XCD a contiguous run of the job list.
@@ -166,73 +196,66 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
   }
   const GemmJob job = jobs[job_id];
   const NsUnit u = units[job.unit];
+  const T* const xt_in = reinterpret_cast<const T*>(args.cur ? u.xt[1] : u.xt[0]);
 
+  // operands: G1 X^T (as [k][m] tiles); G2 A, A; G3 B, X^T (K-contiguous rows)
   const T* P;
   const T* Q;
   int64_t ldP, ldQ;
   int Prows, Qrows, K;
   if (PHASE == kG1) {
-    P = reinterpret_cast<const T*>(u.x); Q = P; ldP = ldQ = u.ld_s; Prows = Qrows = u.r; K = u.ld_s;
+    P = xt_in; Q = xt_in; ldP = ldQ = u.ld_r; Prows = Qrows = u.ld_s; K = u.ld_s;
   } else if (PHASE == kG2) {
     P = reinterpret_cast<const T*>(u.a); Q = P; ldP = ldQ = u.ld_r; Prows = Qrows = u.r; K = u.ld_r;
   } else {
-    P = reinterpret_cast<const T*>(u.b); Q = reinterpret_cast<const T*>((args.cur ? u.xt[1] : u.xt[0]));
-    ldP = u.ld_r; ldQ = u.ld_r; Prows = u.r; Qrows = u.s; K = u.ld_r;
+    P = reinterpret_cast<const T*>(u.b); Q = xt_in;
+    ldP = u.ld_r; ldQ = u.ld_r; Prows = u.r; Qrows = u.ld_s; K = u.ld_r;
   }
   const int row0 = job.tm * BM, col0 = job.tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
+  // Pre-scale of the first iteration, read now so its latency is hidden.
+  double sig = 1.0;
+  if (args.first) sig = 1.0 / (sqrt(args.st.sums[2 * u.norm_slot]) + (double)args.eps);
+
   // Accumulator seed.  G3 starts from a X (the a X term of the update; 1 * X0
   // for K = 0) and G2 from (b / c) A, so B = c (A A + (b / c) A) (c = 0: B =
-  // b A with no product); G1 starts from zero.  The seed is read in the
-  // accumulator layout (32 lanes cover 32 consecutive columns) before the
-  // first operand stage, so its latency hides behind the operand loads and
-  // the epilogue issues no global reads.
+  // b A with no product); G1 starts from zero.  In the accumulator layout a
+  // lane holds rows m..m+3 of one column n: X(m..m+3, n) is X^T(n, m..m+3),
+  // and A(m..m+3, n) is A(n, m..m+3), so each group of 4 is one 8 / 16-byte
+  // load, issued before the first operand stage.
   const float g2_seed = args.c != 0.f ? args.b / args.c : args.b;
   const float g2_mul = args.c != 0.f ? args.c : 1.f;
+  const int lrow = 4 * (lane >> 5), lcol = lane & 31;  // accumulator-layout offsets
   f32x16_t acc[MI][NI];
-  {
-    const int rbase = row0 + wm * WM + 4 * (lane >> 5), cbase = col0 + wn * WN + (lane & 31);
-    if (PHASE == kG1) {
+  if (PHASE == kG1) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    } else if (PHASE == kG3 && !args.first && u.x32 != nullptr) {
-      const MUONH_GLOBAL float* src = gmem(u.x32);
-      const float coef = args.no_mma ? 1.f : args.a;
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  } else {
+    const bool m32 = PHASE == kG3 && !args.first && u.x32 != nullptr;  // fp32 master
+    const T* src = PHASE == kG2 ? reinterpret_cast<const T*>(u.a) : xt_in;
+    const int nlim = PHASE == kG2 ? u.r : u.ld_s;  // rows of the source
+    const float coef = PHASE == kG2 ? g2_seed : (args.no_mma ? 1.f : args.a);
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = rbase + i * 32 + 8 * (v >> 2) + (v & 3), col = cbase + j * 32;
-            const bool ok = row < u.r && col < u.ld_s;
-            const float x = src[ok ? (int64_t)row * u.ld_s + col : 0];  // clamped: always in bounds
-            acc[i][j][v] = ok ? coef * x : 0.f;
-          }
-    } else {
-      // G2: A (r x ld_r); G3: X in operand precision (first iteration, or no
-      // fp32 master)
-      const T* src = reinterpret_cast<const T*>(PHASE == kG2 ? u.a : u.x);
-      const int64_t ld = PHASE == kG2 ? u.ld_r : u.ld_s;
-      const float coef = PHASE == kG2 ? g2_seed : (args.no_mma ? 1.f : args.a);
+        for (int q = 0; q < 4; ++q) {
+          const int m0 = row0 + wm * WM + i * 32 + 8 * q + lrow, n = col0 + wn * WN + j * 32 + lcol;
+          const bool ok = n < nlim && m0 < u.ld_r;
+          const int64_t o = ok ? (int64_t)n * u.ld_r + m0 : 0;  // clamped: always in bounds
+          float x[4];
+          if (m32) load4(u.x32, o, x);
+          else load4(src, o, x);
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = rbase + i * 32 + 8 * (v >> 2) + (v & 3), col = cbase + j * 32;
-            const bool ok = row < u.r && col < ld;
-            const float x = St<T>::ld(src, ok ? (int64_t)row * ld + col : 0);
-            acc[i][j][v] = ok ? coef * x : 0.f;
-          }
-    }
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = ok ? coef * x[e] : 0.f;
+        }
   }
 
   const int nstage = (args.no_mma || (PHASE == kG2 && args.c == 0.f)) ? 0 : K / BK;
@@ -246,54 +269,104 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
   constexpr int NPF = (MI * NI >= 16) ? 1 : MUONH_NPF;
   constexpr int NL = P_LOADS + Q_LOADS;
   u32x4_t ring[NPF][NL];
-  // Per-thread load coordinates (fixed for the whole K loop).
+  // Per-thread load coordinates (fixed for the whole K loop) and the step
+  // between stages, in 16-byte units.
   const MUONH_GLOBAL u32x4_t* gsrc[NL];
+  const int64_t kstride = TR ? (int64_t)BK * u.ld_r / VEC : BK / VEC;
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
     const bool isp = l < P_LOADS;
     const int ll = isp ? l : l - P_LOADS;
     const int c = (tid + ll * kThreads) % CPR, rr = (tid + ll * kThreads) / CPR;
-    // Rows past the operand's edge are clamped to its last row instead of
-    // masked: the loads stay branch-free, and those rows only feed output
-    // rows / columns >= r (or >= s) that the epilogue writes as zeros.
-    const int gr = isp ? min(row0 + rr, Prows - 1) : min(col0 + rr, Qrows - 1);
-    const T* base = isp ? P + (int64_t)gr * ldP : Q + (int64_t)gr * ldQ;
-    gsrc[l] = reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(base + c * VEC));
+    const T* base;
+    if (TR) {
+      // row rr of the stage (k), 8 consecutive m; chunks past the padded
+      // width are clamped to its last chunk (they feed only outputs >= ld_r)
+      const int mc = min((isp ? row0 : col0) + c * VEC, u.ld_r - VEC);
+      base = P + (int64_t)rr * ldP + mc;
+    } else {
+      // Rows past the operand's edge are clamped to its last row instead of
+      // masked: the loads stay branch-free, and those rows only feed output
+      // rows / columns the epilogue writes as zeros or not at all.
+      const int gr = isp ? min(row0 + rr, Prows - 1) : min(col0 + rr, Qrows - 1);
+      base = (isp ? P + (int64_t)gr * ldP : Q + (int64_t)gr * ldQ) + c * VEC;
+    }
+    gsrc[l] = reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(base));
   }
-#define MUONH_GLOAD(slot, ks)                                                 \
-  do {                                                                        \
-    const int kofs_ = (ks) * BK / VEC;                                        \
-    _Pragma("unroll") for (int l = 0; l < NL; ++l) ring[slot][l] = gsrc[l][kofs_]; \
+#define MUONH_GLOAD(slot, ks)                                                              \
+  do {                                                                                     \
+    const int64_t kofs_ = (int64_t)(ks) * kstride;                                         \
+    _Pragma("unroll") for (int l = 0; l < NL; ++l) ring[slot][l] = gsrc[l][kofs_];         \
   } while (0)
-#define MUONH_LSTORE(buf, slot)                                                              \
-  do {                                                                                       \
-    _Pragma("unroll") for (int l = 0; l < NL; ++l) {                                         \
-      const bool isp_ = l < P_LOADS;                                                         \
-      const int ll_ = isp_ ? l : l - P_LOADS;                                                \
-      const int c_ = (tid + ll_ * kThreads) % CPR, r_ = (tid + ll_ * kThreads) / CPR;        \
-      T* dst_ = isp_ ? &sP[buf][r_ * LDK + c_ * VEC] : &sQ[buf][r_ * LDK + c_ * VEC];        \
-      *reinterpret_cast<u32x4_t*>(dst_) = ring[slot][l];                                    \
-    }                                                                                        \
+#define MUONH_LSTORE(buf, slot)                                                                        \
+  do {                                                                                                 \
+    _Pragma("unroll") for (int l = 0; l < NL; ++l) {                                                   \
+      const bool isp_ = l < P_LOADS;                                                                   \
+      const int ll_ = isp_ ? l : l - P_LOADS;                                                          \
+      const int c_ = (tid + ll_ * kThreads) % CPR, r_ = (tid + ll_ * kThreads) / CPR;                  \
+      const int o_ = TR ? r_ * BM + ((c_ * VEC + ROT * (r_ % RN)) & (BM - 1)) : r_ * LDK + c_ * VEC;   \
+      T* dst_ = isp_ ? sP + (buf) * PSZ + o_ : sQ + (buf) * QSZ + o_;                                  \
+      *reinterpret_cast<u32x4_t*>(dst_) = ring[slot][l];                                              \
+    }                                                                                                  \
   } while (0)
 
+  // Per-lane fragment offsets inside an operand stage.
+  int pofs[MI], qofs[NI];
+  if (TR) {
+    if (sizeof(T) == 2) {
+      // lane = 16 g + j: rows 8 (g / 2) + j / 4 (+ 4 for the second read),
+      // elements 16 (g % 2) + 4 (j % 4) of the 32-wide block
+      const int j16 = lane & 15, g = lane >> 4;
+      const int krow = 8 * (g >> 1) + (j16 >> 2);
+      const int msub = 16 * (g & 1) + 4 * (j16 & 3) + ROT * (j16 >> 2);  // krow % 4 == j16 / 4
+#pragma unroll
+      for (int i = 0; i < MI; ++i) pofs[i] = krow * BM + ((wm * WM + i * 32 + msub) & (BM - 1));
+#pragma unroll
+      for (int j = 0; j < NI; ++j) qofs[j] = krow * BM + ((wn * WN + j * 32 + msub) & (BM - 1));
+    } else {
+      // fp32: lane reads k = lane / 32, m = lane % 32 (row k rotated by k % 2)
+      const int krow = lane >> 5, msub = (lane & 31) + ROT * krow;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) pofs[i] = krow * BM + ((wm * WM + i * 32 + msub) & (BM - 1));
+#pragma unroll
+      for (int j = 0; j < NI; ++j) qofs[j] = krow * BM + ((wn * WN + j * 32 + msub) & (BM - 1));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) pofs[i] = (wm * WM + i * 32 + lcol) * LDK + (lane >> 5) * (KSTEP / 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) qofs[j] = (wn * WN + j * 32 + lcol) * LDK + (lane >> 5) * (KSTEP / 2);
+  }
+  // Fragment of k-step kk from an operand stage.
+  auto frag = [&](const T* stage, int ofs, int kk) -> typename M::frag {
+    if constexpr (!TR) {
+      return M::ld(stage + ofs + kk * KSTEP);
+    } else if constexpr (sizeof(T) == 2) {
+      const bf16_t* p = reinterpret_cast<const bf16_t*>(stage) + ofs + kk * KSTEP * BM;
+      return ld_tr8(p, p + 4 * BM);
+    } else {
+      return stage[ofs + kk * KSTEP * BM];
+    }
+  };
+
   auto compute = [&](int buf) {
-    const T* sp = sP[buf] + (wm * WM + (lane & 31)) * LDK + (lane >> 5) * (KSTEP / 2);
-    const T* sq = sQ[buf] + (wn * WN + (lane & 31)) * LDK + (lane >> 5) * (KSTEP / 2);
+    const T* sp = sP + buf * PSZ;
+    const T* sq = sQ + buf * QSZ;
     // Fragments double-buffered in registers: step kk+1's LDS reads are in
     // flight while step kk's MFMAs run.
     typename M::frag fa[2][MI], fb[2][NI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[0][i] = M::ld(sp + i * 32 * LDK);
+    for (int i = 0; i < MI; ++i) fa[0][i] = frag(sp, pofs[i], 0);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) fb[0][j] = M::ld(sq + j * 32 * LDK);
+    for (int j = 0; j < NI; ++j) fb[0][j] = frag(sq, qofs[j], 0);
 #pragma unroll
     for (int kk = 0; kk < BK / KSTEP; ++kk) {
       const int c = kk & 1;
       if (kk + 1 < BK / KSTEP) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) fa[c ^ 1][i] = M::ld(sp + i * 32 * LDK + (kk + 1) * KSTEP);
+        for (int i = 0; i < MI; ++i) fa[c ^ 1][i] = frag(sp, pofs[i], kk + 1);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) fb[c ^ 1][j] = M::ld(sq + j * 32 * LDK + (kk + 1) * KSTEP);
+        for (int j = 0; j < NI; ++j) fb[c ^ 1][j] = frag(sq, qofs[j], kk + 1);
       }
       // Fence: the next step's reads are issued before this step's MFMAs
       // (the default schedule sinks each read next to its use and waits).
@@ -340,30 +413,54 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
 #undef MUONH_GLOAD
 #undef MUONH_LSTORE
 
+  const int r = u.r;
+  // ------------------------------------------------ G3, not the last iteration
+  // The new X^T (and fp32 master) straight from the accumulators: rows
+  // m..m+3 of column n are X^T(n, m..m+3).  Rows >= r and columns >= s are
+  // zero padding.
+  if (PHASE == kG3 && !args.last) {
+    T* const xo = reinterpret_cast<T*>(args.cur ? u.xt[0] : u.xt[1]);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m0 = row0 + wm * WM + i * 32 + 8 * q + lrow, n = col0 + wn * WN + j * 32 + lcol;
+          if (n < u.ld_s && m0 < u.ld_r) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float t = acc[i][j][4 * q + e];
+              if (args.first) t = (float)((double)t * sig);
+              v[e] = (m0 + e < r && n < u.s) ? t : 0.f;
+            }
+            const int64_t o = (int64_t)n * u.ld_r + m0;
+            store4(xo, o, v);
+            if (u.x32 != nullptr) store4(u.x32, o, v);
+          }
+        }
+    return;
+  }
+
   // ----------------------------------------------------------------- epilogue
-  // The fp32 tile goes through LDS in slabs of SLAB rows, stored with its
-  // 16-byte granules XOR-swizzled by (row / 8) so that the accumulator
-  // writes, the row reads (one granule per lane) and the column reads (8 rows
-  // per lane) avoid bank conflicts.  Outputs are then written with
-  // row-contiguous accesses: a row pass (X, x32, A, B, O in X orientation)
-  // and a column pass (X^T for G3, O when the caller's layout is transposed,
-  // and the mirrored tile of the symmetric A and B).
+  // G1 / G2 (A or B and their mirrored tiles) and the last G3 (O in the
+  // caller's layout).  The fp32 tile goes through LDS in slabs of SLAB rows,
+  // stored with its 16-byte granules XOR-swizzled by (row / 8) so that the
+  // accumulator writes, the row reads (one granule per lane) and the column
+  // reads (8 rows per lane) avoid bank conflicts.  Outputs are then written
+  // with row-contiguous accesses: a row pass (A, B, O in X orientation) and a
+  // column pass (mirrored A / B tiles, O when the caller's layout is X^T).
   float* Ct = reinterpret_cast<float*>(smem);
   constexpr int GPR = BN / 4;  // granules per tile row
   static_assert(GPR >= 16, "swizzle needs 16 granules per row");
   auto cidx = [](int rl, int cl) -> int { return rl * BN + ((((cl >> 2) ^ ((rl >> 3) & 15))) << 2) + (cl & 3); };
 
-  double sig = 1.0;
-  if (args.first) {
-    const double n2 = args.st.sums[2 * u.norm_slot];
-    sig = 1.0 / (sqrt(n2) + (double)args.eps);
-  }
-  const int r = u.r;
   float osq = 0.f;
   const bool mirror = (PHASE != kG3) && (job.tm != job.tn);  // symmetric outputs: also write the transpose
-  const bool col_pass = (PHASE == kG3) ? (!args.last || u.o_trans) : mirror;
+  const bool col_pass = (PHASE == kG3) ? (u.o_trans != 0) : mirror;
   constexpr int ROWS_PER_IT = kThreads / GPR;    // row pass: one granule (4 values) per thread
-  constexpr int RB = SLAB / ROWS_PER_IT;         // row-pass iterations per slab (all batched)
+  constexpr int RB = SLAB / ROWS_PER_IT;         // row-pass iterations per slab
   constexpr int CPC = SLAB / 8;                  // column pass: 8-row chunks per slab column
   constexpr int COLS_PER_IT = kThreads / CPC;
   static_assert(SLAB % ROWS_PER_IT == 0 && kThreads % CPC == 0 && BN % COLS_PER_IT == 0, "epilogue shape");
@@ -384,8 +481,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
       for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int rl = rbase - sl * SLAB + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const int cl = wn * WN + j * 32 + (lane & 31);
+          const int rl = rbase - sl * SLAB + 8 * (v >> 2) + lrow + (v & 3);
+          const int cl = wn * WN + j * 32 + lcol;
           Ct[cidx(rl, cl)] = acc[i][j][v];
         }
     }
@@ -420,25 +517,16 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
           for (int e = 0; e < 4; ++e) v[e] = 0.f;
         }
       } else {
-        // G3: X(row, col) <- acc = a X + B X (times sig on the first iteration)
-        if (grow < r && gcol < u.ld_s) {
-          const int64_t xi = (int64_t)grow * u.ld_s + gcol;
+        // last G3: O = acc = a X + B X (times sig when it is also the first)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float t = v[e];
-            if (args.first) t = (float)((double)t * sig);
-            v[e] = (gcol + e < u.s) ? t : 0.f;
-          }
-          if (!args.last) {
-            store4(reinterpret_cast<T*>(u.x), xi, v);
-            if (u.x32 != nullptr) store4(u.x32, xi, v);
-          } else if (!u.o_trans && grow < u.o_rows) {
-            const int nv = min(4, u.o_cols - gcol);
-            if (nv > 0) osq += store_out4(u.o_ptr, (int64_t)grow * u.o_ld + gcol, v, nv, u.o_dtype, o_vec);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = 0.f;  // rows >= r: zero padding of X^T
+        for (int e = 0; e < 4; ++e) {
+          float t = v[e];
+          if (args.first) t = (float)((double)t * sig);
+          v[e] = t;
+        }
+        if (!u.o_trans && grow < u.o_rows) {
+          const int nv = min(4, u.o_cols - gcol);
+          if (nv > 0) osq += store_out4(u.o_ptr, (int64_t)grow * u.o_ld + gcol, v, nv, u.o_dtype, o_vec);
         }
       }
       if (col_pass) *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
@@ -458,15 +546,13 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
         if (PHASE == kG1 || PHASE == kG2) {
           // mirrored tile: row gn of A (or B), columns gi..gi+7
           if (gn < r && gi < u.ld_r) store8(out12, (int64_t)gn * u.ld_r + gi, v);
-        } else if (!args.last) {
-          if (gn < u.s && gi < u.ld_r) store8(reinterpret_cast<T*>((args.cur ? u.xt[0] : u.xt[1])), (int64_t)gn * u.ld_r + gi, v);
         } else if (gn < u.o_cols && gi < u.o_rows) {
           osq += store_out8(u.o_ptr, (int64_t)gn * u.o_ld + gi, v, min(8, u.o_rows - gi), u.o_dtype, o_vec);
         }
       }
     }
   }
-  if (PHASE == kG3 && args.last) {
+  if (PHASE == kG3) {
     block_partial2<kThreads>((double)osq, 0.0, args.st, u.onorm_slot,
                              u.onorm_part0 + job.tm * u.g3_cols + job.tn);
   }
@@ -475,12 +561,11 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
-// Tile configurations (planner.h): 0 = 128 x 128, BK 64; 1 = 256 x 256, BK 64
-// (bf16 operands); 2 = 128 x 128, BK 32 (smaller LDS footprint, more blocks
-// per CU).  fp32 operands always use 128 x 128 with BK 32.
+// Tiles are 128 x 128; K stages of 64 (bf16 operands) or 32 (fp32 operands).
 hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs, int njobs,
                           float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
                           const SlotTable& st, hipStream_t s) {
+  (void)cfg;
   if (njobs <= 0) return hipSuccess;
   NsIterArgs args{a, b, c, eps, first, last, cur, no_mma, njobs, st};
   dim3 grid(njobs), block(kThreads);
@@ -491,13 +576,8 @@ hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, co
     else if (phase == kG2) MUONH_LAUNCH(T, kG2, B, K); \
     else MUONH_LAUNCH(T, kG3, B, K);                   \
   } while (0)
-  if (op_dt == DT_BF16) {
-    if (cfg == 1) MUONH_PHASES(bf16_t, 256, 64);
-    else if (cfg == 2) MUONH_PHASES(bf16_t, 128, 32);
-    else MUONH_PHASES(bf16_t, 128, 64);
-  } else {
-    MUONH_PHASES(float, 128, 32);
-  }
+  if (op_dt == DT_BF16) MUONH_PHASES(bf16_t, 128, 64);
+  else MUONH_PHASES(float, 128, 32);
 #undef MUONH_PHASES
 #undef MUONH_LAUNCH
   return hipGetLastError();

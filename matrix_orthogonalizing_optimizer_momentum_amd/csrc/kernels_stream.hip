@@ -1,8 +1,8 @@
 // HBM-streaming kernels of the MuonH step (gfx950):
 //   k_momentum_prep  M <- beta*M + G (Muon explainer, momentum recap /
 //                    Equation 1), the Frobenius sum of squares of the stored M
-//                    per Newton-Schulz unit, and X0 = M written in both
-//                    Newton-Schulz layouts (the wide-side orientation of the
+//                    per Newton-Schulz unit, and X0^T written into the
+//                    unit's workspace (the wide-side orientation of the
 //                    Muon explainer's code section is a layout choice here,
 //                    never a copy of its own);
 //   k_hook_reduce    pass 1 of the Hyperball / RadialBrake hook: per-matrix
@@ -106,48 +106,40 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
       c0 %= T;
     }
     const NsUnit u = units[unit_id];
-    // "direct" buffer keeps M's orientation, "flipped" buffer is its transpose.
-    OT* dir;
-    OT* flp;
-    int64_t ld_dir, ld_flp;
-    if (mm.trans) {  // X = M^T: X^T layout == M layout
-      dir = reinterpret_cast<OT*>(u.xt[0]); ld_dir = u.ld_r;
-      flp = reinterpret_cast<OT*>(u.x);     ld_flp = u.ld_s;
-    } else {
-      dir = reinterpret_cast<OT*>(u.x);     ld_dir = u.ld_s;
-      flp = reinterpret_cast<OT*>(u.xt[0]); ld_flp = u.ld_r;
-    }
-    // Valid rows of the two buffers (in-unit coordinates).
-    const int64_t dir_rows = mm.tile_T > 0 ? mm.tile_T : H;
-    const int64_t flp_rows = mm.tile_T > 0 ? mm.tile_T : W;
-    // Direct write: same element positions as loaded.
+    // X0^T into xt[0]: ld_s rows of ld_r.  The block grid spans the padded
+    // extent and its values outside the matrix are zero, so the padding is
+    // written too.
+    OT* const xt = reinterpret_cast<OT*>(u.xt[0]);
+    const int64_t ld = u.ld_r;
+    if (mm.trans) {
+      // X = M^T: X^T has M's layout; same element positions as loaded.
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int lr = rr + 32 * p;
-      const int64_t row = r0 + lr;
-      const int64_t col = c0 + cc * 8;
-      if (row < dir_rows && col + 8 <= ld_dir) {
-        float v[8];
+      for (int p = 0; p < 2; ++p) {
+        const int lr = rr + 32 * p;
+        const int64_t row = r0 + lr;
+        const int64_t col = c0 + cc * 8;
+        if (row < u.ld_s && col + 8 <= ld) {
+          float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = tile[lr][cc * 8 + k];
-        store8(dir, row * ld_dir + col, v);
+          for (int k = 0; k < 8; ++k) v[k] = tile[lr][cc * 8 + k];
+          store8(xt, row * ld + col, v);
+        }
       }
-    }
-    __syncthreads();
-    // Flipped write: row = M column, 16 consecutive M rows per thread.
-    {
-      const int lc = t >> 2;          // column of the block -> flipped row
-      const int seg = (t & 3) * 16;   // 16 M rows
+    } else {
+      // X = M: X^T row = M column, 16 consecutive M rows per thread.
+      __syncthreads();
+      const int lc = t >> 2;
+      const int seg = (t & 3) * 16;
       const int64_t frow = c0 + lc;
       const int64_t fcol = r0 + seg;
-      if (frow < flp_rows) {
+      if (frow < u.ld_s) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          if (fcol + 8 * h + 8 <= ld_flp) {
+          if (fcol + 8 * h + 8 <= ld) {
             float v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = tile[seg + 8 * h + k][lc];
-            store8(flp, frow * ld_flp + fcol + 8 * h, v);
+            store8(xt, frow * ld + fcol + 8 * h, v);
           }
         }
       }

@@ -26,31 +26,11 @@ UnitBytes unit_bytes(int r, int s, int op_dt, int x32) {
   const int64_t es = esize(op_dt);
   const int64_t ld_s = pad_up(s, kPad), ld_r = pad_up(r, kPad);
   UnitBytes u;
-  u.x = align256((int64_t)r * ld_s * es);
-  u.xt = align256((int64_t)s * ld_r * es);
-  u.x32 = (x32 && op_dt == DT_BF16) ? align256((int64_t)r * ld_s * 4) : 0;
+  u.xt = align256(ld_s * ld_r * es);
+  u.x32 = (x32 && op_dt == DT_BF16) ? align256(ld_s * ld_r * 4) : 0;
   u.a = align256((int64_t)r * ld_r * es);
   u.b = u.a;
   return u;
-}
-
-// Tile configuration of a unit.  MUONH_GEMM_CFG (0/1/2) forces one for
-// tuning runs; fp32 operands always use configuration 0's 128 x 128 tile.
-static int forced_cfg() {
-  static int v = -2;
-  if (v == -2) {
-    const char* e = std::getenv("MUONH_GEMM_CFG");
-    v = (e && *e) ? std::atoi(e) : -1;
-    if (v < 0 || v >= kGemmCfgs) v = -1;
-  }
-  return v;
-}
-
-int unit_gemm_cfg(int r, int op_dt) {
-  if (op_dt != DT_BF16) return 0;
-  const int f = forced_cfg();
-  if (f >= 0) return f;
-  return 0;
 }
 
 static int64_t jobs_per_iter(int r, int s, int op_dt) {
@@ -174,7 +154,6 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       u.s = m.s;
       u.ld_s = (int32_t)pad_up(m.s, kPad);
       u.ld_r = (int32_t)pad_up(m.r, kPad);
-      u.x = carve(ub.x);
       u.xt[0] = carve(ub.xt);
       u.xt[1] = carve(ub.xt);
       u.x32 = ub.x32 ? reinterpret_cast<float*>(carve(ub.x32)) : nullptr;

@@ -53,8 +53,8 @@ struct Plan {
 
 // Byte sizes of one unit's workspace pieces (each rounded to 256 B).
 struct UnitBytes {
-  int64_t x, xt, x32, a, b;
-  int64_t total() const { return x + 2 * xt + x32 + a + b; }
+  int64_t xt, x32, a, b;
+  int64_t total() const { return 2 * xt + x32 + a + b; }
 };
 UnitBytes unit_bytes(int r, int s, int op_dt, int x32);
 
@@ -65,11 +65,10 @@ inline int esize(int dt) { return dt == DT_F32 ? 4 : 2; }
 int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan);
 
 // Host tables of one chunk (everything a launch sequence needs).
-// GEMM tile configurations: 0 = 128 x 128 (BK 64), 1 = 256 x 256 (BK 64,
-// bf16 operands), 2 = 128 x 128 (BK 32, bf16 operands).
-constexpr int kGemmCfgs = 3;
-inline int gemm_tile_side(int cfg) { return cfg == 1 ? 256 : 128; }
-int unit_gemm_cfg(int r, int op_dt);
+// GEMM tile configuration: 128 x 128 output tiles.
+constexpr int kGemmCfgs = 1;
+inline int gemm_tile_side(int cfg) { return (void)cfg, 128; }
+inline int unit_gemm_cfg(int r, int op_dt) { return (void)r, (void)op_dt, 0; }
 
 // Hierarchical Muon with T <= kTileResidentMax runs on the resident-tile
 // kernel (one workgroup per tile for the whole step, momentum fused, no
