@@ -70,9 +70,12 @@ enum { MUONH_F32 = 0, MUONH_BF16 = 1 };
 
 /* How bf16 Newton-Schulz keeps X between iterations (MFMA operands are bf16
  * and accumulation is fp32 in both):
+ *   MUONH_NS_FOLD -- X itself is stored in bf16, as in the Muon explainer's
+ *                    code section; a*X + B*X is formed in fp32 and rounded
+ *                    once per iteration (default);
  *   MUONH_NS_X32  -- an fp32 master copy of X carries the a*X term, a bf16
- *                    shadow feeds the matrix cores (default);
- *   MUONH_NS_FOLD -- X itself is stored in bf16.
+ *                    shadow feeds the matrix cores (8 more bytes of traffic
+ *                    per element and iteration).
  * Both fold the 1/(||M||+eps) pre-scale into the first iteration instead of
  * rounding the pre-scaled X0 to bf16.  Ignored when ns_dtype is MUONH_F32. */
 enum { MUONH_NS_X32 = 0, MUONH_NS_FOLD = 1 };
@@ -85,7 +88,7 @@ typedef struct muonh_opts {
   int          state_dtype;     /* dtype of grads, momentum, ns_orthogonalize in/out and
                                    frob_project's U: MUONH_BF16 (default) or MUONH_F32 */
   int          ns_dtype;        /* Newton-Schulz operand dtype: MUONH_BF16 (default) or MUONH_F32 */
-  int          ns_precision;    /* MUONH_NS_X32 (default) or MUONH_NS_FOLD */
+  int          ns_precision;    /* MUONH_NS_FOLD (default) or MUONH_NS_X32 */
   const float* coeffs;          /* host, 3*K floats: (a,b,c) for iteration k at [3k..3k+2];
                                    NULL = (3.4445, -4.7750, 2.0315) every iteration */
   float        ns_eps;          /* added to ||M||_F before dividing; default 1e-7 */

@@ -15,7 +15,7 @@ Entry points mirror the C ABI in ``include/muonh.h``:
   ``profile_begin()``, ``profile_read()``, ``strerror(code)``, ``version()``
 
 ``opts`` keywords: ``ns_dtype`` ("bf16" | "f32"), ``ns_precision``
-("x32" | "fold"), ``coeffs`` (K rows of (a, b, c)), ``ns_eps``,
+("fold" | "x32"), ``coeffs`` (K rows of (a, b, c)), ``ns_eps``,
 ``zero_rel_eps``, ``hook`` ("hyperball" | "radial_brake"), ``outward``,
 ``inward``, ``rb_eps``, ``workspace_limit`` (bytes), ``stream``
 (a torch.cuda.Stream; default: the current stream).
@@ -169,7 +169,7 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
 
 
-def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="x32", coeffs=None, ns_eps=None,
+def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coeffs=None, ns_eps=None,
               zero_rel_eps=None, hook="hyperball", outward=None, inward=None, rb_eps=None,
               workspace_limit=0, stream=None, K=None):
     """Build an Opts struct; returns (opts, keepalive) where keepalive holds

@@ -540,7 +540,7 @@ void muonh_default_opts(muonh_opts* o) {
   o->stream = nullptr;
   o->state_dtype = MUONH_BF16;
   o->ns_dtype = MUONH_BF16;
-  o->ns_precision = MUONH_NS_X32;
+  o->ns_precision = MUONH_NS_FOLD;
   o->coeffs = nullptr;
   o->ns_eps = 1e-7f;
   o->zero_rel_eps = 1e-6f;

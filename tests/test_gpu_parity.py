@@ -119,7 +119,8 @@ def test_ns_zero_input_is_zero():
     assert not torch.any(out != 0)
 
 
-def test_ns_spectrum_example_bf16_768():
+@pytest.mark.parametrize("prec", ["fold", "x32"])
+def test_ns_spectrum_example_bf16_768(prec):
     # Muon explainer, code section closing check: a 768x768 matrix with
     # singular values 0.9, 0.3, 0.1, 0.01, 0.001 and 763 more near 0.011, run
     # in bf16, stays close to the scalar polynomial (the page quotes 0.005
@@ -130,12 +131,12 @@ def test_ns_spectrum_example_bf16_768():
     # X_new = a X + B X cancels terms ~3x larger than the result, so a few
     # 2^-9 roundings reach ~7e-3 on this spectrum (the same rounding points
     # emulated on the CPU give 7.0e-3; the page's own cast-every-result loop
-    # gives 1.8e-2).
-    banner("ns bf16 768 spectrum example")
+    # gives 1.8e-2; bf16 X between iterations, 7.2e-3).
+    banner(f"ns bf16 768 spectrum example {prec}")
     n = 768
     s = np.array([0.9, 0.3, 0.1, 0.01, 0.001] + [0.011] * 763)
     Xb = gen.store(gen.with_singular_values(n, n, s, 77), "bf16")
-    out = host(mm.ns_orthogonalize([dev(Xb, torch.bfloat16)], K=5, ns_dtype="bf16")[0])
+    out = host(mm.ns_orthogonalize([dev(Xb, torch.bfloat16)], K=5, ns_dtype="bf16", ns_precision=prec)[0])
     got = np.sort(np.linalg.svd(out, compute_uv=False))
     sb = np.linalg.svd(Xb.astype(np.float64), compute_uv=False)
     x = sb / (np.linalg.norm(sb) + 1e-7)
