@@ -99,10 +99,20 @@ def make_device_inputs(shapes, nsets, seed, torch):
     return Ws, Ms, Gsets, rho
 
 
-def cpu_baseline(shapes, layer_size, budget_s=12.0):
-    """The fp64 numpy oracle, as it stands, on a bounded sample: whole layers
-    (layer_size consecutive matrices) of the same workload until ~budget_s of
-    CPU time, extrapolated to the full matrix set."""
+def _ns_flops(H, W, K, T):
+    def full(h, w):
+        r, q = min(h, w), max(h, w)
+        return K * (4.0 * r * r * q + 2.0 * r ** 3)
+    if T <= 0:
+        return full(H, W)
+    return sum(full(min(T, H - a), min(T, W - b)) for a in range(0, H, T) for b in range(0, W, T))
+
+
+def cpu_baseline(shapes, K, tile_T, hook, budget_s=12.0):
+    """The fp64 numpy oracle, as it stands, on a bounded sample of the same
+    workload: whole matrices in the workload's order until ~budget_s of CPU
+    time; when the set is not finished, the time is extrapolated to the full
+    set by its share of the Newton-Schulz flops (which dominate the oracle)."""
     import numpy as np
     from oracle import muonh_oracle as orc
     from synth import gen
@@ -111,24 +121,24 @@ def cpu_baseline(shapes, layer_size, budget_s=12.0):
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    nlayers_total = max(1, len(shapes) // layer_size)
-    t_layers = []
-    done = 0
+    total_f = sum(_ns_flops(h, w, K, tile_T) for h, w in shapes)
+    t_sum, f_sum, done = 0.0, 0.0, 0
     t_all = time.perf_counter()
-    while done < nlayers_total and (time.perf_counter() - t_all) < budget_s:
-        sub = shapes[done * layer_size:(done + 1) * layer_size]
+    while done < len(shapes) and (time.perf_counter() - t_all) < budget_s:
+        sub = [shapes[done]]
         Ws, Gs, Ms = gen.model_set(sub, 2, 1)
         rho = [float(np.linalg.norm(w.astype(np.float64))) for w in Ws]
         t0 = time.perf_counter()
-        orc.muonh_step(Ws, Gs, Ms, 0.02, 0.95, 5, rho, state_bf16=True)
-        t_layers.append(time.perf_counter() - t0)
+        orc.muonh_step(Ws, Gs, Ms, 0.02, 0.95, K, rho, tile_T=tile_T, hook=hook, state_bf16=True)
+        t_sum += time.perf_counter() - t0
+        f_sum += _ns_flops(sub[0][0], sub[0][1], K, tile_T)
         done += 1
-    per_layer = sum(t_layers) / len(t_layers)
-    step_s = per_layer * nlayers_total
+    step_s = t_sum if done == len(shapes) else t_sum * total_f / f_sum
+    how = ("the whole set" if done == len(shapes) else
+           f"extrapolated to the full set by its Newton-Schulz flops ({f_sum / total_f:.2%} sampled)")
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {nlayers_total} layers ({done * layer_size} of {len(shapes)} matrices) "
-                      f"timed with the fp64 numpy oracle, {sum(t_layers):.1f} s; value extrapolated to the "
-                      f"full set ({step_s:.1f} s/step)"}
+            "sample": f"{done} of {len(shapes)} matrices timed with the fp64 numpy oracle, {t_sum:.1f} s; "
+                      f"{how}: {step_s:.1f} s/step"}
 
 
 def main():
@@ -139,6 +149,7 @@ def main():
     ap.add_argument("--workload", default="gpt2")
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--ns-precision", default="fold", choices=["fold", "x32"])
+    ap.add_argument("--hook", default="hyperball", choices=["hyperball", "radial_brake"])
     ap.add_argument("--K", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-sets", type=int, default=4)
@@ -177,7 +188,7 @@ def main():
 
     def step(i):
         mm.muonh_step(Ws, Gsets[i % len(Gsets)], Ms, eta=0.02, beta=0.95, K=K, rho=rho, tile_T=args.tile,
-                      ns_precision=args.ns_precision, workspace_limit=ws_limit)
+                      ns_precision=args.ns_precision, workspace_limit=ws_limit, hook=args.hook)
 
     for i in range(args.warmup):
         step(i)
@@ -248,8 +259,11 @@ def main():
         "data": "synthetic (seeded device RNG: W0 ~ N(0, 0.02^2); grads N(0, 1e-3^2) + rank-4 10x spike)",
         "config": {"workload": f"{wdesc}; MuonH step, K={K} quintic NS "
                                f"{'tiled T=' + str(args.tile) if args.tile else 'full-matrix'}, "
-                               f"bf16 grads/momentum, fp32 master weights, Hyperball rho=||W0||_F",
+                               f"bf16 grads/momentum, fp32 master weights, "
+                               + ("Hyperball rho=||W0||_F" if args.hook == "hyperball"
+                                  else "RadialBrake (outward 0.5, inward 1.0, eta 0.02)"),
                    "matrices": len(shapes), "K": K, "tile_T": args.tile, "ns_precision": args.ns_precision,
+                   "hook": args.hook,
                    "elements": sum(h * w for h, w in shapes), "chunks": q["chunks"]},
         "ns_tflops": round(ns_tflops, 2) if ns_tflops else None,
         "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
@@ -262,8 +276,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        layer = {"gpt2": 4, "qwen1p2b": 7, "dense8b": 7, "single256": 1}[args.workload]
-        out["cpu_baseline"] = cpu_baseline(shapes, layer)
+        out["cpu_baseline"] = cpu_baseline(shapes, K, args.tile, args.hook)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
