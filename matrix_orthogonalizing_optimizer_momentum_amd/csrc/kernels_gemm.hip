@@ -151,7 +151,7 @@ __device__ __forceinline__ bf16x8_t ld_tr8(const bf16_t* p0, const bf16_t* p1) {
 // Block tile BM x BN (BM == BN), 4 waves in 2 x 2, each wave (BM/2) x (BN/2)
 // built from 32 x 32 MFMA tiles; BK elements of K per LDS stage.
 template <typename T, int PHASE, int BM, int BN, int BK>
-__global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__ units,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_gemm(const NsUnit* __restrict__ units,
                                                      const GemmJob* __restrict__ jobs, NsIterArgs args) {
   using M = Mf<T>;
   constexpr bool TR = PHASE == kG1;  // operands are X^T tiles stored [k][m]
@@ -349,7 +349,10 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
     }
   };
 
-  auto compute = [&](int buf) {
+  // One stage of MFMAs from LDS buffer buf; mid() runs after the first
+  // k-step's MFMAs are issued (the next stage's LDS stores and global loads
+  // then overlap with this stage's matrix work).
+  auto compute = [&](int buf, auto&& mid) {
     const T* sp = sP + buf * PSZ;
     const T* sq = sQ + buf * QSZ;
     // Fragments double-buffered in registers: step kk+1's LDS reads are in
@@ -376,25 +379,35 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
 #pragma unroll
         for (int j = 0; j < NI; ++j) acc[i][j] = M::mma(fa[c][i], fb[c][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) {
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
   if (nstage > 0) {
-    // Straight-line steady state (no conditionals, so the compiler's wait
-    // counts stay exact): the prefetch index is clamped to the last stage, a
-    // clamped reload is never used; the nstage % NPF tail is peeled.
+    // Stage s lives in ring slot s % NPF from its global load until its LDS
+    // store.  While stage ks is computed from LDS buffer ks % 2, stage ks+1
+    // is stored into the other buffer and its ring slot is refilled with
+    // stage ks+1+NPF, so a load has NPF stages of work to arrive.  The loop
+    // is straight-line (no conditionals, so the compiler's wait counts stay
+    // exact): load indices are clamped to the last stage and a store past the
+    // end only fills the unused buffer; the nstage % NPF tail is peeled.
 #pragma unroll
     for (int p = 0; p < NPF; ++p) MUONH_GLOAD(p, min(p, nstage - 1));
     MUONH_LSTORE(0, 0);
+    MUONH_GLOAD(0, min(NPF, nstage - 1));
     __syncthreads();
     const int ngroups = nstage / NPF;
     for (int g = 0; g < ngroups; ++g) {
 #pragma unroll
       for (int j = 0; j < NPF; ++j) {
         const int ks = g * NPF + j;  // ks % NPF == j
-        MUONH_GLOAD(j, min(ks + NPF, nstage - 1));
-        compute(ks & 1);
-        MUONH_LSTORE((ks + 1) & 1, (j + 1) % NPF);  // after the last stage: an unused buffer
+        compute(ks & 1, [&] {
+          MUONH_LSTORE((ks + 1) & 1, (j + 1) % NPF);
+          MUONH_GLOAD((j + 1) % NPF, min(ks + 1 + NPF, nstage - 1));
+        });
         __syncthreads();
       }
     }
@@ -402,11 +415,10 @@ __global__ __launch_bounds__(kThreads) void k_ns_gemm(const NsUnit* __restrict__
     for (int j = 0; j < NPF - 1; ++j) {
       const int ks = ngroups * NPF + j;
       if (ks < nstage) {
-        compute(ks & 1);
-        if (ks + 1 < nstage) {
-          MUONH_LSTORE((ks + 1) & 1, (j + 1) % NPF);
-          __syncthreads();
-        }
+        compute(ks & 1, [&] {
+          if (ks + 1 < nstage) MUONH_LSTORE((ks + 1) & 1, (j + 1) % NPF);
+        });
+        __syncthreads();
       }
     }
   }
