@@ -148,15 +148,18 @@ __device__ __forceinline__ bf16x8_t ld_tr8(const bf16_t* p0, const bf16_t* p1) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Block tile BM x BN (BM == BN), 4 waves in 2 x 2, each wave (BM/2) x (BN/2)
-// built from 32 x 32 MFMA tiles; BK elements of K per LDS stage.
-template <typename T, int PHASE, int BM, int BN, int BK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_gemm(const NsUnit* __restrict__ units,
-                                                     const GemmJob* __restrict__ jobs, NsIterArgs args) {
+// Block tile BM x BN (BM == BN) on WGM x WGN waves, each wave (BM/WGM) x
+// (BN/WGN) built from 32 x 32 MFMA tiles; BK elements of K per LDS stage.
+// Register budgets keep two waves per SIMD: 128-tiles run two workgroups of
+// 4 waves per CU, 256-tiles one workgroup of 8 waves.
+template <typename T, int PHASE, int BM, int BN, int BK, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_gemm(
+    const NsUnit* __restrict__ units, const GemmJob* __restrict__ jobs, NsIterArgs args) {
   using M = Mf<T>;
-  constexpr bool TR = PHASE == kG1;  // operands are X^T tiles stored [k][m]
+  constexpr int NT = 64 * WGM * WGN;  // threads
+  constexpr bool TR = PHASE == kG1;   // operands are X^T tiles stored [k][m]
   constexpr int VEC = M::VEC, KSTEP = M::KSTEP;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MI = WM / 32, NI = WN / 32;
   // LDS operand tiles: K-contiguous rows [m][k] with pitch LDK, or (TR)
   // [k][m] rows of BM elements, row k rotated by ROT * (k % RN) elements so
@@ -166,10 +169,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int PSZ = TR ? BK * BM : BM * LDK;  // elements per operand stage
   constexpr int QSZ = TR ? BK * BN : BN * LDK;
   constexpr int CPR = TR ? BM / VEC : BK / VEC;  // 16-byte chunks per LDS row
-  constexpr int P_LOADS = BM * BK / VEC / kThreads;
-  constexpr int Q_LOADS = BN * BK / VEC / kThreads;
+  constexpr int P_LOADS = BM * BK / VEC / NT;
+  constexpr int Q_LOADS = BN * BK / VEC / NT;
   static_assert(BM == BN, "square block tiles");
-  static_assert(BM * BK % (VEC * kThreads) == 0, "tile/thread mismatch");
+  static_assert(BM * BK % (VEC * NT) == 0, "tile/thread mismatch");
   static_assert(BK % KSTEP == 0 && kPad % BK == 0, "K stage must divide the padding granule");
   static_assert(!TR || (BM % (ROT * RN) == 0 && BK % (RN * KSTEP / 2) == 0), "rotation layout");
 
@@ -177,9 +180,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // same LDS for its fp32 slabs.
   constexpr int kStage = 2 * (PSZ + QSZ) * (int)sizeof(T);
   // Slab rows: fit the stage buffers, and keep the batched row-pass reads of
-  // a slab (SLAB * BN / kThreads values per thread) within 64 registers.
+  // a slab (SLAB * BN / NT values per thread) within 64 registers.
   constexpr int SLAB_LDS = (BM * BN * 4 <= kStage) ? BM : ((BM / 2) * BN * 4 <= kStage ? BM / 2 : BM / 4);
-  constexpr int SLAB_REG = 64 * kThreads / BN;
+  constexpr int SLAB_REG = 64 * NT / BN;
   constexpr int SLAB = SLAB_LDS < SLAB_REG ? SLAB_LDS : SLAB_REG;
   constexpr int kSmem = kStage > SLAB * BN * 4 ? kStage : SLAB * BN * 4;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   const int row0 = job.tm * BM, col0 = job.tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // Pre-scale of the first iteration, read now so its latency is hidden.
   double sig = 1.0;
@@ -241,20 +244,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const T* src = PHASE == kG2 ? reinterpret_cast<const T*>(u.a) : xt_in;
     const int nlim = PHASE == kG2 ? u.r : u.ld_s;  // rows of the source
     const float coef = PHASE == kG2 ? g2_seed : (args.no_mma ? 1.f : args.a);
+    // Loaded straight into the accumulators (clamped offsets keep every load
+    // in bounds), then scaled, with out-of-range positions zeroed.
+    auto seed_off = [&](int i, int j, int q, bool& ok) -> int64_t {
+      const int m0 = row0 + wm * WM + i * 32 + 8 * q + lrow, n = col0 + wn * WN + j * 32 + lcol;
+      ok = n < nlim && m0 < u.ld_r;
+      return ok ? (int64_t)n * u.ld_r + m0 : 0;
+    };
+    if (m32) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bool ok;
+            const f32x4_t x = *reinterpret_cast<const MUONH_GLOBAL f32x4_t*>(gmem(u.x32) + seed_off(i, j, q, ok));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = x[e];
+          }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bool ok;
+            float x[4];
+            load4(src, seed_off(i, j, q, ok), x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = x[e];
+          }
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int m0 = row0 + wm * WM + i * 32 + 8 * q + lrow, n = col0 + wn * WN + j * 32 + lcol;
-          const bool ok = n < nlim && m0 < u.ld_r;
-          const int64_t o = ok ? (int64_t)n * u.ld_r + m0 : 0;  // clamped: always in bounds
-          float x[4];
-          if (m32) load4(u.x32, o, x);
-          else load4(src, o, x);
+          bool ok;
+          (void)seed_off(i, j, q, ok);
+          const float mul = ok ? coef : 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = ok ? coef * x[e] : 0.f;
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] *= mul;
         }
   }
 
@@ -266,44 +299,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #ifndef MUONH_NPF
 #define MUONH_NPF 2
 #endif
-  constexpr int NPF = (MI * NI >= 16) ? 1 : MUONH_NPF;
+  constexpr int NPF = (MI * NI >= 8) ? 1 : MUONH_NPF;
   constexpr int NL = P_LOADS + Q_LOADS;
   u32x4_t ring[NPF][NL];
-  // Per-thread load coordinates (fixed for the whole K loop) and the step
-  // between stages, in 16-byte units.
-  const MUONH_GLOBAL u32x4_t* gsrc[NL];
-  const int64_t kstride = TR ? (int64_t)BK * u.ld_r / VEC : BK / VEC;
+  // Per-thread load coordinates: a 32-bit byte offset from the operand's
+  // base (fixed for the whole K loop; operands are below 2 GiB), and the
+  // uniform step between stages, so each load is one scalar-base + vector
+  // offset access.
+  const char* const Pb = reinterpret_cast<const char*>(P);
+  const char* const Qb = reinterpret_cast<const char*>(Q);
+  uint32_t goff[NL];
+  const int64_t kstride = TR ? (int64_t)BK * u.ld_r * (int64_t)sizeof(T) : (int64_t)BK * (int64_t)sizeof(T);
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
     const bool isp = l < P_LOADS;
     const int ll = isp ? l : l - P_LOADS;
-    const int c = (tid + ll * kThreads) % CPR, rr = (tid + ll * kThreads) / CPR;
-    const T* base;
+    const int c = (tid + ll * NT) % CPR, rr = (tid + ll * NT) / CPR;
+    int64_t e;
     if (TR) {
       // row rr of the stage (k), 8 consecutive m; chunks past the padded
       // width are clamped to its last chunk (they feed only outputs >= ld_r)
       const int mc = min((isp ? row0 : col0) + c * VEC, u.ld_r - VEC);
-      base = P + (int64_t)rr * ldP + mc;
+      e = (int64_t)rr * ldP + mc;
     } else {
       // Rows past the operand's edge are clamped to its last row instead of
       // masked: the loads stay branch-free, and those rows only feed output
       // rows / columns the epilogue writes as zeros or not at all.
       const int gr = isp ? min(row0 + rr, Prows - 1) : min(col0 + rr, Qrows - 1);
-      base = (isp ? P + (int64_t)gr * ldP : Q + (int64_t)gr * ldQ) + c * VEC;
+      e = (int64_t)gr * (isp ? ldP : ldQ) + c * VEC;
     }
-    gsrc[l] = reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(base));
+    goff[l] = (uint32_t)(e * (int64_t)sizeof(T));
   }
-#define MUONH_GLOAD(slot, ks)                                                              \
-  do {                                                                                     \
-    const int64_t kofs_ = (int64_t)(ks) * kstride;                                         \
-    _Pragma("unroll") for (int l = 0; l < NL; ++l) ring[slot][l] = gsrc[l][kofs_];         \
+#define MUONH_GLOAD(slot, ks)                                                                       \
+  do {                                                                                              \
+    const int64_t kofs_ = (int64_t)(ks) * kstride;                                                  \
+    const MUONH_GLOBAL char* pk_ = gmem(Pb + kofs_);                                                \
+    const MUONH_GLOBAL char* qk_ = gmem(Qb + kofs_);                                                \
+    _Pragma("unroll") for (int l = 0; l < NL; ++l) ring[slot][l] =                                  \
+        *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>((l < P_LOADS ? pk_ : qk_) + goff[l]);        \
   } while (0)
 #define MUONH_LSTORE(buf, slot)                                                                        \
   do {                                                                                                 \
     _Pragma("unroll") for (int l = 0; l < NL; ++l) {                                                   \
       const bool isp_ = l < P_LOADS;                                                                   \
       const int ll_ = isp_ ? l : l - P_LOADS;                                                          \
-      const int c_ = (tid + ll_ * kThreads) % CPR, r_ = (tid + ll_ * kThreads) / CPR;                  \
+      const int c_ = (tid + ll_ * NT) % CPR, r_ = (tid + ll_ * NT) / CPR;                  \
       const int o_ = TR ? r_ * BM + ((c_ * VEC + ROT * (r_ % RN)) & (BM - 1)) : r_ * LDK + c_ * VEC;   \
       T* dst_ = isp_ ? sP + (buf) * PSZ + o_ : sQ + (buf) * QSZ + o_;                                  \
       *reinterpret_cast<u32x4_t*>(dst_) = ring[slot][l];                                              \
@@ -471,11 +511,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float osq = 0.f;
   const bool mirror = (PHASE != kG3) && (job.tm != job.tn);  // symmetric outputs: also write the transpose
   const bool col_pass = (PHASE == kG3) ? (u.o_trans != 0) : mirror;
-  constexpr int ROWS_PER_IT = kThreads / GPR;    // row pass: one granule (4 values) per thread
+  constexpr int ROWS_PER_IT = NT / GPR;    // row pass: one granule (4 values) per thread
   constexpr int RB = SLAB / ROWS_PER_IT;         // row-pass iterations per slab
   constexpr int CPC = SLAB / 8;                  // column pass: 8-row chunks per slab column
-  constexpr int COLS_PER_IT = kThreads / CPC;
-  static_assert(SLAB % ROWS_PER_IT == 0 && kThreads % CPC == 0 && BN % COLS_PER_IT == 0, "epilogue shape");
+  constexpr int COLS_PER_IT = NT / CPC;
+  static_assert(SLAB % ROWS_PER_IT == 0 && NT % CPC == 0 && BN % COLS_PER_IT == 0, "epilogue shape");
   const int gran = tid % GPR, rsub = tid / GPR;
   const int q = tid % CPC, csub = tid / CPC;
   const bool o_vec = (u.o_dtype == DT_BF16) ? ((u.o_ld % 8) == 0 && ((uintptr_t)u.o_ptr % 16) == 0)
@@ -565,7 +605,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
   if (PHASE == kG3) {
-    block_partial2<kThreads>((double)osq, 0.0, args.st, u.onorm_slot,
+    block_partial2<NT>((double)osq, 0.0, args.st, u.onorm_slot,
                              u.onorm_part0 + job.tm * u.g3_cols + job.tn);
   }
 }
@@ -573,23 +613,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
-// Tiles are 128 x 128; K stages of 64 (bf16 operands) or 32 (fp32 operands).
+// Tile configurations (planner.h): 0 = 128 x 128 on 2 x 2 waves, K stages of
+// 64 (bf16) or 32 (fp32); 1 = 256 x 256 on 4 x 2 waves (bf16 operands,
+// large units).
 hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs, int njobs,
                           float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
                           const SlotTable& st, hipStream_t s) {
-  (void)cfg;
   if (njobs <= 0) return hipSuccess;
   NsIterArgs args{a, b, c, eps, first, last, cur, no_mma, njobs, st};
-  dim3 grid(njobs), block(kThreads);
-#define MUONH_LAUNCH(T, PH, B, K) hipLaunchKernelGGL((k_ns_gemm<T, PH, B, B, K>), grid, block, 0, s, units, jobs, args)
-#define MUONH_PHASES(T, B, K)                          \
-  do {                                                 \
-    if (phase == kG1) MUONH_LAUNCH(T, kG1, B, K);      \
-    else if (phase == kG2) MUONH_LAUNCH(T, kG2, B, K); \
-    else MUONH_LAUNCH(T, kG3, B, K);                   \
+  dim3 grid(njobs);
+#define MUONH_LAUNCH(T, PH, B, K, GM, GN) \
+  hipLaunchKernelGGL((k_ns_gemm<T, PH, B, B, K, GM, GN>), grid, dim3(64 * GM * GN), 0, s, units, jobs, args)
+#define MUONH_PHASES(T, B, K, GM, GN)                          \
+  do {                                                         \
+    if (phase == kG1) MUONH_LAUNCH(T, kG1, B, K, GM, GN);      \
+    else if (phase == kG2) MUONH_LAUNCH(T, kG2, B, K, GM, GN); \
+    else MUONH_LAUNCH(T, kG3, B, K, GM, GN);                   \
   } while (0)
-  if (op_dt == DT_BF16) MUONH_PHASES(bf16_t, 128, 64);
-  else MUONH_PHASES(float, 128, 32);
+  if (op_dt == DT_BF16) {
+    if (cfg == 1) MUONH_PHASES(bf16_t, 256, 64, 4, 2);
+    else MUONH_PHASES(bf16_t, 128, 64, 2, 2);
+  } else {
+    MUONH_PHASES(float, 128, 32, 2, 2);
+  }
 #undef MUONH_PHASES
 #undef MUONH_LAUNCH
   return hipGetLastError();

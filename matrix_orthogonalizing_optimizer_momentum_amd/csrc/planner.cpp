@@ -33,10 +33,29 @@ UnitBytes unit_bytes(int r, int s, int op_dt, int x32) {
   return u;
 }
 
+// 256-tiles for bf16 units with r >= 1024 (>= 10 upper tiles for G1 / G2,
+// >= 16 tiles for G3 per unit); smaller units keep 128-tiles, which fill the
+// chip better.  MUONH_GEMM_BIG=0 / 2 forces 128 / 256 tiles (bf16) for
+// tuning runs; results do not depend on the choice beyond summation order.
+int unit_gemm_cfg(int r, int op_dt, bool phase12) {
+  (void)phase12;
+  if (op_dt != DT_BF16) return 0;
+  static int mode = -1;
+  if (mode < 0) {
+    const char* e = std::getenv("MUONH_GEMM_BIG");
+    mode = (e && *e) ? std::atoi(e) : 1;
+  }
+  if (mode == 0) return 0;
+  if (mode == 2) return 1;
+  return r >= 1024 ? 1 : 0;
+}
+
 static int64_t jobs_per_iter(int r, int s, int op_dt) {
-  const int B = gemm_tile_side(unit_gemm_cfg(r, op_dt));
-  const int64_t nr = (pad_up(r, kPad) + B - 1) / B, ns = (pad_up(s, kPad) + B - 1) / B;
-  return 2 * (nr * (nr + 1) / 2) + nr * ns;  // symmetric G1, G2 + G3
+  const int B12 = gemm_tile_side(unit_gemm_cfg(r, op_dt, true));
+  const int B3 = gemm_tile_side(unit_gemm_cfg(r, op_dt, false));
+  const int64_t nr12 = (pad_up(r, kPad) + B12 - 1) / B12;
+  const int64_t nr = (pad_up(r, kPad) + B3 - 1) / B3, ns = (pad_up(s, kPad) + B3 - 1) / B3;
+  return 2 * (nr12 * (nr12 + 1) / 2) + nr * ns;  // symmetric G1, G2 + G3
 }
 
 static double ns_flops_true(int64_t h, int64_t w, int K) {
@@ -92,6 +111,8 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
       m.trans = m.H > m.W ? 1 : 0;
       m.nunits = 1;
       m.ntr = m.ntc = 1;
+      // GEMM operand loads address a unit's X^T with 32-bit byte offsets.
+      if (pad_up(m.r, kPad) * pad_up(m.s, kPad) * esize(cfg.op_dt) >= ((int64_t)1 << 32)) return MUONH_ENOTIMPL;
       const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32);
       m.ws_bytes += ub.total();
       plan.ns_flops += ns_flops_true(m.H, m.W, cfg.K);
@@ -238,22 +259,23 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
         u.o_cols = m.s;
         u.o_ptr = out;
       }
-      const int gc = unit_gemm_cfg(u.r, cfg.op_dt);
-      const int B = gemm_tile_side(gc);
-      const int g3r = (u.ld_r + B - 1) / B, g3c = (u.ld_s + B - 1) / B;
+      const int gc12 = unit_gemm_cfg(u.r, cfg.op_dt, true), gc3 = unit_gemm_cfg(u.r, cfg.op_dt, false);
+      const int B12 = gemm_tile_side(gc12), B3 = gemm_tile_side(gc3);
+      const int n12 = (u.ld_r + B12 - 1) / B12;
+      const int g3r = (u.ld_r + B3 - 1) / B3, g3c = (u.ld_s + B3 - 1) / B3;
       u.g3_cols = g3c;
       part += g3r * g3c;
       const int uid = unit0[mi] + k;
       // A and B are symmetric: only tiles on or above the diagonal, the
       // epilogue mirrors the off-diagonal ones.
-      for (int tm = 0; tm < g3r; ++tm)
-        for (int tn = tm; tn < g3r; ++tn) t.g12_jobs[gc].push_back({uid, tm, tn, u.ld_r / 64});
+      for (int tm = 0; tm < n12; ++tm)
+        for (int tn = tm; tn < n12; ++tn) t.g12_jobs[gc12].push_back({uid, tm, tn, u.ld_r / 64});
       for (int tn = 0; tn < g3c; ++tn)
-        for (int tm = 0; tm < g3r; ++tm) t.g3_jobs[gc].push_back({uid, tm, tn, u.ld_r / 64});
+        for (int tm = 0; tm < g3r; ++tm) t.g3_jobs[gc3].push_back({uid, tm, tn, u.ld_r / 64});
       const double r = (double)std::min(h, w), s = (double)std::max(h, w);
-      t.flops_g1[gc] += 2.0 * r * r * s;
-      t.flops_g2[gc] += 2.0 * r * r * r;
-      t.flops_g3[gc] += 2.0 * r * r * s;
+      t.flops_g1[gc12] += 2.0 * r * r * s;
+      t.flops_g2[gc12] += 2.0 * r * r * r;
+      t.flops_g3[gc3] += 2.0 * r * r * s;
     }
     t.nparts[s_onorm0 + mi] = part;
   }

@@ -65,10 +65,14 @@ inline int esize(int dt) { return dt == DT_F32 ? 4 : 2; }
 int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan);
 
 // Host tables of one chunk (everything a launch sequence needs).
-// GEMM tile configuration: 128 x 128 output tiles.
-constexpr int kGemmCfgs = 1;
-inline int gemm_tile_side(int cfg) { return (void)cfg, 128; }
-inline int unit_gemm_cfg(int r, int op_dt) { return (void)r, (void)op_dt, 0; }
+// GEMM tile configurations: 0 = 128 x 128 output tiles (4 waves, two
+// workgroups per CU); 1 = 256 x 256 (8 waves of 64 x 128, one workgroup per
+// CU, bf16 operands): a third less LDS traffic per MFMA, for units large
+// enough to fill the chip with them.
+constexpr int kGemmCfgs = 2;
+inline int gemm_tile_side(int cfg) { return cfg == 1 ? 256 : 128; }
+// Configuration of a unit's G1/G2 (phase12) or G3 products.
+int unit_gemm_cfg(int r, int op_dt, bool phase12);
 
 // Hierarchical Muon with T <= kTileResidentMax runs on the resident-tile
 // kernel (one workgroup per tile for the whole step, momentum fused, no

@@ -62,7 +62,7 @@ def test_ns_fp32_small(shape):
 
 @pytest.mark.parametrize("prec", ["x32", "fold"])
 @pytest.mark.parametrize("shape", [(768, 768), (768, 3072), (3072, 768), (768, 2304), (300, 700), (500, 1300),
-                                   (1300, 500), (256, 256), (1024, 2048)],
+                                   (1300, 500), (256, 256), (1024, 2048), (1100, 1700), (2500, 1300)],
                          ids=lambda s: f"{s[0]}x{s[1]}" if isinstance(s, tuple) else s)
 def test_ns_bf16_spiked(shape, prec):
     H, W = shape
@@ -318,6 +318,29 @@ def test_step_exact_cancel_restores_radius(shape, ns):
 def _gpt2_like(shapes, cfg=2, step=1):
     Ws, Gs, Ms = gen.model_set(shapes, cfg, step)
     return Ws, Gs, Ms
+
+
+@pytest.mark.parametrize("prec", ["fold", "x32"])
+def test_step_large_units_bf16(prec):
+    # Units with r >= 1024 run on the 256 x 256 tile configuration; ragged
+    # sides (1100, 1300) leave partial tiles in every product.
+    banner(f"large-unit step bf16 {prec}")
+    shapes = [(1024, 2048), (2048, 1024), (1100, 1300), (1300, 2600)]
+    Ws, Gs, Ms = _gpt2_like(shapes, cfg=3)
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    w_t = [dev(w) for w in Ws]
+    m_t = [dev(m, torch.bfloat16) for m in Ms]
+    mm.muonh_step(w_t, [dev(g, torch.bfloat16) for g in Gs], m_t, eta=0.02, beta=0.95, K=5, rho=rhos,
+                  ns_precision=prec)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        Wn, Mn, _, _ = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.02, np.float32(0.95), 5, [rhos[i]],
+                                      state_bf16=True)
+        assert np.array_equal(host(m_t[i]), Mn[0])
+        assert abs(np.linalg.norm(host(w_t[i])) / rhos[i] - 1) <= 1e-5
+        err = rel(host(w_t[i]) - Ws[i], Wn[0] - Ws[i])
+        print(f"  matrix {i} {shapes[i]} step rel err {err:.3e}")
+        assert err <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("prec", ["x32", "fold"])
