@@ -33,7 +33,9 @@ pages give, with no blocking, fusion or reordering.  Sources (page titles):
 
 Readings taken where the pages are silent:
 
-* momentum is the plain sum M <- beta*M + G, no Nesterov blend;
+* momentum is the plain sum M <- beta*M + G, no Nesterov blend, unless asked
+  for: the exponential-average buffer and the Nesterov blend follow [MUON]
+  code section (``lerp_`` forms); with the plain sum the blend is G + beta*M;
 * the NS eps is added to the Frobenius norm (not a max);
 * a matrix is transposed iff it has more rows than columns (square: not);
 * a HiMuon tile is zero-padded to T x T, gets its own pre-scale, and the grid
@@ -103,10 +105,24 @@ def momentum_update(M, G, beta) -> np.ndarray:
 
 def momentum_update_ema(M, G, beta) -> np.ndarray:
     """The exponential-average form of the same buffer, beta*M + (1-beta)*G,
-    as in [MUON] code section (``lerp_``).  Only used to check that both forms
-    give the same orthogonalized direction."""
+    as in [MUON] code section (the buffer is lerped toward the gradient by
+    1 - mu)."""
     b = float(beta)
     return b * _f64(M) + (1.0 - b) * _f64(G)
+
+
+def nesterov_input(G, M_new, beta, ema: bool) -> np.ndarray:
+    """The Newton-Schulz input of a Nesterov step, from the fresh gradient and
+    the already-updated buffer.
+
+    [MUON] code section: the update is the gradient lerped toward the buffer
+    by mu, (1 - mu) G + mu M.  For the plain-sum buffer of Equation 1 (which
+    carries no (1 - mu) factor on G) the same look-ahead is G + mu M.
+    """
+    b = float(beta)
+    if ema:
+        return (1.0 - b) * _f64(G) + b * _f64(M_new)
+    return _f64(G) + b * _f64(M_new)
 
 
 # ---------------------------------------------------------------------------
@@ -251,6 +267,16 @@ def radial_brake(W, O, eta, outward: float = 0.5, inward: float = 1.0, eps: floa
     return Wp
 
 
+def plain_update(W, O, eta, weight_decay: float = 0.0):
+    """Muon's own weight update with no hook ([MUON] code section, ``step``):
+    decoupled weight decay W <- W (1 - eta * wd), then W <- W - eta * O'
+    with the shape-scaled direction O' = max(1, H/W)^0.5 O."""
+    W = _f64(W)
+    H, Wd = W.shape
+    W = W * (1.0 - float(eta) * float(weight_decay))
+    return W - float(eta) * shape_scale(H, Wd) * _f64(O)
+
+
 # ---------------------------------------------------------------------------
 # frob_project and the whole step
 # ---------------------------------------------------------------------------
@@ -264,28 +290,36 @@ def frob_project(W, U, eta, rho, zero_rel_eps: float = 1e-6):
 
 def muonh_step(Ws, Gs, Ms, eta, beta, K, rhos, tile_T: int = 0, hook: str = "hyperball",
                coeffs=None, outward: float = 0.5, inward: float = 1.0,
-               zero_rel_eps: float = 1e-6, state_bf16: bool = False):
-    """One MuonH (or HiMuon-H / Muon+RadialBrake) step over a list of matrices.
+               zero_rel_eps: float = 1e-6, state_bf16: bool = False,
+               ema: bool = False, nesterov: bool = False, weight_decay: float = 0.0):
+    """One MuonH (or HiMuon-H / Muon+RadialBrake / plain Muon) step over a
+    list of matrices.
 
-    Per matrix, in the pages' order: momentum ([MUON] Eq. 1) -> NS on the
-    momentum ([MUON] Eq. 6 / code; tiled per [HIMUON] when tile_T > 0) ->
-    Hyperball ([HB] Algorithm 1) or RadialBrake ([HOOKS]).
+    Per matrix, in the pages' order: momentum ([MUON] Eq. 1, or the
+    exponential average of the code section with ``ema``) -> the Newton-Schulz
+    input (the buffer, or the Nesterov blend with ``nesterov``) -> NS ([MUON]
+    Eq. 6 / code; tiled per [HIMUON] when tile_T > 0) -> Hyperball ([HB]
+    Algorithm 1), RadialBrake ([HOOKS]) or no hook (``"none"``: Muon's own
+    update with decoupled weight decay).
 
     ``state_bf16`` models a bf16 momentum buffer: the updated M is stored
-    rounded to bf16 and NS reads the stored value.
+    rounded to bf16 and the NS input is formed from the stored value.
 
     Returns (new_Ws, new_Ms, Os, flags).
     """
     new_W, new_M, Os, flags = [], [], [], []
     for i, (W, G, M) in enumerate(zip(Ws, Gs, Ms)):
-        m = momentum_update(M, G, beta)
+        m = momentum_update_ema(M, G, beta) if ema else momentum_update(M, G, beta)
         if state_bf16:
             m = round_to_bf16(m)
-        O = orthogonalize(m, K, tile_T, coeffs)
+        x = nesterov_input(G, m, beta, ema) if nesterov else m
+        O = orthogonalize(x, K, tile_T, coeffs)
         if hook == "hyperball":
             w, f = hyperball(W, O, eta, rhos[i], zero_rel_eps)
         elif hook == "radial_brake":
             w, f = radial_brake(W, O, eta, outward, inward), None
+        elif hook == "none":
+            w, f = plain_update(W, O, eta, weight_decay), None
         else:
             raise ValueError("unknown hook")
         new_W.append(w)

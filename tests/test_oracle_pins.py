@@ -276,6 +276,63 @@ def test_momentum_ema_and_sum_give_same_direction():
     assert np.abs(orc.newton_schulz(Ms, 5) - orc.newton_schulz(Me, 5)).max() < 1e-6
 
 
+@pytest.mark.parametrize("ema", [False, True])
+def test_nesterov_with_zero_beta_is_the_gradient(ema):
+    # mu = 0: the blend (1 - mu) G + mu M (or G + mu M) is the fresh gradient
+    G = gen.gaussian((6, 9), 1.0, 21).astype(np.float64)
+    M0 = gen.gaussian((6, 9), 1.0, 22).astype(np.float64)
+    W = gen.gaussian((6, 9), 0.1, 23).astype(np.float64)
+    _, _, Os, _ = orc.muonh_step([W], [G], [M0], 0.1, 0.0, 5, [1.0], hook="none", ema=ema, nesterov=True)
+    assert np.abs(Os[0] - orc.newton_schulz(G, 5)).max() < 1e-14
+
+
+@pytest.mark.parametrize("ema,buf,direction", [
+    # worked by hand from the Muon explainer's code section with mu = 0.5,
+    # G = (1, 0), M0 = (0, 1): the buffer lerps toward G by 1 - mu, the update
+    # lerps G toward the buffer by mu
+    (True, (0.5, 0.5), (3.0, 1.0)),    # (1-mu)G + mu M1 = (0.75, 0.25)
+    # plain-sum buffer: M1 = mu M0 + G = (1, 0.5); look-ahead G + mu M1 = (1.5, 0.25)
+    (False, (1.0, 0.5), (6.0, 1.0)),
+], ids=["ema", "sum"])
+def test_nesterov_worked_example(ema, buf, direction):
+    G = np.array([[1.0, 0.0]])
+    M0 = np.array([[0.0, 1.0]])
+    W = np.array([[0.3, -0.2]])
+    _, Ms, Os, _ = orc.muonh_step([W], [G], [M0], 0.1, 0.5, 5, [1.0], hook="none", ema=ema, nesterov=True)
+    assert np.array_equal(Ms[0], np.array([buf]))
+    d = np.array([direction]) / np.linalg.norm(direction)
+    # a row vector keeps its direction through NS (one singular value)
+    assert np.abs(Os[0] / np.linalg.norm(Os[0]) - d).max() < 1e-15
+
+
+def test_nesterov_constant_gradient_keeps_direction():
+    # with a constant gradient from M0 = 0 both buffer and blend are positive
+    # multiples of G, so the orthogonalized update is NS(G) up to the eps
+    G = gen.gaussian((12, 20), 1.0, 31).astype(np.float64)
+    M = np.zeros_like(G)
+    for _ in range(4):
+        W = np.zeros_like(G) + 0.01
+        _, Ms, Os, _ = orc.muonh_step([W], [G], [M], 0.1, 0.9, 5, [1.0], hook="none", nesterov=True)
+        M = Ms[0]
+        assert np.abs(Os[0] - orc.newton_schulz(G, 5)).max() < 1e-6
+
+
+@pytest.mark.parametrize("H,W,wd", [(16, 16, 0.0), (16, 16, 0.1), (32, 16, 0.05)])
+def test_plain_update_closed_form(H, W, wd):
+    # G with orthonormal columns (or rows): NS gives p^K(1/(sqrt(r)+eps)) G,
+    # and Muon's update is W (1 - eta wd) - eta max(1, H/W)^0.5 O
+    Q, _ = np.linalg.qr(gen.gaussian((H, W), 1.0, 41).astype(np.float64))
+    r = min(H, W)
+    x = scalar_iterate(1.0 / (math.sqrt(r) + 1e-7), 5)
+    W0 = gen.gaussian((H, W), 0.02, 42).astype(np.float64)
+    eta = 0.02
+    Wn, _, Os, _ = orc.muonh_step([W0], [Q], [np.zeros((H, W))], eta, 0.9, 5, [1.0], hook="none",
+                                  weight_decay=wd)
+    assert np.abs(Os[0] - x * Q).max() < 1e-13
+    expect = W0 * (1 - eta * wd) - eta * math.sqrt(max(1.0, H / W)) * x * Q
+    assert np.abs(Wn[0] - expect).max() < 1e-14
+
+
 def test_round_to_bf16_matches_torch():
     torch = pytest.importorskip("torch")
     x = gen.gaussian((1000,), 3.0, 4)
