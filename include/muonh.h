@@ -81,7 +81,7 @@ enum { MUONH_F32 = 0, MUONH_BF16 = 1 };
 enum { MUONH_NS_X32 = 0, MUONH_NS_FOLD = 1 };
 
 /* weight-update hook */
-enum { MUONH_HOOK_HYPERBALL = 0, MUONH_HOOK_RADIAL_BRAKE = 1 };
+enum { MUONH_HOOK_HYPERBALL = 0, MUONH_HOOK_RADIAL_BRAKE = 1, MUONH_HOOK_NONE = 2 };
 
 typedef struct muonh_opts {
   void*        stream;          /* hipStream_t to queue on; NULL = null stream */
@@ -94,12 +94,19 @@ typedef struct muonh_opts {
   float        ns_eps;          /* added to ||M||_F before dividing; default 1e-7 */
   float        zero_rel_eps;    /* Hyperball: ||W - eta*U_hat|| < zero_rel_eps*rho counts as
                                    zero and restores the radius; default 1e-6 */
-  int          hook;            /* MUONH_HOOK_HYPERBALL (default) or MUONH_HOOK_RADIAL_BRAKE */
+  int          hook;            /* MUONH_HOOK_HYPERBALL (default), MUONH_HOOK_RADIAL_BRAKE or
+                                   MUONH_HOOK_NONE (Muon's own update, see weight_decay) */
   float        outward;         /* RadialBrake factor when the norm grows, in [0,1]; default 0.5 */
   float        inward;          /* RadialBrake factor otherwise, in [0,1]; default 1.0 */
   float        rb_eps;          /* RadialBrake: post-update norm <= rb_eps leaves W'; default 1e-15 */
   size_t       workspace_limit; /* bytes the library may hold as workspace; 0 = 3/4 of free HBM.
                                    Matrices are processed in chunks that fit it. */
+  int          momentum_ema;    /* 0: M <- beta*M + G (default); 1: M <- beta*M + (1-beta)*G */
+  int          nesterov;        /* 0: NS input is M (default); 1: the Nesterov blend,
+                                   G + beta*M (sum form) or (1-beta)*G + beta*M (EMA form),
+                                   formed from the updated M (Muon explainer, code section) */
+  float        weight_decay;    /* MUONH_HOOK_NONE only: W <- W*(1 - eta*weight_decay) before
+                                   the update (decoupled); finite, >= 0; default 0 */
 } muonh_opts;
 
 /* Fill *o with the defaults listed above. */
@@ -107,6 +114,8 @@ void muonh_default_opts(muonh_opts* o);
 
 /*
  * muonh_step -- one full optimizer step (momentum -> NS -> hook) for n matrices.
+ * With MUONH_HOOK_NONE the update is Muon's own (Muon explainer, code
+ * section): W <- W*(1 - eta*weight_decay) - eta*max(1, H/W)^0.5 * O.
  *
  *   params[i]  device, fp32, shapes[2i] x shapes[2i+1], updated in place (W)
  *   grads[i]   device, state_dtype, same shape, read only (G)
@@ -119,7 +128,7 @@ void muonh_default_opts(muonh_opts* o);
  *   beta       momentum coefficient, in [0, 1)
  *   K          Newton-Schulz iterations, 0..64 (0: O = M / (||M|| + eps))
  *   rho        host, n floats: Hyperball radius per matrix (finite, > 0);
- *              ignored (may be NULL) for RadialBrake
+ *              ignored (may be NULL) for RadialBrake and MUONH_HOOK_NONE
  *   tile_T     0 = full-matrix NS; > 0 = Hierarchical Muon with tile side tile_T
  *              (1..128, or a multiple of 64 up to 8192); the hook always acts on
  *              the full matrix

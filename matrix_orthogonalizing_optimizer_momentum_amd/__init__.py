@@ -16,9 +16,10 @@ Entry points mirror the C ABI in ``include/muonh.h``:
 
 ``opts`` keywords: ``ns_dtype`` ("bf16" | "f32"), ``ns_precision``
 ("fold" | "x32"), ``coeffs`` (K rows of (a, b, c)), ``ns_eps``,
-``zero_rel_eps``, ``hook`` ("hyperball" | "radial_brake"), ``outward``,
-``inward``, ``rb_eps``, ``workspace_limit`` (bytes), ``stream``
-(a torch.cuda.Stream; default: the current stream).
+``zero_rel_eps``, ``hook`` ("hyperball" | "radial_brake" | "none"),
+``outward``, ``inward``, ``rb_eps``, ``workspace_limit`` (bytes),
+``momentum`` ("sum" | "ema"), ``nesterov`` (bool), ``weight_decay`` (for
+hook "none"), ``stream`` (a torch.cuda.Stream; default: the current stream).
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuonh.so
 MUONH_OK, MUONH_EINVAL, MUONH_ENOMEM, MUONH_EHIP, MUONH_ENOTIMPL = 0, -1, -2, -3, -4
 MUONH_F32, MUONH_BF16 = 0, 1
 MUONH_NS_X32, MUONH_NS_FOLD = 0, 1
-MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE = 0, 1
+MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE, MUONH_HOOK_NONE = 0, 1, 2
 
 EXPORTED = (
     "muonh_default_opts", "muonh_step", "ns_orthogonalize", "frob_project", "muonh_get_flags",
@@ -67,6 +68,9 @@ class Opts(ctypes.Structure):
         ("inward", c_float),
         ("rb_eps", c_float),
         ("workspace_limit", c_size_t),
+        ("momentum_ema", c_int),
+        ("nesterov", c_int),
+        ("weight_decay", c_float),
     ]
 
 
@@ -171,7 +175,7 @@ def _dtype_code(t) -> int:
 
 def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coeffs=None, ns_eps=None,
               zero_rel_eps=None, hook="hyperball", outward=None, inward=None, rb_eps=None,
-              workspace_limit=0, stream=None, K=None):
+              workspace_limit=0, stream=None, K=None, momentum="sum", nesterov=False, weight_decay=None):
     """Build an Opts struct; returns (opts, keepalive) where keepalive holds
     buffers the struct points to."""
     lib = load()
@@ -192,7 +196,12 @@ def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coef
         o.ns_eps = ns_eps
     if zero_rel_eps is not None:
         o.zero_rel_eps = zero_rel_eps
-    o.hook = {"hyperball": MUONH_HOOK_HYPERBALL, "radial_brake": MUONH_HOOK_RADIAL_BRAKE}[hook]
+    o.hook = {"hyperball": MUONH_HOOK_HYPERBALL, "radial_brake": MUONH_HOOK_RADIAL_BRAKE,
+              "none": MUONH_HOOK_NONE}[hook]
+    o.momentum_ema = {"sum": 0, "ema": 1}[momentum]
+    o.nesterov = 1 if nesterov else 0
+    if weight_decay is not None:
+        o.weight_decay = weight_decay
     if outward is not None:
         o.outward = outward
     if inward is not None:

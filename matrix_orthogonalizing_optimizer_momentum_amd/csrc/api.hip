@@ -25,12 +25,12 @@ namespace muonh {
 // launchers (kernels_*.hip)
 hipError_t launch_momentum_prep(int state_dt, int op_dt, const MomMat* mats, const MomBlock* blocks,
                                 int nblocks, const NsUnit* units, const SlotTable& st, float beta,
-                                hipStream_t s);
+                                float gcoef, int nesterov, hipStream_t s);
 hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
                               const SlotTable& st, float eta, hipStream_t s);
 hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
                              const SlotTable& st, float eta, float zero_rel_eps, float outward,
-                             float inward, float rb_eps, Flags* flags, hipStream_t s);
+                             float inward, float rb_eps, float decay, Flags* flags, hipStream_t s);
 hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
                         hipStream_t s);
 hipError_t launch_finalize(const SlotTable& st, int slot0, int nslots, hipStream_t s);
@@ -171,7 +171,10 @@ int resolve(const muonh_opts* in, int K, Resolved& r) {
   if (o.state_dtype != MUONH_BF16 && o.state_dtype != MUONH_F32) return MUONH_EINVAL;
   if (o.ns_dtype != MUONH_BF16 && o.ns_dtype != MUONH_F32) return MUONH_EINVAL;
   if (o.ns_precision != MUONH_NS_X32 && o.ns_precision != MUONH_NS_FOLD) return MUONH_EINVAL;
-  if (o.hook != MUONH_HOOK_HYPERBALL && o.hook != MUONH_HOOK_RADIAL_BRAKE) return MUONH_EINVAL;
+  if (o.hook != MUONH_HOOK_HYPERBALL && o.hook != MUONH_HOOK_RADIAL_BRAKE && o.hook != MUONH_HOOK_NONE)
+    return MUONH_EINVAL;
+  if ((o.momentum_ema != 0 && o.momentum_ema != 1) || (o.nesterov != 0 && o.nesterov != 1)) return MUONH_EINVAL;
+  if (!finite_f(o.weight_decay) || o.weight_decay < 0.f) return MUONH_EINVAL;
   if (!finite_f(o.ns_eps) || o.ns_eps < 0.f) return MUONH_EINVAL;
   if (!finite_f(o.zero_rel_eps) || o.zero_rel_eps < 0.f) return MUONH_EINVAL;
   if (!finite_f(o.rb_eps) || o.rb_eps < 0.f) return MUONH_EINVAL;
@@ -216,7 +219,8 @@ Cfg make_cfg(int kind, int n, int K, int tile_T, const Resolved& r, size_t limit
   c.state_dt = r.o.state_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.op_dt = r.o.ns_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.x32 = (c.op_dt == DT_BF16 && r.o.ns_precision == MUONH_NS_X32) ? 1 : 0;
-  c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB : kModeHB;
+  c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB : r.o.hook == MUONH_HOOK_NONE ? kModeNone : kModeHB;
+  if (kind == CALL_PROJ) c.hook = kModeHB;  // frob_project is the Hyperball projection
   c.ws_limit = limit;
   return c;
 }
@@ -302,7 +306,7 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   key.push_back((uint64_t)(uintptr_t)st.ws);
   uint32_t eb;
   memcpy(&eb, &p.eta, 4);
-  key.push_back(cfg.hook == kModeRB ? eb : 0);  // RadialBrake tables hold eta * shape scale
+  key.push_back(cfg.hook != kModeHB ? eb : 0);  // RadialBrake / plain tables hold eta * shape scale
   for (int i = 0; i < 2 * cfg.n; ++i) key.push_back((uint64_t)shapes[i]);
   key_push_ptrs(key, p.params, cfg.kind == CALL_NS ? 0 : cfg.n);
   key_push_ptrs(key, p.grads, cfg.n);
@@ -467,6 +471,8 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
       ta.K = cfg.K;
       ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
       ta.beta = beta;
+      ta.gcoef = (kind == CALL_STEP && r.o.momentum_ema) ? 1.f - beta : 1.f;
+      ta.nesterov = (kind == CALL_STEP && r.o.nesterov) ? 1 : 0;
       ta.eps = r.o.ns_eps;
       ta.st = sl;
       {
@@ -478,8 +484,10 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
     } else if (kind != CALL_PROJ) {
       {
         Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
+        const bool stp = kind == CALL_STEP;
         MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
-                                           sl, kind == CALL_STEP ? beta : 0.f, s));
+                                           sl, stp ? beta : 0.f, (stp && r.o.momentum_ema) ? 1.f - beta : 1.f,
+                                           (stp && r.o.nesterov) ? 1 : 0, s));
       }
       {
         Prof pf(st, s, PC_FIN, 0, 0);
@@ -494,18 +502,20 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
       MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||U||^2 per matrix
     }
     if (kind != CALL_NS) {
-      {
-        Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
-        MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta, s));
-      }
-      {
+      if (cfg.hook != kModeNone) {  // Muon's own update needs no norms
+        {
+          Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
+          MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta, s));
+        }
         Prof pf(st, s, PC_FIN, 0, 0);
         MUONH_TRY_HIP(launch_finalize(sl, d.nunits + d.nmats, d.nmats, s));  // hook sums per matrix
       }
       {
         Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
+        const float decay = cfg.hook == kModeNone ? 1.f - p.eta * r.o.weight_decay : 1.f;
         MUONH_TRY_HIP(launch_hook_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta,
-                                        r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, st.flags, s));
+                                        r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, st.flags,
+                                        s));
       }
     }
   }
@@ -549,6 +559,9 @@ void muonh_default_opts(muonh_opts* o) {
   o->inward = 1.0f;
   o->rb_eps = 1e-15f;
   o->workspace_limit = 0;
+  o->momentum_ema = 0;
+  o->nesterov = 0;
+  o->weight_decay = 0.f;
 }
 
 int muonh_step(void* const params[], const void* const grads[], void* const moms[], const int64_t shapes[],

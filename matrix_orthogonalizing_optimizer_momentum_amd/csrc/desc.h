@@ -122,13 +122,16 @@ struct TileArgs {
   int K;                    // iterations
   int fold;                 // 1: round the master X to bf16 after every iteration
   float beta;               // momentum coefficient (used when TileMat::g is set)
+  float gcoef;              // weight of G in the buffer update: 1 (sum) or 1 - beta (EMA)
+  int nesterov;             // 1: NS input is gcoef*G + beta*M (Nesterov blend)
   float eps;                // pre-scale eps
   SlotTable st;
 };
 
 // Hook modes.
-constexpr int kModeHB = 0;  // Hyperball
-constexpr int kModeRB = 1;  // RadialBrake
+constexpr int kModeHB = 0;    // Hyperball
+constexpr int kModeRB = 1;    // RadialBrake
+constexpr int kModeNone = 2;  // Muon's own update (decoupled weight decay)
 
 // Elements per block of the flat hook / norm passes (256 threads x 32).
 constexpr int kHookBlockElems = 8192;

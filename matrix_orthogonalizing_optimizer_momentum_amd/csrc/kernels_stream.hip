@@ -29,7 +29,7 @@ static_assert(kHookBlockElems == kHookThreads * kHookPerThread, "hook block size
 template <typename ST, typename OT>
 __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
     const MomMat* __restrict__ mats, const MomBlock* __restrict__ blocks,
-    const NsUnit* __restrict__ units, SlotTable st, float beta) {
+    const NsUnit* __restrict__ units, SlotTable st, float beta, float gcoef, int nesterov) {
   __shared__ float tile[64][65];
   const MomBlock blk = blocks[blockIdx.x];
   const MomMat mm = mats[blk.mat];
@@ -60,12 +60,18 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
     const int lr = rr + 32 * p;
     const int64_t row = (int64_t)blk.br * 64 + lr;
     const int64_t col0 = (int64_t)blk.bc * 64 + cc * 8;
+    // v: the stored buffer; the NS input is v, or the Nesterov blend
+    // gcoef*G + beta*v (Muon explainer, code section)
     float v[8];
     if (fast[p]) {
       if (m != nullptr) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = St<ST>::round(fmaf(beta, mv[p][k], gv[p][k]));
+        for (int k = 0; k < 8; ++k) v[k] = St<ST>::round(fmaf(beta, mv[p][k], gcoef * gv[p][k]));
         store8(m, row * W + col0, v);
+        if (nesterov) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = fmaf(beta, v[k], gcoef * gv[p][k]);
+        }
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = gv[p][k];
@@ -79,8 +85,9 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
           const int64_t idx = row * W + col;
           float gg = St<ST>::ld(g, idx);
           if (m != nullptr) {
-            x = St<ST>::round(fmaf(beta, St<ST>::ld(m, idx), gg));
+            x = St<ST>::round(fmaf(beta, St<ST>::ld(m, idx), gcoef * gg));
             St<ST>::st(m, idx, x);
+            if (nesterov) x = fmaf(beta, x, gcoef * gg);
           } else {
             x = gg;
           }
@@ -158,7 +165,7 @@ __device__ __forceinline__ void load8_dyn(const void* p, int64_t i, int dtype, f
 
 // Coefficient applied to O in W' = W - coef * O.
 __device__ __forceinline__ float hook_coef(const HookMat& hm, const SlotTable& st, float eta, int mode) {
-  if (mode == kModeRB) return hm.oscale;
+  if (mode != kModeHB) return hm.oscale;
   if (hm.o == nullptr || hm.onorm_slot < 0) return 0.f;
   const double n2 = st.sums[2 * hm.onorm_slot];
   if (!(n2 > 0.0)) return 0.f;
@@ -202,17 +209,21 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_reduce(
 template <int MODE>
 __global__ __launch_bounds__(kHookThreads) void k_hook_write(
     const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st, float eta,
-    float zero_rel_eps, float outward, float inward, float rb_eps, Flags* flags) {
+    float zero_rel_eps, float outward, float inward, float rb_eps, float decay, Flags* flags) {
   const HookBlock hb = blocks[blockIdx.x];
   const HookMat hm = mats[hb.mat];
   const float coef = hook_coef(hm, st, eta, MODE);
-  const double v0 = st.sums[2 * hm.slot];      // ||W'||^2
-  const double v1 = st.sums[2 * hm.slot + 1];  // ||W||^2
+  // pass-1 sums (none for Muon's own update)
+  const double v0 = MODE == kModeNone ? 0.0 : st.sums[2 * hm.slot];      // ||W'||^2
+  const double v1 = MODE == kModeNone ? 0.0 : st.sums[2 * hm.slot + 1];  // ||W||^2
   const double nwp = sqrt(v0), nw = sqrt(v1);
   // Per-matrix decision, identical in every block of the matrix.
   int branch;          // 0: scale W', 1: scale W (restore), 2: leave W
   double scale;
-  if (MODE == kModeRB) {
+  if (MODE == kModeNone) {
+    branch = 0;
+    scale = 1.0;
+  } else if (MODE == kModeRB) {
     const double s = (nwp > nw) ? (double)outward : (double)inward;
     if (nwp > (double)rb_eps) { branch = 0; scale = (nw + s * (nwp - nw)) / nwp; }
     else { branch = 0; scale = 1.0; }
@@ -252,8 +263,13 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
     float r[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float base_v = (branch == 0) ? fmaf(-coef, o[k], w[k]) : w[k];
-      r[k] = (float)((double)base_v * scale);
+      if (MODE == kModeNone) {
+        // Muon explainer, code section: decoupled decay, then W - eta * O'
+        r[k] = fmaf(-coef, o[k], w[k] * decay);
+      } else {
+        const float base_v = (branch == 0) ? fmaf(-coef, o[k], w[k]) : w[k];
+        r[k] = (float)((double)base_v * scale);
+      }
     }
     if (full) {
       store8(hm.w, i, r);
@@ -314,17 +330,16 @@ __global__ __launch_bounds__(256) void k_finalize(SlotTable st, int slot0) {
 // ---------------------------------------------------------------------------
 hipError_t launch_momentum_prep(int state_dt, int op_dt, const MomMat* mats, const MomBlock* blocks,
                                 int nblocks, const NsUnit* units, const SlotTable& st, float beta,
-                                hipStream_t s) {
+                                float gcoef, int nesterov, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
   dim3 grid(nblocks), block(kMomThreads);
-  if (state_dt == DT_BF16 && op_dt == DT_BF16)
-    hipLaunchKernelGGL((k_momentum_prep<bf16_t, bf16_t>), grid, block, 0, s, mats, blocks, units, st, beta);
-  else if (state_dt == DT_BF16 && op_dt == DT_F32)
-    hipLaunchKernelGGL((k_momentum_prep<bf16_t, float>), grid, block, 0, s, mats, blocks, units, st, beta);
-  else if (state_dt == DT_F32 && op_dt == DT_BF16)
-    hipLaunchKernelGGL((k_momentum_prep<float, bf16_t>), grid, block, 0, s, mats, blocks, units, st, beta);
-  else
-    hipLaunchKernelGGL((k_momentum_prep<float, float>), grid, block, 0, s, mats, blocks, units, st, beta);
+#define MUONH_MOM(ST, OT) \
+  hipLaunchKernelGGL((k_momentum_prep<ST, OT>), grid, block, 0, s, mats, blocks, units, st, beta, gcoef, nesterov)
+  if (state_dt == DT_BF16 && op_dt == DT_BF16) MUONH_MOM(bf16_t, bf16_t);
+  else if (state_dt == DT_BF16 && op_dt == DT_F32) MUONH_MOM(bf16_t, float);
+  else if (state_dt == DT_F32 && op_dt == DT_BF16) MUONH_MOM(float, bf16_t);
+  else MUONH_MOM(float, float);
+#undef MUONH_MOM
   return hipGetLastError();
 }
 
@@ -340,14 +355,15 @@ hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* bl
 
 hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
                              const SlotTable& st, float eta, float zero_rel_eps, float outward,
-                             float inward, float rb_eps, Flags* flags, hipStream_t s) {
+                             float inward, float rb_eps, float decay, Flags* flags, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
-  if (mode == kModeRB)
-    hipLaunchKernelGGL((k_hook_write<kModeRB>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st,
-                       eta, zero_rel_eps, outward, inward, rb_eps, flags);
-  else
-    hipLaunchKernelGGL((k_hook_write<kModeHB>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st,
-                       eta, zero_rel_eps, outward, inward, rb_eps, flags);
+#define MUONH_HW(MODE)                                                                                   \
+  hipLaunchKernelGGL((k_hook_write<MODE>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, eta, \
+                     zero_rel_eps, outward, inward, rb_eps, decay, flags)
+  if (mode == kModeRB) MUONH_HW(kModeRB);
+  else if (mode == kModeNone) MUONH_HW(kModeNone);
+  else MUONH_HW(kModeHB);
+#undef MUONH_HW
   return hipGetLastError();
 }
 

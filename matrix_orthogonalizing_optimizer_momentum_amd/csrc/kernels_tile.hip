@@ -146,8 +146,12 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
       const bool ok = row < h && col < w;
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = tg ? St<ST>::round(fmaf(args.beta, mv[c][e], gv[c][e])) : mv[c][e];
+      for (int e = 0; e < 8; ++e) x[e] = tg ? St<ST>::round(fmaf(args.beta, mv[c][e], args.gcoef * gv[c][e])) : mv[c][e];
       if (tg && ok) store8(tm, (int64_t)row * ldm + col, x);
+      if (tg && args.nesterov) {  // NS input: the Nesterov blend of G and the updated buffer
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = fmaf(args.beta, x[e], args.gcoef * gv[c][e]);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[e] = ok ? x[e] : 0.f;
@@ -168,8 +172,10 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
           const int64_t o = (int64_t)row * ldm + col + e;
           x = St<ST>::ld(tm, o);
           if (tg) {
-            x = St<ST>::round(fmaf(args.beta, x, St<ST>::ld(tg, o)));
+            const float gg = St<ST>::ld(tg, o);
+            x = St<ST>::round(fmaf(args.beta, x, args.gcoef * gg));
             St<ST>::st(tm, o, x);
+            if (args.nesterov) x = fmaf(args.beta, x, args.gcoef * gg);
           }
         }
         sq = fmaf(x, x, sq);

@@ -122,7 +122,9 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
     plan.units += m.nunits;
     const double sb = cfg.state_dt == DT_F32 ? 4 : 2;
     const double ob = esize(cfg.op_dt);
-    if (cfg.kind == CALL_STEP) plan.stream_bytes += (double)numel * (3 * sb + (4 + ob) + (4 + ob + 4));
+    // momentum 3 passes; hook pass 1 (not for Muon's own update) and pass 2
+    if (cfg.kind == CALL_STEP)
+      plan.stream_bytes += (double)numel * (3 * sb + (cfg.hook == kModeNone ? 0 : 4 + ob) + (4 + ob + 4));
     else plan.stream_bytes += (double)numel * (sb + sb);  // NS: read input, write output
   }
   // chunks
@@ -359,7 +361,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       t.hook_mats.push_back(hm);
       for (int b = 0; b < hm.nblocks; ++b) t.hook_blocks.push_back({idx, b});
       const double ob = hm.o ? esize(hm.o_dtype) : 0;
-      t.bytes_hook1 += (double)hm.numel * (4 + ob);
+      if (cfg.hook != kModeNone) t.bytes_hook1 += (double)hm.numel * (4 + ob);
       t.bytes_hook2 += (double)hm.numel * (4 + ob + 4);
       if (cfg.kind == CALL_PROJ && hm.o) t.bytes_sumsq += (double)hm.numel * ob;
     }

@@ -75,10 +75,33 @@ def test_step_validation_rejects(kw):
 
 def test_step_rejects_bad_options():
     for field, val in [("state_dtype", 7), ("ns_dtype", 3), ("ns_precision", 9), ("hook", 5),
-                       ("outward", 1.5), ("inward", -0.1), ("ns_eps", float("nan"))]:
+                       ("outward", 1.5), ("inward", -0.1), ("ns_eps", float("nan")), ("momentum_ema", 2),
+                       ("nesterov", -1), ("weight_decay", -0.5), ("weight_decay", float("inf"))]:
         o = _opts()
         setattr(o, field, val)
         assert _step(opts=o) == mm.MUONH_EINVAL, field
+
+
+def test_default_options():
+    o = _opts()
+    assert (o.state_dtype, o.ns_dtype, o.ns_precision, o.hook) == (mm.MUONH_BF16, mm.MUONH_BF16, mm.MUONH_NS_FOLD,
+                                                                   mm.MUONH_HOOK_HYPERBALL)
+    assert (o.momentum_ema, o.nesterov, o.weight_decay, o.workspace_limit) == (0, 0, 0.0, 0)
+    assert abs(o.ns_eps - 1e-7) < 1e-12 and abs(o.zero_rel_eps - 1e-6) < 1e-11
+    assert (o.outward, o.inward) == (0.5, 1.0)
+
+
+def test_plain_update_needs_no_radius_and_no_hook_pass():
+    # Muon's own update: rho may be NULL, and the plan has no Hyperball pass 1
+    o = _opts()
+    o.hook = mm.MUONH_HOOK_NONE
+    q_hb = mm.plan_query([(64, 64)], K=5)  # default hook: Hyperball
+    assert q_hb["stream_bytes"] == 64 * 64 * 22
+    lib = mm.load()
+    out = (ctypes.c_int64 * 6)()
+    sh = (ctypes.c_int64 * 2)(64, 64)
+    assert lib.muonh_plan_query(sh, 1, 5, 0, ctypes.byref(o), 0, out) == mm.MUONH_OK
+    assert out[5] == 64 * 64 * 16  # 6 (momentum) + 10 (update pass)
 
 
 def test_step_rejects_null_pointers_and_aliasing():
