@@ -232,26 +232,50 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   const float g2_mul = args.c != 0.f ? args.c : 1.f;
   const int lrow = 4 * (lane >> 5), lcol = lane & 31;  // accumulator-layout offsets
   f32x16_t acc[MI][NI];
-  if (PHASE == kG1) {
+  auto zero_acc = [&] {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  };
+  // With bf16 seeds on 128-tiles the seed is "late": its packed loads are
+  // issued here into registers of their own and added after the main loop,
+  // so their latency never delays the first MFMA.  fp32 master seeds and
+  // 256-tiles (no spare registers) load into the accumulators up front.
+  constexpr bool kLateSeed = sizeof(T) == 2 && MI * NI <= 4;
+  u32x2_t seedv[kLateSeed ? MI : 1][kLateSeed ? NI : 1][4];
+  bool late = false;
+  const T* const seed_src = PHASE == kG2 ? reinterpret_cast<const T*>(u.a) : xt_in;
+  const int seed_nlim = PHASE == kG2 ? u.r : u.ld_s;  // rows of the seed source
+  const float seed_coef = PHASE == kG2 ? g2_seed : (args.no_mma ? 1.f : args.a);
+  auto seed_off = [&](int i, int j, int q, bool& ok) -> int64_t {
+    const int m0 = row0 + wm * WM + i * 32 + 8 * q + lrow, n = col0 + wn * WN + j * 32 + lcol;
+    ok = n < seed_nlim && m0 < u.ld_r;
+    return ok ? (int64_t)n * u.ld_r + m0 : 0;  // clamped: always in bounds
+  };
+  if (PHASE == kG1) {
+    zero_acc();
   } else {
     const bool m32 = PHASE == kG3 && !args.first && u.x32 != nullptr;  // fp32 master
-    const T* src = PHASE == kG2 ? reinterpret_cast<const T*>(u.a) : xt_in;
-    const int nlim = PHASE == kG2 ? u.r : u.ld_s;  // rows of the source
-    const float coef = PHASE == kG2 ? g2_seed : (args.no_mma ? 1.f : args.a);
-    // Loaded straight into the accumulators (clamped offsets keep every load
-    // in bounds), then scaled, with out-of-range positions zeroed.
-    auto seed_off = [&](int i, int j, int q, bool& ok) -> int64_t {
-      const int m0 = row0 + wm * WM + i * 32 + 8 * q + lrow, n = col0 + wn * WN + j * 32 + lcol;
-      ok = n < nlim && m0 < u.ld_r;
-      return ok ? (int64_t)n * u.ld_r + m0 : 0;
-    };
-    if (m32) {
+    const T* src = seed_src;
+    const float coef = seed_coef;
+    late = kLateSeed && !m32;
+    if (late) {
+      if constexpr (kLateSeed) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              bool ok;
+              seedv[i][j][q] = *reinterpret_cast<const MUONH_GLOBAL u32x2_t*>(gmem(src) + seed_off(i, j, q, ok));
+            }
+      }
+      zero_acc();
+    } else if (m32) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -277,18 +301,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
             for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = x[e];
           }
     }
+    if (!late) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
+        for (int j = 0; j < NI; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bool ok;
-          (void)seed_off(i, j, q, ok);
-          const float mul = ok ? coef : 0.f;
+          for (int q = 0; q < 4; ++q) {
+            bool ok;
+            (void)seed_off(i, j, q, ok);
+            const float mul = ok ? coef : 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] *= mul;
-        }
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] *= mul;
+          }
+    }
   }
 
   const int nstage = (args.no_mma || (PHASE == kG2 && args.c == 0.f)) ? 0 : K / BK;
@@ -464,6 +490,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   }
 #undef MUONH_GLOAD
 #undef MUONH_LSTORE
+
+  if constexpr (kLateSeed) {
+    if (late) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bool ok;
+            (void)seed_off(i, j, q, ok);
+            const float mul = ok ? seed_coef : 0.f;
+            const u32x2_t w = seedv[i][j][q];
+            acc[i][j][4 * q + 0] = fmaf(mul, __uint_as_float(w[0] << 16), acc[i][j][4 * q + 0]);
+            acc[i][j][4 * q + 1] = fmaf(mul, __uint_as_float(w[0] & 0xffff0000u), acc[i][j][4 * q + 1]);
+            acc[i][j][4 * q + 2] = fmaf(mul, __uint_as_float(w[1] << 16), acc[i][j][4 * q + 2]);
+            acc[i][j][4 * q + 3] = fmaf(mul, __uint_as_float(w[1] & 0xffff0000u), acc[i][j][4 * q + 3]);
+          }
+    }
+  }
 
   const int r = u.r;
   // ------------------------------------------------ G3, not the last iteration
