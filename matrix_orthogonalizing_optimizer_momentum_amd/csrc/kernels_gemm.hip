@@ -240,10 +240,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   };
-  // With bf16 seeds on 128-tiles the seed is "late": its packed loads are
-  // issued here into registers of their own and added after the main loop,
-  // so their latency never delays the first MFMA.  fp32 master seeds and
-  // 256-tiles (no spare registers) load into the accumulators up front.
+  const int nstage = (args.no_mma || (PHASE == kG2 && args.c == 0.f)) ? 0 : K / BK;
+  // With bf16 seeds on 128-tiles the seed is "late": it is held in registers
+  // of its own and added after the main loop, so it never delays the first
+  // MFMA.  The seed block of X^T (or of A) is a sub-block of this tile's own
+  // Q operand, so it is copied out of the LDS stage that holds it (seed_pull
+  // below) instead of being read from HBM a second time; with no stages
+  // (K = 0) it is loaded directly.  fp32 master seeds and 256-tiles (no spare
+  // registers) load into the accumulators up front.
   constexpr bool kLateSeed = sizeof(T) == 2 && MI * NI <= 4;
   u32x2_t seedv[kLateSeed ? MI : 1][kLateSeed ? NI : 1][4];
   bool late = false;
@@ -271,7 +275,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               bool ok;
-              seedv[i][j][q] = *reinterpret_cast<const MUONH_GLOBAL u32x2_t*>(gmem(src) + seed_off(i, j, q, ok));
+              if (nstage > 0) seedv[i][j][q] = u32x2_t{0u, 0u};  // filled from LDS in the main loop
+              else seedv[i][j][q] = *reinterpret_cast<const MUONH_GLOBAL u32x2_t*>(gmem(src) + seed_off(i, j, q, ok));
             }
       }
       zero_acc();
@@ -317,15 +322,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  const int nstage = (args.no_mma || (PHASE == kG2 && args.c == 0.f)) ? 0 : K / BK;
   // Global prefetch ring: stage ks+NPF's loads are issued when stage ks
   // starts, so each load has NPF-1 stages of MFMA work to arrive before its
   // LDS store; LDS itself is double buffered.  The ring is indexed only by
   // compile-time constants (fully unrolled), so it lives in registers.
 #ifndef MUONH_NPF
-#define MUONH_NPF 2
+#define MUONH_NPF 1
 #endif
-  constexpr int NPF = (MI * NI >= 8) ? 1 : MUONH_NPF;
+  constexpr int NPF = (MI * NI >= 8) ? 1 : (PHASE == kG1 ? 2 : MUONH_NPF);  // G1 has no seed registers
   constexpr int NL = P_LOADS + Q_LOADS;
   u32x4_t ring[NPF][NL];
   // Per-thread load coordinates: a 32-bit byte offset from the operand's
@@ -452,6 +456,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
+  // Seed rows of accumulator block i (rows row0 + wm*WM + i*32 .. +31, i.e.
+  // K indices of this tile's Q operand) sit in one K stage; during that stage
+  // each lane copies its 4-row groups out of the Q buffer: Q row n holds
+  // X^T(n, m) (G3) or A(n, m) (G2).
+  auto seed_pull = [&](int buf, int ks) {
+    if constexpr (kLateSeed && PHASE != kG1) {
+      if (!late) return;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int rb = row0 + wm * WM + i * 32;
+        if (rb / BK != ks) continue;  // uniform per wave
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const T* p = sQ + buf * QSZ + (wn * WN + j * 32 + lcol) * LDK + (rb % BK) + 8 * q + lrow;
+            seedv[i][j][q] = *reinterpret_cast<const u32x2_t*>(p);
+          }
+      }
+    }
+  };
+
   if (nstage > 0) {
     // Stage s lives in ring slot s % NPF from its global load until its LDS
     // store.  While stage ks is computed from LDS buffer ks % 2, stage ks+1
@@ -471,6 +497,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
       for (int j = 0; j < NPF; ++j) {
         const int ks = g * NPF + j;  // ks % NPF == j
         compute(ks & 1, [&] {
+          seed_pull(ks & 1, ks);
           MUONH_LSTORE((ks + 1) & 1, (j + 1) % NPF);
           MUONH_GLOAD((j + 1) % NPF, min(ks + 1 + NPF, nstage - 1));
         });
@@ -482,6 +509,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
       const int ks = ngroups * NPF + j;
       if (ks < nstage) {
         compute(ks & 1, [&] {
+          seed_pull(ks & 1, ks);
           if (ks + 1 < nstage) MUONH_LSTORE((ks + 1) & 1, (j + 1) % NPF);
         });
         __syncthreads();
@@ -515,29 +543,68 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   // ------------------------------------------------ G3, not the last iteration
   // The new X^T (and fp32 master) straight from the accumulators: rows
   // m..m+3 of column n are X^T(n, m..m+3).  Rows >= r and columns >= s are
-  // zero padding.
+  // zero padding.  For each pair of 8-row groups, v_permlane32_swap trades
+  // the upper half-wave's first group for the lower half-wave's second, so
+  // that every lane holds 8 consecutive rows (lanes l and l+32 then cover 16
+  // adjacent rows of X^T row n) and stores them with one 16-byte access (two
+  // for the fp32 master).  The swaps run with every lane active; only the
+  // stores are guarded.
   if (PHASE == kG3 && !args.last) {
     T* const xo = reinterpret_cast<T*>(args.cur ? u.xt[0] : u.xt[1]);
+    const int hi = lane >> 5;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
+      for (int j = 0; j < NI; ++j) {
+        const int n = col0 + wn * WN + j * 32 + lcol;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m0 = row0 + wm * WM + i * 32 + 8 * q + lrow, n = col0 + wn * WN + j * 32 + lcol;
-          if (n < u.ld_s && m0 < u.ld_r) {
-            float v[4];
+        for (int pq = 0; pq < 2; ++pq) {
+          float v[2][4];  // groups q = 2pq, 2pq+1 of this lane's rows
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int q = 2 * pq + h, m0 = row0 + wm * WM + i * 32 + 8 * q + lrow;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float t = acc[i][j][4 * q + e];
               if (args.first) t = (float)((double)t * sig);
-              v[e] = (m0 + e < r && n < u.s) ? t : 0.f;
+              v[h][e] = (m0 + e < r && n < u.s) ? t : 0.f;
             }
-            const int64_t o = (int64_t)n * u.ld_r + m0;
-            store4(xo, o, v);
-            if (u.x32 != nullptr) store4(u.x32, o, v);
+          }
+          // after the swaps: rows row0 + wm*WM + i*32 + 16*pq + 8*hi + 0..7
+          const int ms = row0 + wm * WM + i * 32 + 16 * pq + 8 * hi;
+          const bool ok = n < u.ld_s && ms < u.ld_r;
+          const int64_t o = (int64_t)(ok ? n : 0) * u.ld_r + (ok ? ms : 0);
+          if constexpr (sizeof(T) == 2) {
+            uint32_t w0 = pack_bf16x2(v[0][0], v[0][1]), w1 = pack_bf16x2(v[0][2], v[0][3]);
+            uint32_t w2 = pack_bf16x2(v[1][0], v[1][1]), w3 = pack_bf16x2(v[1][2], v[1][3]);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+            const u32x4_t pk = {s0[0], s1[0], s0[1], s1[1]};
+            if (ok) *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(reinterpret_cast<bf16_t*>(xo) + o)) = pk;
+          } else {
+            float vs[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][e]), __float_as_uint(v[1][e]),
+                                                               false, false);
+              vs[e] = __uint_as_float(sw[0]);
+              vs[4 + e] = __uint_as_float(sw[1]);
+            }
+            if (ok) store8(reinterpret_cast<float*>(xo), o, vs);
+          }
+          if (u.x32 != nullptr) {
+            float vs[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][e]), __float_as_uint(v[1][e]),
+                                                               false, false);
+              vs[e] = __uint_as_float(sw[0]);
+              vs[4 + e] = __uint_as_float(sw[1]);
+            }
+            if (ok) store8(u.x32, o, vs);
           }
         }
+      }
     return;
   }
 
