@@ -10,13 +10,16 @@ turn, so the timed region only runs optimizer steps on HBM-resident data.
 
 One step = momentum, Newton-Schulz, Hyperball for all 48 matrices (the whole
 hot path).  Timing: W untimed steps, then exactly K timed steps between two
-device synchronizations.  A second pass of the same K steps records a HIP
-event pair around every kernel launch (on the stream it runs on) to get the
-per-kernel average durations behind the roofline figures; the headline value
-comes from the first, event-free pass.
+device synchronizations, with the library's lanes (concurrent streams) as
+chosen by --lanes.  A second pass of the same K steps records a HIP event
+pair around every kernel launch (on the stream it runs on) to get the
+per-kernel average durations behind the roofline figures; it runs with
+--profile-lanes (default 1: no concurrent lanes, so a launch's duration is
+its own).  The headline value comes from the first, event-free pass.
 
     python bench.py [--steps K] [--warmup W] [--workload gpt2|qwen1p2b|dense8b|single256]
-                    [--tile T] [--ns-precision x32|fold] [--no-cpu-baseline]
+                    [--tile T] [--ns-precision x32|fold] [--lanes L] [--profile-lanes L]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -48,7 +51,8 @@ def measured_traffic(cls, args):
     import glob
     import hashlib
     path = os.path.join(ROOT, "profiles", "muonh_step_gpt2_small_hbm_traffic.json")
-    if (args.workload, args.tile, args.K, args.ns_precision, args.ws_limit_mib) != ("gpt2", 0, 5, "fold", 0):
+    if (args.workload, args.tile, args.K, args.ns_precision, args.ws_limit_mib, args.profile_lanes) != \
+            ("gpt2", 0, 5, "fold", 0, 1):
         return None
     if not os.path.exists(path):
         return None
@@ -151,6 +155,10 @@ def main():
     ap.add_argument("--ns-precision", default="fold", choices=["fold", "x32"])
     ap.add_argument("--hook", default="hyperball", choices=["hyperball", "radial_brake"])
     ap.add_argument("--K", type=int, default=5)
+    ap.add_argument("--lanes", type=int, default=0, choices=[0, 1, 2, 3, 4],
+                    help="concurrent lanes of a timed step (0: the library's automatic choice)")
+    ap.add_argument("--profile-lanes", type=int, default=1, choices=[0, 1, 2, 3, 4],
+                    help="lanes of the per-launch timing pass (1: every launch has the GPU to itself)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-sets", type=int, default=4)
     ap.add_argument("--ws-limit-mib", type=int, default=0,
@@ -175,7 +183,10 @@ def main():
     K = args.K
     Ws, Ms, Gsets, rho = make_device_inputs(shapes, args.grad_sets, 1234, torch)
     ws_limit = args.ws_limit_mib << 20
-    q = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision, workspace_limit=ws_limit)
+    q = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision, workspace_limit=ws_limit,
+                      lanes=args.lanes)
+    qb = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision, workspace_limit=ws_limit,
+                       lanes=args.profile_lanes)
     if args.copy_calib_mib:
         # a plain copy kernel of known size: reads and writes copy_calib_mib MiB each
         n = args.copy_calib_mib * (1 << 20) // 4
@@ -186,8 +197,9 @@ def main():
         del src, dst
     torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, lanes=args.lanes):
         mm.muonh_step(Ws, Gsets[i % len(Gsets)], Ms, eta=0.02, beta=0.95, K=K, rho=rho, tile_T=args.tile,
+                      lanes=lanes,
                       ns_precision=args.ns_precision, workspace_limit=ws_limit, hook=args.hook)
 
     for i in range(args.warmup):
@@ -202,11 +214,16 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # pass B: same steps with per-launch HIP events
+    # pass B: same steps with per-launch HIP events.  By default the lanes are
+    # off here, so each launch's duration is its own and not shared with a
+    # concurrent lane's kernels.
+    for i in range(2):
+        step(i, args.profile_lanes)
+    torch.cuda.synchronize()
     mm.profile_begin()
     tb0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step(i, args.profile_lanes)
     torch.cuda.synchronize()
     tb1 = time.perf_counter()
     prof = mm.profile_read()
@@ -226,14 +243,14 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dom, args),
-                "flops_per_launch": per_launch, "avg_launch_ms": d["avg_ms"]}
+                "flops_per_launch": per_launch, "avg_launch_ms": d["avg_ms"], "timing_lanes": qb["lanes"]}
     else:
         per_launch = d["bytes"] / d["launches"]
         achieved = per_launch / (d["avg_ms"] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": measured_traffic(dom, args),
-                "bytes_per_launch": per_launch, "avg_launch_ms": d["avg_ms"]}
+                "bytes_per_launch": per_launch, "avg_launch_ms": d["avg_ms"], "timing_lanes": qb["lanes"]}
 
     kernels = {c: {"launches_per_step": v["launches"] / args.steps, "avg_ms": round(v["avg_ms"], 5),
                    "ms_per_step": round(v["total_ms"] / args.steps, 5)} for c, v in prof.items()}
@@ -264,7 +281,7 @@ def main():
                                   else "RadialBrake (outward 0.5, inward 1.0, eta 0.02)"),
                    "matrices": len(shapes), "K": K, "tile_T": args.tile, "ns_precision": args.ns_precision,
                    "hook": args.hook,
-                   "elements": sum(h * w for h, w in shapes), "chunks": q["chunks"]},
+                   "elements": sum(h * w for h, w in shapes), "chunks": q["chunks"], "lanes": q["lanes"]},
         "ns_tflops": round(ns_tflops, 2) if ns_tflops else None,
         "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
         "ns_ms_per_step": round(ns_ms, 4),

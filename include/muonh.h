@@ -37,6 +37,11 @@
  *   - Every argument is validated before any GPU work is queued; a call that
  *     returns an error has changed nothing.
  *   - Work is queued asynchronously on opts->stream (NULL: the null stream).
+ *     A call over two or more matrices that fit one workspace chunk runs
+ *     some of them on library-owned side streams (opts->lanes), which start
+ *     after earlier work on opts->stream and which opts->stream waits for
+ *     before its next work: ordering is as if everything ran on
+ *     opts->stream (opts->lanes = 1 keeps all work there).
  *     No entry point synchronizes the host except muonh_get_flags and
  *     muonh_profile_read.  GPU-side faults surface at the caller's next sync.
  *   - Zero norms are not errors: they follow the rules above and bump the
@@ -107,6 +112,15 @@ typedef struct muonh_opts {
                                    formed from the updated M (Muon explainer, code section) */
   float        weight_decay;    /* MUONH_HOOK_NONE only: W <- W*(1 - eta*weight_decay) before
                                    the update (decoupled); finite, >= 0; default 0 */
+  int          lanes;           /* concurrent lanes, 1..4; 0 = automatic: 2, but 1 for
+                                   full-matrix Newton-Schulz when one iteration over the set
+                                   exceeds 2e12 flops (long products gain nothing from lanes).
+                                   A call over
+                                   two or more matrices that fit one workspace chunk is cut
+                                   into that many runs of matrices, lane 0 on opts->stream and
+                                   the others on library-owned side streams (see the stream
+                                   convention above); 1: all work on opts->stream.  Results
+                                   are identical for every value. */
 } muonh_opts;
 
 /* Fill *o with the defaults listed above. */
@@ -176,16 +190,18 @@ void muonh_release(void);
 
 /*
  * Host-only planning query (no GPU call): how a muonh_step with these
- * arguments would be split.  out[0] = chunks, out[1] = workspace bytes of the
- * largest chunk, out[2] = Newton-Schulz units (matrices or tiles),
+ * arguments would be split.  out[0] = chunks run one after another,
+ * out[1] = workspace bytes the call needs (the largest chunk; when the set
+ * fits in one chunk and holds two or more matrices, the sum over the lanes
+ * that run side by side), out[2] = Newton-Schulz units (matrices or tiles),
  * out[3] = dense NS flops per step (sum of K (4 r^2 s + 2 r^3) over units,
  * with r, s the true (unpadded) sides), out[4] = GEMM tile jobs per NS
  * iteration, out[5] = streaming bytes per step (momentum 3 passes + hook
- * 2 passes, algorithmic).  Returns MUONH_OK, MUONH_EINVAL or MUONH_ENOMEM
- * exactly as muonh_step's validation would.
+ * 2 passes, algorithmic), out[6] = concurrent lanes.  Returns MUONH_OK,
+ * MUONH_EINVAL or MUONH_ENOMEM exactly as muonh_step's validation would.
  */
 int muonh_plan_query(const int64_t shapes[], int n, int K, int tile_T,
-                     const muonh_opts* opts, size_t workspace_limit, int64_t out[6]);
+                     const muonh_opts* opts, size_t workspace_limit, int64_t out[7]);
 
 /*
  * Per-kernel timing for measurement.  muonh_profile_begin() makes every later

@@ -19,7 +19,8 @@ Entry points mirror the C ABI in ``include/muonh.h``:
 ``zero_rel_eps``, ``hook`` ("hyperball" | "radial_brake" | "none"),
 ``outward``, ``inward``, ``rb_eps``, ``workspace_limit`` (bytes),
 ``momentum`` ("sum" | "ema"), ``nesterov`` (bool), ``weight_decay`` (for
-hook "none"), ``stream`` (a torch.cuda.Stream; default: the current stream).
+hook "none"), ``lanes`` (concurrent lanes 1..4; 0: library default),
+``stream`` (a torch.cuda.Stream; default: the current stream).
 """
 from __future__ import annotations
 
@@ -71,6 +72,7 @@ class Opts(ctypes.Structure):
         ("momentum_ema", c_int),
         ("nesterov", c_int),
         ("weight_decay", c_float),
+        ("lanes", c_int),
     ]
 
 
@@ -175,7 +177,7 @@ def _dtype_code(t) -> int:
 
 def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coeffs=None, ns_eps=None,
               zero_rel_eps=None, hook="hyperball", outward=None, inward=None, rb_eps=None,
-              workspace_limit=0, stream=None, K=None, momentum="sum", nesterov=False, weight_decay=None):
+              workspace_limit=0, stream=None, K=None, momentum="sum", nesterov=False, weight_decay=None, lanes=0):
     """Build an Opts struct; returns (opts, keepalive) where keepalive holds
     buffers the struct points to."""
     lib = load()
@@ -202,6 +204,7 @@ def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coef
     o.nesterov = 1 if nesterov else 0
     if weight_decay is not None:
         o.weight_decay = weight_decay
+    o.lanes = int(lanes)
     if outward is not None:
         o.outward = outward
     if inward is not None:
@@ -328,7 +331,7 @@ def release():
 
 
 def plan_query(shapes, K=5, tile_T=0, workspace_limit=0, **opts):
-    """Host-only planning query: dict(chunks, ws_bytes, units, ns_flops, jobs_per_iter, stream_bytes)."""
+    """Host-only planning query: dict(chunks, ws_bytes, units, ns_flops, jobs_per_iter, stream_bytes, lanes)."""
     lib = load()
     flat = [int(v) for hw in shapes for v in hw]
     arr = (c_int64 * len(flat))(*flat)
@@ -338,12 +341,14 @@ def plan_query(shapes, K=5, tile_T=0, workspace_limit=0, **opts):
         o.ns_dtype = {"bf16": MUONH_BF16, "f32": MUONH_F32}[opts["ns_dtype"]]
     if "ns_precision" in opts:
         o.ns_precision = {"x32": MUONH_NS_X32, "fold": MUONH_NS_FOLD}[opts["ns_precision"]]
+    if "lanes" in opts:
+        o.lanes = int(opts["lanes"])
     if "state_dtype" in opts:
         o.state_dtype = {"bf16": MUONH_BF16, "f32": MUONH_F32}[opts["state_dtype"]]
-    out = (c_int64 * 6)()
+    out = (c_int64 * 7)()
     rc = lib.muonh_plan_query(arr, len(shapes), int(K), int(tile_T), ctypes.byref(o), int(workspace_limit), out)
     _check(rc, "muonh_plan_query")
-    keys = ("chunks", "ws_bytes", "units", "ns_flops", "jobs_per_iter", "stream_bytes")
+    keys = ("chunks", "ws_bytes", "units", "ns_flops", "jobs_per_iter", "stream_bytes", "lanes")
     return dict(zip(keys, (int(v) for v in out)))
 
 

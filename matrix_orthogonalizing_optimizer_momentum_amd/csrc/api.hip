@@ -66,6 +66,8 @@ struct DevTables {  // one chunk's tables on the device
   int64_t parts_total = 0;
   int nslots = 0;
   int nunits = 0, nmats = 0;  // slot ranges: [0,nunits) norms, then nmats O norms, then nmats hook sums
+  int64_t part_off = 0;       // lanes: this chunk's first partial / slot in the shared arrays
+  int slot_off = 0;
   double flops_g1[kGemmCfgs] = {}, flops_g2[kGemmCfgs] = {}, flops_g3[kGemmCfgs] = {};
   double bytes_mom = 0, bytes_hook1 = 0, bytes_hook2 = 0, bytes_sumsq = 0;
 };
@@ -73,8 +75,9 @@ struct DevTables {  // one chunk's tables on the device
 struct CachedPlan {
   std::vector<uint64_t> key;
   std::vector<DevTables> chunks;
-  int64_t max_parts = 0;
+  int64_t max_parts = 0;  // partials / slots the chunks need (sum over concurrent lanes)
   int max_slots = 0;
+  int lanes = 1;
 };
 
 struct ProfRec {
@@ -94,6 +97,8 @@ struct State {
   int slots_cap = 0;
   Flags* flags = nullptr;
   std::list<CachedPlan> plans;  // most recent first
+  hipStream_t side[kMaxLanes] = {};  // lanes 1.. (created on first use; [0] unused)
+  hipEvent_t ev_gate[kMaxLanes] = {}, ev_join[kMaxLanes] = {};
   bool profiling = false;
   std::vector<ProfRec> prof;
 };
@@ -175,6 +180,7 @@ int resolve(const muonh_opts* in, int K, Resolved& r) {
     return MUONH_EINVAL;
   if ((o.momentum_ema != 0 && o.momentum_ema != 1) || (o.nesterov != 0 && o.nesterov != 1)) return MUONH_EINVAL;
   if (!finite_f(o.weight_decay) || o.weight_decay < 0.f) return MUONH_EINVAL;
+  if (o.lanes < 0 || o.lanes > kMaxLanes) return MUONH_EINVAL;
   if (!finite_f(o.ns_eps) || o.ns_eps < 0.f) return MUONH_EINVAL;
   if (!finite_f(o.zero_rel_eps) || o.zero_rel_eps < 0.f) return MUONH_EINVAL;
   if (!finite_f(o.rb_eps) || o.rb_eps < 0.f) return MUONH_EINVAL;
@@ -222,6 +228,7 @@ Cfg make_cfg(int kind, int n, int K, int tile_T, const Resolved& r, size_t limit
   c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB : r.o.hook == MUONH_HOOK_NONE ? kModeNone : kModeHB;
   if (kind == CALL_PROJ) c.hook = kModeHB;  // frob_project is the Hyperball projection
   c.ws_limit = limit;
+  c.lanes = r.o.lanes;
   return c;
 }
 
@@ -302,6 +309,7 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   key.push_back((uint64_t)cfg.x32);
   key.push_back((uint64_t)cfg.hook);
   key.push_back((uint64_t)plan.chunks.size());
+  key.push_back((uint64_t)plan.lanes);
   for (const auto& c : plan.chunks) key.push_back((uint64_t)c.m1);
   key.push_back((uint64_t)(uintptr_t)st.ws);
   uint32_t eb;
@@ -328,6 +336,7 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   }
   CachedPlan cp;
   cp.key = std::move(key);
+  cp.lanes = plan.lanes;
   for (size_t c = 0; c < plan.chunks.size(); ++c) {
     ChunkTables t;
     fill_chunk(plan, (int)c, cfg, p, st.ws, t);
@@ -338,8 +347,15 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
       free_plan(cp);
       return rc;
     }
-    cp.max_parts = std::max(cp.max_parts, d.parts_total);
-    cp.max_slots = std::max(cp.max_slots, d.nslots);
+    if (plan.lanes > 1) {  // concurrent chunks: disjoint reduction slots
+      d.part_off = cp.max_parts;
+      d.slot_off = cp.max_slots;
+      cp.max_parts += d.parts_total;
+      cp.max_slots += d.nslots;
+    } else {
+      cp.max_parts = std::max(cp.max_parts, d.parts_total);
+      cp.max_slots = std::max(cp.max_slots, d.nslots);
+    }
     cp.chunks.push_back(d);
   }
   const int rc = ensure_meta(st, cp.max_parts, cp.max_slots);
@@ -382,10 +398,10 @@ struct Prof {
 
 SlotTable slot_table(State& st, const DevTables& d) {
   SlotTable t;
-  t.partials = st.partials;
+  t.partials = st.partials + 2 * d.part_off;
   t.nparts = d.nparts;
   t.part_base = d.part_base;
-  t.sums = st.sums;
+  t.sums = st.sums + 2 * (int64_t)d.slot_off;
   return t;
 }
 
@@ -440,6 +456,77 @@ int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, con
   return MUONH_OK;
 }
 
+// One chunk's whole step on stream s.  When rec_open is set it is recorded
+// after the chunk's opening pass (momentum and its norms, or the resident-tile
+// kernel): the point where the next lane may start.
+int run_chunk(State& st, int kind, const Cfg& cfg, const DevTables& d, const Resolved& r, const CallPtrs& p,
+              float beta, hipStream_t s, hipEvent_t rec_open) {
+  int rc = MUONH_OK;
+  const SlotTable sl = slot_table(st, d);
+  if (kind != CALL_PROJ && d.n_tile > 0) {
+    // Hierarchical Muon, resident tiles: momentum, norms and every
+    // Newton-Schulz iteration in one launch.
+    TileArgs ta{};
+    for (int k = 0; k < cfg.K; ++k)
+      for (int j = 0; j < 3; ++j) ta.abc[k][j] = r.coeffs[3 * k + j];
+    ta.T = cfg.tile_T;
+    ta.K = cfg.K;
+    ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
+    ta.beta = beta;
+    ta.gcoef = (kind == CALL_STEP && r.o.momentum_ema) ? 1.f - beta : 1.f;
+    ta.nesterov = (kind == CALL_STEP && r.o.nesterov) ? 1 : 0;
+    ta.eps = r.o.ns_eps;
+    ta.st = sl;
+    {
+      Prof pf(st, s, PC_TILE, d.flops_tile, d.bytes_tile);
+      MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs, d.n_tile, ta, s));
+    }
+    {
+      Prof pf(st, s, PC_FIN, 0, 0);
+      MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
+    }
+    if (rec_open) MUONH_TRY_HIP(hipEventRecord(rec_open, s));
+  } else if (kind != CALL_PROJ) {
+    {
+      Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
+      const bool stp = kind == CALL_STEP;
+      MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
+                                         sl, stp ? beta : 0.f, (stp && r.o.momentum_ema) ? 1.f - beta : 1.f,
+                                         (stp && r.o.nesterov) ? 1 : 0, s));
+    }
+    {
+      Prof pf(st, s, PC_FIN, 0, 0);
+      MUONH_TRY_HIP(launch_finalize(sl, 0, d.nunits, s));  // ||M||^2 per unit
+    }
+    if (rec_open) MUONH_TRY_HIP(hipEventRecord(rec_open, s));
+    rc = run_ns(st, cfg, d, r, sl, s);
+    if (rc != MUONH_OK) return rc;
+  }
+  if (kind == CALL_PROJ && p.grads) {
+    Prof pf(st, s, PC_SQ, 0, d.bytes_sumsq);
+    MUONH_TRY_HIP(launch_sumsq(d.hook_mats, d.hook_blocks, d.n_hook, sl, s));
+    MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||U||^2 per matrix
+  }
+  if (kind != CALL_NS) {
+    if (cfg.hook != kModeNone) {  // Muon's own update needs no norms
+      {
+        Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
+        MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta, s));
+      }
+      Prof pf(st, s, PC_FIN, 0, 0);
+      MUONH_TRY_HIP(launch_finalize(sl, d.nunits + d.nmats, d.nmats, s));  // hook sums per matrix
+    }
+    {
+      Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
+      const float decay = cfg.hook == kModeNone ? 1.f - p.eta * r.o.weight_decay : 1.f;
+      MUONH_TRY_HIP(launch_hook_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta,
+                                      r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, st.flags,
+                                      s));
+    }
+  }
+  return MUONH_OK;
+}
+
 int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Resolved& r,
              const CallPtrs& p, float beta) {
   State& st = S();
@@ -459,65 +546,32 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
   rc = get_plan(st, plan, cfg, p, shapes, cp);
   if (rc != MUONH_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(r.o.stream);
-  for (const DevTables& d : cp->chunks) {
-    const SlotTable sl = slot_table(st, d);
-    if (kind != CALL_PROJ && d.n_tile > 0) {
-      // Hierarchical Muon, resident tiles: momentum, norms and every
-      // Newton-Schulz iteration in one launch.
-      TileArgs ta{};
-      for (int k = 0; k < cfg.K; ++k)
-        for (int j = 0; j < 3; ++j) ta.abc[k][j] = r.coeffs[3 * k + j];
-      ta.T = cfg.tile_T;
-      ta.K = cfg.K;
-      ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
-      ta.beta = beta;
-      ta.gcoef = (kind == CALL_STEP && r.o.momentum_ema) ? 1.f - beta : 1.f;
-      ta.nesterov = (kind == CALL_STEP && r.o.nesterov) ? 1 : 0;
-      ta.eps = r.o.ns_eps;
-      ta.st = sl;
-      {
-        Prof pf(st, s, PC_TILE, d.flops_tile, d.bytes_tile);
-        MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs, d.n_tile, ta, s));
-      }
-      Prof pf(st, s, PC_FIN, 0, 0);
-      MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
-    } else if (kind != CALL_PROJ) {
-      {
-        Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
-        const bool stp = kind == CALL_STEP;
-        MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
-                                           sl, stp ? beta : 0.f, (stp && r.o.momentum_ema) ? 1.f - beta : 1.f,
-                                           (stp && r.o.nesterov) ? 1 : 0, s));
-      }
-      {
-        Prof pf(st, s, PC_FIN, 0, 0);
-        MUONH_TRY_HIP(launch_finalize(sl, 0, d.nunits, s));  // ||M||^2 per unit
-      }
-      rc = run_ns(st, cfg, d, r, sl, s);
+  if (cp->lanes > 1) {
+    // Lane 0 runs on the caller's stream, lane l on the library's side
+    // stream l, started after lane l-1's opening pass (and so after all
+    // earlier work on s); the lanes then run freely side by side, and s
+    // waits for every lane before anything queued after this call.
+    const int L = cp->lanes;
+    for (int l = 0; l < L; ++l) {
+      if (!st.ev_gate[l]) MUONH_TRY_HIP(hipEventCreateWithFlags(&st.ev_gate[l], hipEventDisableTiming));
+      if (!st.ev_join[l]) MUONH_TRY_HIP(hipEventCreateWithFlags(&st.ev_join[l], hipEventDisableTiming));
+      if (l > 0 && !st.side[l]) MUONH_TRY_HIP(hipStreamCreateWithFlags(&st.side[l], hipStreamNonBlocking));
+    }
+    for (int l = 0; l < L; ++l) {
+      hipStream_t ls = l == 0 ? s : st.side[l];
+      if (l > 0) MUONH_TRY_HIP(hipStreamWaitEvent(ls, st.ev_gate[l - 1], 0));
+      rc = run_chunk(st, kind, cfg, cp->chunks[l], r, p, beta, ls, l + 1 < L ? st.ev_gate[l] : nullptr);
       if (rc != MUONH_OK) return rc;
     }
-    if (kind == CALL_PROJ && p.grads) {
-      Prof pf(st, s, PC_SQ, 0, d.bytes_sumsq);
-      MUONH_TRY_HIP(launch_sumsq(d.hook_mats, d.hook_blocks, d.n_hook, sl, s));
-      MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||U||^2 per matrix
+    for (int l = 1; l < L; ++l) {
+      MUONH_TRY_HIP(hipEventRecord(st.ev_join[l], st.side[l]));
+      MUONH_TRY_HIP(hipStreamWaitEvent(s, st.ev_join[l], 0));
     }
-    if (kind != CALL_NS) {
-      if (cfg.hook != kModeNone) {  // Muon's own update needs no norms
-        {
-          Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
-          MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta, s));
-        }
-        Prof pf(st, s, PC_FIN, 0, 0);
-        MUONH_TRY_HIP(launch_finalize(sl, d.nunits + d.nmats, d.nmats, s));  // hook sums per matrix
-      }
-      {
-        Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
-        const float decay = cfg.hook == kModeNone ? 1.f - p.eta * r.o.weight_decay : 1.f;
-        MUONH_TRY_HIP(launch_hook_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta,
-                                        r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, st.flags,
-                                        s));
-      }
-    }
+    return MUONH_OK;
+  }
+  for (const DevTables& d : cp->chunks) {
+    rc = run_chunk(st, kind, cfg, d, r, p, beta, s, nullptr);
+    if (rc != MUONH_OK) return rc;
   }
   return MUONH_OK;
 }
@@ -562,6 +616,7 @@ void muonh_default_opts(muonh_opts* o) {
   o->momentum_ema = 0;
   o->nesterov = 0;
   o->weight_decay = 0.f;
+  o->lanes = 0;
 }
 
 int muonh_step(void* const params[], const void* const grads[], void* const moms[], const int64_t shapes[],
@@ -670,6 +725,13 @@ void muonh_release(void) {
   if (st.partials) (void)hipFree(st.partials);
   if (st.sums) (void)hipFree(st.sums);
   if (st.flags) (void)hipFree(st.flags);
+  for (int l = 0; l < kMaxLanes; ++l) {
+    if (st.side[l]) (void)hipStreamDestroy(st.side[l]);
+    if (st.ev_gate[l]) (void)hipEventDestroy(st.ev_gate[l]);
+    if (st.ev_join[l]) (void)hipEventDestroy(st.ev_join[l]);
+    st.side[l] = nullptr;
+    st.ev_gate[l] = st.ev_join[l] = nullptr;
+  }
   for (auto& r : st.prof) {
     (void)hipEventDestroy(r.e0);
     (void)hipEventDestroy(r.e1);
@@ -687,7 +749,7 @@ void muonh_release(void) {
 }
 
 int muonh_plan_query(const int64_t shapes[], int n, int K, int tile_T, const muonh_opts* opts,
-                     size_t workspace_limit, int64_t out[6]) {
+                     size_t workspace_limit, int64_t out[7]) {
   if (!out) return MUONH_EINVAL;
   int rc = validate_common(shapes, n, K, tile_T);
   if (rc != MUONH_OK) return rc;
@@ -699,12 +761,13 @@ int muonh_plan_query(const int64_t shapes[], int n, int K, int tile_T, const muo
   Plan plan;
   rc = make_plan(shapes, cfg, plan);
   if (rc != MUONH_OK) return rc;
-  out[0] = (int64_t)plan.chunks.size();
+  out[0] = plan.lanes == 2 ? 1 : (int64_t)plan.chunks.size();
   out[1] = plan.ws_bytes;
   out[2] = plan.units;
   out[3] = (int64_t)plan.ns_flops;
   out[4] = plan.jobs_per_iter;
   out[5] = (int64_t)plan.stream_bytes;
+  out[6] = plan.lanes;
   return MUONH_OK;
 }
 

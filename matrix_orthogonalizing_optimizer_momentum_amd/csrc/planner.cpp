@@ -10,7 +10,12 @@
 // Chunks.  Matrices are taken in order and packed into chunks whose
 // workspace fits the limit (the memory-bounded chunking that page lists
 // among the tiled scheme's implementation options); each chunk runs the whole
-// step before the next one reuses the workspace.
+// step before the next one reuses the workspace.  When the whole set fits in
+// one chunk it is cut into up to four runs instead (lanes): the caller runs
+// them on as many streams, so that one lane's launches fill the gaps and
+// drain tails of another's and its streaming passes (momentum, hook) overlap
+// the other lanes' Newton-Schulz products.  Matrices never interact, so the
+// results do not depend on the split.
 #include "planner.h"
 
 #include <algorithm>
@@ -135,14 +140,51 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
     const int64_t b = plan.mats[i].ws_bytes;
     if (b > limit) return MUONH_ENOMEM;
     if (acc + b > limit && i > m0) {
-      plan.chunks.push_back({m0, i, acc});
+      plan.chunks.push_back({m0, i, acc, 0});
       m0 = i;
       acc = 0;
     }
     acc += b;
   }
-  plan.chunks.push_back({m0, n, acc});
+  plan.chunks.push_back({m0, n, acc, 0});
   for (auto& c : plan.chunks) plan.ws_bytes = std::max(plan.ws_bytes, c.ws_bytes);
+  // Automatic choice: two lanes, except for full-matrix Newton-Schulz with a
+  // long iteration, where launch gaps are negligible and the lanes' large
+  // products only contend for the caches (measured slower).
+  const double iter_flops = plan.ns_flops / std::max(cfg.K, 1);
+  const int want = cfg.lanes > 0 ? cfg.lanes : (T == 0 && iter_flops > kAutoLaneIterFlops ? 1 : 2);
+  const int L = std::min(want, n);
+  if (plan.chunks.size() == 1 && L >= 2 && cfg.kind != CALL_PROJ) {
+    // Lanes: cut the set into L runs of matrices whose Newton-Schulz work is
+    // as equal as the order allows (each cut at the prefix sum nearest to
+    // l/L of the total, every run non-empty).  The runs own disjoint
+    // workspace regions (the same total as one chunk) and run concurrently.
+    std::vector<double> f(n), pre(n + 1, 0.0);
+    for (int i = 0; i < n; ++i) {
+      const MatPlan& m = plan.mats[i];
+      f[i] = m.nunits > 1 ? (double)m.nunits * ns_flops_true(m.r, m.s, cfg.K) : ns_flops_true(m.H, m.W, cfg.K);
+      pre[i + 1] = pre[i] + f[i];
+    }
+    std::vector<int> cut(L + 1, 0);
+    cut[L] = n;
+    for (int l = 1; l < L; ++l) {
+      const double target = pre[n] * l / L;
+      int best = cut[l - 1] + 1;
+      for (int i = best; i <= n - (L - l); ++i)
+        if (std::fabs(pre[i] - target) < std::fabs(pre[best] - target)) best = i;
+      cut[l] = best;
+    }
+    plan.chunks.clear();
+    int64_t off = 0;
+    for (int l = 0; l < L; ++l) {
+      int64_t bytes = 0;
+      for (int i = cut[l]; i < cut[l + 1]; ++i) bytes += plan.mats[i].ws_bytes;
+      plan.chunks.push_back({cut[l], cut[l + 1], bytes, off});
+      off += bytes;
+    }
+    plan.ws_bytes = off;
+    plan.lanes = L;
+  }
   return MUONH_OK;
 }
 
@@ -154,7 +196,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   const int es_op = esize(cfg.op_dt);
 
   // --- units and workspace carve
-  int64_t off = 0;
+  int64_t off = ch.ws_off;
   auto carve = [&](int64_t bytes) -> char* {
     char* q = ws + off;
     off += bytes;

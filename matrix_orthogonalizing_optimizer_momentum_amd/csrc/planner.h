@@ -22,8 +22,9 @@ struct Cfg {
   int tile_T;
   int state_dt, op_dt;
   int x32;        // fp32 master X (bf16 operands only)
-  int hook;       // kModeHB / kModeRB
+  int hook;       // kModeHB / kModeRB / kModeNone
   size_t ws_limit;
+  int lanes;      // concurrent lanes, 1..kMaxLanes; 0: automatic (see make_plan)
 };
 
 // Per source matrix.
@@ -36,15 +37,23 @@ struct MatPlan {
   int64_t ws_bytes;
 };
 
+constexpr int kMaxLanes = 4;
+// Automatic lanes: two, except for full-matrix Newton-Schulz when one
+// iteration over the whole set exceeds this many flops (about 1.5 ms of
+// matrix-core work).
+constexpr double kAutoLaneIterFlops = 2e12;
+
 struct ChunkPlan {
   int m0, m1;      // matrices [m0, m1)
   int64_t ws_bytes;
+  int64_t ws_off;  // start of this chunk's region in the workspace
 };
 
 struct Plan {
   std::vector<MatPlan> mats;
   std::vector<ChunkPlan> chunks;
-  int64_t ws_bytes = 0;     // max over chunks
+  int64_t ws_bytes = 0;     // max over chunks (sequential), sum (lanes)
+  int lanes = 1;            // > 1: the chunks are concurrent lanes
   int64_t units = 0;
   double ns_flops = 0;      // dense, true sides
   int64_t jobs_per_iter = 0;

@@ -76,7 +76,8 @@ def test_step_validation_rejects(kw):
 def test_step_rejects_bad_options():
     for field, val in [("state_dtype", 7), ("ns_dtype", 3), ("ns_precision", 9), ("hook", 5),
                        ("outward", 1.5), ("inward", -0.1), ("ns_eps", float("nan")), ("momentum_ema", 2),
-                       ("nesterov", -1), ("weight_decay", -0.5), ("weight_decay", float("inf"))]:
+                       ("nesterov", -1), ("weight_decay", -0.5), ("weight_decay", float("inf")),
+                       ("lanes", -1), ("lanes", 5)]:
         o = _opts()
         setattr(o, field, val)
         assert _step(opts=o) == mm.MUONH_EINVAL, field
@@ -86,9 +87,35 @@ def test_default_options():
     o = _opts()
     assert (o.state_dtype, o.ns_dtype, o.ns_precision, o.hook) == (mm.MUONH_BF16, mm.MUONH_BF16, mm.MUONH_NS_FOLD,
                                                                    mm.MUONH_HOOK_HYPERBALL)
-    assert (o.momentum_ema, o.nesterov, o.weight_decay, o.workspace_limit) == (0, 0, 0.0, 0)
+    assert (o.momentum_ema, o.nesterov, o.weight_decay, o.workspace_limit, o.lanes) == (0, 0, 0.0, 0, 0)
     assert abs(o.ns_eps - 1e-7) < 1e-12 and abs(o.zero_rel_eps - 1e-6) < 1e-11
     assert (o.outward, o.inward) == (0.5, 1.0)
+
+
+def test_lanes_share_one_chunk_workspace():
+    # Concurrent lanes carve disjoint regions out of what one chunk would use.
+    shapes = [(768, 2304), (768, 768), (768, 3072), (3072, 768)] * 3
+    q = mm.plan_query(shapes, K=5)
+    assert q["chunks"] == 1 and q["lanes"] == 2
+    assert q["ws_bytes"] == sum(mm.plan_query([sh], K=5)["ws_bytes"] for sh in shapes)
+    assert mm.plan_query(shapes, K=5, lanes=4)["lanes"] == 4
+    assert mm.plan_query(shapes[:3], K=5, lanes=4)["lanes"] == 3  # never more lanes than matrices
+    assert mm.plan_query(shapes, K=5, lanes=1)["lanes"] == 1
+    assert mm.plan_query(shapes[:1], K=5)["lanes"] == 1
+
+
+def test_automatic_lanes_follow_iteration_work():
+    # Two lanes, but one for full-matrix NS whose iteration exceeds 2e12 flops.
+    small = [(1024, 1024)] * 4   # 4 * 6 * 1024^3 flops per iteration
+    big = [(8192, 8192)] * 2     # 2 * 6 * 8192^3 > 2e12
+    assert mm.plan_query(small, K=5)["lanes"] == 2
+    assert mm.plan_query(big, K=5)["lanes"] == 1
+    assert mm.plan_query(big, K=5, tile_T=128)["lanes"] == 2
+    assert mm.plan_query(big, K=5, lanes=2)["lanes"] == 2
+    # a budget that forces sequential chunks leaves no room for lanes
+    one = mm.plan_query(small[:1], K=5)["ws_bytes"]
+    q = mm.plan_query(small, K=5, workspace_limit=2 * one)
+    assert q["chunks"] == 2 and q["lanes"] == 1
 
 
 def test_plain_update_needs_no_radius_and_no_hook_pass():
@@ -98,7 +125,7 @@ def test_plain_update_needs_no_radius_and_no_hook_pass():
     q_hb = mm.plan_query([(64, 64)], K=5)  # default hook: Hyperball
     assert q_hb["stream_bytes"] == 64 * 64 * 22
     lib = mm.load()
-    out = (ctypes.c_int64 * 6)()
+    out = (ctypes.c_int64 * 7)()
     sh = (ctypes.c_int64 * 2)(64, 64)
     assert lib.muonh_plan_query(sh, 1, 5, 0, ctypes.byref(o), 0, out) == mm.MUONH_OK
     assert out[5] == 64 * 64 * 16  # 6 (momentum) + 10 (update pass)

@@ -580,6 +580,67 @@ def test_chunked_equals_unchunked_bitwise():
         assert np.array_equal(a, b)
 
 
+def _step_with_lanes(lanes, shapes, Ws, Gs, Ms, rhos, **kw):
+    w_t = [dev(w) for w in Ws]
+    m_t = [dev(m, torch.bfloat16) for m in Ms]
+    mm.muonh_step(w_t, [dev(g, torch.bfloat16) for g in Gs], m_t, eta=0.02, beta=0.95, K=5, rho=rhos,
+                  lanes=lanes, **kw)
+    torch.cuda.synchronize()
+    return [host(w) for w in w_t] + [host(m) for m in m_t]
+
+
+@pytest.mark.parametrize("tile,hook,lanes", [(0, "hyperball", 2), (0, "radial_brake", 3), (0, "none", 4),
+                                             (64, "hyperball", 2), (128, "radial_brake", 4), (256, "hyperball", 3)])
+def test_lanes_equal_one_lane_bitwise(tile, hook, lanes):
+    # The lane split only changes which stream a matrix runs on.
+    banner(f"lanes={lanes} tile={tile} hook={hook}")
+    shapes = [(256, 512), (512, 256), (128, 128), (384, 640), (200, 300)]
+    Ws, Gs, Ms = _gpt2_like(shapes, cfg=11)
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    kw = dict(tile_T=tile, hook=hook)
+    if hook == "none":
+        kw["weight_decay"] = 0.1
+    one = _step_with_lanes(1, shapes, Ws, Gs, Ms, rhos, **kw)
+    two = _step_with_lanes(lanes, shapes, Ws, Gs, Ms, rhos, **kw)
+    for a, b in zip(one, two):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("lanes", [2, 4])
+def test_lanes_keep_caller_stream_order(lanes):
+    # Work queued on the caller's stream right after the call sees every
+    # matrix's update, also those run on the library's side stream.
+    banner("lanes stream order")
+    shapes = [(768, 2304), (768, 768), (768, 3072), (3072, 768)] * 2
+    Ws, Gs, Ms = _gpt2_like(shapes, cfg=12)
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    ref = _step_with_lanes(1, shapes, Ws, Gs, Ms, rhos)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        w_t = [dev(w) for w in Ws]
+        m_t = [dev(m, torch.bfloat16) for m in Ms]
+        g_t = [dev(g, torch.bfloat16) for g in Gs]
+        mm.muonh_step(w_t, g_t, m_t, eta=0.02, beta=0.95, K=5, rho=rhos, lanes=lanes)
+        snap = [w.clone() for w in w_t] + [m.clone() for m in m_t]
+    s.synchronize()
+    for a, b in zip(ref, snap):
+        assert np.array_equal(a, host(b))
+
+
+def test_ns_lanes_equal_one_lane_bitwise():
+    banner("lanes ns")
+    shapes = [(256, 512), (640, 384), (96, 96)]
+    Xs = [gen.gaussian(sh, 0.02, 70 + i) for i, sh in enumerate(shapes)]
+    res = []
+    for lanes in (1, 3):
+        outs = [torch.empty(sh, device="cuda", dtype=torch.bfloat16) for sh in shapes]
+        mm.ns_orthogonalize([dev(x, torch.bfloat16) for x in Xs], outs, K=5, lanes=lanes)
+        torch.cuda.synchronize()
+        res.append([host(o) for o in outs])
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
 def test_rerun_is_bitwise_deterministic():
     banner("determinism")
     shapes = [(768, 768), (768, 3072)]
