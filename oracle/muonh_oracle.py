@@ -44,7 +44,10 @@ Readings taken where the pages are silent:
   counts as numerically zero and the radius is restored along the pre-update
   W; if W is zero as well it is left unchanged and flagged;
 * RadialBrake: the update is Muon's O with the shape scale max(1, H/W)^0.5;
-  outward when the norm strictly grows; a post-update norm <= eps leaves W'.
+  outward when the norm strictly grows; a post-update norm <= eps leaves W';
+* RelativeUpdate: the update is rescaled to the pre-update ||W||_F (no
+  post-update step); the Hyperball hook's "normalize to the target radius"
+  wording is the optional radius-sized step, the unit step stays the default.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (closed forms, the pages' worked examples, invariants, brute force on tiny
@@ -209,13 +212,16 @@ def msgn_svd(X) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # a8-a10: Hyperball
 # ---------------------------------------------------------------------------
-def hyperball(W, U, eta, rho, zero_rel_eps: float = 1e-6):
+def hyperball(W, U, eta, rho, zero_rel_eps: float = 1e-6, step: str = "unit"):
     """One Hyperball update of W with base-optimizer direction U.
 
     [HB] Method / §2 eq. 1, Algorithm 1:
       U_hat = U / ||U||_F              (unit Frobenius direction)
       W'    = W - eta * U_hat
       W     <- rho * W' / ||W'||_F     (re-project onto the sphere of radius rho)
+    ``step="radius"`` takes the [HOOKS] PR description's wording instead (the
+    Hyperball hook normalizes the update to the target radius before the
+    update): W' = W - eta * rho * U_hat.
     Zero handling ([HOOKS] review: an exactly cancelling update must restore
     the radius rather than leave zero; numerical zero is tested against an
     eps, not with == 0):
@@ -228,9 +234,11 @@ def hyperball(W, U, eta, rho, zero_rel_eps: float = 1e-6):
     U = _f64(U)
     rho = float(rho)
     eta = float(eta)
+    if step not in ("unit", "radius"):
+        raise ValueError("step must be 'unit' or 'radius'")
     nU = np.linalg.norm(U)
     U_hat = U / nU if nU > 0 else np.zeros_like(U)
-    Wp = W - eta * U_hat
+    Wp = W - (eta * rho if step == "radius" else eta) * U_hat
     n = np.linalg.norm(Wp)
     if n >= zero_rel_eps * rho:
         return rho * Wp / n, FLAG_PROJECTED
@@ -277,21 +285,36 @@ def plain_update(W, O, eta, weight_decay: float = 0.0):
     return W - float(eta) * shape_scale(H, Wd) * _f64(O)
 
 
+def relative_update(W, O, eta):
+    """RelativeUpdate hook ([HOOKS] review summary, file table: the pre-update
+    scaling matches the update's norm to the current weight norm): the update
+    O is rescaled to ||O'||_F = ||W||_F, then W <- W - eta * O', i.e.
+    W - eta * ||W||_F * O / ||O||_F.  A zero O leaves W unchanged.  (The shape
+    scale of Muon's O cancels in the rescaling.)"""
+    W = _f64(W)
+    O = _f64(O)
+    nO = np.linalg.norm(O)
+    if not nO > 0:
+        return W.copy()
+    return W - float(eta) * (np.linalg.norm(W) / nO) * O
+
+
 # ---------------------------------------------------------------------------
 # frob_project and the whole step
 # ---------------------------------------------------------------------------
-def frob_project(W, U, eta, rho, zero_rel_eps: float = 1e-6):
-    """W <- rho * Pi(W - eta * U/||U||); ``U is None`` is the plain projection
-    W <- rho * W / ||W|| ([HB] Method)."""
+def frob_project(W, U, eta, rho, zero_rel_eps: float = 1e-6, step: str = "unit"):
+    """W <- rho * Pi(W - eta * U/||U||) (``step="radius"``: eta * rho * U/||U||);
+    ``U is None`` is the plain projection W <- rho * W / ||W|| ([HB] Method)."""
     if U is None:
         U = np.zeros_like(_f64(W))
-    return hyperball(W, U, eta, rho, zero_rel_eps)
+    return hyperball(W, U, eta, rho, zero_rel_eps, step)
 
 
 def muonh_step(Ws, Gs, Ms, eta, beta, K, rhos, tile_T: int = 0, hook: str = "hyperball",
                coeffs=None, outward: float = 0.5, inward: float = 1.0,
                zero_rel_eps: float = 1e-6, state_bf16: bool = False,
-               ema: bool = False, nesterov: bool = False, weight_decay: float = 0.0):
+               ema: bool = False, nesterov: bool = False, weight_decay: float = 0.0,
+               hb_step: str = "unit"):
     """One MuonH (or HiMuon-H / Muon+RadialBrake / plain Muon) step over a
     list of matrices.
 
@@ -299,8 +322,9 @@ def muonh_step(Ws, Gs, Ms, eta, beta, K, rhos, tile_T: int = 0, hook: str = "hyp
     exponential average of the code section with ``ema``) -> the Newton-Schulz
     input (the buffer, or the Nesterov blend with ``nesterov``) -> NS ([MUON]
     Eq. 6 / code; tiled per [HIMUON] when tile_T > 0) -> Hyperball ([HB]
-    Algorithm 1), RadialBrake ([HOOKS]) or no hook (``"none"``: Muon's own
-    update with decoupled weight decay).
+    Algorithm 1; ``hb_step`` selects the unit or radius-sized step),
+    RadialBrake ([HOOKS]), RelativeUpdate (``"relative"``, [HOOKS]) or no hook
+    (``"none"``: Muon's own update with decoupled weight decay).
 
     ``state_bf16`` models a bf16 momentum buffer: the updated M is stored
     rounded to bf16 and the NS input is formed from the stored value.
@@ -315,7 +339,9 @@ def muonh_step(Ws, Gs, Ms, eta, beta, K, rhos, tile_T: int = 0, hook: str = "hyp
         x = nesterov_input(G, m, beta, ema) if nesterov else m
         O = orthogonalize(x, K, tile_T, coeffs)
         if hook == "hyperball":
-            w, f = hyperball(W, O, eta, rhos[i], zero_rel_eps)
+            w, f = hyperball(W, O, eta, rhos[i], zero_rel_eps, hb_step)
+        elif hook == "relative":
+            w, f = relative_update(W, O, eta), None
         elif hook == "radial_brake":
             w, f = radial_brake(W, O, eta, outward, inward), None
         elif hook == "none":

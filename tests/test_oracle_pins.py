@@ -475,6 +475,75 @@ def test_hyperball_zero_update_projects_only():
     assert np.allclose(got, 4.0 * W / np.linalg.norm(W), rtol=1e-15, atol=0)
 
 
+def test_hyperball_radius_step_turns_by_atan_eta():
+    # Radius-sized step: for an update orthogonal to W the weight turns by
+    # atan(eta) whatever rho is (the unit step turns by atan(eta / rho)).
+    eta = 0.3
+    e1 = np.zeros((3, 5)); e1[0, 1] = 1.0
+    e2 = np.zeros((3, 5)); e2[2, 4] = 1.0
+    for rho in (0.5, 2.0, 7.0):
+        got, flag = orc.hyperball(rho * e1, 9.0 * e2, eta, rho, step="radius")
+        assert flag == orc.FLAG_PROJECTED
+        assert abs(math.atan2(-got[2, 4], got[0, 1]) - math.atan(eta)) < 1e-14
+        unit, _ = orc.hyperball(rho * e1, 9.0 * e2, eta, rho)
+        assert abs(math.atan2(-unit[2, 4], unit[0, 1]) - math.atan(eta / rho)) < 1e-14
+        assert abs(np.linalg.norm(got) - rho) < 1e-14
+
+
+def test_hyperball_radius_step_is_unit_step_at_unit_radius():
+    W = gen.gaussian((6, 9), 1.0, 30).astype(np.float64)
+    W /= np.linalg.norm(W)
+    U = gen.gaussian((6, 9), 1.0, 31)
+    a, _ = orc.hyperball(W, U, 0.05, 1.0)
+    b, _ = orc.hyperball(W, U, 0.05, 1.0, step="radius")
+    assert np.array_equal(a, b)
+
+
+def test_hyperball_radius_step_exact_cancel_restores():
+    # W = eta * rho * U_hat cancels exactly under the radius step.
+    rho, eta = 2.0, 0.5
+    U = np.zeros((4, 4)); U[1, 3] = 3.0
+    W = np.zeros((4, 4)); W[1, 3] = eta * rho
+    got, flag = orc.hyperball(W, U, eta, rho, step="radius")
+    assert flag == orc.FLAG_RESTORED
+    assert got[1, 3] == rho and np.count_nonzero(got) == 1
+
+
+def test_relative_update_worked_example():
+    # ||W|| = 5, O along the second coordinate: W - 0.1 * 5 * (0, 1)
+    got = orc.relative_update(np.array([[3.0, 4.0]]), np.array([[0.0, 2.0]]), 0.1)
+    assert np.array_equal(got, np.array([[3.0, 3.5]]))
+
+
+def test_relative_update_step_length_and_direction():
+    W = gen.gaussian((12, 20), 0.02, 32).astype(np.float64)
+    O = gen.gaussian((12, 20), 1.0, 33).astype(np.float64)
+    eta = 0.07
+    got = orc.relative_update(W, O, eta)
+    d = got - W
+    assert abs(np.linalg.norm(d) - eta * np.linalg.norm(W)) < 1e-15
+    cos = -np.sum(d * O) / (np.linalg.norm(d) * np.linalg.norm(O))
+    assert abs(cos - 1) < 1e-14
+    # invariant to the scale of O (so also to Muon's shape scale)
+    assert np.allclose(orc.relative_update(W, 3.7 * O, eta), got, rtol=0, atol=1e-17)
+
+
+def test_relative_update_zero_update_and_zero_weight():
+    W = gen.gaussian((3, 4), 1.0, 34).astype(np.float64)
+    assert np.array_equal(orc.relative_update(W, np.zeros((3, 4)), 0.1), W)
+    # a zero weight takes no step (its norm sets the step length)
+    assert not orc.relative_update(np.zeros((3, 4)), W, 0.1).any()
+
+
+def test_step_relative_hook_composes_the_pieces():
+    W = gen.gaussian((8, 12), 0.02, 35).astype(np.float64)
+    G = gen.gaussian((8, 12), 0.02, 36).astype(np.float64)
+    M = np.zeros((8, 12))
+    nw, nm, Os, _ = orc.muonh_step([W], [G], [M], 0.02, 0.95, 5, [1.0], hook="relative")
+    m = orc.momentum_update(M, G, 0.95)
+    assert np.array_equal(nw[0], orc.relative_update(W, orc.newton_schulz(m, 5), 0.02))
+
+
 def test_frob_project_plain():
     W = gen.gaussian((3, 7), 1.0, 4).astype(np.float64)
     got, _ = orc.frob_project(W, None, 0.1, 2.5)
