@@ -69,6 +69,14 @@ def measured_traffic(cls, args):
     return k["hbm_bytes_per_launch"] if k else None
 
 
+HOOK_DESC = {
+    "hyperball": "Hyperball rho=||W0||_F",
+    "radial_brake": "RadialBrake (outward 0.5, inward 1.0, eta 0.02)",
+    "relative": "RelativeUpdate (step eta*||W||_F along O/||O||_F)",
+    "none": "Muon's own update (shape-scaled O, no weight decay)",
+}
+
+
 def workload_shapes(name):
     from synth import gen
     if name == "gpt2":
@@ -153,7 +161,7 @@ def main():
     ap.add_argument("--workload", default="gpt2")
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--ns-precision", default="fold", choices=["fold", "x32"])
-    ap.add_argument("--hook", default="hyperball", choices=["hyperball", "radial_brake"])
+    ap.add_argument("--hook", default="hyperball", choices=["hyperball", "radial_brake", "relative", "none"])
     ap.add_argument("--K", type=int, default=5)
     ap.add_argument("--lanes", type=int, default=0, choices=[0, 1, 2, 3, 4],
                     help="concurrent lanes of a timed step (0: the library's automatic choice)")
@@ -277,8 +285,7 @@ def main():
         "config": {"workload": f"{wdesc}; MuonH step, K={K} quintic NS "
                                f"{'tiled T=' + str(args.tile) if args.tile else 'full-matrix'}, "
                                f"bf16 grads/momentum, fp32 master weights, "
-                               + ("Hyperball rho=||W0||_F" if args.hook == "hyperball"
-                                  else "RadialBrake (outward 0.5, inward 1.0, eta 0.02)"),
+                               + HOOK_DESC[args.hook],
                    "matrices": len(shapes), "K": K, "tile_T": args.tile, "ns_precision": args.ns_precision,
                    "hook": args.hook,
                    "elements": sum(h * w for h, w in shapes), "chunks": q["chunks"], "lanes": q["lanes"]},

@@ -86,7 +86,13 @@ enum { MUONH_F32 = 0, MUONH_BF16 = 1 };
 enum { MUONH_NS_X32 = 0, MUONH_NS_FOLD = 1 };
 
 /* weight-update hook */
-enum { MUONH_HOOK_HYPERBALL = 0, MUONH_HOOK_RADIAL_BRAKE = 1, MUONH_HOOK_NONE = 2 };
+enum { MUONH_HOOK_HYPERBALL = 0, MUONH_HOOK_RADIAL_BRAKE = 1, MUONH_HOOK_NONE = 2, MUONH_HOOK_RELATIVE = 3 };
+
+/* Hyperball step length (opts.hyperball_step).  UNIT: W' = W - eta*U_hat, the
+ * Hyperball show notes' Algorithm 1 (default).  RADIUS: W' = W - eta*rho*U_hat,
+ * the hook PR description's wording (the update is normalized to the target
+ * radius before it is applied).  Both then re-project onto radius rho. */
+enum { MUONH_HB_STEP_UNIT = 0, MUONH_HB_STEP_RADIUS = 1 };
 
 typedef struct muonh_opts {
   void*        stream;          /* hipStream_t to queue on; NULL = null stream */
@@ -99,8 +105,11 @@ typedef struct muonh_opts {
   float        ns_eps;          /* added to ||M||_F before dividing; default 1e-7 */
   float        zero_rel_eps;    /* Hyperball: ||W - eta*U_hat|| < zero_rel_eps*rho counts as
                                    zero and restores the radius; default 1e-6 */
-  int          hook;            /* MUONH_HOOK_HYPERBALL (default), MUONH_HOOK_RADIAL_BRAKE or
-                                   MUONH_HOOK_NONE (Muon's own update, see weight_decay) */
+  int          hook;            /* MUONH_HOOK_HYPERBALL (default), MUONH_HOOK_RADIAL_BRAKE,
+                                   MUONH_HOOK_NONE (Muon's own update, see weight_decay) or
+                                   MUONH_HOOK_RELATIVE (hook PR, review summary: the update is
+                                   rescaled to the pre-update ||W||_F, W <- W - eta*||W||*O/||O||;
+                                   O = 0 leaves W; no re-projection, rho ignored) */
   float        outward;         /* RadialBrake factor when the norm grows, in [0,1]; default 0.5 */
   float        inward;          /* RadialBrake factor otherwise, in [0,1]; default 1.0 */
   float        rb_eps;          /* RadialBrake: post-update norm <= rb_eps leaves W'; default 1e-15 */
@@ -121,6 +130,8 @@ typedef struct muonh_opts {
                                    the others on library-owned side streams (see the stream
                                    convention above); 1: all work on opts->stream.  Results
                                    are identical for every value. */
+  int          hyperball_step;  /* MUONH_HB_STEP_UNIT (default) or MUONH_HB_STEP_RADIUS; also
+                                   used by frob_project */
 } muonh_opts;
 
 /* Fill *o with the defaults listed above. */
@@ -135,14 +146,15 @@ void muonh_default_opts(muonh_opts* o);
  *   grads[i]   device, state_dtype, same shape, read only (G)
  *   moms[i]    device, state_dtype, same shape, updated in place (M)
  *   shapes     host, 2*n int64: rows, cols of matrix i (each >= 1; with
-              tile_T = 0 or > 128, pad64(rows) * pad64(cols) * operand bytes
-              must stay below 4 GiB, else MUONH_ENOTIMPL)
+ *              tile_T = 0 or > 128, pad64(rows) * pad64(cols) * operand bytes
+ *              must stay below 4 GiB, else MUONH_ENOTIMPL)
  *   n          number of matrices (>= 1)
  *   eta        learning rate / Hyperball angular step (finite, >= 0)
  *   beta       momentum coefficient, in [0, 1)
  *   K          Newton-Schulz iterations, 0..64 (0: O = M / (||M|| + eps))
  *   rho        host, n floats: Hyperball radius per matrix (finite, > 0);
- *              ignored (may be NULL) for RadialBrake and MUONH_HOOK_NONE
+ *              ignored (may be NULL) for RadialBrake, MUONH_HOOK_NONE and
+ *              MUONH_HOOK_RELATIVE
  *   tile_T     0 = full-matrix NS; > 0 = Hierarchical Muon with tile side tile_T
  *              (1..128, or a multiple of 64 up to 8192); the hook always acts on
  *              the full matrix
@@ -164,6 +176,7 @@ int ns_orthogonalize(const void* const in[], void* const out[], const int64_t sh
 /*
  * frob_project -- the Hyperball projection on its own:
  *   W[i] <- rho[i] * Pi(W[i] - eta * U[i] / ||U[i]||)
+ * (eta * rho[i] * U[i] / ||U[i]|| with opts->hyperball_step = RADIUS)
  * with the same zero rules as muonh_step.  W: device fp32, in place.
  * U: NULL (plain projection W <- rho * W / ||W||) or an array of n device
  * buffers of opts->state_dtype (a NULL entry is treated as a zero update).

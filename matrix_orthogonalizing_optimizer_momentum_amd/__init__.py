@@ -16,7 +16,8 @@ Entry points mirror the C ABI in ``include/muonh.h``:
 
 ``opts`` keywords: ``ns_dtype`` ("bf16" | "f32"), ``ns_precision``
 ("fold" | "x32"), ``coeffs`` (K rows of (a, b, c)), ``ns_eps``,
-``zero_rel_eps``, ``hook`` ("hyperball" | "radial_brake" | "none"),
+``zero_rel_eps``, ``hook`` ("hyperball" | "radial_brake" | "relative" | "none"),
+``hyperball_step`` ("unit" | "radius"),
 ``outward``, ``inward``, ``rb_eps``, ``workspace_limit`` (bytes),
 ``momentum`` ("sum" | "ema"), ``nesterov`` (bool), ``weight_decay`` (for
 hook "none"), ``lanes`` (concurrent lanes 1..4; 0: library default),
@@ -33,7 +34,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuonh.so
 MUONH_OK, MUONH_EINVAL, MUONH_ENOMEM, MUONH_EHIP, MUONH_ENOTIMPL = 0, -1, -2, -3, -4
 MUONH_F32, MUONH_BF16 = 0, 1
 MUONH_NS_X32, MUONH_NS_FOLD = 0, 1
-MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE, MUONH_HOOK_NONE = 0, 1, 2
+MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE, MUONH_HOOK_NONE, MUONH_HOOK_RELATIVE = 0, 1, 2, 3
+MUONH_HB_STEP_UNIT, MUONH_HB_STEP_RADIUS = 0, 1
 
 EXPORTED = (
     "muonh_default_opts", "muonh_step", "ns_orthogonalize", "frob_project", "muonh_get_flags",
@@ -73,6 +75,7 @@ class Opts(ctypes.Structure):
         ("nesterov", c_int),
         ("weight_decay", c_float),
         ("lanes", c_int),
+        ("hyperball_step", c_int),
     ]
 
 
@@ -177,7 +180,8 @@ def _dtype_code(t) -> int:
 
 def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coeffs=None, ns_eps=None,
               zero_rel_eps=None, hook="hyperball", outward=None, inward=None, rb_eps=None,
-              workspace_limit=0, stream=None, K=None, momentum="sum", nesterov=False, weight_decay=None, lanes=0):
+              workspace_limit=0, stream=None, K=None, momentum="sum", nesterov=False, weight_decay=None, lanes=0,
+              hyperball_step="unit"):
     """Build an Opts struct; returns (opts, keepalive) where keepalive holds
     buffers the struct points to."""
     lib = load()
@@ -199,7 +203,8 @@ def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coef
     if zero_rel_eps is not None:
         o.zero_rel_eps = zero_rel_eps
     o.hook = {"hyperball": MUONH_HOOK_HYPERBALL, "radial_brake": MUONH_HOOK_RADIAL_BRAKE,
-              "none": MUONH_HOOK_NONE}[hook]
+              "none": MUONH_HOOK_NONE, "relative": MUONH_HOOK_RELATIVE}[hook]
+    o.hyperball_step = {"unit": MUONH_HB_STEP_UNIT, "radius": MUONH_HB_STEP_RADIUS}[hyperball_step]
     o.momentum_ema = {"sum": 0, "ema": 1}[momentum]
     o.nesterov = 1 if nesterov else 0
     if weight_decay is not None:

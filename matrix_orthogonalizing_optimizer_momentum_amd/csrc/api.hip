@@ -176,7 +176,9 @@ int resolve(const muonh_opts* in, int K, Resolved& r) {
   if (o.state_dtype != MUONH_BF16 && o.state_dtype != MUONH_F32) return MUONH_EINVAL;
   if (o.ns_dtype != MUONH_BF16 && o.ns_dtype != MUONH_F32) return MUONH_EINVAL;
   if (o.ns_precision != MUONH_NS_X32 && o.ns_precision != MUONH_NS_FOLD) return MUONH_EINVAL;
-  if (o.hook != MUONH_HOOK_HYPERBALL && o.hook != MUONH_HOOK_RADIAL_BRAKE && o.hook != MUONH_HOOK_NONE)
+  if (o.hyperball_step != MUONH_HB_STEP_UNIT && o.hyperball_step != MUONH_HB_STEP_RADIUS) return MUONH_EINVAL;
+  if (o.hook != MUONH_HOOK_HYPERBALL && o.hook != MUONH_HOOK_RADIAL_BRAKE && o.hook != MUONH_HOOK_NONE &&
+      o.hook != MUONH_HOOK_RELATIVE)
     return MUONH_EINVAL;
   if ((o.momentum_ema != 0 && o.momentum_ema != 1) || (o.nesterov != 0 && o.nesterov != 1)) return MUONH_EINVAL;
   if (!finite_f(o.weight_decay) || o.weight_decay < 0.f) return MUONH_EINVAL;
@@ -225,8 +227,12 @@ Cfg make_cfg(int kind, int n, int K, int tile_T, const Resolved& r, size_t limit
   c.state_dt = r.o.state_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.op_dt = r.o.ns_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.x32 = (c.op_dt == DT_BF16 && r.o.ns_precision == MUONH_NS_X32) ? 1 : 0;
-  c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB : r.o.hook == MUONH_HOOK_NONE ? kModeNone : kModeHB;
+  c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB
+           : r.o.hook == MUONH_HOOK_NONE        ? kModeNone
+           : r.o.hook == MUONH_HOOK_RELATIVE    ? kModeRel
+                                                : kModeHB;
   if (kind == CALL_PROJ) c.hook = kModeHB;  // frob_project is the Hyperball projection
+  c.hb_radius = r.o.hyperball_step == MUONH_HB_STEP_RADIUS ? 1 : 0;
   c.ws_limit = limit;
   c.lanes = r.o.lanes;
   return c;
@@ -308,13 +314,11 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   key.push_back((uint64_t)cfg.op_dt);
   key.push_back((uint64_t)cfg.x32);
   key.push_back((uint64_t)cfg.hook);
+  key.push_back((uint64_t)cfg.hb_radius);
   key.push_back((uint64_t)plan.chunks.size());
   key.push_back((uint64_t)plan.lanes);
   for (const auto& c : plan.chunks) key.push_back((uint64_t)c.m1);
   key.push_back((uint64_t)(uintptr_t)st.ws);
-  uint32_t eb;
-  memcpy(&eb, &p.eta, 4);
-  key.push_back(cfg.hook != kModeHB ? eb : 0);  // RadialBrake / plain tables hold eta * shape scale
   for (int i = 0; i < 2 * cfg.n; ++i) key.push_back((uint64_t)shapes[i]);
   key_push_ptrs(key, p.params, cfg.kind == CALL_NS ? 0 : cfg.n);
   key_push_ptrs(key, p.grads, cfg.n);
@@ -617,6 +621,7 @@ void muonh_default_opts(muonh_opts* o) {
   o->nesterov = 0;
   o->weight_decay = 0.f;
   o->lanes = 0;
+  o->hyperball_step = MUONH_HB_STEP_UNIT;
 }
 
 int muonh_step(void* const params[], const void* const grads[], void* const moms[], const int64_t shapes[],

@@ -86,7 +86,8 @@ struct HookMat {
   int32_t slot;         // slot for this matrix's pass-1 sums
   int32_t nblocks;      // blocks of this matrix in a pass
   float rho;            // Hyperball radius
-  float oscale;         // RadialBrake: eta * max(1, H/W)^0.5
+  float oscale;         // Hyperball: step scale (1, or rho for the radius-sized step);
+                        // RadialBrake / plain update: shape scale max(1, H/W)^0.5
 };
 
 struct HookBlock {
@@ -132,6 +133,7 @@ struct TileArgs {
 constexpr int kModeHB = 0;    // Hyperball
 constexpr int kModeRB = 1;    // RadialBrake
 constexpr int kModeNone = 2;  // Muon's own update (decoupled weight decay)
+constexpr int kModeRel = 3;   // RelativeUpdate (update scaled to ||W||)
 
 // Elements per block of the flat hook / norm passes (256 threads x 32).
 constexpr int kHookBlockElems = 8192;

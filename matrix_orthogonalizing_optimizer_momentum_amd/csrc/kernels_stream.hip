@@ -5,11 +5,12 @@
 //                    unit's workspace (the wide-side orientation of the
 //                    Muon explainer's code section is a layout choice here,
 //                    never a copy of its own);
-//   k_hook_reduce    pass 1 of the Hyperball / RadialBrake hook: per-matrix
-//                    sums of ||W'||^2 and ||W||^2 in fp64;
-//   k_hook_write     pass 2: re-projection / brake (Hyperball show notes,
-//                    Algorithm 1 and Method; hook PR, PR description and the
-//                    zero-norm review comments);
+//   k_hook_reduce    pass 1 of the Hyperball / RadialBrake / RelativeUpdate
+//                    hook: per-matrix sums of ||W'||^2 and ||W||^2 in fp64;
+//   k_hook_write     pass 2: re-projection / brake / relative step
+//                    (Hyperball show notes, Algorithm 1 and Method; hook PR,
+//                    PR description, review summary and the zero-norm review
+//                    comments);
 //   k_sumsq          per-matrix ||U||^2 for the stand-alone projection.
 // All of them are bandwidth-bound: 16-byte vector accesses, 64x64 blocks
 // with an LDS transpose where a layout flips, one deterministic fp64
@@ -163,13 +164,16 @@ __device__ __forceinline__ void load8_dyn(const void* p, int64_t i, int dtype, f
   else load8(reinterpret_cast<const float*>(p), i, v);
 }
 
-// Coefficient applied to O in W' = W - coef * O.
+// Coefficient applied to O in W' = W - coef * O: eta times the shape scale
+// (RadialBrake, plain update), eta / ||O|| times the step scale (Hyperball:
+// 1 or rho), eta ||W|| / ||O|| (RelativeUpdate, from pass 1's ||W||^2).
 __device__ __forceinline__ float hook_coef(const HookMat& hm, const SlotTable& st, float eta, int mode) {
-  if (mode != kModeHB) return hm.oscale;
+  if (mode == kModeRB || mode == kModeNone) return eta * hm.oscale;
   if (hm.o == nullptr || hm.onorm_slot < 0) return 0.f;
   const double n2 = st.sums[2 * hm.onorm_slot];
   if (!(n2 > 0.0)) return 0.f;
-  return (float)((double)eta / sqrt(n2));
+  if (mode == kModeRel) return (float)((double)eta * sqrt(st.sums[2 * hm.slot + 1]) / sqrt(n2));
+  return (float)((double)eta * (double)hm.oscale / sqrt(n2));
 }
 
 template <int MODE>
@@ -177,7 +181,9 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_reduce(
     const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st, float eta) {
   const HookBlock hb = blocks[blockIdx.x];
   const HookMat hm = mats[hb.mat];
-  const float coef = hook_coef(hm, st, eta, MODE);
+  // RelativeUpdate needs only ||W||^2 here (its coefficient depends on it).
+  const float coef = MODE == kModeRel ? 0.f : hook_coef(hm, st, eta, MODE);
+  const void* const op = MODE == kModeRel ? nullptr : hm.o;
   double s0 = 0.0, s1 = 0.0;
   const int64_t base = (int64_t)hb.blk * kHookBlockElems;
 #pragma unroll
@@ -187,13 +193,13 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_reduce(
     float w[8], o[8];
     if (i + 8 <= hm.numel) {
       load8(hm.w, i, w);
-      if (hm.o) load8_dyn(hm.o, i, hm.o_dtype, o);
+      if (op) load8_dyn(op, i, hm.o_dtype, o);
       else for (int k = 0; k < 8; ++k) o[k] = 0.f;
     } else {
       for (int k = 0; k < 8; ++k) {
         const bool ok = i + k < hm.numel;
         w[k] = ok ? hm.w[i + k] : 0.f;
-        o[k] = (ok && hm.o) ? load_dyn(hm.o, i + k, hm.o_dtype) : 0.f;
+        o[k] = (ok && op) ? load_dyn(op, i + k, hm.o_dtype) : 0.f;
       }
     }
 #pragma unroll
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
   // Per-matrix decision, identical in every block of the matrix.
   int branch;          // 0: scale W', 1: scale W (restore), 2: leave W
   double scale;
-  if (MODE == kModeNone) {
+  if (MODE == kModeNone || MODE == kModeRel) {
     branch = 0;
     scale = 1.0;
   } else if (MODE == kModeRB) {
@@ -234,8 +240,10 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
     else { branch = 2; scale = 1.0; }
   }
   if (hb.blk == 0 && threadIdx.x == 0 && flags != nullptr) {
-    if (MODE == kModeHB) {
+    if (MODE == kModeHB || MODE == kModeRel) {
       if (coef == 0.f && hm.o != nullptr) atomicAdd(&flags->zero_update, 1ull);
+    }
+    if (MODE == kModeHB) {
       if (branch == 1) atomicAdd(&flags->restored, 1ull);
       if (branch == 2) atomicAdd(&flags->unrestorable, 1ull);
     }
@@ -266,6 +274,8 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
       if (MODE == kModeNone) {
         // Muon explainer, code section: decoupled decay, then W - eta * O'
         r[k] = fmaf(-coef, o[k], w[k] * decay);
+      } else if (MODE == kModeRel) {
+        r[k] = fmaf(-coef, o[k], w[k]);
       } else {
         const float base_v = (branch == 0) ? fmaf(-coef, o[k], w[k]) : w[k];
         r[k] = (float)((double)base_v * scale);
@@ -348,6 +358,8 @@ hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* bl
   if (nblocks <= 0) return hipSuccess;
   if (mode == kModeRB)
     hipLaunchKernelGGL((k_hook_reduce<kModeRB>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, eta);
+  else if (mode == kModeRel)
+    hipLaunchKernelGGL((k_hook_reduce<kModeRel>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, eta);
   else
     hipLaunchKernelGGL((k_hook_reduce<kModeHB>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, eta);
   return hipGetLastError();
@@ -362,6 +374,7 @@ hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blo
                      zero_rel_eps, outward, inward, rb_eps, decay, flags)
   if (mode == kModeRB) MUONH_HW(kModeRB);
   else if (mode == kModeNone) MUONH_HW(kModeNone);
+  else if (mode == kModeRel) MUONH_HW(kModeRel);
   else MUONH_HW(kModeHB);
 #undef MUONH_HW
   return hipGetLastError();

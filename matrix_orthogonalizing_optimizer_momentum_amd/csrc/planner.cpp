@@ -127,9 +127,10 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
     plan.units += m.nunits;
     const double sb = cfg.state_dt == DT_F32 ? 4 : 2;
     const double ob = esize(cfg.op_dt);
-    // momentum 3 passes; hook pass 1 (not for Muon's own update) and pass 2
-    if (cfg.kind == CALL_STEP)
-      plan.stream_bytes += (double)numel * (3 * sb + (cfg.hook == kModeNone ? 0 : 4 + ob) + (4 + ob + 4));
+    // momentum 3 passes; hook pass 1 (none for Muon's own update; W only for
+    // RelativeUpdate) and pass 2
+    const double hook1 = cfg.hook == kModeNone ? 0 : cfg.hook == kModeRel ? 4 : 4 + ob;
+    if (cfg.kind == CALL_STEP) plan.stream_bytes += (double)numel * (3 * sb + hook1 + (4 + ob + 4));
     else plan.stream_bytes += (double)numel * (sb + sb);  // NS: read input, write output
   }
   // chunks
@@ -386,7 +387,8 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       hm.nblocks = (int)((hm.numel + kHookBlockElems - 1) / kHookBlockElems);
       hm.slot = s_hook0 + mi;
       hm.rho = p.rho ? p.rho[gi] : 1.0f;
-      hm.oscale = (float)((double)p.eta * std::sqrt(std::max(1.0, (double)m.H / (double)m.W)));
+      hm.oscale = cfg.hook == kModeHB ? (cfg.hb_radius ? hm.rho : 1.0f)
+                                      : (float)std::sqrt(std::max(1.0, (double)m.H / (double)m.W));
       if (cfg.kind == CALL_STEP) {
         hm.o = obuf[mi];
         hm.o_dtype = cfg.op_dt;
@@ -403,7 +405,8 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       t.hook_mats.push_back(hm);
       for (int b = 0; b < hm.nblocks; ++b) t.hook_blocks.push_back({idx, b});
       const double ob = hm.o ? esize(hm.o_dtype) : 0;
-      if (cfg.hook != kModeNone) t.bytes_hook1 += (double)hm.numel * (4 + ob);
+      if (cfg.hook == kModeRel) t.bytes_hook1 += (double)hm.numel * 4;  // ||W||^2 only
+      else if (cfg.hook != kModeNone) t.bytes_hook1 += (double)hm.numel * (4 + ob);
       t.bytes_hook2 += (double)hm.numel * (4 + ob + 4);
       if (cfg.kind == CALL_PROJ && hm.o) t.bytes_sumsq += (double)hm.numel * ob;
     }

@@ -22,7 +22,8 @@ struct Cfg {
   int tile_T;
   int state_dt, op_dt;
   int x32;        // fp32 master X (bf16 operands only)
-  int hook;       // kModeHB / kModeRB / kModeNone
+  int hook;       // kModeHB / kModeRB / kModeNone / kModeRel
+  int hb_radius;  // Hyperball: radius-sized step (eta * rho * U_hat)
   size_t ws_limit;
   int lanes;      // concurrent lanes, 1..kMaxLanes; 0: automatic (see make_plan)
 };

@@ -77,7 +77,7 @@ def test_step_rejects_bad_options():
     for field, val in [("state_dtype", 7), ("ns_dtype", 3), ("ns_precision", 9), ("hook", 5),
                        ("outward", 1.5), ("inward", -0.1), ("ns_eps", float("nan")), ("momentum_ema", 2),
                        ("nesterov", -1), ("weight_decay", -0.5), ("weight_decay", float("inf")),
-                       ("lanes", -1), ("lanes", 5)]:
+                       ("lanes", -1), ("lanes", 5), ("hook", 4), ("hyperball_step", 2)]:
         o = _opts()
         setattr(o, field, val)
         assert _step(opts=o) == mm.MUONH_EINVAL, field
@@ -88,6 +88,7 @@ def test_default_options():
     assert (o.state_dtype, o.ns_dtype, o.ns_precision, o.hook) == (mm.MUONH_BF16, mm.MUONH_BF16, mm.MUONH_NS_FOLD,
                                                                    mm.MUONH_HOOK_HYPERBALL)
     assert (o.momentum_ema, o.nesterov, o.weight_decay, o.workspace_limit, o.lanes) == (0, 0, 0.0, 0, 0)
+    assert o.hyperball_step == mm.MUONH_HB_STEP_UNIT
     assert abs(o.ns_eps - 1e-7) < 1e-12 and abs(o.zero_rel_eps - 1e-6) < 1e-11
     assert (o.outward, o.inward) == (0.5, 1.0)
 
@@ -129,6 +130,16 @@ def test_plain_update_needs_no_radius_and_no_hook_pass():
     sh = (ctypes.c_int64 * 2)(64, 64)
     assert lib.muonh_plan_query(sh, 1, 5, 0, ctypes.byref(o), 0, out) == mm.MUONH_OK
     assert out[5] == 64 * 64 * 16  # 6 (momentum) + 10 (update pass)
+
+
+def test_relative_update_needs_no_radius_and_reads_only_w_in_pass_one():
+    o = _opts()
+    o.hook = mm.MUONH_HOOK_RELATIVE
+    lib = mm.load()
+    out = (ctypes.c_int64 * 7)()
+    sh = (ctypes.c_int64 * 2)(64, 64)
+    assert lib.muonh_plan_query(sh, 1, 5, 0, ctypes.byref(o), 0, out) == mm.MUONH_OK
+    assert out[5] == 64 * 64 * 20  # 6 (momentum) + 4 (||W||^2) + 10 (update pass)
 
 
 def test_step_rejects_null_pointers_and_aliasing():

@@ -522,6 +522,67 @@ def test_step_radial_brake(ns):
         assert rel(host(w_t[i]) - Ws[i], Wn[0] - Ws[i]) <= TOL[ns]
 
 
+@pytest.mark.parametrize("ns,tile", [("f32", 0), ("bf16", 0), ("bf16", 64), ("f32", 192)])
+def test_step_relative_update(ns, tile):
+    # RelativeUpdate: W - eta ||W|| O / ||O||, no radius, no re-projection
+    banner(f"relative update ns={ns} tile={tile}")
+    shapes = [(256, 128), (128, 384), (200, 200)]
+    Ws, Gs, Ms = [], [], []
+    for i, (H, W) in enumerate(shapes):
+        Ws.append(gen.gaussian((H, W), 0.02, 320 + i))
+        Gs.append(gen.gaussian((H, W), 0.02, 420 + i))
+        Ms.append(gen.gaussian((H, W), 0.02, 520 + i))
+    w_t = [dev(w) for w in Ws]
+    mm.muonh_step(w_t, [dev(g) for g in Gs], [dev(m) for m in Ms], eta=0.02, beta=0.95, K=5, rho=None,
+                  tile_T=tile, hook="relative", ns_dtype=ns)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        Wn, _, _, _ = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.02, np.float32(0.95), 5, None, tile_T=tile,
+                                     hook="relative")
+        d_gpu, d_ref = host(w_t[i]) - Ws[i], Wn[0] - Ws[i]
+        err = rel(d_gpu, d_ref)
+        print(f"  matrix {i} {shapes[i]} step rel err {err:.3e}")
+        assert err <= TOL[ns]
+        # the step length is eta ||W|| by construction, whatever the NS precision
+        w64 = Ws[i].astype(np.float64)
+        assert abs(np.linalg.norm(d_gpu) / (0.02 * np.linalg.norm(w64)) - 1) < 1e-4
+
+
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+def test_step_hyperball_radius_step(ns):
+    banner(f"hyperball radius step ns={ns}")
+    shapes = [(128, 64), (64, 192), (96, 96)]
+    Ws, Gs, Ms = [], [], []
+    for i, (H, W) in enumerate(shapes):
+        Ws.append(gen.gaussian((H, W), 0.02, 330 + i))
+        Gs.append(gen.gaussian((H, W), 0.02, 430 + i))
+        Ms.append(gen.gaussian((H, W), 0.02, 530 + i))
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    w_t = [dev(w) for w in Ws]
+    mm.muonh_step(w_t, [dev(g) for g in Gs], [dev(m) for m in Ms], eta=0.2, beta=0.95, K=5, rho=rhos,
+                  hyperball_step="radius", ns_dtype=ns)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        Wn, _, _, flags = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.2, np.float32(0.95), 5, [rhos[i]],
+                                         hb_step="radius")
+        got = host(w_t[i])
+        assert flags[0] == orc.FLAG_PROJECTED
+        assert abs(np.linalg.norm(got) / float(rhos[i]) - 1) <= 1e-5
+        assert rel(got - Ws[i], Wn[0] - Ws[i]) <= TOL[ns]
+
+
+def test_frob_project_radius_step():
+    banner("frob_project radius step")
+    Ws = [gen.gaussian((50, 70), 1.0, 11), gen.gaussian((128, 32), 1.0, 12)]
+    Us = [gen.gaussian((50, 70), 1.0, 13), gen.gaussian((128, 32), 1.0, 14)]
+    rho = [2.5, 0.75]
+    wt = [dev(w) for w in Ws]
+    mm.frob_project(wt, [dev(u) for u in Us], 0.3, rho, hyperball_step="radius")
+    torch.cuda.synchronize()
+    for w, u, g, r in zip(Ws, Us, wt, rho):
+        assert np.allclose(host(g), orc.frob_project(w, u, 0.3, r, step="radius")[0], rtol=1e-5, atol=1e-6)
+
+
 def test_radial_brake_tiny_matrix():
     # A 3x4 weight along a 3-4-5 direction with a gradient against it.
     banner("radial brake 3x4")
@@ -590,7 +651,8 @@ def _step_with_lanes(lanes, shapes, Ws, Gs, Ms, rhos, **kw):
 
 
 @pytest.mark.parametrize("tile,hook,lanes", [(0, "hyperball", 2), (0, "radial_brake", 3), (0, "none", 4),
-                                             (64, "hyperball", 2), (128, "radial_brake", 4), (256, "hyperball", 3)])
+                                             (64, "hyperball", 2), (128, "radial_brake", 4), (256, "hyperball", 3),
+                                             (0, "relative", 2)])
 def test_lanes_equal_one_lane_bitwise(tile, hook, lanes):
     # The lane split only changes which stream a matrix runs on.
     banner(f"lanes={lanes} tile={tile} hook={hook}")
