@@ -30,6 +30,11 @@ pages give, with no blocking, fusion or reordering.  Sources (page titles):
   independently, reassemble.
 * [NMUON] "The Newton-Muon Optimizer" -- abstract: msgn(X) = U V^T for a
   compact SVD X = U S V^T (used only as a sanity band, never as the target).
+* Adam (for AdamH): [MUON] Equation 2 and its text (two running averages,
+  the gradient's divided by the square root of the squared gradient's); the
+  equation itself did not survive extraction, so the bias-corrected form of
+  the Adam paper on [HB]'s reference list is taken, with the betas of the
+  [MUON] code section's AdamW (0.9, 0.95) as defaults and eps = 1e-8.
 
 Readings taken where the pages are silent:
 
@@ -353,6 +358,65 @@ def muonh_step(Ws, Gs, Ms, eta, beta, K, rhos, tile_T: int = 0, hook: str = "hyp
         Os.append(O)
         flags.append(f)
     return new_W, new_M, Os, flags
+
+
+# ---------------------------------------------------------------------------
+# AdamH: Hyperball around Adam's preconditioned update
+# ---------------------------------------------------------------------------
+def adam_direction(M, V, G, beta1, beta2, eps, t):
+    """Adam's per-coordinate update direction ([MUON] Equation 2 and the text
+    around it: a running average of the gradient and one of its square, the
+    first divided by the square root of the second; the Adam paper cited on
+    the Hyperball page's reference list adds the bias corrections):
+      m <- beta1 m + (1 - beta1) g,   v <- beta2 v + (1 - beta2) g^2,
+      U  = (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps).
+    Returns (m, v, U) in float64; t >= 1 counts this step."""
+    M, V, G = _f64(M), _f64(V), _f64(G)
+    b1, b2, t = float(beta1), float(beta2), int(t)
+    m = b1 * M + (1.0 - b1) * G
+    v = b2 * V + (1.0 - b2) * G * G
+    U = (m / (1.0 - b1 ** t)) / (np.sqrt(v / (1.0 - b2 ** t)) + float(eps))
+    return m, v, U
+
+
+def adamh_step(Ws, Gs, Ms, Vs, eta, beta1, beta2, eps, t, rhos=None, hook: str = "hyperball",
+               outward: float = 0.5, inward: float = 1.0, zero_rel_eps: float = 1e-6,
+               weight_decay: float = 0.0, hb_step: str = "unit", state_f32: bool = True):
+    """AdamH ([HB] Method: Hyperball wraps any base optimizer step, Adam's
+    preconditioned update named first; Key claims and Results report AdamH).
+    Per matrix: Adam's direction U (``adam_direction``), then the hook:
+    Hyperball (default), RadialBrake, RelativeUpdate, or ``"none"`` -- plain
+    AdamW, W <- W (1 - eta wd) - eta U.  There is no shape scale (that is
+    Muon's).  ``state_f32`` models fp32 storage of m and v: U is formed from
+    the stored (fp32-rounded) moments.  Returns (new_Ws, new_Ms, new_Vs, Us, flags)."""
+    out_w, out_m, out_v, Us, flags = [], [], [], [], []
+    for i, (W, G, M, V) in enumerate(zip(Ws, Gs, Ms, Vs)):
+        m, v, U = adam_direction(M, V, G, beta1, beta2, eps, t)
+        if state_f32:
+            m = m.astype(np.float32).astype(np.float64)
+            v = v.astype(np.float32).astype(np.float64)
+            b1, b2 = float(beta1), float(beta2)
+            U = (m / (1.0 - b1 ** int(t))) / (np.sqrt(v / (1.0 - b2 ** int(t))) + float(eps))
+        Wd = _f64(W)
+        if hook == "hyperball":
+            w, f = hyperball(Wd, U, eta, rhos[i], zero_rel_eps, hb_step)
+        elif hook == "relative":
+            w, f = relative_update(Wd, U, eta), None
+        elif hook == "radial_brake":
+            Wp = Wd - float(eta) * U
+            n0, n1 = np.linalg.norm(Wd), np.linalg.norm(Wp)
+            s = float(outward) if n1 > n0 else float(inward)
+            w, f = (Wp * ((n0 + s * (n1 - n0)) / n1) if n1 > RB_EPS else Wp), None
+        elif hook == "none":
+            w, f = Wd * (1.0 - float(eta) * float(weight_decay)) - float(eta) * U, None
+        else:
+            raise ValueError("unknown hook")
+        out_w.append(w)
+        out_m.append(m)
+        out_v.append(v)
+        Us.append(U)
+        flags.append(f)
+    return out_w, out_m, out_v, Us, flags
 
 
 # ---------------------------------------------------------------------------

@@ -662,3 +662,77 @@ def test_planted_unnormalized_update_fails_hyperball_pin():
     expect = rho * (W - eta * U / 7.0) / math.hypot(rho, eta)
     assert np.abs(good - expect).max() < 1e-14
     assert np.abs(wrong - expect).max() > 1e-2
+
+
+# ---------------------------------------------------------------------------
+# AdamH
+# ---------------------------------------------------------------------------
+
+def test_adam_first_step_is_sign_like():
+    # From zero moments the bias corrections give m_hat = g, v_hat = g^2, so
+    # U = g / (|g| + eps) exactly.
+    G = gen.gaussian((5, 7), 1e-3, 40).astype(np.float64)
+    m, v, U = orc.adam_direction(np.zeros((5, 7)), np.zeros((5, 7)), G, 0.9, 0.95, 1e-8, 1)
+    assert np.allclose(U, G / (np.abs(G) + 1e-8), rtol=1e-14, atol=0)
+    assert np.allclose(m, 0.1 * G, rtol=1e-15, atol=0) and np.allclose(v, 0.05 * G * G, rtol=1e-15, atol=0)
+
+
+def test_adam_constant_gradient_bias_correction_is_exact():
+    # m_t = (1 - b1^t) g and v_t = (1 - b2^t) g^2: the corrected ratio stays g / (|g| + eps)
+    G = np.array([[2e-3, -5e-4], [1e-3, 3e-3]])
+    M = np.zeros_like(G); V = np.zeros_like(G)
+    for t in range(1, 9):
+        M, V, U = orc.adam_direction(M, V, G, 0.9, 0.95, 1e-8, t)
+        assert np.allclose(M, (1 - 0.9 ** t) * G, rtol=1e-13, atol=0)
+        assert np.allclose(V, (1 - 0.95 ** t) * G * G, rtol=1e-13, atol=0)
+        assert np.allclose(U, G / (np.abs(G) + 1e-8), rtol=1e-12, atol=0)
+
+
+def test_adam_worked_numbers():
+    # one coordinate by hand: m = 0.9*0.2 + 0.1*0.5 = 0.23, v = 0.95*0.04 + 0.05*0.25 = 0.0505,
+    # t = 2: U = (0.23/0.19) / (sqrt(0.0505/0.0975) + 1e-8)
+    m, v, U = orc.adam_direction(np.array([[0.2]]), np.array([[0.04]]), np.array([[0.5]]), 0.9, 0.95, 1e-8, 2)
+    assert abs(m[0, 0] - 0.23) < 1e-15 and abs(v[0, 0] - 0.0505) < 1e-15
+    assert abs(U[0, 0] - (0.23 / 0.19) / (math.sqrt(0.0505 / 0.0975) + 1e-8)) < 1e-14
+
+
+def test_adamh_keeps_radius_and_steps_along_minus_u():
+    W = gen.gaussian((16, 24), 0.02, 41).astype(np.float64)
+    rho = float(np.linalg.norm(W))
+    G = gen.gaussian((16, 24), 1e-3, 42)
+    nw, nm, nv, Us, fl = orc.adamh_step([W], [G], [np.zeros((16, 24))], [np.zeros((16, 24))], 0.02, 0.9, 0.95,
+                                        1e-8, 1, [rho])
+    assert fl[0] == orc.FLAG_PROJECTED
+    assert abs(np.linalg.norm(nw[0]) - rho) < 1e-13
+    # same as the Hyperball of the Adam direction
+    ref, _ = orc.hyperball(W, Us[0], 0.02, rho)
+    assert np.array_equal(nw[0], ref)
+
+
+def test_adamw_closed_form_first_step():
+    W = gen.gaussian((6, 9), 0.02, 43).astype(np.float64)
+    G = gen.gaussian((6, 9), 1e-3, 44).astype(np.float64)
+    Z = np.zeros((6, 9))
+    nw, _, _, _, _ = orc.adamh_step([W], [G], [Z], [Z], 0.01, 0.9, 0.95, 1e-8, 1, hook="none", weight_decay=0.1,
+                                    state_f32=False)
+    assert np.allclose(nw[0], W * (1 - 0.001) - 0.01 * G / (np.abs(G) + 1e-8), rtol=1e-14, atol=1e-18)
+
+
+def test_adamh_zero_gradient_projects_only():
+    W = gen.gaussian((4, 4), 1.0, 45).astype(np.float64)
+    Z = np.zeros((4, 4))
+    nw, _, _, Us, fl = orc.adamh_step([W], [Z], [Z], [Z], 0.1, 0.9, 0.95, 1e-8, 1, [3.0])
+    assert not Us[0].any() and fl[0] == orc.FLAG_PROJECTED
+    assert np.allclose(nw[0], 3.0 * W / np.linalg.norm(W), rtol=1e-15, atol=0)
+
+
+def test_adam_hooks_match_the_muon_hooks_without_shape_scale():
+    # wide matrix: Muon's shape scale is 1, so the brake and the relative step
+    # of the Adam direction equal the stand-alone hooks applied to U
+    W = gen.gaussian((6, 10), 0.02, 46).astype(np.float64)
+    G = gen.gaussian((6, 10), 1e-3, 47).astype(np.float64)
+    Z = np.zeros((6, 10))
+    for hook, ref in (("radial_brake", lambda U: orc.radial_brake(W, U, 0.02)),
+                      ("relative", lambda U: orc.relative_update(W, U, 0.02))):
+        nw, _, _, Us, _ = orc.adamh_step([W], [G], [Z], [Z], 0.02, 0.9, 0.95, 1e-8, 3, hook=hook)
+        assert np.array_equal(nw[0], ref(Us[0]))
