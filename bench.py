@@ -40,7 +40,7 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 NS_CLASSES = ("ns_gram_G1", "ns_poly_G2", "ns_update_G3", "ns_tile_resident")
-STREAM_CLASSES = ("momentum_prep", "hook_reduce", "hook_write")
+STREAM_CLASSES = ("momentum_prep", "hook_reduce", "hook_write", "adam_moments", "adam_write")
 
 
 def measured_traffic(cls, args):
@@ -153,6 +153,37 @@ def cpu_baseline(shapes, K, tile_T, hook, budget_s=12.0):
                       f"{how}: {step_s:.1f} s/step"}
 
 
+def cpu_baseline_adamh(shapes, hook, budget_s=12.0):
+    """The fp64 oracle's AdamH step on the same matrix set (streaming only,
+    so the whole set fits the budget on the host's cores; else extrapolated by
+    element count)."""
+    import numpy as np
+    from oracle import muonh_oracle as orc
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    total = sum(h * w for h, w in shapes)
+    t_sum, e_sum, done = 0.0, 0, 0
+    t_all = time.perf_counter()
+    while done < len(shapes) and (time.perf_counter() - t_all) < budget_s:
+        sub = [shapes[done]]
+        Ws, Gs, _ = gen.model_set(sub, 2, 1)
+        Z = [np.zeros(s) for s in sub]
+        rho = [float(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+        t0 = time.perf_counter()
+        orc.adamh_step(Ws, Gs, Z, Z, 0.02, 0.9, 0.95, 1e-8, 1, rho, hook=hook)
+        t_sum += time.perf_counter() - t0
+        e_sum += sub[0][0] * sub[0][1]
+        done += 1
+    step_s = t_sum if done == len(shapes) else t_sum * total / e_sum
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(shapes)} matrices timed with the fp64 numpy oracle's AdamH step, "
+                      f"{t_sum:.1f} s; {step_s:.2f} s/step"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +193,8 @@ def main():
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--ns-precision", default="fold", choices=["fold", "x32"])
     ap.add_argument("--hook", default="hyperball", choices=["hyperball", "radial_brake", "relative", "none"])
+    ap.add_argument("--optimizer", default="muonh", choices=["muonh", "adamh"],
+                    help="adamh: the Hyperball wrapper around Adam (streaming only, no Newton-Schulz)")
     ap.add_argument("--K", type=int, default=5)
     ap.add_argument("--lanes", type=int, default=0, choices=[0, 1, 2, 3, 4],
                     help="concurrent lanes of a timed step (0: the library's automatic choice)")
@@ -205,7 +238,17 @@ def main():
         del src, dst
     torch.cuda.synchronize()
 
+    if args.optimizer == "adamh":
+        Ms = [torch.zeros(w.shape, device="cuda") for w in Ws]  # fp32 Adam moments
+        Vs = [torch.zeros(w.shape, device="cuda") for w in Ws]
+    counter = [0]
+
     def step(i, lanes=args.lanes):
+        if args.optimizer == "adamh":
+            counter[0] += 1
+            mm.adamh_step(Ws, Gsets[i % len(Gsets)], Ms, Vs, 0.02, counter[0], rho=rho, hook=args.hook,
+                          workspace_limit=ws_limit)
+            return
         mm.muonh_step(Ws, Gsets[i % len(Gsets)], Ms, eta=0.02, beta=0.95, K=K, rho=rho, tile_T=args.tile,
                       lanes=lanes,
                       ns_precision=args.ns_precision, workspace_limit=ws_limit, hook=args.hook)
@@ -269,8 +312,15 @@ def main():
         if c in prof and prof[c]["total_ms"] > 0:
             kernels[c]["gbps"] = round(prof[c]["bytes"] / (prof[c]["total_ms"] * 1e-3) / 1e9, 1)
 
+    if args.optimizer == "adamh":
+        opt_desc = ("AdamH step (Adam betas 0.9/0.95, eps 1e-8, bias-corrected), bf16 grads, fp32 moments "
+                    "and master weights, " + HOOK_DESC[args.hook])
+    else:
+        opt_desc = (f"MuonH step, K={K} quintic NS "
+                    f"{'tiled T=' + str(args.tile) if args.tile else 'full-matrix'}, "
+                    f"bf16 grads/momentum, fp32 master weights, " + HOOK_DESC[args.hook])
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.optimizer == "muonh" else "AdamH optimizer steps/sec, HBM GB/s",
         "value": round(1000.0 / ms_per_step, 3),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -280,15 +330,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.optimizer == "muonh" else "f32",
         "data": "synthetic (seeded device RNG: W0 ~ N(0, 0.02^2); grads N(0, 1e-3^2) + rank-4 10x spike)",
-        "config": {"workload": f"{wdesc}; MuonH step, K={K} quintic NS "
-                               f"{'tiled T=' + str(args.tile) if args.tile else 'full-matrix'}, "
-                               f"bf16 grads/momentum, fp32 master weights, "
-                               + HOOK_DESC[args.hook],
+        "config": {"workload": f"{wdesc}; {opt_desc}", "optimizer": args.optimizer,
                    "matrices": len(shapes), "K": K, "tile_T": args.tile, "ns_precision": args.ns_precision,
                    "hook": args.hook,
-                   "elements": sum(h * w for h, w in shapes), "chunks": q["chunks"], "lanes": q["lanes"]},
+                   "elements": sum(h * w for h, w in shapes),
+                   "chunks": q["chunks"] if args.optimizer == "muonh" else 1,
+                   "lanes": q["lanes"] if args.optimizer == "muonh" else 1},
         "ns_tflops": round(ns_tflops, 2) if ns_tflops else None,
         "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
         "ns_ms_per_step": round(ns_ms, 4),
@@ -300,7 +349,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shapes, K, args.tile, args.hook)
+        out["cpu_baseline"] = (cpu_baseline(shapes, K, args.tile, args.hook) if args.optimizer == "muonh"
+                               else cpu_baseline_adamh(shapes, args.hook))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -166,6 +166,39 @@ int muonh_step(void* const params[], const void* const grads[], void* const moms
                const float rho[], int tile_T, const muonh_opts* opts);
 
 /*
+ * adamh_step -- AdamH: the Hyperball wrapper around Adam's update (Hyperball
+ * show notes, Method: any base step, Adam's preconditioned update first
+ * among them; Key claims and Results report AdamH).  Adam itself (Muon
+ * explainer, Equation 2 and its text; the bias-corrected form of the Adam
+ * paper the Hyperball page cites):
+ *   m <- beta1*m + (1-beta1)*g,   v <- beta2*v + (1-beta2)*g^2,
+ *   U  = (m / (1-beta1^step)) / (sqrt(v / (1-beta2^step)) + eps)
+ * then opts->hook acts on U as on Muon's O, without Muon's shape scale:
+ * Hyperball (default; opts->hyperball_step honored), RadialBrake,
+ * MUONH_HOOK_RELATIVE, or MUONH_HOOK_NONE = plain AdamW,
+ * W <- W*(1 - eta*weight_decay) - eta*U.
+ *
+ *   params[i]      device, fp32, updated in place (W)
+ *   grads[i]       device, opts->state_dtype, read only (g)
+ *   exp_avg[i]     device, fp32, updated in place (m)
+ *   exp_avg_sq[i]  device, fp32, updated in place (v)
+ *   shapes         host, 2*n int64 rows, cols (each >= 1)
+ *   eta            learning rate (finite, >= 0)
+ *   beta1, beta2   in [0, 1); eps finite > 0 (1e-8 is Adam's usual value)
+ *   step           1-based count of this step (bias corrections), >= 1
+ *   rho            host, n floats, Hyperball radius (finite, > 0); ignored
+ *                  (may be NULL) for the other hooks
+ * Two streaming passes: moments + the hook's norms (||U||^2, <W,U>,
+ * ||W||^2; ||W - c U||^2 is formed from them), then the hook.  U is
+ * recomputed in pass 2 from the stored moments, never stored.
+ * Buffers of different matrices must not overlap; grads, exp_avg and
+ * exp_avg_sq of one matrix must be distinct.
+ */
+int adamh_step(void* const params[], const void* const grads[], void* const exp_avg[],
+               void* const exp_avg_sq[], const int64_t shapes[], int n, float eta, float beta1,
+               float beta2, float eps, int64_t step, const float rho[], const muonh_opts* opts);
+
+/*
  * ns_orthogonalize -- out[i] = NS_K(in[i]) (tile_T > 0: tiled), no momentum,
  * no hook.  in/out are device buffers of opts->state_dtype; out[i] may alias
  * in[i].  Same shape, K and tile_T rules as muonh_step.

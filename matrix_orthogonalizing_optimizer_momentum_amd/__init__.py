@@ -9,6 +9,7 @@ point raises ``MuonhUnavailable``.
 Entry points mirror the C ABI in ``include/muonh.h``:
 
 * ``muonh_step(params, grads, moms, eta, beta, K, rho, tile_T=0, **opts)``
+* ``adamh_step(params, grads, exp_avg, exp_avg_sq, eta, step, beta1, beta2, eps, rho, **opts)``
 * ``ns_orthogonalize(inputs, outputs=None, K=5, tile_T=0, **opts)``
 * ``frob_project(W, U, eta, rho, **opts)``
 * ``get_flags()``, ``reset_flags()``, ``release()``, ``plan_query(...)``,
@@ -38,7 +39,7 @@ MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE, MUONH_HOOK_NONE, MUONH_HOOK_RELAT
 MUONH_HB_STEP_UNIT, MUONH_HB_STEP_RADIUS = 0, 1
 
 EXPORTED = (
-    "muonh_default_opts", "muonh_step", "ns_orthogonalize", "frob_project", "muonh_get_flags",
+    "muonh_default_opts", "muonh_step", "adamh_step", "ns_orthogonalize", "frob_project", "muonh_get_flags",
     "muonh_reset_flags", "muonh_strerror", "muonh_release", "muonh_plan_query",
     "muonh_profile_begin", "muonh_profile_read", "muonh_version", "muonh_last_error",
 )
@@ -117,6 +118,9 @@ def load(path: str = LIB_PATH):
     lib.muonh_step.argtypes = [pp, pp, pp, POINTER(c_int64), c_int, c_float, c_float, c_int,
                                POINTER(c_float), c_int, POINTER(Opts)]
     lib.muonh_step.restype = c_int
+    lib.adamh_step.argtypes = [pp, pp, pp, pp, POINTER(c_int64), c_int, c_float, c_float, c_float, c_float,
+                               c_int64, POINTER(c_float), POINTER(Opts)]
+    lib.adamh_step.restype = c_int
     lib.ns_orthogonalize.argtypes = [pp, pp, POINTER(c_int64), c_int, c_int, c_int, POINTER(Opts)]
     lib.ns_orthogonalize.restype = c_int
     lib.frob_project.argtypes = [pp, pp, POINTER(c_int64), c_int, c_float, POINTER(c_float), POINTER(Opts)]
@@ -274,6 +278,32 @@ def muonh_step(params, grads, moms, eta, beta, K, rho=None, tile_T=0, **opts):
     rc = lib.muonh_step(_ptrs(params), _ptrs(grads), _ptrs(moms), _shapes(params), n, float(eta), float(beta),
                         int(K), rho_arr, int(tile_T), ctypes.byref(o))
     _check(rc, "muonh_step")
+
+
+def adamh_step(params, grads, exp_avg, exp_avg_sq, eta, step, beta1=0.9, beta2=0.95, eps=1e-8, rho=None,
+               **opts):
+    """One AdamH step (Hyperball around Adam's update; ``hook="none"``: AdamW)
+    in place on ``params`` (fp32) and the fp32 moments; ``step`` is 1-based."""
+    import torch
+    lib = load()
+    n = len(params)
+    if not (len(grads) == n and len(exp_avg) == n and len(exp_avg_sq) == n) or n == 0:
+        raise ValueError("params, grads and moments must be non-empty lists of equal length")
+    for name, ts in (("params", params), ("grads", grads), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _check_dev(ts, name)
+    for p, g, m, v in zip(params, grads, exp_avg, exp_avg_sq):
+        if p.dtype != torch.float32 or m.dtype != torch.float32 or v.dtype != torch.float32:
+            raise TypeError("params and Adam moments must be float32")
+        if not (p.shape == g.shape == m.shape == v.shape):
+            raise ValueError("param, grad and moment shapes differ")
+    sd = _dtype_code(grads[0])
+    if any(_dtype_code(g) != sd for g in grads):
+        raise TypeError("all grads must share a dtype")
+    o, keep = make_opts(state_dtype=sd, **opts)
+    rho_arr = (c_float * n)(*[float(r) for r in rho]) if rho is not None else None
+    rc = lib.adamh_step(_ptrs(params), _ptrs(grads), _ptrs(exp_avg), _ptrs(exp_avg_sq), _shapes(params), n,
+                        float(eta), float(beta1), float(beta2), float(eps), int(step), rho_arr, ctypes.byref(o))
+    _check(rc, "adamh_step")
 
 
 def ns_orthogonalize(inputs, outputs=None, K=5, tile_T=0, **opts):

@@ -31,6 +31,11 @@ hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* bl
 hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
                              const SlotTable& st, float eta, float zero_rel_eps, float outward,
                              float inward, float rb_eps, float decay, Flags* flags, hipStream_t s);
+hipError_t launch_adam_moments(int g_dt, bool sums, const HookMat* mats, const HookBlock* blocks, int nblocks,
+                               const SlotTable& st, const AdamArgs& a, hipStream_t s);
+hipError_t launch_adam_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
+                             const AdamArgs& a, float eta, float zero_rel_eps, float outward, float inward,
+                             float rb_eps, float decay, Flags* flags, hipStream_t s);
 hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
                         hipStream_t s);
 hipError_t launch_finalize(const SlotTable& st, int slot0, int nslots, hipStream_t s);
@@ -108,9 +113,10 @@ State& S() {
   return s;
 }
 
-const char* kClassNames[] = {"momentum_prep", "ns_gram_G1", "ns_poly_G2", "ns_update_G3", "hook_reduce",
-                             "hook_write",    "sumsq",      "finalize",   "ns_tile_resident"};
-enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_FIN, PC_TILE, PC_N };
+const char* kClassNames[] = {"momentum_prep", "ns_gram_G1", "ns_poly_G2",       "ns_update_G3",
+                             "hook_reduce",   "hook_write", "sumsq",            "finalize",
+                             "ns_tile_resident", "adam_moments", "adam_write"};
+enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_FIN, PC_TILE, PC_AM, PC_AW, PC_N };
 
 // ------------------------------------------------------------------ helpers
 void free_plan(CachedPlan& p) {
@@ -322,7 +328,8 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   for (int i = 0; i < 2 * cfg.n; ++i) key.push_back((uint64_t)shapes[i]);
   key_push_ptrs(key, p.params, cfg.kind == CALL_NS ? 0 : cfg.n);
   key_push_ptrs(key, p.grads, cfg.n);
-  key_push_ptrs(key, p.moms, cfg.kind == CALL_STEP ? cfg.n : 0);
+  key_push_ptrs(key, p.moms, (cfg.kind == CALL_STEP || cfg.kind == CALL_ADAM) ? cfg.n : 0);
+  key_push_ptrs(key, p.vs, cfg.kind == CALL_ADAM ? cfg.n : 0);
   key_push_ptrs(key, p.outs, cfg.kind == CALL_NS ? cfg.n : 0);
   if (p.rho && cfg.kind != CALL_NS) {
     for (int i = 0; i < cfg.n; ++i) {
@@ -490,7 +497,7 @@ int run_chunk(State& st, int kind, const Cfg& cfg, const DevTables& d, const Res
       MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
     }
     if (rec_open) MUONH_TRY_HIP(hipEventRecord(rec_open, s));
-  } else if (kind != CALL_PROJ) {
+  } else if (!no_ns(kind)) {
     {
       Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
       const bool stp = kind == CALL_STEP;
@@ -505,6 +512,23 @@ int run_chunk(State& st, int kind, const Cfg& cfg, const DevTables& d, const Res
     if (rec_open) MUONH_TRY_HIP(hipEventRecord(rec_open, s));
     rc = run_ns(st, cfg, d, r, sl, s);
     if (rc != MUONH_OK) return rc;
+  }
+  if (kind == CALL_ADAM) {
+    // AdamH: moments and norms, the per-matrix sums, then the hook
+    const bool sums = cfg.hook != kModeNone;
+    {
+      Prof pf(st, s, PC_AM, 0, d.bytes_hook1);
+      MUONH_TRY_HIP(launch_adam_moments(cfg.state_dt, sums, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.adam, s));
+    }
+    if (sums) {
+      Prof pf(st, s, PC_FIN, 0, 0);
+      MUONH_TRY_HIP(launch_finalize(sl, d.nunits, 2 * d.nmats, s));  // (||U||^2, <W,U>), (0, ||W||^2)
+    }
+    Prof pf(st, s, PC_AW, 0, d.bytes_hook2);
+    const float decay = cfg.hook == kModeNone ? 1.f - p.eta * r.o.weight_decay : 1.f;
+    MUONH_TRY_HIP(launch_adam_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.adam, p.eta,
+                                    r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, st.flags, s));
+    return MUONH_OK;
   }
   if (kind == CALL_PROJ && p.grads) {
     Prof pf(st, s, PC_SQ, 0, d.bytes_sumsq);
@@ -643,6 +667,38 @@ int muonh_step(void* const params[], const void* const grads[], void* const moms
     if (grads[i] == moms[i]) return MUONH_EINVAL;
   CallPtrs p{params, grads, moms, nullptr, r.o.hook == MUONH_HOOK_HYPERBALL ? rho : nullptr, eta};
   return run_call(CALL_STEP, shapes, n, K, tile_T, r, p, beta);
+}
+
+int adamh_step(void* const params[], const void* const grads[], void* const exp_avg[], void* const exp_avg_sq[],
+               const int64_t shapes[], int n, float eta, float beta1, float beta2, float eps, int64_t step,
+               const float rho[], const muonh_opts* opts) {
+  if (!shapes || n <= 0) return MUONH_EINVAL;
+  for (int i = 0; i < 2 * n; ++i)
+    if (shapes[i] < 1) return MUONH_EINVAL;
+  if (bad_ptrs(params, n) || bad_ptrs(grads, n) || bad_ptrs((const void* const*)exp_avg, n) ||
+      bad_ptrs((const void* const*)exp_avg_sq, n))
+    return MUONH_EINVAL;
+  if (!std::isfinite(eta) || eta < 0.f) return MUONH_EINVAL;
+  if (!std::isfinite(beta1) || beta1 < 0.f || beta1 >= 1.f) return MUONH_EINVAL;
+  if (!std::isfinite(beta2) || beta2 < 0.f || beta2 >= 1.f) return MUONH_EINVAL;
+  if (!std::isfinite(eps) || eps <= 0.f || step < 1) return MUONH_EINVAL;
+  Resolved r;
+  int rc = resolve(opts, 0, r);
+  if (rc != MUONH_OK) return rc;
+  if (r.o.hook == MUONH_HOOK_HYPERBALL) {
+    if (!rho) return MUONH_EINVAL;
+    for (int i = 0; i < n; ++i)
+      if (!std::isfinite(rho[i]) || rho[i] <= 0.f) return MUONH_EINVAL;
+  }
+  for (int i = 0; i < n; ++i)
+    if (exp_avg[i] == exp_avg_sq[i] || grads[i] == exp_avg[i] || grads[i] == exp_avg_sq[i]) return MUONH_EINVAL;
+  CallPtrs p{params, grads, exp_avg, nullptr, r.o.hook == MUONH_HOOK_HYPERBALL ? rho : nullptr, eta};
+  p.vs = exp_avg_sq;
+  // bias corrections in double, from the step count
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step), bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  if (!(bc1 > 0.0) || !(bc2 > 0.0)) return MUONH_EINVAL;
+  p.adam = AdamArgs{beta1, beta2, (float)(1.0 / bc1), (float)(1.0 / bc2), eps};
+  return run_call(CALL_ADAM, shapes, n, 0, 0, r, p, 0.f);
 }
 
 int ns_orthogonalize(const void* const in[], void* const out[], const int64_t shapes[], int n, int K,

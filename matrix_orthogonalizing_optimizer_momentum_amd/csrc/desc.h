@@ -79,11 +79,15 @@ struct MomBlock {
 // Hook / projection / norm passes: one full matrix, streamed flat.
 struct HookMat {
   float* w;             // fp32 weights (M layout), updated in pass 2
-  const void* o;        // update direction (o_dtype), nullptr = zero update
+  const void* o;        // update direction (o_dtype), nullptr = zero update;
+                        // AdamH: the gradient (o_dtype), the direction is Adam's
+  float* am;            // AdamH: first moment (fp32, in place); else nullptr
+  float* av;            // AdamH: second moment (fp32, in place); else nullptr
   int64_t numel;
   int32_t o_dtype;
-  int32_t onorm_slot;   // slot of ||O||^2 (Hyperball); -1: none (zero update)
-  int32_t slot;         // slot for this matrix's pass-1 sums
+  int32_t onorm_slot;   // slot of ||O||^2 (Hyperball); -1: none (zero update);
+                        // AdamH: (||U||^2, <W, U>)
+  int32_t slot;         // slot for this matrix's pass-1 sums (AdamH: (0, ||W||^2))
   int32_t nblocks;      // blocks of this matrix in a pass
   float rho;            // Hyperball radius
   float oscale;         // Hyperball: step scale (1, or rho for the radius-sized step);
@@ -134,6 +138,13 @@ constexpr int kModeHB = 0;    // Hyperball
 constexpr int kModeRB = 1;    // RadialBrake
 constexpr int kModeNone = 2;  // Muon's own update (decoupled weight decay)
 constexpr int kModeRel = 3;   // RelativeUpdate (update scaled to ||W||)
+
+// Adam's step constants (AdamH): m <- b1 m + (1 - b1) g,
+// v <- b2 v + (1 - b2) g^2, U = (m * ibc1) / (sqrt(v * ibc2) + eps) with the
+// bias corrections ibc = 1 / (1 - b^t).
+struct AdamArgs {
+  float b1, b2, ibc1, ibc2, eps;
+};
 
 // Elements per block of the flat hook / norm passes (256 threads x 32).
 constexpr int kHookBlockElems = 8192;

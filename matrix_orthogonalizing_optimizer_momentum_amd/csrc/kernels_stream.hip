@@ -11,7 +11,9 @@
 //                    (Hyperball show notes, Algorithm 1 and Method; hook PR,
 //                    PR description, review summary and the zero-norm review
 //                    comments);
-//   k_sumsq          per-matrix ||U||^2 for the stand-alone projection.
+//   k_sumsq          per-matrix ||U||^2 for the stand-alone projection;
+//   k_adam_moments,  AdamH: Adam's moments and the norms behind its hook,
+//   k_adam_write     then the hook on Adam's direction (two passes in all).
 // All of them are bandwidth-bound: 16-byte vector accesses, 64x64 blocks
 // with an LDS transpose where a layout flips, one deterministic fp64
 // reduction commit per block.
@@ -176,6 +178,40 @@ __device__ __forceinline__ float hook_coef(const HookMat& hm, const SlotTable& s
   return (float)((double)eta * (double)hm.oscale / sqrt(n2));
 }
 
+// Per-matrix decision of pass 2, identical in every block of the matrix,
+// from ||W'||^2 (v0) and ||W||^2 (v1).  branch 0: scale W', 1: scale W
+// (Hyperball restore), 2: leave W.
+struct HookDecision {
+  int branch;
+  double scale;
+};
+__device__ __forceinline__ HookDecision hook_decide(int mode, double v0, double v1, float rho_f, float zero_rel_eps,
+                                                    float outward, float inward, float rb_eps) {
+  const double nwp = sqrt(v0), nw = sqrt(v1);
+  if (mode == kModeNone || mode == kModeRel) return {0, 1.0};
+  if (mode == kModeRB) {
+    const double s = (nwp > nw) ? (double)outward : (double)inward;
+    if (nwp > (double)rb_eps) return {0, (nw + s * (nwp - nw)) / nwp};
+    return {0, 1.0};
+  }
+  const double rho = (double)rho_f;
+  if (nwp >= (double)zero_rel_eps * rho) return {0, rho / nwp};
+  if (nw > 0.0) return {1, rho / nw};
+  return {2, 1.0};
+}
+
+// Device flag counters for one matrix (called once per matrix).
+__device__ __forceinline__ void hook_flags(int mode, float coef, bool has_o, int branch, double v0, double v1,
+                                           Flags* flags) {
+  if (flags == nullptr) return;
+  if ((mode == kModeHB || mode == kModeRel) && coef == 0.f && has_o) atomicAdd(&flags->zero_update, 1ull);
+  if (mode == kModeHB) {
+    if (branch == 1) atomicAdd(&flags->restored, 1ull);
+    if (branch == 2) atomicAdd(&flags->unrestorable, 1ull);
+  }
+  if (!isfinite(v0) || !isfinite(v1)) atomicAdd(&flags->nonfinite, 1ull);
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kHookThreads) void k_hook_reduce(
     const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st, float eta) {
@@ -222,33 +258,10 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
   // pass-1 sums (none for Muon's own update)
   const double v0 = MODE == kModeNone ? 0.0 : st.sums[2 * hm.slot];      // ||W'||^2
   const double v1 = MODE == kModeNone ? 0.0 : st.sums[2 * hm.slot + 1];  // ||W||^2
-  const double nwp = sqrt(v0), nw = sqrt(v1);
-  // Per-matrix decision, identical in every block of the matrix.
-  int branch;          // 0: scale W', 1: scale W (restore), 2: leave W
-  double scale;
-  if (MODE == kModeNone || MODE == kModeRel) {
-    branch = 0;
-    scale = 1.0;
-  } else if (MODE == kModeRB) {
-    const double s = (nwp > nw) ? (double)outward : (double)inward;
-    if (nwp > (double)rb_eps) { branch = 0; scale = (nw + s * (nwp - nw)) / nwp; }
-    else { branch = 0; scale = 1.0; }
-  } else {
-    const double rho = (double)hm.rho;
-    if (nwp >= (double)zero_rel_eps * rho) { branch = 0; scale = rho / nwp; }
-    else if (nw > 0.0) { branch = 1; scale = rho / nw; }
-    else { branch = 2; scale = 1.0; }
-  }
-  if (hb.blk == 0 && threadIdx.x == 0 && flags != nullptr) {
-    if (MODE == kModeHB || MODE == kModeRel) {
-      if (coef == 0.f && hm.o != nullptr) atomicAdd(&flags->zero_update, 1ull);
-    }
-    if (MODE == kModeHB) {
-      if (branch == 1) atomicAdd(&flags->restored, 1ull);
-      if (branch == 2) atomicAdd(&flags->unrestorable, 1ull);
-    }
-    if (!isfinite(v0) || !isfinite(v1)) atomicAdd(&flags->nonfinite, 1ull);
-  }
+  const HookDecision dec = hook_decide(MODE, v0, v1, hm.rho, zero_rel_eps, outward, inward, rb_eps);
+  const int branch = dec.branch;
+  const double scale = dec.scale;
+  if (hb.blk == 0 && threadIdx.x == 0) hook_flags(MODE, coef, hm.o != nullptr, branch, v0, v1, flags);
   if (branch == 2) return;
   const int64_t base = (int64_t)hb.blk * kHookBlockElems;
 #pragma unroll
@@ -279,6 +292,150 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
       } else {
         const float base_v = (branch == 0) ? fmaf(-coef, o[k], w[k]) : w[k];
         r[k] = (float)((double)base_v * scale);
+      }
+    }
+    if (full) {
+      store8(hm.w, i, r);
+    } else {
+      for (int k = 0; k < 8; ++k)
+        if (i + k < hm.numel) hm.w[i + k] = r[k];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// AdamH (Hyperball show notes, Method: the wrapper around Adam's
+// preconditioned update; Muon explainer, Equation 2 text for Adam itself)
+// ---------------------------------------------------------------------------
+// Adam's direction for one element from the updated moments.
+__device__ __forceinline__ float adam_u(float m, float v, const AdamArgs& a) {
+  return (m * a.ibc1) / (sqrtf(v * a.ibc2) + a.eps);
+}
+
+// Pass 1: the moment updates (stored in place) and, per matrix, ||U||^2,
+// <W, U> and ||W||^2 in fp64, from which pass 2 gets ||W - coef U||^2
+// without a pass of its own (the plain AdamW update needs none of them).
+template <typename GT, bool SUMS>
+__global__ __launch_bounds__(kHookThreads) void k_adam_moments(
+    const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st, AdamArgs a) {
+  const HookBlock hb = blocks[blockIdx.x];
+  const HookMat hm = mats[hb.mat];
+  const GT* const g = reinterpret_cast<const GT*>(hm.o);
+  const float c1 = 1.f - a.b1, c2 = 1.f - a.b2;
+  double s_uu = 0.0, s_wu = 0.0, s_ww = 0.0;
+  const int64_t base = (int64_t)hb.blk * kHookBlockElems;
+#pragma unroll
+  for (int it = 0; it < kHookPerThread / 8; ++it) {
+    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
+    if (i >= hm.numel) break;
+    const bool full = i + 8 <= hm.numel;
+    float gv[8], m[8], v[8], w[8];
+    if (full) {
+      load8(g, i, gv);
+      load8(hm.am, i, m);
+      load8(hm.av, i, v);
+      if (SUMS) load8(hm.w, i, w);
+    } else {
+      for (int k = 0; k < 8; ++k) {
+        const bool ok = i + k < hm.numel;
+        gv[k] = ok ? load_dyn(g, i + k, hm.o_dtype) : 0.f;
+        m[k] = ok ? hm.am[i + k] : 0.f;
+        v[k] = ok ? hm.av[i + k] : 0.f;
+        w[k] = (ok && SUMS) ? hm.w[i + k] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      m[k] = fmaf(a.b1, m[k], c1 * gv[k]);
+      v[k] = fmaf(a.b2, v[k], c2 * (gv[k] * gv[k]));
+      if (SUMS) {
+        const double u = (double)adam_u(m[k], v[k], a), wd = (double)w[k];
+        s_uu = fma(u, u, s_uu);
+        s_wu = fma(wd, u, s_wu);
+        s_ww = fma(wd, wd, s_ww);
+      }
+    }
+    if (full) {
+      store8(hm.am, i, m);
+      store8(hm.av, i, v);
+    } else {
+      for (int k = 0; k < 8; ++k)
+        if (i + k < hm.numel) { hm.am[i + k] = m[k]; hm.av[i + k] = v[k]; }
+    }
+  }
+  if (!SUMS) return;
+  constexpr int NW = kHookThreads / 64;
+  __shared__ double red[3][NW];
+  const int wv = threadIdx.x >> 6;
+  s_uu = wave_sum(s_uu);
+  s_wu = wave_sum(s_wu);
+  s_ww = wave_sum(s_ww);
+  if ((threadIdx.x & 63) == 0) { red[0][wv] = s_uu; red[1][wv] = s_wu; red[2][wv] = s_ww; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t0 = 0.0, t1 = 0.0, t2 = 0.0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) { t0 += red[0][q]; t1 += red[1][q]; t2 += red[2][q]; }
+    const int64_t pa = st.part_base[hm.onorm_slot] + hb.blk, pb = st.part_base[hm.slot] + hb.blk;
+    gmem(st.partials)[2 * pa] = t0;
+    gmem(st.partials)[2 * pa + 1] = t1;
+    gmem(st.partials)[2 * pb] = 0.0;
+    gmem(st.partials)[2 * pb + 1] = t2;
+  }
+}
+
+// Pass 2: the hook applied to Adam's direction, recomputed from the stored
+// moments (bitwise the values pass 1 summed).  ||W - coef U||^2 is expanded as
+// ||W||^2 - 2 coef <W, U> + coef^2 ||U||^2 in fp64.
+template <int MODE>
+__global__ __launch_bounds__(kHookThreads) void k_adam_write(
+    const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st, AdamArgs a, float eta,
+    float zero_rel_eps, float outward, float inward, float rb_eps, float decay, Flags* flags) {
+  const HookBlock hb = blocks[blockIdx.x];
+  const HookMat hm = mats[hb.mat];
+  float coef = eta;
+  double v0 = 0.0, v1 = 0.0;
+  if (MODE != kModeNone) {
+    const double uu = st.sums[2 * hm.onorm_slot], wu = st.sums[2 * hm.onorm_slot + 1];
+    v1 = st.sums[2 * hm.slot + 1];
+    if (MODE == kModeHB) coef = uu > 0.0 ? (float)((double)eta * (double)hm.oscale / sqrt(uu)) : 0.f;
+    else if (MODE == kModeRel) coef = uu > 0.0 ? (float)((double)eta * sqrt(v1) / sqrt(uu)) : 0.f;
+    const double c = (double)coef;
+    v0 = fmax(v1 - 2.0 * c * wu + c * c * uu, 0.0);
+  }
+  const HookDecision dec = hook_decide(MODE, v0, v1, hm.rho, zero_rel_eps, outward, inward, rb_eps);
+  if (hb.blk == 0 && threadIdx.x == 0) hook_flags(MODE, coef, true, dec.branch, v0, v1, flags);
+  if (dec.branch == 2) return;
+  const int64_t base = (int64_t)hb.blk * kHookBlockElems;
+#pragma unroll
+  for (int it = 0; it < kHookPerThread / 8; ++it) {
+    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
+    if (i >= hm.numel) break;
+    const bool full = i + 8 <= hm.numel;
+    float w[8], m[8], v[8];
+    if (full) {
+      load8(hm.w, i, w);
+      load8(hm.am, i, m);
+      load8(hm.av, i, v);
+    } else {
+      for (int k = 0; k < 8; ++k) {
+        const bool ok = i + k < hm.numel;
+        w[k] = ok ? hm.w[i + k] : 0.f;
+        m[k] = ok ? hm.am[i + k] : 0.f;
+        v[k] = ok ? hm.av[i + k] : 1.f;
+      }
+    }
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float u = adam_u(m[k], v[k], a);
+      if (MODE == kModeNone) {
+        r[k] = fmaf(-coef, u, w[k] * decay);  // AdamW: decoupled decay, then W - eta U
+      } else if (MODE == kModeRel) {
+        r[k] = fmaf(-coef, u, w[k]);
+      } else {
+        const float base_v = (dec.branch == 0) ? fmaf(-coef, u, w[k]) : w[k];
+        r[k] = (float)((double)base_v * dec.scale);
       }
     }
     if (full) {
@@ -377,6 +534,37 @@ hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blo
   else if (mode == kModeRel) MUONH_HW(kModeRel);
   else MUONH_HW(kModeHB);
 #undef MUONH_HW
+  return hipGetLastError();
+}
+
+hipError_t launch_adam_moments(int g_dt, bool sums, const HookMat* mats, const HookBlock* blocks, int nblocks,
+                               const SlotTable& st, const AdamArgs& a, hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+#define MUONH_AM(GT, S) \
+  hipLaunchKernelGGL((k_adam_moments<GT, S>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, a)
+  if (g_dt == DT_BF16) {
+    if (sums) MUONH_AM(bf16_t, true);
+    else MUONH_AM(bf16_t, false);
+  } else {
+    if (sums) MUONH_AM(float, true);
+    else MUONH_AM(float, false);
+  }
+#undef MUONH_AM
+  return hipGetLastError();
+}
+
+hipError_t launch_adam_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
+                             const AdamArgs& a, float eta, float zero_rel_eps, float outward, float inward,
+                             float rb_eps, float decay, Flags* flags, hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+#define MUONH_AW(MODE)                                                                                    \
+  hipLaunchKernelGGL((k_adam_write<MODE>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, a, eta, \
+                     zero_rel_eps, outward, inward, rb_eps, decay, flags)
+  if (mode == kModeRB) MUONH_AW(kModeRB);
+  else if (mode == kModeNone) MUONH_AW(kModeNone);
+  else if (mode == kModeRel) MUONH_AW(kModeRel);
+  else MUONH_AW(kModeHB);
+#undef MUONH_AW
   return hipGetLastError();
 }
 

@@ -63,6 +63,13 @@ static int64_t jobs_per_iter(int r, int s, int op_dt) {
   return 2 * (nr12 * (nr12 + 1) / 2) + nr * ns;  // symmetric G1, G2 + G3
 }
 
+// AdamH bytes per element: pass 1 reads g, m, v (and W for the hook's
+// norms) and writes m, v; pass 2 reads W, m, v and writes W.
+static double adam_bytes_per_elem(const Cfg& cfg) {
+  const double gb = esize(cfg.state_dt);
+  return (gb + 16 + (cfg.hook == kModeNone ? 0 : 4)) + 16;
+}
+
 static double ns_flops_true(int64_t h, int64_t w, int K) {
   const double r = (double)std::min(h, w), s = (double)std::max(h, w);
   return (double)K * (4.0 * r * r * s + 2.0 * r * r * r);
@@ -81,14 +88,15 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
     if (m.H * m.W > ((int64_t)1 << 40)) return MUONH_EINVAL;
     m.ws_bytes = 0;
     const int64_t numel = m.H * m.W;
-    if (cfg.kind == CALL_PROJ) {
+    if (no_ns(cfg.kind)) {
       m.r = (int)std::min(m.H, m.W);
       m.s = (int)std::max(m.H, m.W);
       m.trans = m.H > m.W;
       m.nunits = 0;
       m.ntr = m.ntc = 0;
       const double ob = cfg.state_dt == DT_F32 ? 4 : 2;
-      plan.stream_bytes += (double)numel * (ob + (4 + ob) + (4 + ob + 4));
+      if (cfg.kind == CALL_PROJ) plan.stream_bytes += (double)numel * (ob + (4 + ob) + (4 + ob + 4));
+      else plan.stream_bytes += (double)numel * adam_bytes_per_elem(cfg);
       continue;
     }
     if (T > 0) {
@@ -155,7 +163,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
   const double iter_flops = plan.ns_flops / std::max(cfg.K, 1);
   const int want = cfg.lanes > 0 ? cfg.lanes : (T == 0 && iter_flops > kAutoLaneIterFlops ? 1 : 2);
   const int L = std::min(want, n);
-  if (plan.chunks.size() == 1 && L >= 2 && cfg.kind != CALL_PROJ) {
+  if (plan.chunks.size() == 1 && L >= 2 && !no_ns(cfg.kind)) {
     // Lanes: cut the set into L runs of matrices whose Newton-Schulz work is
     // as equal as the order allows (each cut at the prefix sum nearest to
     // l/L of the total, every run non-empty).  The runs own disjoint
@@ -208,7 +216,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   for (int mi = 0; mi < nm; ++mi) {
     const MatPlan& m = plan.mats[ch.m0 + mi];
     unit0[mi] = (int)t.units.size();
-    if (cfg.kind == CALL_PROJ) continue;
+    if (no_ns(cfg.kind)) continue;
     if (resident_tiles(cfg)) {
       if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
       continue;
@@ -230,7 +238,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
     if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
   }
   const int nunits = (int)t.units.size();
-  const bool resident = resident_tiles(cfg) && cfg.kind != CALL_PROJ;
+  const bool resident = resident_tiles(cfg) && !no_ns(cfg.kind);
 
   // --- slots: [unit norms][matrix O norms][matrix hook sums]; the
   // resident-tile kernel forms its tile norms itself, so it has no unit slots.
@@ -275,7 +283,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   for (int mi = 0; mi < nm; ++mi) {
     const int gi = ch.m0 + mi;
     const MatPlan& m = plan.mats[gi];
-    if (cfg.kind == CALL_PROJ || resident) continue;
+    if (no_ns(cfg.kind) || resident) continue;
     void* out = cfg.kind == CALL_STEP ? (void*)obuf[mi] : p.outs[gi];
     const int out_dt = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
     const int oes = esize(out_dt);
@@ -326,7 +334,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   }
 
   // --- momentum / prep blocks
-  if (cfg.kind != CALL_PROJ && !resident) {
+  if (!no_ns(cfg.kind) && !resident) {
     for (int mi = 0; mi < nm; ++mi) {
       const int gi = ch.m0 + mi;
       const MatPlan& m = plan.mats[gi];
@@ -389,6 +397,24 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       hm.rho = p.rho ? p.rho[gi] : 1.0f;
       hm.oscale = cfg.hook == kModeHB ? (cfg.hb_radius ? hm.rho : 1.0f)
                                       : (float)std::sqrt(std::max(1.0, (double)m.H / (double)m.W));
+      if (cfg.kind == CALL_ADAM) {
+        // Adam's direction has no shape scale (that is Muon's)
+        if (cfg.hook != kModeHB) hm.oscale = 1.0f;
+        hm.o = p.grads[gi];
+        hm.o_dtype = cfg.state_dt;
+        hm.am = static_cast<float*>(p.moms[gi]);
+        hm.av = static_cast<float*>(p.vs[gi]);
+        hm.onorm_slot = s_onorm0 + mi;
+        t.nparts[s_onorm0 + mi] = hm.nblocks;
+        t.nparts[s_hook0 + mi] = hm.nblocks;
+        const int idx = (int)t.hook_mats.size();
+        t.hook_mats.push_back(hm);
+        for (int b = 0; b < hm.nblocks; ++b) t.hook_blocks.push_back({idx, b});
+        const double gb = esize(cfg.state_dt);
+        t.bytes_hook1 += (double)hm.numel * (gb + 16 + (cfg.hook == kModeNone ? 0 : 4));
+        t.bytes_hook2 += (double)hm.numel * 16;
+        continue;
+      }
       if (cfg.kind == CALL_STEP) {
         hm.o = obuf[mi];
         hm.o_dtype = cfg.op_dt;

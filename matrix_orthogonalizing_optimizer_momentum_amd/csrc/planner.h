@@ -13,7 +13,9 @@
 
 namespace muonh {
 
-enum CallKind { CALL_STEP = 0, CALL_NS = 1, CALL_PROJ = 2 };
+enum CallKind { CALL_STEP = 0, CALL_NS = 1, CALL_PROJ = 2, CALL_ADAM = 3 };
+// Calls with no Newton-Schulz work (pure streaming passes).
+inline bool no_ns(int kind) { return kind == CALL_PROJ || kind == CALL_ADAM; }
 
 struct Cfg {
   int kind;
@@ -107,12 +109,14 @@ struct ChunkTables {
 };
 
 struct CallPtrs {
-  void* const* params;        // STEP, PROJ
-  const void* const* grads;   // STEP: grads; NS: inputs; PROJ: U (may be null)
-  void* const* moms;          // STEP
+  void* const* params;        // STEP, PROJ, ADAM
+  const void* const* grads;   // STEP, ADAM: grads; NS: inputs; PROJ: U (may be null)
+  void* const* moms;          // STEP; ADAM: first moments
   void* const* outs;          // NS
-  const float* rho;           // STEP (HB), PROJ
+  const float* rho;           // STEP (HB), PROJ, ADAM (HB)
   float eta;
+  void* const* vs = nullptr;  // ADAM: second moments
+  AdamArgs adam{};            // ADAM
 };
 
 // Fill the tables of chunk c; ws is the data workspace base (device).

@@ -27,7 +27,7 @@ def header_functions():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for n in ("muonh_step", "ns_orthogonalize", "frob_project", "muonh_strerror", "muonh_get_flags",
-              "muonh_release", "muonh_plan_query"):
+              "muonh_release", "muonh_plan_query", "adamh_step"):
         assert n in names
 
 
@@ -236,3 +236,32 @@ def test_plan_query_chunking_under_a_budget():
 def test_x32_needs_more_workspace_than_fold():
     s = [(768, 3072)]
     assert mm.plan_query(s, ns_precision="x32")["ws_bytes"] > mm.plan_query(s, ns_precision="fold")["ws_bytes"]
+
+
+def _adam(n=1, eta=0.01, b1=0.9, b2=0.95, eps=1e-8, step=1, null_rho=False, alias=None, opts=None):
+    lib = mm.load()
+    P = ctypes.c_void_p * max(n, 1)
+    ps, gs = P(*([0x1000] * max(n, 1))), P(*([0x2000] * max(n, 1)))
+    ms = P(*([0x3000] * max(n, 1)))
+    vs = P(*([0x3000 if alias == "mv" else 0x4000] * max(n, 1)))
+    if alias == "gm":
+        ms = P(*([0x2000] * max(n, 1)))
+    sh = (ctypes.c_int64 * (2 * max(n, 1)))(*([8, 8] * max(n, 1)))
+    rh = None if null_rho else (ctypes.c_float * max(n, 1))(*([1.0] * max(n, 1)))
+    o = opts or _opts()
+    return lib.adamh_step(ps, gs, ms, vs, sh, n, eta, b1, b2, eps, step, rh, ctypes.byref(o))
+
+
+# Each of these is rejected by host validation, before any HIP call.
+@pytest.mark.parametrize("kw", [
+    dict(n=0), dict(eta=-1.0), dict(b1=1.0), dict(b2=-0.1), dict(eps=0.0), dict(eps=float("nan")),
+    dict(step=0), dict(null_rho=True), dict(alias="mv"), dict(alias="gm"),
+])
+def test_adamh_validation_rejects(kw):
+    assert _adam(**kw) == mm.MUONH_EINVAL
+
+
+def test_adamh_rejects_bad_hook_option():
+    o = _opts()
+    o.hook = 9
+    assert _adam(opts=o) == mm.MUONH_EINVAL

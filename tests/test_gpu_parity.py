@@ -743,3 +743,81 @@ def test_zero_weight_fixed_radius():
                                      [2.0])
     assert flags[0] == orc.FLAG_PROJECTED
     assert np.allclose(host(w), Wn[0], rtol=1e-4, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# AdamH (Hyperball around Adam's update) and plain AdamW
+# ---------------------------------------------------------------------------
+ADAM_SHAPES = [(128, 64), (64, 192), (200, 300), (33, 17), (1, 1000)]
+
+
+def _adam_inputs(seed):
+    Ws, Gs, Ms, Vs = [], [], [], []
+    for i, sh in enumerate(ADAM_SHAPES):
+        Ws.append(gen.gaussian(sh, 0.02, seed + i))
+        Gs.append(gen.gaussian(sh, 1e-3, seed + 100 + i))
+        Ms.append(gen.gaussian(sh, 1e-4, seed + 200 + i))
+        Vs.append((gen.gaussian(sh, 1e-3, seed + 300 + i) ** 2).astype(np.float32))
+    return Ws, Gs, Ms, Vs
+
+
+@pytest.mark.parametrize("hook,gdt", [("hyperball", torch.bfloat16), ("hyperball", torch.float32),
+                                      ("radial_brake", torch.bfloat16), ("relative", torch.float32),
+                                      ("none", torch.bfloat16)])
+def test_adamh_step_matches_oracle(hook, gdt):
+    banner(f"adamh hook={hook} grads={gdt}")
+    Ws, Gs, Ms, Vs = _adam_inputs(900)
+    if gdt == torch.bfloat16:
+        Gs = [orc.round_to_bf16(g).astype(np.float32) for g in Gs]
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    b1, b2, eps, t, eta = np.float32(0.9), np.float32(0.95), 1e-8, 3, 0.02
+    w_t = [dev(w) for w in Ws]
+    m_t = [dev(m) for m in Ms]
+    v_t = [dev(v) for v in Vs]
+    mm.adamh_step(w_t, [dev(g, gdt) for g in Gs], m_t, v_t, eta, t, beta1=b1, beta2=b2, eps=eps,
+                  rho=rhos if hook == "hyperball" else None, hook=hook, weight_decay=0.1)
+    torch.cuda.synchronize()
+    nw, nm_, nv, _, fl = orc.adamh_step(Ws, Gs, Ms, Vs, eta, b1, b2, eps, t, rhos, hook=hook, weight_decay=0.1)
+    for i in range(len(ADAM_SHAPES)):
+        assert np.abs(host(m_t[i]) - nm_[i]).max() <= 2e-7 * np.abs(nm_[i]).max()
+        assert np.abs(host(v_t[i]) - nv[i]).max() <= 2e-7 * np.abs(nv[i]).max()
+        got = host(w_t[i])
+        err = rel(got - Ws[i], nw[i] - Ws[i])
+        print(f"  matrix {i} {ADAM_SHAPES[i]} step rel err {err:.3e}")
+        assert err <= 1e-4
+        if hook == "hyperball":
+            assert fl[i] == orc.FLAG_PROJECTED
+            assert abs(np.linalg.norm(got) / float(rhos[i]) - 1) <= 1e-5
+
+
+def test_adamh_trajectory_fp32():
+    banner("adamh 6-step trajectory")
+    Ws, _, _, _ = _adam_inputs(950)
+    shapes = ADAM_SHAPES
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    w_t = [dev(w) for w in Ws]
+    m_t = [torch.zeros(sh, device=DEV) for sh in shapes]
+    v_t = [torch.zeros(sh, device=DEV) for sh in shapes]
+    Wr = [w.astype(np.float64) for w in Ws]
+    Mr = [np.zeros(sh) for sh in shapes]
+    Vr = [np.zeros(sh) for sh in shapes]
+    for t in range(1, 7):
+        Gs = [gen.gaussian(sh, 1e-3, 2000 + 10 * t + i) for i, sh in enumerate(shapes)]
+        mm.adamh_step(w_t, [dev(g) for g in Gs], m_t, v_t, 0.05, t, rho=rhos)
+        Wr, Mr, Vr, _, _ = orc.adamh_step(Wr, Gs, Mr, Vr, 0.05, np.float32(0.9), np.float32(0.95), 1e-8, t, rhos)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        got = host(w_t[i])
+        assert rel(got - Ws[i], Wr[i] - Ws[i]) <= 1e-4
+        assert abs(np.linalg.norm(got) / float(rhos[i]) - 1) <= 1e-5
+
+
+def test_adamh_zero_gradient_projects_only():
+    banner("adamh zero gradient")
+    W = gen.gaussian((64, 96), 0.5, 970)
+    w_t = [dev(W)]
+    mm.adamh_step(w_t, [torch.zeros(64, 96, device=DEV)], [torch.zeros(64, 96, device=DEV)],
+                  [torch.zeros(64, 96, device=DEV)], 0.1, 1, rho=[2.0])
+    torch.cuda.synchronize()
+    w64 = W.astype(np.float64)
+    assert np.allclose(host(w_t[0]), 2.0 * w64 / np.linalg.norm(w64), rtol=1e-6, atol=1e-7)
