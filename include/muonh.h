@@ -132,6 +132,11 @@ typedef struct muonh_opts {
                                    are identical for every value. */
   int          hyperball_step;  /* MUONH_HB_STEP_UNIT (default) or MUONH_HB_STEP_RADIUS; also
                                    used by frob_project */
+  const int*   tile_sizes;      /* host, n entries, read during the call: per-matrix tile side
+                                   for muonh_step / ns_orthogonalize (0: full-matrix NS; else
+                                   the tile_T rules), overriding tile_T -- per-layer tile
+                                   sizes (Hierarchical Muon page, discussion of tile choice
+                                   by aspect ratio).  NULL (default): tile_T for every matrix */
 } muonh_opts;
 
 /* Fill *o with the defaults listed above. */

@@ -18,7 +18,7 @@ Entry points mirror the C ABI in ``include/muonh.h``:
 ``opts`` keywords: ``ns_dtype`` ("bf16" | "f32"), ``ns_precision``
 ("fold" | "x32"), ``coeffs`` (K rows of (a, b, c)), ``ns_eps``,
 ``zero_rel_eps``, ``hook`` ("hyperball" | "radial_brake" | "relative" | "none"),
-``hyperball_step`` ("unit" | "radius"),
+``hyperball_step`` ("unit" | "radius"), ``tile_sizes`` (per-matrix tile sides, 0 = full),
 ``outward``, ``inward``, ``rb_eps``, ``workspace_limit`` (bytes),
 ``momentum`` ("sum" | "ema"), ``nesterov`` (bool), ``weight_decay`` (for
 hook "none"), ``lanes`` (concurrent lanes 1..4; 0: library default),
@@ -77,6 +77,7 @@ class Opts(ctypes.Structure):
         ("weight_decay", c_float),
         ("lanes", c_int),
         ("hyperball_step", c_int),
+        ("tile_sizes", POINTER(c_int)),
     ]
 
 
@@ -173,6 +174,12 @@ def _check(rc: int, where: str):
 # marshalling helpers
 # --------------------------------------------------------------------------
 
+def _check_tile_sizes(opts, n):
+    ts = opts.get("tile_sizes")
+    if ts is not None and len(ts) != n:
+        raise ValueError(f"tile_sizes needs one entry per matrix ({n}), got {len(ts)}")
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -185,7 +192,7 @@ def _dtype_code(t) -> int:
 def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coeffs=None, ns_eps=None,
               zero_rel_eps=None, hook="hyperball", outward=None, inward=None, rb_eps=None,
               workspace_limit=0, stream=None, K=None, momentum="sum", nesterov=False, weight_decay=None, lanes=0,
-              hyperball_step="unit"):
+              hyperball_step="unit", tile_sizes=None):
     """Build an Opts struct; returns (opts, keepalive) where keepalive holds
     buffers the struct points to."""
     lib = load()
@@ -209,6 +216,10 @@ def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coef
     o.hook = {"hyperball": MUONH_HOOK_HYPERBALL, "radial_brake": MUONH_HOOK_RADIAL_BRAKE,
               "none": MUONH_HOOK_NONE, "relative": MUONH_HOOK_RELATIVE}[hook]
     o.hyperball_step = {"unit": MUONH_HB_STEP_UNIT, "radius": MUONH_HB_STEP_RADIUS}[hyperball_step]
+    if tile_sizes is not None:
+        ts = (c_int * len(tile_sizes))(*[int(v) for v in tile_sizes])
+        keep.append(ts)
+        o.tile_sizes = ctypes.cast(ts, POINTER(c_int))
     o.momentum_ema = {"sum": 0, "ema": 1}[momentum]
     o.nesterov = 1 if nesterov else 0
     if weight_decay is not None:
@@ -273,6 +284,7 @@ def muonh_step(params, grads, moms, eta, beta, K, rho=None, tile_T=0, **opts):
     sd = _dtype_code(grads[0])
     if any(_dtype_code(g) != sd for g in grads):
         raise TypeError("all grads must share a dtype")
+    _check_tile_sizes(opts, n)
     o, keep = make_opts(state_dtype=sd, K=K, **opts)
     rho_arr = (c_float * n)(*[float(r) for r in rho]) if rho is not None else None
     rc = lib.muonh_step(_ptrs(params), _ptrs(grads), _ptrs(moms), _shapes(params), n, float(eta), float(beta),
@@ -320,6 +332,7 @@ def ns_orthogonalize(inputs, outputs=None, K=5, tile_T=0, **opts):
     for x, y in zip(inputs, outputs):
         if x.shape != y.shape or _dtype_code(x) != sd or _dtype_code(y) != sd:
             raise ValueError("inputs and outputs must match in shape and share one dtype")
+    _check_tile_sizes(opts, n)
     o, keep = make_opts(state_dtype=sd, K=K, **opts)
     rc = lib.ns_orthogonalize(_ptrs(inputs), _ptrs(outputs), _shapes(inputs), n, int(K), int(tile_T),
                               ctypes.byref(o))
@@ -378,6 +391,12 @@ def plan_query(shapes, K=5, tile_T=0, workspace_limit=0, **opts):
         o.ns_precision = {"x32": MUONH_NS_X32, "fold": MUONH_NS_FOLD}[opts["ns_precision"]]
     if "lanes" in opts:
         o.lanes = int(opts["lanes"])
+    keep = []
+    if opts.get("tile_sizes") is not None:
+        _check_tile_sizes(opts, len(shapes))
+        ts = (c_int * len(shapes))(*[int(v) for v in opts["tile_sizes"]])
+        keep.append(ts)
+        o.tile_sizes = ctypes.cast(ts, POINTER(c_int))
     if "state_dtype" in opts:
         o.state_dtype = {"bf16": MUONH_BF16, "f32": MUONH_F32}[opts["state_dtype"]]
     out = (c_int64 * 7)()

@@ -63,6 +63,7 @@ struct DevTables {  // one chunk's tables on the device
   TileMat* tile_mats = nullptr;
   TileJob* tile_jobs = nullptr;
   int n_tile = 0;
+  std::vector<TileGroup> tile_groups;  // host copy: launch parameters
   double flops_tile = 0, bytes_tile = 0;
   int32_t* nparts = nullptr;
   int64_t* part_base = nullptr;
@@ -213,6 +214,13 @@ int check_tile(int tile_T) {
   return MUONH_EINVAL;
 }
 
+int check_tile_sizes(const int* sizes, int n) {
+  if (!sizes) return MUONH_OK;
+  for (int i = 0; i < n; ++i)
+    if (check_tile(sizes[i]) != MUONH_OK) return MUONH_EINVAL;
+  return MUONH_OK;
+}
+
 // 3/4 of the HBM free at the first call (fixed afterwards, so that chunking
 // does not change as the library's own workspace grows).
 size_t default_limit() {
@@ -241,6 +249,7 @@ Cfg make_cfg(int kind, int n, int K, int tile_T, const Resolved& r, size_t limit
   c.hb_radius = r.o.hyperball_step == MUONH_HB_STEP_RADIUS ? 1 : 0;
   c.ws_limit = limit;
   c.lanes = r.o.lanes;
+  c.tile_sizes = no_ns(kind) ? nullptr : r.o.tile_sizes;
   return c;
 }
 
@@ -288,6 +297,7 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   d.tile_mats = reinterpret_cast<TileMat*>(d.mem + o_tm);
   d.tile_jobs = reinterpret_cast<TileJob*>(d.mem + o_tj);
   d.n_tile = (int)t.tile_jobs.size();
+  d.tile_groups = t.tile_groups;
   d.flops_tile = t.flops_tile;
   d.bytes_tile = t.bytes_tile;
   d.nparts = reinterpret_cast<int32_t*>(d.mem + o_np);
@@ -316,6 +326,9 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   key.push_back((uint64_t)cfg.kind);
   key.push_back((uint64_t)cfg.n);
   key.push_back((uint64_t)cfg.tile_T);
+  key.push_back(cfg.tile_sizes ? 1 : 0);
+  if (cfg.tile_sizes)
+    for (int i = 0; i < cfg.n; ++i) key.push_back((uint64_t)(uint32_t)cfg.tile_sizes[i]);
   key.push_back((uint64_t)cfg.state_dt);
   key.push_back((uint64_t)cfg.op_dt);
   key.push_back((uint64_t)cfg.x32);
@@ -474,44 +487,47 @@ int run_chunk(State& st, int kind, const Cfg& cfg, const DevTables& d, const Res
               float beta, hipStream_t s, hipEvent_t rec_open) {
   int rc = MUONH_OK;
   const SlotTable sl = slot_table(st, d);
-  if (kind != CALL_PROJ && d.n_tile > 0) {
-    // Hierarchical Muon, resident tiles: momentum, norms and every
-    // Newton-Schulz iteration in one launch.
-    TileArgs ta{};
-    for (int k = 0; k < cfg.K; ++k)
-      for (int j = 0; j < 3; ++j) ta.abc[k][j] = r.coeffs[3 * k + j];
-    ta.T = cfg.tile_T;
-    ta.K = cfg.K;
-    ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
-    ta.beta = beta;
-    ta.gcoef = (kind == CALL_STEP && r.o.momentum_ema) ? 1.f - beta : 1.f;
-    ta.nesterov = (kind == CALL_STEP && r.o.nesterov) ? 1 : 0;
-    ta.eps = r.o.ns_eps;
-    ta.st = sl;
-    {
-      Prof pf(st, s, PC_TILE, d.flops_tile, d.bytes_tile);
-      MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs, d.n_tile, ta, s));
+  if (!no_ns(kind)) {
+    const bool gemm = d.n_mom > 0;  // matrices whose units go through the GEMM engine
+    if (d.n_tile > 0) {
+      // Hierarchical Muon, resident tiles: momentum, norms and every
+      // Newton-Schulz iteration in one launch per tile side.
+      TileArgs ta{};
+      for (int k = 0; k < cfg.K; ++k)
+        for (int j = 0; j < 3; ++j) ta.abc[k][j] = r.coeffs[3 * k + j];
+      ta.K = cfg.K;
+      ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
+      ta.beta = beta;
+      ta.gcoef = (kind == CALL_STEP && r.o.momentum_ema) ? 1.f - beta : 1.f;
+      ta.nesterov = (kind == CALL_STEP && r.o.nesterov) ? 1 : 0;
+      ta.eps = r.o.ns_eps;
+      ta.st = sl;
+      for (const TileGroup& g : d.tile_groups) {
+        ta.T = g.T;
+        Prof pf(st, s, PC_TILE, g.flops, g.bytes);
+        MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs + g.job0, g.njobs, ta, s));
+      }
+      if (!gemm) {
+        Prof pf(st, s, PC_FIN, 0, 0);
+        MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
+      }
     }
-    {
-      Prof pf(st, s, PC_FIN, 0, 0);
-      MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
-    }
-    if (rec_open) MUONH_TRY_HIP(hipEventRecord(rec_open, s));
-  } else if (!no_ns(kind)) {
-    {
-      Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
-      const bool stp = kind == CALL_STEP;
-      MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
-                                         sl, stp ? beta : 0.f, (stp && r.o.momentum_ema) ? 1.f - beta : 1.f,
-                                         (stp && r.o.nesterov) ? 1 : 0, s));
-    }
-    {
+    if (gemm) {
+      {
+        Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
+        const bool stp = kind == CALL_STEP;
+        MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
+                                           sl, stp ? beta : 0.f, (stp && r.o.momentum_ema) ? 1.f - beta : 1.f,
+                                           (stp && r.o.nesterov) ? 1 : 0, s));
+      }
       Prof pf(st, s, PC_FIN, 0, 0);
       MUONH_TRY_HIP(launch_finalize(sl, 0, d.nunits, s));  // ||M||^2 per unit
     }
     if (rec_open) MUONH_TRY_HIP(hipEventRecord(rec_open, s));
-    rc = run_ns(st, cfg, d, r, sl, s);
-    if (rc != MUONH_OK) return rc;
+    if (gemm) {
+      rc = run_ns(st, cfg, d, r, sl, s);  // ends with ||O||^2 of every matrix of the chunk
+      if (rc != MUONH_OK) return rc;
+    }
   }
   if (kind == CALL_ADAM) {
     // AdamH: moments and norms, the per-matrix sums, then the hook
@@ -646,6 +662,7 @@ void muonh_default_opts(muonh_opts* o) {
   o->weight_decay = 0.f;
   o->lanes = 0;
   o->hyperball_step = MUONH_HB_STEP_UNIT;
+  o->tile_sizes = nullptr;
 }
 
 int muonh_step(void* const params[], const void* const grads[], void* const moms[], const int64_t shapes[],
@@ -657,6 +674,8 @@ int muonh_step(void* const params[], const void* const grads[], void* const moms
   if (!std::isfinite(beta) || beta < 0.f || beta >= 1.f) return MUONH_EINVAL;
   Resolved r;
   rc = resolve(opts, K, r);
+  if (rc != MUONH_OK) return rc;
+  rc = check_tile_sizes(r.o.tile_sizes, n);
   if (rc != MUONH_OK) return rc;
   if (r.o.hook == MUONH_HOOK_HYPERBALL) {
     if (!rho) return MUONH_EINVAL;
@@ -708,6 +727,8 @@ int ns_orthogonalize(const void* const in[], void* const out[], const int64_t sh
   if (bad_ptrs(in, n) || bad_ptrs((const void* const*)out, n)) return MUONH_EINVAL;
   Resolved r;
   rc = resolve(opts, K, r);
+  if (rc != MUONH_OK) return rc;
+  rc = check_tile_sizes(r.o.tile_sizes, n);
   if (rc != MUONH_OK) return rc;
   CallPtrs p{nullptr, in, nullptr, out, nullptr, 0.f};
   return run_call(CALL_NS, shapes, n, K, tile_T, r, p, 0.f);
@@ -817,12 +838,14 @@ int muonh_plan_query(const int64_t shapes[], int n, int K, int tile_T, const muo
   Resolved r;
   rc = resolve(opts, K, r);
   if (rc != MUONH_OK) return rc;
+  rc = check_tile_sizes(r.o.tile_sizes, n);
+  if (rc != MUONH_OK) return rc;
   if (workspace_limit == 0) workspace_limit = (size_t)1 << 62;
   Cfg cfg = make_cfg(CALL_STEP, n, K, tile_T, r, workspace_limit);
   Plan plan;
   rc = make_plan(shapes, cfg, plan);
   if (rc != MUONH_OK) return rc;
-  out[0] = plan.lanes == 2 ? 1 : (int64_t)plan.chunks.size();
+  out[0] = plan.lanes > 1 ? 1 : (int64_t)plan.chunks.size();
   out[1] = plan.ws_bytes;
   out[2] = plan.units;
   out[3] = (int64_t)plan.ns_flops;

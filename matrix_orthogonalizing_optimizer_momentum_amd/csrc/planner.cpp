@@ -79,9 +79,12 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
   plan = Plan();
   const int n = cfg.n;
   plan.mats.resize(n);
-  const int T = cfg.tile_T;
+  bool all_full = true;
   for (int i = 0; i < n; ++i) {
     MatPlan& m = plan.mats[i];
+    const int T = mat_tile(cfg, i);
+    m.T = no_ns(cfg.kind) ? 0 : T;
+    all_full = all_full && m.T == 0;
     m.H = shapes[2 * i];
     m.W = shapes[2 * i + 1];
     if (m.H < 1 || m.W < 1 || m.H > (int64_t)1 << 30 || m.W > (int64_t)1 << 30) return MUONH_EINVAL;
@@ -111,7 +114,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
           const int64_t w = std::min<int64_t>(T, m.W - (int64_t)b * T);
           plan.ns_flops += ns_flops_true(h, w, cfg.K);
         }
-      if (resident_tiles(cfg)) {
+      if (resident_tile(T)) {
         plan.jobs_per_iter += m.nunits;  // one workgroup per tile runs every iteration
       } else {
         const UnitBytes ub = unit_bytes(T, T, cfg.op_dt, cfg.x32);
@@ -161,7 +164,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
   // long iteration, where launch gaps are negligible and the lanes' large
   // products only contend for the caches (measured slower).
   const double iter_flops = plan.ns_flops / std::max(cfg.K, 1);
-  const int want = cfg.lanes > 0 ? cfg.lanes : (T == 0 && iter_flops > kAutoLaneIterFlops ? 1 : 2);
+  const int want = cfg.lanes > 0 ? cfg.lanes : (all_full && iter_flops > kAutoLaneIterFlops ? 1 : 2);
   const int L = std::min(want, n);
   if (plan.chunks.size() == 1 && L >= 2 && !no_ns(cfg.kind)) {
     // Lanes: cut the set into L runs of matrices whose Newton-Schulz work is
@@ -200,7 +203,6 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
 void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char* ws, ChunkTables& t) {
   t = ChunkTables();
   const ChunkPlan& ch = plan.chunks[c];
-  const int T = cfg.tile_T;
   const int nm = ch.m1 - ch.m0;
   const int es_op = esize(cfg.op_dt);
 
@@ -217,7 +219,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
     const MatPlan& m = plan.mats[ch.m0 + mi];
     unit0[mi] = (int)t.units.size();
     if (no_ns(cfg.kind)) continue;
-    if (resident_tiles(cfg)) {
+    if (resident_tile(m.T)) {
       if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
       continue;
     }
@@ -238,7 +240,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
     if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
   }
   const int nunits = (int)t.units.size();
-  const bool resident = resident_tiles(cfg) && !no_ns(cfg.kind);
+  auto resident = [&](const MatPlan& m) { return !no_ns(cfg.kind) && resident_tile(m.T); };
 
   // --- slots: [unit norms][matrix O norms][matrix hook sums]; the
   // resident-tile kernel forms its tile norms itself, so it has no unit slots.
@@ -246,36 +248,51 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   const int nslots = nunits + 2 * nm;
   t.nparts.assign(nslots, 0);
 
-  // --- resident tiles: one job per tile, momentum fused
-  if (resident) {
-    const double sb = esize(cfg.state_dt);
+  // --- resident tiles: one job per tile, momentum fused; one launch per
+  // distinct tile side, in increasing order
+  {
+    std::vector<int> sides;
     for (int mi = 0; mi < nm; ++mi) {
-      const int gi = ch.m0 + mi;
-      const MatPlan& m = plan.mats[gi];
-      TileMat tm{};
-      tm.g = cfg.kind == CALL_STEP ? p.grads[gi] : nullptr;
-      tm.m = cfg.kind == CALL_STEP ? p.moms[gi] : const_cast<void*>(p.grads[gi]);
-      tm.out = cfg.kind == CALL_STEP ? (void*)obuf[mi] : p.outs[gi];
-      tm.H = m.H;
-      tm.W = m.W;
-      tm.out_dtype = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
-      tm.onorm_slot = s_onorm0 + mi;
-      // 8-element (16 / 32-byte) chunks need 8-aligned rows and tile origins
-      // and 16-byte aligned buffers.
-      auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
-      tm.vec = (m.W % 8 == 0 && T % 8 == 0 && a16(tm.g) && a16(tm.m) && a16(tm.out)) ? 1 : 0;
-      const int idx = (int)t.tile_mats.size();
-      t.tile_mats.push_back(tm);
-      for (int a = 0; a < m.ntr; ++a)
-        for (int b = 0; b < m.ntc; ++b) {
-          t.tile_jobs.push_back({idx, a, b, a * m.ntc + b});
-          const int64_t h = std::min<int64_t>(T, m.H - (int64_t)a * T);
-          const int64_t w = std::min<int64_t>(T, m.W - (int64_t)b * T);
-          t.flops_tile += ns_flops_true(h, w, cfg.K);
-        }
-      t.nparts[s_onorm0 + mi] = m.nunits;
-      const double numel = (double)m.H * m.W;
-      t.bytes_tile += cfg.kind == CALL_STEP ? numel * (3 * sb + es_op) : numel * 2 * sb;
+      const MatPlan& m = plan.mats[ch.m0 + mi];
+      if (resident(m) && std::find(sides.begin(), sides.end(), m.T) == sides.end()) sides.push_back(m.T);
+    }
+    std::sort(sides.begin(), sides.end());
+    const double sb = esize(cfg.state_dt);
+    for (const int T : sides) {
+      TileGroup grp{T, (int)t.tile_jobs.size(), 0, 0.0, 0.0};
+      for (int mi = 0; mi < nm; ++mi) {
+        const int gi = ch.m0 + mi;
+        const MatPlan& m = plan.mats[gi];
+        if (!resident(m) || m.T != T) continue;
+        TileMat tm{};
+        tm.g = cfg.kind == CALL_STEP ? p.grads[gi] : nullptr;
+        tm.m = cfg.kind == CALL_STEP ? p.moms[gi] : const_cast<void*>(p.grads[gi]);
+        tm.out = cfg.kind == CALL_STEP ? (void*)obuf[mi] : p.outs[gi];
+        tm.H = m.H;
+        tm.W = m.W;
+        tm.out_dtype = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
+        tm.onorm_slot = s_onorm0 + mi;
+        // 8-element (16 / 32-byte) chunks need 8-aligned rows and tile origins
+        // and 16-byte aligned buffers.
+        auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+        tm.vec = (m.W % 8 == 0 && T % 8 == 0 && a16(tm.g) && a16(tm.m) && a16(tm.out)) ? 1 : 0;
+        const int idx = (int)t.tile_mats.size();
+        t.tile_mats.push_back(tm);
+        for (int a = 0; a < m.ntr; ++a)
+          for (int b = 0; b < m.ntc; ++b) {
+            t.tile_jobs.push_back({idx, a, b, a * m.ntc + b});
+            const int64_t h = std::min<int64_t>(T, m.H - (int64_t)a * T);
+            const int64_t w = std::min<int64_t>(T, m.W - (int64_t)b * T);
+            grp.flops += ns_flops_true(h, w, cfg.K);
+          }
+        t.nparts[s_onorm0 + mi] = m.nunits;
+        const double numel = (double)m.H * m.W;
+        grp.bytes += cfg.kind == CALL_STEP ? numel * (3 * sb + es_op) : numel * 2 * sb;
+      }
+      grp.njobs = (int)t.tile_jobs.size() - grp.job0;
+      t.flops_tile += grp.flops;
+      t.bytes_tile += grp.bytes;
+      t.tile_groups.push_back(grp);
     }
   }
 
@@ -283,7 +300,8 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   for (int mi = 0; mi < nm; ++mi) {
     const int gi = ch.m0 + mi;
     const MatPlan& m = plan.mats[gi];
-    if (no_ns(cfg.kind) || resident) continue;
+    if (no_ns(cfg.kind) || resident(m)) continue;
+    const int T = m.T;
     void* out = cfg.kind == CALL_STEP ? (void*)obuf[mi] : p.outs[gi];
     const int out_dt = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
     const int oes = esize(out_dt);
@@ -334,10 +352,12 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   }
 
   // --- momentum / prep blocks
-  if (!no_ns(cfg.kind) && !resident) {
+  if (!no_ns(cfg.kind)) {
     for (int mi = 0; mi < nm; ++mi) {
       const int gi = ch.m0 + mi;
       const MatPlan& m = plan.mats[gi];
+      if (resident(m)) continue;
+      const int T = m.T;
       MomMat mm{};
       mm.g = p.grads[gi];
       mm.m = cfg.kind == CALL_STEP ? p.moms[gi] : nullptr;

@@ -28,11 +28,13 @@ struct Cfg {
   int hb_radius;  // Hyperball: radius-sized step (eta * rho * U_hat)
   size_t ws_limit;
   int lanes;      // concurrent lanes, 1..kMaxLanes; 0: automatic (see make_plan)
+  const int32_t* tile_sizes;  // host, n per-matrix tile sides (0: full matrix); nullptr: tile_T for all
 };
 
 // Per source matrix.
 struct MatPlan {
   int64_t H, W;
+  int T;           // tile side (0: full-matrix Newton-Schulz)
   int r, s;        // full mode: oriented sides; tile mode: T, T
   int trans;       // full mode: H > W
   int nunits;      // 1, or tiles
@@ -89,7 +91,15 @@ int unit_gemm_cfg(int r, int op_dt, bool phase12);
 // Hierarchical Muon with T <= kTileResidentMax runs on the resident-tile
 // kernel (one workgroup per tile for the whole step, momentum fused, no
 // workspace but the step's O buffer); larger tiles go through the GEMM engine.
-inline bool resident_tiles(const Cfg& c) { return c.tile_T > 0 && c.tile_T <= kTileResidentMax; }
+inline bool resident_tile(int T) { return T > 0 && T <= kTileResidentMax; }
+inline int mat_tile(const Cfg& c, int i) { return c.tile_sizes ? c.tile_sizes[i] : c.tile_T; }
+
+// Resident-tile launches of one chunk: one per distinct tile side.
+struct TileGroup {
+  int T;
+  int job0, njobs;
+  double flops, bytes;
+};
 
 struct ChunkTables {
   std::vector<NsUnit> units;
@@ -100,6 +110,7 @@ struct ChunkTables {
   std::vector<HookBlock> hook_blocks;
   std::vector<TileMat> tile_mats;
   std::vector<TileJob> tile_jobs;
+  std::vector<TileGroup> tile_groups;
   std::vector<int32_t> nparts;
   std::vector<int64_t> part_base;
   int64_t parts_total = 0;

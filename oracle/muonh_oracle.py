@@ -319,7 +319,7 @@ def muonh_step(Ws, Gs, Ms, eta, beta, K, rhos, tile_T: int = 0, hook: str = "hyp
                coeffs=None, outward: float = 0.5, inward: float = 1.0,
                zero_rel_eps: float = 1e-6, state_bf16: bool = False,
                ema: bool = False, nesterov: bool = False, weight_decay: float = 0.0,
-               hb_step: str = "unit"):
+               hb_step: str = "unit", tile_sizes=None):
     """One MuonH (or HiMuon-H / Muon+RadialBrake / plain Muon) step over a
     list of matrices.
 
@@ -333,6 +333,8 @@ def muonh_step(Ws, Gs, Ms, eta, beta, K, rhos, tile_T: int = 0, hook: str = "hyp
 
     ``state_bf16`` models a bf16 momentum buffer: the updated M is stored
     rounded to bf16 and the NS input is formed from the stored value.
+    ``tile_sizes`` gives each matrix its own tile side (0: full matrix;
+    [HIMUON] discussion: tile sizes chosen per layer).
 
     Returns (new_Ws, new_Ms, Os, flags).
     """
@@ -342,7 +344,7 @@ def muonh_step(Ws, Gs, Ms, eta, beta, K, rhos, tile_T: int = 0, hook: str = "hyp
         if state_bf16:
             m = round_to_bf16(m)
         x = nesterov_input(G, m, beta, ema) if nesterov else m
-        O = orthogonalize(x, K, tile_T, coeffs)
+        O = orthogonalize(x, K, tile_T if tile_sizes is None else tile_sizes[i], coeffs)
         if hook == "hyperball":
             w, f = hyperball(W, O, eta, rhos[i], zero_rel_eps, hb_step)
         elif hook == "relative":

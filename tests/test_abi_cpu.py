@@ -265,3 +265,24 @@ def test_adamh_rejects_bad_hook_option():
     o = _opts()
     o.hook = 9
     assert _adam(opts=o) == mm.MUONH_EINVAL
+
+
+def test_per_matrix_tile_sizes_plan():
+    shapes = [(768, 2304), (768, 768), (768, 3072), (3072, 768)]
+    # uniform sizes reproduce the tile_T plan
+    for T in (0, 64, 256):
+        a = mm.plan_query(shapes, K=5, tile_T=T)
+        b = mm.plan_query(shapes, K=5, tile_sizes=[T] * 4)
+        assert a == b
+    # mixed: full, resident 128, GEMM-engine 256, resident 96 (ragged)
+    q = mm.plan_query(shapes, K=5, tile_sizes=[0, 128, 256, 96])
+    assert q["units"] == 1 + 36 + 36 + 32 * 8
+    each = [mm.plan_query([sh], K=5, tile_T=T)["ns_flops"] for sh, T in zip(shapes, [0, 128, 256, 96])]
+    assert abs(q["ns_flops"] - sum(each)) <= 4
+
+
+def test_per_matrix_tile_sizes_validation():
+    with pytest.raises(mm.MuonhError):
+        mm.plan_query([(64, 64), (64, 64)], K=5, tile_sizes=[0, 200])  # 200: not a multiple of 64 above 128
+    with pytest.raises(ValueError):
+        mm.plan_query([(64, 64), (64, 64)], K=5, tile_sizes=[64])

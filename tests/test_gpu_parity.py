@@ -821,3 +821,40 @@ def test_adamh_zero_gradient_projects_only():
     torch.cuda.synchronize()
     w64 = W.astype(np.float64)
     assert np.allclose(host(w_t[0]), 2.0 * w64 / np.linalg.norm(w64), rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# per-matrix tile sizes (Hierarchical Muon: a tile side per layer)
+# ---------------------------------------------------------------------------
+MIXED_SHAPES = [(768, 2304), (768, 768), (768, 3072), (3072, 768), (300, 700)]
+MIXED_SIZES = [0, 128, 256, 64, 96]
+
+
+def test_step_per_matrix_tile_sizes_bitwise_vs_separate_calls():
+    banner("per-matrix tile sizes vs separate calls")
+    Ws, Gs, Ms = _gpt2_like(MIXED_SHAPES, cfg=13)
+    rhos = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    w_t = [dev(w) for w in Ws]
+    m_t = [dev(m, torch.bfloat16) for m in Ms]
+    mm.muonh_step(w_t, [dev(g, torch.bfloat16) for g in Gs], m_t, eta=0.02, beta=0.95, K=5, rho=rhos,
+                  tile_sizes=MIXED_SIZES)
+    torch.cuda.synchronize()
+    for i, T in enumerate(MIXED_SIZES):
+        w1 = [dev(Ws[i])]
+        m1 = [dev(Ms[i], torch.bfloat16)]
+        mm.muonh_step(w1, [dev(Gs[i], torch.bfloat16)], m1, eta=0.02, beta=0.95, K=5, rho=[rhos[i]], tile_T=T)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(w_t[i]), host(w1[0])), f"matrix {i} T={T}"
+        assert np.array_equal(host(m_t[i]), host(m1[0]))
+
+
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+def test_ns_per_matrix_tile_sizes_vs_oracle(ns):
+    banner(f"ns per-matrix tile sizes {ns}")
+    shapes = [(256, 384), (200, 130), (128, 512), (96, 96)]
+    sizes = [0, 64, 256, 17]
+    Xs = [gen.gaussian(sh, 0.02, 80 + i) for i, sh in enumerate(shapes)]
+    outs = mm.ns_orthogonalize([dev(x) for x in Xs], K=5, tile_sizes=sizes, ns_dtype=ns)
+    torch.cuda.synchronize()
+    for x, o, T in zip(Xs, outs, sizes):
+        assert rel(host(o), orc.orthogonalize(x, 5, T)) <= TOL[ns]

@@ -736,3 +736,16 @@ def test_adam_hooks_match_the_muon_hooks_without_shape_scale():
                       ("relative", lambda U: orc.relative_update(W, U, 0.02))):
         nw, _, _, Us, _ = orc.adamh_step([W], [G], [Z], [Z], 0.02, 0.9, 0.95, 1e-8, 3, hook=hook)
         assert np.array_equal(nw[0], ref(Us[0]))
+
+
+def test_step_per_matrix_tile_sizes_route_each_matrix():
+    shapes = [(40, 70), (64, 32), (50, 50)]
+    sizes = [0, 16, 32]
+    Ws = [gen.gaussian(sh, 0.02, 60 + i).astype(np.float64) for i, sh in enumerate(shapes)]
+    Gs = [gen.gaussian(sh, 0.02, 70 + i).astype(np.float64) for i, sh in enumerate(shapes)]
+    Ms = [np.zeros(sh) for sh in shapes]
+    rhos = [float(np.linalg.norm(w)) for w in Ws]
+    nw, _, Os, _ = orc.muonh_step(Ws, Gs, Ms, 0.02, 0.95, 5, rhos, tile_sizes=sizes)
+    for i in range(3):
+        one, _, O1, _ = orc.muonh_step([Ws[i]], [Gs[i]], [Ms[i]], 0.02, 0.95, 5, [rhos[i]], tile_T=sizes[i])
+        assert np.array_equal(nw[i], one[0]) and np.array_equal(Os[i], O1[0])
