@@ -30,7 +30,7 @@ hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* bl
                               const SlotTable& st, float eta, hipStream_t s);
 hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
                              const SlotTable& st, float eta, float zero_rel_eps, float outward,
-                             float inward, float rb_eps, float decay, Flags* flags, hipStream_t s);
+                             float inward, float rb_eps, float decay, bool fused, Flags* flags, hipStream_t s);
 hipError_t launch_adam_moments(int g_dt, bool sums, const HookMat* mats, const HookBlock* blocks, int nblocks,
                                const SlotTable& st, const AdamArgs& a, hipStream_t s);
 hipError_t launch_adam_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
@@ -72,6 +72,7 @@ struct DevTables {  // one chunk's tables on the device
   int64_t parts_total = 0;
   int nslots = 0;
   int nunits = 0, nmats = 0;  // slot ranges: [0,nunits) norms, then nmats O norms, then nmats hook sums
+  bool fused = false;         // hook norms summed by the producer of O
   int64_t part_off = 0;       // lanes: this chunk's first partial / slot in the shared arrays
   int slot_off = 0;
   double flops_g1[kGemmCfgs] = {}, flops_g2[kGemmCfgs] = {}, flops_g3[kGemmCfgs] = {};
@@ -298,6 +299,7 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   d.tile_jobs = reinterpret_cast<TileJob*>(d.mem + o_tj);
   d.n_tile = (int)t.tile_jobs.size();
   d.tile_groups = t.tile_groups;
+  d.fused = t.fused;
   d.flops_tile = t.flops_tile;
   d.bytes_tile = t.bytes_tile;
   d.nparts = reinterpret_cast<int32_t*>(d.mem + o_np);
@@ -476,7 +478,8 @@ int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, con
     }
   }
   Prof pf(st, s, PC_FIN, 0, 0);
-  MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
+  // ||O||^2 per matrix (fused: with <W, O>, then the (0, ||W||^2) hook slots)
+  MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.fused ? 2 * d.nmats : d.nmats, s));
   return MUONH_OK;
 }
 
@@ -509,7 +512,7 @@ int run_chunk(State& st, int kind, const Cfg& cfg, const DevTables& d, const Res
       }
       if (!gemm) {
         Prof pf(st, s, PC_FIN, 0, 0);
-        MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 per matrix
+        MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.fused ? 2 * d.nmats : d.nmats, s));  // ||O||^2 per matrix
       }
     }
     if (gemm) {
@@ -552,7 +555,7 @@ int run_chunk(State& st, int kind, const Cfg& cfg, const DevTables& d, const Res
     MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||U||^2 per matrix
   }
   if (kind != CALL_NS) {
-    if (cfg.hook != kModeNone) {  // Muon's own update needs no norms
+    if (cfg.hook != kModeNone && !d.fused) {  // Muon's own update needs no norms
       {
         Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
         MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta, s));
@@ -564,8 +567,8 @@ int run_chunk(State& st, int kind, const Cfg& cfg, const DevTables& d, const Res
       Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
       const float decay = cfg.hook == kModeNone ? 1.f - p.eta * r.o.weight_decay : 1.f;
       MUONH_TRY_HIP(launch_hook_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta,
-                                      r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, st.flags,
-                                      s));
+                                      r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, d.fused,
+                                      st.flags, s));
     }
   }
   return MUONH_OK;

@@ -68,6 +68,21 @@ __device__ __forceinline__ void load8(const float* p, int64_t i, float (&v)[8]) 
   v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
   v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
 }
+// 8 floats from memory the running kernel does not write, read through the
+// constant address space so the loads may be issued ahead of the kernel's
+// own stores (p + i 16-byte aligned).
+__device__ __forceinline__ void load8_ro(const float* p, int64_t i, float (&v)[8]) {
+  typedef __attribute__((address_space(4))) const f32x4_t cf4;
+  const f32x4_t a = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(p + i));
+  const f32x4_t b = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(p + i + 4));
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+}
+__device__ __forceinline__ float load1_ro(const float* p, int64_t i) {
+  typedef __attribute__((address_space(4))) const float cf1;
+  return *reinterpret_cast<cf1*>(reinterpret_cast<uintptr_t>(p + i));
+}
+
 __device__ __forceinline__ void store8(bf16_t* p, int64_t i, const float (&v)[8]) {
   u32x4_t w;
 #pragma unroll
@@ -122,6 +137,31 @@ __device__ void block_partial2(double v0, double v1, const SlotTable& st, int sl
     const int64_t p = st.part_base[slot] + part;
     gmem(st.partials)[2 * p] = t0;
     gmem(st.partials)[2 * p + 1] = t1;
+  }
+}
+
+// Three per-block sums: (a, b) into slot_a, (0, c) into slot_b, both at
+// partial index part (one shared-memory round, deterministic order).
+template <int NT>
+__device__ void block_partial3(double a, double b, double c, const SlotTable& st, int slot_a, int slot_b, int part) {
+  static_assert(NT % 64 == 0, "block must be whole waves");
+  constexpr int NW = NT / 64;
+  __shared__ double red3[3][NW];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  c = wave_sum(c);
+  if (l == 0) { red3[0][w] = a; red3[1][w] = b; red3[2][w] = c; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t0 = 0.0, t1 = 0.0, t2 = 0.0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) { t0 += red3[0][i]; t1 += red3[1][i]; t2 += red3[2][i]; }
+    const int64_t pa = st.part_base[slot_a] + part, pb = st.part_base[slot_b] + part;
+    gmem(st.partials)[2 * pa] = t0;
+    gmem(st.partials)[2 * pa + 1] = t1;
+    gmem(st.partials)[2 * pb] = 0.0;
+    gmem(st.partials)[2 * pb + 1] = t2;
   }
 }
 

@@ -45,6 +45,10 @@ struct NsUnit {
   float* x32;           // fp32 master X^T (XT layout) or nullptr
   void* a;              // op-dtype A = X X^T (r rows, ld_r)
   void* b;              // op-dtype B = b A + c A A (r rows, ld_r)
+  const float* w_ptr;   // weights at the output origin (O's layout) or nullptr: the last
+                        // iteration then also sums <W, O> and ||W||^2 for the hook
+  int32_t hook_slot;    // slot receiving (0, ||W||^2) when w_ptr is set
+  int32_t pad_;
 };
 
 // One output macro-tile of a grouped GEMM launch.
@@ -110,9 +114,10 @@ struct TileMat {
   void* out;            // orthogonalized output (H x W, ld = W)
   int64_t H, W;
   int32_t out_dtype;
-  int32_t onorm_slot;   // slot collecting this matrix's ||O||^2
+  int32_t onorm_slot;   // slot collecting this matrix's ||O||^2 (and <W, O> with w)
   int32_t vec;          // 1: rows and tile origins allow 16-byte accesses
-  int32_t pad_;
+  int32_t hook_slot;    // slot receiving (0, ||W||^2) when w is set
+  const float* w;       // weights (H x W, ld = W) or nullptr (see NsUnit::w_ptr)
 };
 
 struct TileJob {

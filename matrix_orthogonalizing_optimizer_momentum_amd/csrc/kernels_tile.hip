@@ -370,7 +370,11 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
 #pragma unroll
       for (int v = 0; v < 16; ++v) stg[(wr + i * 32 + acc_row(v, lane)) * SP + wc + j * 32 + lc] = x32[i][j][v];
   __syncthreads();
-  float osq = 0.f;
+  // ||O||^2 of the stored values and, for the weight-update hook, <W, O> and
+  // ||W||^2 at the same positions (fp64 per thread: the hook forms
+  // ||W - c O||^2 from them, which must resolve an exactly cancelling step).
+  double osq = 0.0, swo = 0.0, sww = 0.0;
+  const float* const wp = mt.w;
   const int64_t obase = r0 * ldm + c0;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -388,17 +392,32 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
       if (mt.out_dtype == DT_BF16) store8(reinterpret_cast<bf16_t*>(mt.out), o, x);
       else store8(reinterpret_cast<float*>(mt.out), o, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) osq = fmaf(x[e], x[e], osq);
+      for (int e = 0; e < 8; ++e) osq = fma((double)x[e], (double)x[e], osq);
+      if (wp != nullptr) {
+        float wv[8];
+        load8_ro(wp, o, wv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          swo = fma((double)wv[e], (double)x[e], swo);
+          sww = fma((double)wv[e], (double)wv[e], sww);
+        }
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (col + e < w) {
           store_dyn(mt.out, o + e, x[e], mt.out_dtype);
-          osq = fmaf(x[e], x[e], osq);
+          osq = fma((double)x[e], (double)x[e], osq);
+          if (wp != nullptr) {
+            const double wv = (double)load1_ro(wp, o + e);
+            swo = fma(wv, (double)x[e], swo);
+            sww = fma(wv, wv, sww);
+          }
         }
     }
   }
-  block_partial2<kTileThreads>((double)osq, 0.0, args.st, mt.onorm_slot, job.part);
+  if (wp != nullptr) block_partial3<kTileThreads>(osq, swo, sww, args.st, mt.onorm_slot, mt.hook_slot, job.part);
+  else block_partial2<kTileThreads>(osq, 0.0, args.st, mt.onorm_slot, job.part);
 }
 
 namespace {
