@@ -445,8 +445,11 @@ int hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, #x);        \
   } while (0)
 
-int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, const SlotTable& sl,
-           hipStream_t s) {
+// Newton-Schulz iteration k of a chunk (K == 0: the single O = X0/||X0||
+// pass): G1, G2, G3 over every unit; the last one ends with the per-matrix
+// finalize of ||O||^2 (and, fused, of <W, O> and ||W||^2).
+int run_ns_iter(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, const SlotTable& sl, hipStream_t s,
+                int k) {
   const float eps = r.o.ns_eps;
   if (cfg.K == 0) {
     for (int g = 0; g < kGemmCfgs; ++g) {
@@ -454,8 +457,7 @@ int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, con
       MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], 1.f, 0.f, 0.f, eps, 1, 1, 0, 1,
                                    sl, s));
     }
-  }
-  for (int k = 0; k < cfg.K; ++k) {
+  } else {
     const float a = r.coeffs[3 * k], b = r.coeffs[3 * k + 1], c = r.coeffs[3 * k + 2];
     const int first = k == 0, last = k == cfg.K - 1, cur = k & 1;
     for (int g = 0; g < kGemmCfgs; ++g) {
@@ -476,6 +478,7 @@ int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, con
       MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], a, b, c, eps, first, last, cur, 0,
                                    sl, s));
     }
+    if (!last) return MUONH_OK;
   }
   Prof pf(st, s, PC_FIN, 0, 0);
   // ||O||^2 per matrix (fused: with <W, O>, then the (0, ||W||^2) hook slots)
@@ -483,55 +486,66 @@ int run_ns(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, con
   return MUONH_OK;
 }
 
-// One chunk's whole step on stream s.  When rec_open is set it is recorded
-// after the chunk's opening pass (momentum and its norms, or the resident-tile
-// kernel): the point where the next lane may start.
-int run_chunk(State& st, int kind, const Cfg& cfg, const DevTables& d, const Resolved& r, const CallPtrs& p,
-              float beta, hipStream_t s, hipEvent_t rec_open) {
-  int rc = MUONH_OK;
+// Newton-Schulz iterations a chunk runs through the GEMM engine (0: none).
+int ns_stage_count(int kind, const Cfg& cfg, const DevTables& d) {
+  return (!no_ns(kind) && d.n_mom > 0) ? std::max(cfg.K, 1) : 0;
+}
+
+// Stages of one chunk's step: 0 = the opening pass, 1..n = the Newton-Schulz
+// iterations through the GEMM engine, n + 1 = the closing passes.
+int chunk_stages(int kind, const Cfg& cfg, const DevTables& d) { return 2 + ns_stage_count(kind, cfg, d); }
+
+// One stage of a chunk's step on stream s (see chunk_stages).  When
+// rec_open is set it is recorded after the opening pass (momentum and its
+// norms, or the resident-tile kernel): the point where the next lane may
+// start.
+int run_chunk_stage(State& st, int kind, const Cfg& cfg, const DevTables& d, const Resolved& r, const CallPtrs& p,
+                    float beta, hipStream_t s, int stage, hipEvent_t rec_open) {
   const SlotTable sl = slot_table(st, d);
-  if (!no_ns(kind)) {
-    const bool gemm = d.n_mom > 0;  // matrices whose units go through the GEMM engine
-    if (d.n_tile > 0) {
-      // Hierarchical Muon, resident tiles: momentum, norms and every
-      // Newton-Schulz iteration in one launch per tile side.
-      TileArgs ta{};
-      for (int k = 0; k < cfg.K; ++k)
-        for (int j = 0; j < 3; ++j) ta.abc[k][j] = r.coeffs[3 * k + j];
-      ta.K = cfg.K;
-      ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
-      ta.beta = beta;
-      ta.gcoef = (kind == CALL_STEP && r.o.momentum_ema) ? 1.f - beta : 1.f;
-      ta.nesterov = (kind == CALL_STEP && r.o.nesterov) ? 1 : 0;
-      ta.eps = r.o.ns_eps;
-      ta.st = sl;
-      for (const TileGroup& g : d.tile_groups) {
-        ta.T = g.T;
-        Prof pf(st, s, PC_TILE, g.flops, g.bytes);
-        MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs + g.job0, g.njobs, ta, s));
+  const int nk = ns_stage_count(kind, cfg, d);
+  if (stage >= 1 && stage <= nk) return run_ns_iter(st, cfg, d, r, sl, s, stage - 1);
+  if (stage == 0) {
+    if (!no_ns(kind)) {
+      const bool gemm = d.n_mom > 0;  // matrices whose units go through the GEMM engine
+      if (d.n_tile > 0) {
+        // Hierarchical Muon, resident tiles: momentum, norms and every
+        // Newton-Schulz iteration in one launch per tile side.
+        TileArgs ta{};
+        for (int k = 0; k < cfg.K; ++k)
+          for (int j = 0; j < 3; ++j) ta.abc[k][j] = r.coeffs[3 * k + j];
+        ta.K = cfg.K;
+        ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
+        ta.beta = beta;
+        ta.gcoef = (kind == CALL_STEP && r.o.momentum_ema) ? 1.f - beta : 1.f;
+        ta.nesterov = (kind == CALL_STEP && r.o.nesterov) ? 1 : 0;
+        ta.eps = r.o.ns_eps;
+        ta.st = sl;
+        for (const TileGroup& g : d.tile_groups) {
+          ta.T = g.T;
+          Prof pf(st, s, PC_TILE, g.flops, g.bytes);
+          MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs + g.job0, g.njobs, ta, s));
+        }
+        if (!gemm) {
+          Prof pf(st, s, PC_FIN, 0, 0);
+          MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.fused ? 2 * d.nmats : d.nmats, s));  // ||O||^2 per matrix
+        }
       }
-      if (!gemm) {
+      if (gemm) {
+        {
+          Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
+          const bool stp = kind == CALL_STEP;
+          MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
+                                             sl, stp ? beta : 0.f, (stp && r.o.momentum_ema) ? 1.f - beta : 1.f,
+                                             (stp && r.o.nesterov) ? 1 : 0, s));
+        }
         Prof pf(st, s, PC_FIN, 0, 0);
-        MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.fused ? 2 * d.nmats : d.nmats, s));  // ||O||^2 per matrix
+        MUONH_TRY_HIP(launch_finalize(sl, 0, d.nunits, s));  // ||M||^2 per unit
       }
-    }
-    if (gemm) {
-      {
-        Prof pf(st, s, PC_MOM, 0, d.bytes_mom);
-        const bool stp = kind == CALL_STEP;
-        MUONH_TRY_HIP(launch_momentum_prep(cfg.state_dt, cfg.op_dt, d.mom_mats, d.mom_blocks, d.n_mom, d.units,
-                                           sl, stp ? beta : 0.f, (stp && r.o.momentum_ema) ? 1.f - beta : 1.f,
-                                           (stp && r.o.nesterov) ? 1 : 0, s));
-      }
-      Prof pf(st, s, PC_FIN, 0, 0);
-      MUONH_TRY_HIP(launch_finalize(sl, 0, d.nunits, s));  // ||M||^2 per unit
     }
     if (rec_open) MUONH_TRY_HIP(hipEventRecord(rec_open, s));
-    if (gemm) {
-      rc = run_ns(st, cfg, d, r, sl, s);  // ends with ||O||^2 of every matrix of the chunk
-      if (rc != MUONH_OK) return rc;
-    }
+    return MUONH_OK;
   }
+  // closing passes
   if (kind == CALL_ADAM) {
     // AdamH: moments and norms, the per-matrix sums, then the hook
     const bool sums = cfg.hook != kModeNone;
@@ -604,22 +618,32 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
       if (!st.ev_join[l]) MUONH_TRY_HIP(hipEventCreateWithFlags(&st.ev_join[l], hipEventDisableTiming));
       if (l > 0 && !st.side[l]) MUONH_TRY_HIP(hipStreamCreateWithFlags(&st.side[l], hipStreamNonBlocking));
     }
-    for (int l = 0; l < L; ++l) {
-      hipStream_t ls = l == 0 ? s : st.side[l];
-      if (l > 0) MUONH_TRY_HIP(hipStreamWaitEvent(ls, st.ev_gate[l - 1], 0));
-      rc = run_chunk(st, kind, cfg, cp->chunks[l], r, p, beta, ls, l + 1 < L ? st.ev_gate[l] : nullptr);
-      if (rc != MUONH_OK) return rc;
-    }
+    // Submission is interleaved stage by stage, so that the side lanes'
+    // launches are queued as early as the caller's lane's (queued whole, one
+    // lane after the other, a lane would wait for the host to submit the
+    // lanes before it).
+    int nst = 0;
+    for (int l = 0; l < L; ++l) nst = std::max(nst, chunk_stages(kind, cfg, cp->chunks[l]));
+    for (int stage = 0; stage < nst; ++stage)
+      for (int l = 0; l < L; ++l) {
+        const DevTables& d = cp->chunks[l];
+        if (stage >= chunk_stages(kind, cfg, d)) continue;
+        hipStream_t ls = l == 0 ? s : st.side[l];
+        if (stage == 0 && l > 0) MUONH_TRY_HIP(hipStreamWaitEvent(ls, st.ev_gate[l - 1], 0));
+        rc = run_chunk_stage(st, kind, cfg, d, r, p, beta, ls, stage, stage == 0 && l + 1 < L ? st.ev_gate[l] : nullptr);
+        if (rc != MUONH_OK) return rc;
+      }
     for (int l = 1; l < L; ++l) {
       MUONH_TRY_HIP(hipEventRecord(st.ev_join[l], st.side[l]));
       MUONH_TRY_HIP(hipStreamWaitEvent(s, st.ev_join[l], 0));
     }
     return MUONH_OK;
   }
-  for (const DevTables& d : cp->chunks) {
-    rc = run_chunk(st, kind, cfg, d, r, p, beta, s, nullptr);
-    if (rc != MUONH_OK) return rc;
-  }
+  for (const DevTables& d : cp->chunks)
+    for (int stage = 0; stage < chunk_stages(kind, cfg, d); ++stage) {
+      rc = run_chunk_stage(st, kind, cfg, d, r, p, beta, s, stage, nullptr);
+      if (rc != MUONH_OK) return rc;
+    }
   return MUONH_OK;
 }
 
