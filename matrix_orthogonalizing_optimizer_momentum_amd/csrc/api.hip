@@ -30,7 +30,7 @@ hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* bl
                               const SlotTable& st, float eta, hipStream_t s);
 hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
                              const SlotTable& st, float eta, float zero_rel_eps, float outward,
-                             float inward, float rb_eps, float decay, bool fused, Flags* flags, hipStream_t s);
+                             float inward, float rb_eps, float decay, Flags* flags, hipStream_t s);
 hipError_t launch_adam_moments(int g_dt, bool sums, const HookMat* mats, const HookBlock* blocks, int nblocks,
                                const SlotTable& st, const AdamArgs& a, hipStream_t s);
 hipError_t launch_adam_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
@@ -60,6 +60,8 @@ struct DevTables {  // one chunk's tables on the device
   MomBlock* mom_blocks = nullptr;
   HookMat* hook_mats = nullptr;
   HookBlock* hook_blocks = nullptr;
+  HookBlock* hook1_blocks = nullptr;  // pass-1 blocks (matrices without fused norms)
+  int n_hook1 = 0;
   TileMat* tile_mats = nullptr;
   TileJob* tile_jobs = nullptr;
   int n_tile = 0;
@@ -72,7 +74,6 @@ struct DevTables {  // one chunk's tables on the device
   int64_t parts_total = 0;
   int nslots = 0;
   int nunits = 0, nmats = 0;  // slot ranges: [0,nunits) norms, then nmats O norms, then nmats hook sums
-  bool fused = false;         // hook norms summed by the producer of O
   int64_t part_off = 0;       // lanes: this chunk's first partial / slot in the shared arrays
   int slot_off = 0;
   double flops_g1[kGemmCfgs] = {}, flops_g2[kGemmCfgs] = {}, flops_g3[kGemmCfgs] = {};
@@ -273,6 +274,8 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   put(blob, t.mom_blocks, o_mb);
   put(blob, t.hook_mats, o_hm);
   put(blob, t.hook_blocks, o_hb);
+  size_t o_hb1;
+  put(blob, t.hook1_blocks, o_hb1);
   put(blob, t.tile_mats, o_tm);
   put(blob, t.tile_jobs, o_tj);
   put(blob, t.nparts, o_np);
@@ -295,11 +298,12 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   d.mom_blocks = reinterpret_cast<MomBlock*>(d.mem + o_mb);
   d.hook_mats = reinterpret_cast<HookMat*>(d.mem + o_hm);
   d.hook_blocks = reinterpret_cast<HookBlock*>(d.mem + o_hb);
+  d.hook1_blocks = reinterpret_cast<HookBlock*>(d.mem + o_hb1);
+  d.n_hook1 = (int)t.hook1_blocks.size();
   d.tile_mats = reinterpret_cast<TileMat*>(d.mem + o_tm);
   d.tile_jobs = reinterpret_cast<TileJob*>(d.mem + o_tj);
   d.n_tile = (int)t.tile_jobs.size();
   d.tile_groups = t.tile_groups;
-  d.fused = t.fused;
   d.flops_tile = t.flops_tile;
   d.bytes_tile = t.bytes_tile;
   d.nparts = reinterpret_cast<int32_t*>(d.mem + o_np);
@@ -481,8 +485,8 @@ int run_ns_iter(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r
     if (!last) return MUONH_OK;
   }
   Prof pf(st, s, PC_FIN, 0, 0);
-  // ||O||^2 per matrix (fused: with <W, O>, then the (0, ||W||^2) hook slots)
-  MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.fused ? 2 * d.nmats : d.nmats, s));
+  // ||O||^2 per matrix (resident-tile matrices: with <W, O>)
+  MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));
   return MUONH_OK;
 }
 
@@ -527,7 +531,7 @@ int run_chunk_stage(State& st, int kind, const Cfg& cfg, const DevTables& d, con
         }
         if (!gemm) {
           Prof pf(st, s, PC_FIN, 0, 0);
-          MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.fused ? 2 * d.nmats : d.nmats, s));  // ||O||^2 per matrix
+          MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 (and <W, O>) per matrix
         }
       }
       if (gemm) {
@@ -569,10 +573,10 @@ int run_chunk_stage(State& st, int kind, const Cfg& cfg, const DevTables& d, con
     MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||U||^2 per matrix
   }
   if (kind != CALL_NS) {
-    if (cfg.hook != kModeNone && !d.fused) {  // Muon's own update needs no norms
-      {
+    if (cfg.hook != kModeNone) {  // Muon's own update needs no norms
+      if (d.n_hook1 > 0) {  // matrices whose norms were not summed where O was stored
         Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
-        MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta, s));
+        MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook1_blocks, d.n_hook1, sl, p.eta, s));
       }
       Prof pf(st, s, PC_FIN, 0, 0);
       MUONH_TRY_HIP(launch_finalize(sl, d.nunits + d.nmats, d.nmats, s));  // hook sums per matrix
@@ -581,8 +585,8 @@ int run_chunk_stage(State& st, int kind, const Cfg& cfg, const DevTables& d, con
       Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
       const float decay = cfg.hook == kModeNone ? 1.f - p.eta * r.o.weight_decay : 1.f;
       MUONH_TRY_HIP(launch_hook_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta,
-                                      r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, d.fused,
-                                      st.flags, s));
+                                      r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, st.flags,
+                                      s));
     }
   }
   return MUONH_OK;

@@ -45,10 +45,6 @@ struct NsUnit {
   float* x32;           // fp32 master X^T (XT layout) or nullptr
   void* a;              // op-dtype A = X X^T (r rows, ld_r)
   void* b;              // op-dtype B = b A + c A A (r rows, ld_r)
-  const float* w_ptr;   // weights at the output origin (O's layout) or nullptr: the last
-                        // iteration then also sums <W, O> and ||W||^2 for the hook
-  int32_t hook_slot;    // slot receiving (0, ||W||^2) when w_ptr is set
-  int32_t pad_;
 };
 
 // One output macro-tile of a grouped GEMM launch.
@@ -96,6 +92,8 @@ struct HookMat {
   float rho;            // Hyperball radius
   float oscale;         // Hyperball: step scale (1, or rho for the radius-sized step);
                         // RadialBrake / plain update: shape scale max(1, H/W)^0.5
+  int32_t fused;        // 1: <W, O> and ||W||^2 were summed where O was stored (no pass 1)
+  int32_t pad_;
 };
 
 struct HookBlock {
@@ -117,7 +115,8 @@ struct TileMat {
   int32_t onorm_slot;   // slot collecting this matrix's ||O||^2 (and <W, O> with w)
   int32_t vec;          // 1: rows and tile origins allow 16-byte accesses
   int32_t hook_slot;    // slot receiving (0, ||W||^2) when w is set
-  const float* w;       // weights (H x W, ld = W) or nullptr (see NsUnit::w_ptr)
+  const float* w;       // weights (H x W, ld = W) or nullptr: the step's hook norms
+                        // <W, O> and ||W||^2 are then summed where O is stored
 };
 
 struct TileJob {

@@ -96,40 +96,12 @@ __device__ __forceinline__ void store4(float* p, int64_t i, const float (&v)[4])
   *reinterpret_cast<MUONH_GLOBAL f32x4_t*>(gmem(p + i)) = a;
 }
 
-// Sums the last iteration forms from the stored O: ||O||^2 and, for the
-// weight-update hook, <W, O> and ||W||^2 at the same positions (fp64: the
-// hook forms ||W - c O||^2 from them, which must resolve an exactly
-// cancelling step).
-struct OSums {
-  double oo, wo, ww;
-};
-
-// N weights at offset i (zeros past n), vectorized when aligned.  Read
-// through the constant address space: the weights are read-only while the
-// kernel runs, which lets these loads move ahead of the output stores.
-template <int N>
-__device__ __forceinline__ void load_w(const float* w, int64_t i, int n, bool wvec, float (&wv)[N]) {
-  typedef __attribute__((address_space(4))) const f32x4_t cf4;
-  typedef __attribute__((address_space(4))) const float cf1;
-  if (wvec && n == N) {
-#pragma unroll
-    for (int h = 0; h < N / 4; ++h) {
-      const f32x4_t q = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(w + i + 4 * h));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) wv[4 * h + e] = q[e];
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < N; ++e) wv[e] = e < n ? *reinterpret_cast<cf1*>(reinterpret_cast<uintptr_t>(w + i + e)) : 0.f;
-  }
-}
-
 // Store n (<= N) output values of O (run-time dtype), vectorized when the
-// caller's layout allows it, and add the stored (rounded) values to s; with
-// has_w also <W, O> and ||W||^2 from wv, the weights at the same offsets.
+// caller's layout allows it; adds the squares of the stored (rounded)
+// values to osq (fp64).
 template <int N>
-__device__ __forceinline__ void store_out(void* p, bool has_w, const float (&wv)[N], int64_t i, const float (&v)[N],
-                                          int n, int dtype, bool vec, OSums& s) {
+__device__ __forceinline__ void store_out(void* p, int64_t i, const float (&v)[N], int n, int dtype, bool vec,
+                                          double& osq) {
   float rv[N];
   if (vec && n == N) {
 #pragma unroll
@@ -146,14 +118,7 @@ __device__ __forceinline__ void store_out(void* p, bool has_w, const float (&wv)
     for (int e = 0; e < N; ++e) rv[e] = e < n ? store_dyn(p, i + e, v[e], dtype) : 0.f;
   }
 #pragma unroll
-  for (int e = 0; e < N; ++e) s.oo = fma((double)rv[e], (double)rv[e], s.oo);
-  if (has_w) {
-#pragma unroll
-    for (int e = 0; e < N; ++e) {
-      s.wo = fma((double)wv[e], (double)rv[e], s.wo);
-      s.ww = fma((double)wv[e], (double)wv[e], s.ww);
-    }
-  }
+  for (int e = 0; e < N; ++e) osq = fma((double)rv[e], (double)rv[e], osq);
 }
 
 // Two transposing LDS reads (gfx950 ds_read_b64_tr_b16) form one bf16 MFMA
@@ -641,7 +606,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   static_assert(GPR >= 16, "swizzle needs 16 granules per row");
   auto cidx = [](int rl, int cl) -> int { return rl * BN + ((((cl >> 2) ^ ((rl >> 3) & 15))) << 2) + (cl & 3); };
 
-  OSums osum{0.0, 0.0, 0.0};
+  double osq = 0.0;
   const bool mirror = (PHASE != kG3) && (job.tm != job.tn);  // symmetric outputs: also write the transpose
   const bool col_pass = (PHASE == kG3) ? (u.o_trans != 0) : mirror;
   constexpr int ROWS_PER_IT = NT / GPR;    // row pass: one granule (4 values) per thread
@@ -653,14 +618,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   const int q = tid % CPC, csub = tid / CPC;
   const bool o_vec = (u.o_dtype == DT_BF16) ? ((u.o_ld % 8) == 0 && ((uintptr_t)u.o_ptr % 16) == 0)
                                             : ((u.o_ld % 4) == 0 && ((uintptr_t)u.o_ptr % 16) == 0);
-  const bool w_vec = (u.o_ld % 4) == 0 && ((uintptr_t)u.w_ptr % 16) == 0;
   T* const out12 = reinterpret_cast<T*>(PHASE == kG1 ? u.a : u.b);
 
-  // Last G3 with the hook's norms: the weights at each output position are
-  // read through the constant address space (W is not written by this
-  // kernel), so the compiler may issue them ahead of earlier O stores.
   constexpr int NCOL_IT = BN / COLS_PER_IT;
-  const bool wfuse = PHASE == kG3 && u.w_ptr != nullptr;
 #pragma unroll 1
   for (int sl = 0; sl < BM / SLAB; ++sl) {
     __syncthreads();  // LDS free (main loop or previous slab done)
@@ -717,12 +677,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
         }
         if (!u.o_trans && grow < u.o_rows) {
           const int nv = min(4, u.o_cols - gcol);
-          if (nv > 0) {
-            const int64_t oi = (int64_t)grow * u.o_ld + gcol;
-            float wv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (wfuse) load_w<4>(u.w_ptr, oi, nv, w_vec, wv);
-            store_out<4>(u.o_ptr, wfuse, wv, oi, v, nv, u.o_dtype, o_vec, osum);
-          }
+          if (nv > 0) store_out<4>(u.o_ptr, (int64_t)grow * u.o_ld + gcol, v, nv, u.o_dtype, o_vec, osq);
         }
       }
       if (col_pass) *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
@@ -743,19 +698,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
           // mirrored tile: row gn of A (or B), columns gi..gi+7
           if (gn < r && gi < u.ld_r) store8(out12, (int64_t)gn * u.ld_r + gi, v);
         } else if (gn < u.o_cols && gi < u.o_rows) {
-          const int64_t oi = (int64_t)gn * u.o_ld + gi;
-          const int nv = min(8, u.o_rows - gi);
-          float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (wfuse) load_w<8>(u.w_ptr, oi, nv, w_vec, wv);
-          store_out<8>(u.o_ptr, wfuse, wv, oi, v, nv, u.o_dtype, o_vec, osum);
+          store_out<8>(u.o_ptr, (int64_t)gn * u.o_ld + gi, v, min(8, u.o_rows - gi), u.o_dtype, o_vec, osq);
         }
       }
     }
   }
   if (PHASE == kG3) {
-    const int part = u.onorm_part0 + job.tm * u.g3_cols + job.tn;
-    if (u.w_ptr != nullptr) block_partial3<NT>(osum.oo, osum.wo, osum.ww, args.st, u.onorm_slot, u.hook_slot, part);
-    else block_partial2<NT>(osum.oo, 0.0, args.st, u.onorm_slot, part);
+    block_partial2<NT>(osq, 0.0, args.st, u.onorm_slot, u.onorm_part0 + job.tm * u.g3_cols + job.tn);
   }
 }
 

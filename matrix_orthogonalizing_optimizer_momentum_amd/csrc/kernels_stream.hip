@@ -248,11 +248,12 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_reduce(
   block_partial2<kHookThreads>(s0, s1, st, hm.slot, hb.blk);
 }
 
-// FUSED: the producer of O summed <W, O> (second value of the O-norm slot)
-// and ||W||^2 (second value of the hook slot) at its store, and
-// ||W - coef O||^2 is expanded as ||W||^2 - 2 coef <W, O> + coef^2 ||O||^2 in
-// fp64; otherwise pass 1 (k_hook_reduce) summed ||W'||^2 and ||W||^2.
-template <int MODE, bool FUSED>
+// Per matrix: when HookMat::fused is set, the producer of O summed <W, O>
+// (second value of the O-norm slot) and ||W||^2 (second value of the hook
+// slot) at its store, and ||W - coef O||^2 is expanded as
+// ||W||^2 - 2 coef <W, O> + coef^2 ||O||^2 in fp64; otherwise pass 1
+// (k_hook_reduce) summed ||W'||^2 and ||W||^2.
+template <int MODE>
 __global__ __launch_bounds__(kHookThreads) void k_hook_write(
     const HookMat* __restrict__ mats, const HookBlock* __restrict__ blocks, SlotTable st, float eta,
     float zero_rel_eps, float outward, float inward, float rb_eps, float decay, Flags* flags) {
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
   double v0 = 0.0, v1 = 0.0;  // ||W'||^2, ||W||^2 (none for Muon's own update)
   if (MODE != kModeNone) {
     v1 = st.sums[2 * hm.slot + 1];
-    if (FUSED) {
+    if (hm.fused) {
       const double c = (double)coef;
       const double uu = hm.onorm_slot >= 0 ? st.sums[2 * hm.onorm_slot] : 0.0;
       const double wo = hm.onorm_slot >= 0 ? st.sums[2 * hm.onorm_slot + 1] : 0.0;
@@ -537,21 +538,15 @@ hipError_t launch_hook_reduce(int mode, const HookMat* mats, const HookBlock* bl
 
 hipError_t launch_hook_write(int mode, const HookMat* mats, const HookBlock* blocks, int nblocks,
                              const SlotTable& st, float eta, float zero_rel_eps, float outward,
-                             float inward, float rb_eps, float decay, bool fused, Flags* flags, hipStream_t s) {
+                             float inward, float rb_eps, float decay, Flags* flags, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
-#define MUONH_HW(MODE, F)                                                                                    \
-  hipLaunchKernelGGL((k_hook_write<MODE, F>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, eta, \
+#define MUONH_HW(MODE)                                                                                   \
+  hipLaunchKernelGGL((k_hook_write<MODE>), dim3(nblocks), dim3(kHookThreads), 0, s, mats, blocks, st, eta, \
                      zero_rel_eps, outward, inward, rb_eps, decay, flags)
-  if (mode == kModeNone) MUONH_HW(kModeNone, false);
-  else if (fused) {
-    if (mode == kModeRB) MUONH_HW(kModeRB, true);
-    else if (mode == kModeRel) MUONH_HW(kModeRel, true);
-    else MUONH_HW(kModeHB, true);
-  } else {
-    if (mode == kModeRB) MUONH_HW(kModeRB, false);
-    else if (mode == kModeRel) MUONH_HW(kModeRel, false);
-    else MUONH_HW(kModeHB, false);
-  }
+  if (mode == kModeRB) MUONH_HW(kModeRB);
+  else if (mode == kModeNone) MUONH_HW(kModeNone);
+  else if (mode == kModeRel) MUONH_HW(kModeRel);
+  else MUONH_HW(kModeHB);
 #undef MUONH_HW
   return hipGetLastError();
 }

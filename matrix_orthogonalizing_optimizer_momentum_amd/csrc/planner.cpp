@@ -140,8 +140,10 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
     const double ob = esize(cfg.op_dt);
     // momentum 3 passes; hook pass 1 (none for Muon's own update; W only for
     // RelativeUpdate) and pass 2
-    // (the producer of O reads W for the hook's norms: 4 bytes)
-    const double hook1 = cfg.hook == kModeNone ? 0 : 4;
+    // hook pass 1: W and O (RelativeUpdate: W only); with resident tiles
+    // the tile kernel reads W for the norms instead (4 bytes)
+    const bool fused_mat = cfg.kind == CALL_STEP && cfg.hook != kModeNone && resident_tile(T);
+    const double hook1 = cfg.hook == kModeNone ? 0 : (cfg.hook == kModeRel || fused_mat) ? 4 : 4 + ob;
     if (cfg.kind == CALL_STEP) plan.stream_bytes += (double)numel * (3 * sb + hook1 + (4 + ob + 4));
     else plan.stream_bytes += (double)numel * (sb + sb);  // NS: read input, write output
   }
@@ -242,8 +244,11 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
   }
   const int nunits = (int)t.units.size();
   auto resident = [&](const MatPlan& m) { return !no_ns(cfg.kind) && resident_tile(m.T); };
-  // The step's hook norms (<W, O>, ||W||^2) are summed where O is stored.
-  t.fused = cfg.kind == CALL_STEP && cfg.hook != kModeNone;
+  // A step's hook norms (<W, O>, ||W||^2) are summed where O is stored for
+  // matrices run as resident tiles: the tile kernel reads W at little cost,
+  // while in the GEMM engine's last epilogue the extra read costs more than
+  // the separate norm pass it would replace.
+  auto fused = [&](const MatPlan& m) { return cfg.kind == CALL_STEP && cfg.hook != kModeNone && resident(m); };
 
   // --- slots: [unit norms][matrix O norms][matrix hook sums]; the
   // resident-tile kernel forms its tile norms itself, so it has no unit slots.
@@ -276,7 +281,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
         tm.out_dtype = cfg.kind == CALL_STEP ? cfg.op_dt : cfg.state_dt;
         tm.onorm_slot = s_onorm0 + mi;
         tm.hook_slot = s_hook0 + mi;
-        tm.w = t.fused ? static_cast<const float*>(p.params[gi]) : nullptr;
+        tm.w = fused(m) ? static_cast<const float*>(p.params[gi]) : nullptr;
         // 8-element (16 / 32-byte) chunks need 8-aligned rows and tile origins
         // and 16-byte aligned buffers.
         auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
@@ -315,7 +320,6 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       NsUnit& u = t.units[unit0[mi] + k];
       u.norm_slot = s_norm0 + unit0[mi] + k;
       u.onorm_slot = s_onorm0 + mi;
-      u.hook_slot = s_hook0 + mi;
       u.onorm_part0 = part;
       u.o_dtype = out_dt;
       u.o_ld = m.W;
@@ -328,7 +332,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
         u.o_rows = (int32_t)h;
         u.o_cols = (int32_t)w;
         u.o_ptr = static_cast<char*>(out) + ((int64_t)a * T * m.W + (int64_t)b * T) * oes;
-        if (t.fused) u.w_ptr = static_cast<const float*>(p.params[gi]) + ((int64_t)a * T * m.W + (int64_t)b * T);
+
       } else {
         h = m.H;
         w = m.W;
@@ -336,7 +340,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
         u.o_rows = m.r;
         u.o_cols = m.s;
         u.o_ptr = out;
-        if (t.fused) u.w_ptr = static_cast<const float*>(p.params[gi]);
+
       }
       const int gc12 = unit_gemm_cfg(u.r, cfg.op_dt, true), gc3 = unit_gemm_cfg(u.r, cfg.op_dt, false);
       const int B12 = gemm_tile_side(gc12), B3 = gemm_tile_side(gc3);
@@ -454,13 +458,17 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
         hm.onorm_slot = U ? s_onorm0 + mi : -1;
         if (U) t.nparts[s_onorm0 + mi] = hm.nblocks;
       }
-      // fused: one (0, ||W||^2) partial per O-norm partial of the matrix
-      t.nparts[s_hook0 + mi] = t.fused ? t.nparts[s_onorm0 + mi] : hm.nblocks;
+      // fused: one (0, ||W||^2) partial per O-norm partial (per tile)
+      hm.fused = fused(m) ? 1 : 0;
+      t.nparts[s_hook0 + mi] = hm.fused ? t.nparts[s_onorm0 + mi] : hm.nblocks;
       const int idx = (int)t.hook_mats.size();
       t.hook_mats.push_back(hm);
-      for (int b = 0; b < hm.nblocks; ++b) t.hook_blocks.push_back({idx, b});
+      for (int b = 0; b < hm.nblocks; ++b) {
+        t.hook_blocks.push_back({idx, b});
+        if (!hm.fused) t.hook1_blocks.push_back({idx, b});
+      }
       const double ob = hm.o ? esize(hm.o_dtype) : 0;
-      if (t.fused) {
+      if (hm.fused) {
         // no pass 1
       } else if (cfg.hook == kModeRel) {
         t.bytes_hook1 += (double)hm.numel * 4;  // ||W||^2 only

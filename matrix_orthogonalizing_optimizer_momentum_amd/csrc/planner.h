@@ -111,7 +111,7 @@ struct ChunkTables {
   std::vector<TileMat> tile_mats;
   std::vector<TileJob> tile_jobs;
   std::vector<TileGroup> tile_groups;
-  bool fused = false;  // the hook's norms come from the producer of O (no hook pass 1)
+  std::vector<HookBlock> hook1_blocks;  // pass-1 blocks: matrices whose norms are not fused
   std::vector<int32_t> nparts;
   std::vector<int64_t> part_base;
   int64_t parts_total = 0;

@@ -124,8 +124,9 @@ def test_plain_update_needs_no_radius_and_no_hook_pass():
     o = _opts()
     o.hook = mm.MUONH_HOOK_NONE
     q_hb = mm.plan_query([(64, 64)], K=5)  # default hook: Hyperball
-    # momentum 6, the W read where O is stored (the hook's norms) 4, update pass 10
-    assert q_hb["stream_bytes"] == 64 * 64 * 20
+    assert q_hb["stream_bytes"] == 64 * 64 * 22  # momentum 6, hook pass 1 6, update pass 10
+    # resident tiles sum the hook's norms where O is stored: a W read (4) instead of pass 1
+    assert mm.plan_query([(64, 64)], K=5, tile_T=64)["stream_bytes"] == 64 * 64 * 20
     lib = mm.load()
     out = (ctypes.c_int64 * 7)()
     sh = (ctypes.c_int64 * 2)(64, 64)
@@ -188,9 +189,8 @@ def test_plan_query_gpt2_accounting():
     assert q["chunks"] == 1 and q["units"] == 48
     assert q["ns_flops"] == _dense_flops(shapes, 5)
     elems = sum(H * W for H, W in shapes)
-    # bf16 state, bf16 operands: momentum 6 B + the W read where O is stored (4; the hook's
-    # norms, no pass of their own) + the update pass (4 + 2 + 4) = 20 B/elem
-    assert q["stream_bytes"] == 20 * elems
+    # bf16 state, bf16 operands: momentum 6 B + hook pass 1 (4 + 2) + pass 2 (4 + 2 + 4) = 22 B/elem
+    assert q["stream_bytes"] == 22 * elems
 
 
 def test_plan_query_tiled_units_and_flops():
