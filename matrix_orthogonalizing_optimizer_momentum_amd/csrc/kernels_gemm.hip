@@ -30,6 +30,8 @@
 // (v_mfma_f32_32x32x2_f32), accumulation is fp32, LDS stages are double
 // buffered with a register prefetch ring of the next stages, and MFMA
 // fragments are double buffered in registers.
+#include <type_traits>
+
 #include "common.h"
 
 namespace muonh {
@@ -74,6 +76,16 @@ struct NsIterArgs {
 };
 
 constexpr int kThreads = 256;
+
+
+// s_waitcnt immediates (gfx9 field layout: vmcnt [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]): wait on one counter, leave the others at maximum.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | (((N >> 4) & 3) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // 4 consecutive elements as float.
 __device__ __forceinline__ void load4(const bf16_t* p, int64_t i, float (&v)[4]) {
@@ -149,7 +161,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   // LDS operand tiles: K-contiguous rows [m][k] with pitch LDK, or (TR)
   // [k][m] rows of BM elements, row k rotated by ROT * (k % RN) elements so
   // that the rows one fragment read touches land in different banks.
-  constexpr int LDK = BK + M::PAD;
+  // 256-tiles with bf16 operands run the ping-pong main loop (below): no
+  // row padding (direct loads write whole 1 KB runs), XOR-swizzled chunks.
+  constexpr bool PP = sizeof(T) == 2 && WGM * WGN == 8;
+  constexpr int LDK = PP ? BK : BK + M::PAD;
   constexpr int RN = sizeof(T) == 2 ? 4 : 2, ROT = 32;
   constexpr int PSZ = TR ? BK * BM : BM * LDK;  // elements per operand stage
   constexpr int QSZ = TR ? BK * BN : BN * LDK;
@@ -236,6 +251,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   constexpr bool kLateSeed = sizeof(T) == 2 && MI * NI <= 4;
   u32x2_t seedv[kLateSeed ? MI : 1][kLateSeed ? NI : 1][4];
   bool late = false;
+  // 256-tiles (ping-pong loop) start from zero accumulators: with bf16
+  // seeds each wave adds its seed block while the half stage of Q that holds
+  // it is in LDS; fp32 master seeds, and seeds with no stages, are added
+  // after the main loop.
+  bool pp_late = false, pp_after = false;
   const T* const seed_src = PHASE == kG2 ? reinterpret_cast<const T*>(u.a) : xt_in;
   const int seed_nlim = PHASE == kG2 ? u.r : u.ld_s;  // rows of the seed source
   const float seed_coef = PHASE == kG2 ? g2_seed : (args.no_mma ? 1.f : args.a);
@@ -246,6 +266,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   };
   if (PHASE == kG1) {
     zero_acc();
+  } else if (PP) {
+    zero_acc();
+    const bool m32 = PHASE == kG3 && !args.first && u.x32 != nullptr;
+    pp_late = nstage > 0 && !m32;
+    pp_after = !pp_late;
   } else {
     const bool m32 = PHASE == kG3 && !args.first && u.x32 != nullptr;  // fp32 master
     const T* src = seed_src;
@@ -463,7 +488,205 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  if (nstage > 0) {
+  if constexpr (PP) {
+    if (nstage > 0) {
+      // Ping-pong: waves w and w + 4 share a SIMD.  Group 0 (waves 0-3) and
+      // group 1 (waves 4-7) alternate between a memory phase (fragments of
+      // half a stage, LDS -> registers) and a compute phase (that half
+      // stage's MFMAs from registers), one phase apart, so one wave of each
+      // SIMD feeds the matrix core while the other moves data; every phase
+      // ends at a barrier of all 8 waves.
+      //
+      // LDS holds two stages [P | Q] of BK = 64 (128-byte rows: direct loads
+      // of whole 128-byte row segments run at close to twice the rate of
+      // 64-byte ones).  Phases of stage ks are 4 ks + 0..3 (group 0: memory
+      // half 0, compute, memory half 1, compute; group 1 one phase behind).
+      // Stage ks + 1 overwrites the buffer of stage ks - 1, whose last reads
+      // (group 1, half 1) ended at phase 4 ks - 1.  Its direct global -> LDS
+      // loads (group 0: the P half, group 1: the Q half, eight 1 KB runs per
+      // wave) ride in the compute phases 4 ks (group 1) and 4 ks + 1
+      // (group 0), one after every other MFMA, so their issue (the texture
+      // path takes about 16 cycles per run) overlaps matrix work; both
+      // groups wait for theirs at the end of phase 4 ks + 3, before the
+      // stage's first read at phase 4 ks + 4.
+      //
+      // A 1 KB direct load writes lane l's 16 bytes at byte 16 l of the run,
+      // so the global source of each lane is permuted to realise the XOR
+      // swizzle of K-contiguous rows or the rotation of the transposed tiles.
+      static_assert(BM == 256 && PSZ == QSZ && BK == 64, "ping-pong layout: square 256-tiles, 64-deep stages");
+      constexpr int STAGE_B = (PSZ + QSZ) * (int)sizeof(T);
+      constexpr int NDMA = STAGE_B / 1024;  // 1 KB direct loads per stage
+      constexpr int DPW = NDMA / 8;         // per wave: a quarter of its group's half
+      constexpr int CPRK = BK / VEC;        // 16-byte chunks per K-contiguous row
+      constexpr int RPR = 64 / CPRK;        // K-contiguous rows per run
+      static_assert(NDMA * 1024 == STAGE_B && DPW * 8 == NDMA && 2 * STAGE_B <= kSmem, "stage layout");
+      static_assert(CPRK == 8, "swizzle: 8 chunks per row");
+      constexpr int NKH = BK / KSTEP / 2;   // k-steps per half stage
+      // Swizzle of K-contiguous rows: chunk c of row r sits at c ^ swz(r),
+      // which spreads any 16 consecutive rows of one chunk over all banks.
+      auto swz = [](int r) { return (r >> 1) & 7; };
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      const int grp = wv >> 2;
+      // A wave's runs are (wave % 4) + 4 p of its group's operand; run
+      // (wave % 4) + 4 p is read from a per-lane byte offset (p = 0, stage
+      // 0) plus the uniform p * rstride (the swizzle and rotation terms
+      // depend only on the run modulo 4).  Operand buffers are padded to
+      // whole 256-row tiles (and the transposed tiles' column overrun), so
+      // no run is clamped.
+      uint32_t voff;
+      int64_t rstride;
+      {
+        const int ii = wv & 3;
+        const int64_t ld = grp == 0 ? ldP : ldQ;
+        const int base = grp == 0 ? row0 : col0;
+        int64_t e;
+        if (TR) {
+          // two rows k of 256 elements per run; physical chunk pc holds
+          // logical chunk (pc - 4 (k % 4)) % 32
+          const int k = 2 * ii + (lane >> 5), pc = lane & 31;
+          const int c = (pc - 4 * (k & 3)) & 31;
+          e = (int64_t)k * ld + base + c * VEC;
+          rstride = 8 * ld * (int64_t)sizeof(T);
+        } else {
+          const int rr = RPR * ii + lane / CPRK, pc = lane % CPRK;
+          const int c = pc ^ swz(rr);
+          e = (int64_t)(base + rr) * ld + c * VEC;
+          rstride = 4 * RPR * ld * (int64_t)sizeof(T);
+        }
+        voff = (uint32_t)(e * (int64_t)sizeof(T));
+      }
+      const char* const opb = grp == 0 ? Pb : Qb;
+      const int half = (grp == 0 ? 0 : PSZ * (int)sizeof(T)) + (wv & 3) * 1024;
+      // run (wave % 4) + 4 p of stage ks
+      auto dma_run = [&](int ks, int p) {
+        const char* src = opb + (int64_t)ks * kstride + p * rstride;
+        __builtin_amdgcn_global_load_lds((MUONH_GLOBAL void*)(gmem(src) + voff),
+                                         (__attribute__((address_space(3))) void*)(smem + (ks & 1) * STAGE_B + half +
+                                                                                   4 * p * 1024),
+                                         16, 0, 0);
+      };
+      auto dma = [&](int ks) {
+#pragma unroll
+        for (int p = 0; p < DPW; ++p) dma_run(ks, p);
+      };
+      // fragment offsets (elements) inside a stage's P / Q halves
+      int xk[2 * NKH];
+#pragma unroll
+      for (int kk = 0; kk < 2 * NKH; ++kk) xk[kk] = ((2 * kk + (lane >> 5)) ^ swz(lcol)) * VEC;
+      int pb[MI], qb[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) pb[i] = TR ? pofs[i] : (wm * WM + i * 32 + lcol) * BK;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) qb[j] = TR ? qofs[j] : (wn * WN + j * 32 + lcol) * BK;
+      typename M::frag fa[NKH][MI], fb[NKH][NI];
+      // fragments of half sh (k-steps NKH sh ..) of stage ks
+      auto read_half = [&](int ks, int sh) {
+        const T* sp = reinterpret_cast<const T*>(smem + (ks & 1) * STAGE_B);
+        const T* sq = sp + PSZ;
+#pragma unroll
+        for (int h = 0; h < NKH; ++h) {
+          const int kk = NKH * sh + h;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) fa[h][i] = TR ? frag(sp, pb[i], kk) : M::ld(sp + pb[i] + xk[kk]);
+#pragma unroll
+          for (int j = 0; j < NI; ++j) fb[h][j] = TR ? frag(sq, qb[j], kk) : M::ld(sq + qb[j] + xk[kk]);
+        }
+      };
+      // Seed rows of accumulator block i are the 32 K rows of the half stage
+      // with 32 (2 ks + sh) == row0 + wm * WM + i * 32: Q row n holds
+      // X^T(n, m) (G3) or A(n, m) (G2), and a lane's 4 rows m are one 8-byte
+      // piece of it.
+      auto seed_pull_pp = [&](int ks, int sh) {
+        if constexpr (PHASE != kG1) {
+          if (!pp_late) return;
+          const T* sq = reinterpret_cast<const T*>(smem + (ks & 1) * STAGE_B) + PSZ;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            if (ks * BK + 32 * sh != row0 + wm * WM + i * 32) continue;  // uniform per wave
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+              const int nl = wn * WN + j * 32 + lcol;
+              // rows m of a stage are below K = ld_r; columns n past the
+              // seed source's rows get no seed
+              const float mul = col0 + nl < seed_nlim ? seed_coef : 0.f;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const u32x2_t w =
+                    *reinterpret_cast<const u32x2_t*>(sq + nl * BK + ((4 * sh + q) ^ swz(nl)) * VEC + lrow);
+                acc[i][j][4 * q + 0] = fmaf(mul, __uint_as_float(w[0] << 16), acc[i][j][4 * q + 0]);
+                acc[i][j][4 * q + 1] = fmaf(mul, __uint_as_float(w[0] & 0xffff0000u), acc[i][j][4 * q + 1]);
+                acc[i][j][4 * q + 2] = fmaf(mul, __uint_as_float(w[1] << 16), acc[i][j][4 * q + 2]);
+                acc[i][j][4 * q + 3] = fmaf(mul, __uint_as_float(w[1] & 0xffff0000u), acc[i][j][4 * q + 3]);
+              }
+            }
+          }
+        }
+      };
+      // The half stage's MFMAs; with lks >= 0 this wave's runs of stage lks
+      // are issued in between, one after every MPL MFMAs.
+      constexpr int NMF = NKH * MI * NI, MPL = NMF / DPW;
+      static_assert(MPL * DPW == NMF, "loads spread evenly over the MFMAs");
+      auto mma_half = [&](int lks) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+          const int h = t / (MI * NI), i = (t / NI) % MI, j = t % NI;
+          acc[i][j] = M::mma(fa[h][i], fb[h][j], acc[i][j]);
+          if (t % MPL == MPL - 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (lks >= 0) dma_run(lks, t / MPL);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto bar = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      dma(0);
+      wait_vmcnt<0>();
+      bar();
+      if (grp == 0) {
+        for (int ks = 0; ks < nstage; ++ks) {
+          read_half(ks, 0);                          // phase 4 ks
+          seed_pull_pp(ks, 0);
+          wait_lgkmcnt0();
+          bar();
+          mma_half(ks + 1 < nstage ? ks + 1 : -1);   // phase 4 ks + 1
+          bar();
+          read_half(ks, 1);                          // phase 4 ks + 2
+          seed_pull_pp(ks, 1);
+          wait_lgkmcnt0();
+          bar();
+          mma_half(-1);                              // phase 4 ks + 3
+          wait_vmcnt<0>();
+          bar();
+        }
+      } else {
+        for (int ks = 0; ks < nstage; ++ks) {
+          if (ks > 0) mma_half(ks + 1 < nstage ? ks + 1 : -1);  // phase 4 ks
+          else if (nstage > 1) dma(1);
+          bar();
+          read_half(ks, 0);                          // phase 4 ks + 1
+          seed_pull_pp(ks, 0);
+          wait_lgkmcnt0();
+          bar();
+          mma_half(-1);                              // phase 4 ks + 2
+          bar();
+          read_half(ks, 1);                          // phase 4 ks + 3
+          seed_pull_pp(ks, 1);
+          wait_lgkmcnt0();
+          wait_vmcnt<0>();
+          bar();
+        }
+        mma_half(-1);
+      }
+    }
+  } else if (nstage > 0) {
     // Stage s lives in ring slot s % NPF from its global load until its LDS
     // store.  While stage ks is computed from LDS buffer ks % 2, stage ks+1
     // is stored into the other buffer and its ring slot is refilled with
@@ -504,6 +727,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 #undef MUONH_GLOAD
 #undef MUONH_LSTORE
 
+  if constexpr (PP && PHASE != kG1) {
+    if (pp_after) {
+      // fp32 master seeds (or no stages): from HBM, one accumulator row
+      // block at a time
+      const bool m32 = PHASE == kG3 && !args.first && u.x32 != nullptr;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bool ok;
+            const int64_t o = seed_off(i, j, q, ok);
+            const float mul = ok ? seed_coef : 0.f;
+            float x[4];
+            if (m32) {
+              const f32x4_t t = *reinterpret_cast<const MUONH_GLOBAL f32x4_t*>(gmem(u.x32) + o);
+              x[0] = t[0]; x[1] = t[1]; x[2] = t[2]; x[3] = t[3];
+            } else {
+              load4(seed_src, o, x);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = fmaf(mul, x[e], acc[i][j][4 * q + e]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
   if constexpr (kLateSeed) {
     if (late) {
 #pragma unroll

@@ -30,20 +30,25 @@ namespace muonh {
 UnitBytes unit_bytes(int r, int s, int op_dt, int x32) {
   const int64_t es = esize(op_dt);
   const int64_t ld_s = pad_up(s, kPad), ld_r = pad_up(r, kPad);
+  // GEMM operands hold whole 256-row tiles, and X^T a further 256 elements
+  // (the column overrun of a transposed 256-wide tile on its last row): the
+  // 256-tile main loop loads whole tiles without clamping; the rows past the
+  // true sides only feed outputs that are never stored.
+  const int64_t rows_s = pad_up(s, 256), rows_r = pad_up(r, 256);
   UnitBytes u;
-  u.xt = align256(ld_s * ld_r * es);
+  u.xt = align256((rows_s * ld_r + 256) * es);
   u.x32 = (x32 && op_dt == DT_BF16) ? align256(ld_s * ld_r * 4) : 0;
-  u.a = align256((int64_t)r * ld_r * es);
+  u.a = align256(rows_r * ld_r * es);
   u.b = u.a;
   return u;
 }
 
-// 256-tiles for bf16 units with r >= 1024 (>= 10 upper tiles for G1 / G2,
-// >= 16 tiles for G3 per unit); smaller units keep 128-tiles, which fill the
-// chip better.  MUONH_GEMM_BIG=0 / 2 forces 128 / 256 tiles (bf16) for
-// tuning runs; results do not depend on the choice beyond summation order.
+// 256-tiles (the ping-pong main loop) for bf16 units with r >= 1024 (>= 10
+// upper tiles for G1 / G2, >= 16 tiles for G3 per unit), and for G3 already
+// from r >= 512; smaller units keep 128-tiles, which fill the chip better.
+// MUONH_GEMM_BIG=0 / 2 forces 128 / 256 tiles (bf16) for tuning runs;
+// results do not depend on the choice beyond summation order.
 int unit_gemm_cfg(int r, int op_dt, bool phase12) {
-  (void)phase12;
   if (op_dt != DT_BF16) return 0;
   static int mode = -1;
   if (mode < 0) {
@@ -52,7 +57,7 @@ int unit_gemm_cfg(int r, int op_dt, bool phase12) {
   }
   if (mode == 0) return 0;
   if (mode == 2) return 1;
-  return r >= 1024 ? 1 : 0;
+  return r >= (phase12 ? 1024 : 512) ? 1 : 0;
 }
 
 static int64_t jobs_per_iter(int r, int s, int op_dt) {
@@ -128,7 +133,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
       m.nunits = 1;
       m.ntr = m.ntc = 1;
       // GEMM operand loads address a unit's X^T with 32-bit byte offsets.
-      if (pad_up(m.r, kPad) * pad_up(m.s, kPad) * esize(cfg.op_dt) >= ((int64_t)1 << 32)) return MUONH_ENOTIMPL;
+      if ((pad_up(m.s, 256) * pad_up(m.r, kPad) + 256) * esize(cfg.op_dt) >= ((int64_t)1 << 32)) return MUONH_ENOTIMPL;
       const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32);
       m.ws_bytes += ub.total();
       plan.ns_flops += ns_flops_true(m.H, m.W, cfg.K);
