@@ -62,7 +62,8 @@ def test_ns_fp32_small(shape):
 
 @pytest.mark.parametrize("prec", ["x32", "fold"])
 @pytest.mark.parametrize("shape", [(768, 768), (768, 3072), (3072, 768), (768, 2304), (300, 700), (500, 1300),
-                                   (1300, 500), (256, 256), (1024, 2048), (1100, 1700), (2500, 1300)],
+                                   (1300, 500), (600, 1000), (1000, 600), (256, 256), (1024, 2048), (1100, 1700),
+                                   (2500, 1300)],
                          ids=lambda s: f"{s[0]}x{s[1]}" if isinstance(s, tuple) else s)
 def test_ns_bf16_spiked(shape, prec):
     H, W = shape
@@ -82,6 +83,20 @@ def test_ns_iteration_counts(K):
     out = mm.ns_orthogonalize([dev(X)], K=K, ns_dtype="f32")[0]
     torch.cuda.synchronize()
     assert rel(host(out), orc.newton_schulz(X, K)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("K", [0, 1, 2])
+def test_ns_iteration_counts_bf16_large(K):
+    # 1100 x 1200: every product runs on 256-tiles with a partial last tile
+    # row (Gram side 1100 of 1152 padded); K = 0 takes the no-product path
+    # (O = X0 / (||X0|| + eps) through the update epilogue).
+    banner(f"ns bf16 K={K} 1100x1200")
+    G = gen.store(gen.spiked_grad(1100, 1200, 1e-3, seed=77), "bf16")
+    out = mm.ns_orthogonalize([dev(G, torch.bfloat16)], K=K, ns_dtype="bf16")[0]
+    torch.cuda.synchronize()
+    err = rel(host(out), orc.newton_schulz(G, K))
+    print(f"  rel err {err:.3e}")
+    assert err <= TOL["bf16"]
 
 
 def test_ns_coefficient_table_two_stage():
