@@ -27,9 +27,16 @@
 // list of BM x BN output tiles; job order is remapped so that the jobs one XCD
 // runs are contiguous in the list (operand panels shared in its L2).
 // Operands are bf16 (v_mfma_f32_32x32x16_bf16) or fp32
-// (v_mfma_f32_32x32x2_f32), accumulation is fp32, LDS stages are double
-// buffered with a register prefetch ring of the next stages, and MFMA
-// fragments are double buffered in registers.
+// (v_mfma_f32_32x32x2_f32), accumulation is fp32.  Two main loops:
+//   - 128 x 128 tiles (4 waves, two workgroups per CU): LDS stages double
+//     buffered behind a register prefetch ring of 16-byte global loads, MFMA
+//     fragments double buffered in registers;
+//   - 256 x 256 tiles with bf16 operands (8 waves, one workgroup per CU): an
+//     8-wave ping-pong, waves w and w + 4 alternating between reading a half
+//     stage's fragments from LDS and running its MFMAs, with the operands
+//     brought in by direct global -> LDS loads interleaved with the MFMAs.
+// The epilogues (seeded accumulators, mirrored symmetric tiles, X^T stored
+// from registers, O in the caller's layout) are shared.
 #include <type_traits>
 
 #include "common.h"
