@@ -151,8 +151,9 @@ void muonh_default_opts(muonh_opts* o);
  *   grads[i]   device, state_dtype, same shape, read only (G)
  *   moms[i]    device, state_dtype, same shape, updated in place (M)
  *   shapes     host, 2*n int64: rows, cols of matrix i (each >= 1; with
- *              tile_T = 0 or > 128, pad64(rows) * pad64(cols) * operand bytes
- *              must stay below 4 GiB, else MUONH_ENOTIMPL)
+ *              tile_T = 0 or > 128, (pad256(longer side) * pad64(shorter
+ *              side) + 256) * operand bytes must stay below 4 GiB, else
+ *              MUONH_ENOTIMPL)
  *   n          number of matrices (>= 1)
  *   eta        learning rate / Hyperball angular step (finite, >= 0)
  *   beta       momentum coefficient, in [0, 1)

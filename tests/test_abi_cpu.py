@@ -288,3 +288,19 @@ def test_per_matrix_tile_sizes_validation():
         mm.plan_query([(64, 64), (64, 64)], K=5, tile_sizes=[0, 200])  # 200: not a multiple of 64 above 128
     with pytest.raises(ValueError):
         mm.plan_query([(64, 64), (64, 64)], K=5, tile_sizes=[64])
+
+
+def test_plan_query_32bit_operand_offset_limit():
+    # The GEMM engine addresses an operand buffer with 32-bit byte offsets:
+    # (pad256(longer side) * pad64(shorter side) + 256) * operand bytes must
+    # stay below 4 GiB.  bf16: 32704 x 65536 is the largest side pair at
+    # 65536 rows of X^T (65536 * 32704 * 2 + 512 < 2^32); 32768 x 65536 is not.
+    q = mm.plan_query([(32704, 65536)], K=5, workspace_limit=1 << 40)
+    assert q["units"] == 1
+    with pytest.raises(mm.MuonhError) as e:
+        mm.plan_query([(32768, 65536)], K=5, workspace_limit=1 << 40)
+    assert e.value.code == mm.MUONH_ENOTIMPL
+    # the longer side counts padded to 256 rows: 65409 pads to 65472 at 64
+    # (which would fit) but to 65536 at 256
+    with pytest.raises(mm.MuonhError):
+        mm.plan_query([(32768, 65409)], K=5, workspace_limit=1 << 40)
