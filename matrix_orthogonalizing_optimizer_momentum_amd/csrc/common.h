@@ -120,11 +120,13 @@ __device__ __forceinline__ double wave_sum(double v) {
 // `part` of reduction slot `slot`.  No fence: a later finalize kernel (a
 // kernel boundary later) sums the slot's partials in a fixed order, so the
 // result is bitwise reproducible.  Must be called by every thread.
+// block_partial2_at takes its LDS scratch (2 NT / 64 doubles) from the
+// caller; block_partial2 uses a static array of its own.
 template <int NT>
-__device__ void block_partial2(double v0, double v1, const SlotTable& st, int slot, int part) {
+__device__ void block_partial2_at(double v0, double v1, const SlotTable& st, int slot, int part,
+                                  double (*red)[NT / 64]) {
   static_assert(NT % 64 == 0, "block must be whole waves");
   constexpr int NW = NT / 64;
-  __shared__ double red[2][NW];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   v0 = wave_sum(v0);
   v1 = wave_sum(v1);
@@ -138,6 +140,11 @@ __device__ void block_partial2(double v0, double v1, const SlotTable& st, int sl
     gmem(st.partials)[2 * p] = t0;
     gmem(st.partials)[2 * p + 1] = t1;
   }
+}
+template <int NT>
+__device__ void block_partial2(double v0, double v1, const SlotTable& st, int slot, int part) {
+  __shared__ double red[2][NT / 64];
+  block_partial2_at<NT>(v0, v1, st, slot, part, red);
 }
 
 // Three per-block sums: (a, b) into slot_a, (0, c) into slot_b, both at

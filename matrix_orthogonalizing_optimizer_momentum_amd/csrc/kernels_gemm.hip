@@ -171,6 +171,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   // 256-tiles with bf16 operands run the ping-pong main loop (below): no
   // row padding (direct loads write whole 1 KB runs), XOR-swizzled chunks.
   constexpr bool PP = sizeof(T) == 2 && WGM * WGN == 8;
+  // G3 on the ping-pong loop keeps its operands in a ring of five 32 KB
+  // slots instead of two 64 KB stages (see the main loop)
+  constexpr bool RING5 = PP && PHASE == kG3;
   constexpr int LDK = PP ? BK : BK + M::PAD;
   constexpr int RN = sizeof(T) == 2 ? 4 : 2, ROT = 32;
   constexpr int PSZ = TR ? BK * BM : BM * LDK;  // elements per operand stage
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 
   // Main loop: P and Q stages (double buffered).  The epilogue reuses the
   // same LDS for its fp32 slabs.
-  constexpr int kStage = 2 * (PSZ + QSZ) * (int)sizeof(T);
+  constexpr int kStage = RING5 ? 5 * PSZ * (int)sizeof(T) : 2 * (PSZ + QSZ) * (int)sizeof(T);
   // Slab rows: fit the stage buffers, and keep the batched row-pass reads of
   // a slab (SLAB * BN / NT values per thread) within 64 registers.
   constexpr int SLAB_LDS = (BM * BN * 4 <= kStage) ? BM : ((BM / 2) * BN * 4 <= kStage ? BM / 2 : BM / 4);
@@ -495,7 +498,190 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  if constexpr (PP) {
+  if constexpr (RING5) {
+    if (nstage > 0) {
+      // The ping-pong of the two-stage loop below (groups 0 and 1 one phase
+      // apart, memory and compute phases of half a 64-deep stage, a barrier
+      // of all 8 waves after every phase), with the operands in a ring of
+      // five 32 KB slots, each the P or the Q of a stage: stage s uses slots
+      // 2 s and 2 s + 1 (mod 5).  The slots of stage ks - 1 (last read in
+      // phase 4 ks - 1) receive Q of stage ks + 1 (phases 4 ks, 4 ks + 1) and
+      // P of stage ks + 2 (phases 4 ks + 2, 4 ks + 3); P of stage ks + 1 came
+      // during stage ks - 1.  So every compute phase carries four 1 KB
+      // direct loads per wave, one after every fourth MFMA, and at the end of
+      // phase 4 ks + 3 each wave waits for all but its newest four loads
+      // (everything of stage ks + 1).  Measured against the two-stage loop:
+      // faster for G3, slower for the symmetric G1 / G2, hence G3 only.
+      static_assert(BM == 256 && PSZ == QSZ && BK == 64, "ping-pong layout: square 256-tiles, 64-deep stages");
+      constexpr int SLOT_B = PSZ * (int)sizeof(T);
+      constexpr int NRUN = SLOT_B / 1024;  // 1 KB direct loads per operand slot
+      constexpr int RPW = NRUN / 8;        // per wave and phase
+      constexpr int CPRK = BK / VEC;       // 16-byte chunks per K-contiguous row
+      constexpr int RPR = 64 / CPRK;       // K-contiguous rows per run
+      static_assert(NRUN * 1024 == SLOT_B && RPW * 8 == NRUN && 5 * SLOT_B <= kSmem, "slot layout");
+      static_assert(CPRK == 8 && RPW == 4, "swizzle: 8 chunks per row; four loads per wave and phase");
+      constexpr int NKH = BK / KSTEP / 2;  // k-steps per half stage
+      auto swz = [](int r) { return (r >> 1) & 7; };
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      const int grp = wv >> 2;
+      auto slot_p = [&](int ks) { return smem + ((2 * ks) % 5) * SLOT_B; };
+      auto slot_q = [&](int ks) { return smem + ((2 * ks + 1) % 5) * SLOT_B; };
+      // A wave's loads of one operand slot: runs 16 grp + (wave % 4) + 4 p,
+      // p < 4, each from a per-lane byte offset (the wave's first run, stage
+      // 0) plus the uniform p * rstride.  Operand buffers are padded to whole
+      // 256-row tiles, so no run is clamped.
+      uint32_t voff[2];
+      int64_t rstride;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ii = 16 * grp + (wv & 3);
+        const int64_t ld = h == 0 ? ldP : ldQ;
+        const int base = h == 0 ? row0 : col0;
+        const int rr = RPR * ii + lane / CPRK, pc = lane % CPRK;
+        const int c = pc ^ swz(rr);
+        const int64_t e = (int64_t)(base + rr) * ld + c * VEC;
+        rstride = 4 * RPR * ld * (int64_t)sizeof(T);
+        voff[h] = (uint32_t)(e * (int64_t)sizeof(T));
+      }
+      const int run0 = 16 * grp + (wv & 3);
+      // run run0 + 4 p of operand h (0: P, 1: Q) of stage ks
+      auto dma_run = [&](int ks, int h, int p) {
+        const char* src = (h == 0 ? Pb : Qb) + (int64_t)ks * kstride + p * rstride;
+        char* const dst = (h == 0 ? slot_p(ks) : slot_q(ks)) + (run0 + 4 * p) * 1024;
+        __builtin_amdgcn_global_load_lds((MUONH_GLOBAL void*)(gmem(src) + voff[h]),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      };
+      int xk[2 * NKH];
+#pragma unroll
+      for (int kk = 0; kk < 2 * NKH; ++kk) xk[kk] = ((2 * kk + (lane >> 5)) ^ swz(lcol)) * VEC;
+      int pb[MI], qb[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) pb[i] = (wm * WM + i * 32 + lcol) * BK;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) qb[j] = (wn * WN + j * 32 + lcol) * BK;
+      typename M::frag fa[NKH][MI], fb[NKH][NI];
+      auto read_half = [&](int ks, int sh) {
+        const T* sp = reinterpret_cast<const T*>(slot_p(ks));
+        const T* sq = reinterpret_cast<const T*>(slot_q(ks));
+#pragma unroll
+        for (int h = 0; h < NKH; ++h) {
+          const int kk = NKH * sh + h;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) fa[h][i] = M::ld(sp + pb[i] + xk[kk]);
+#pragma unroll
+          for (int j = 0; j < NI; ++j) fb[h][j] = M::ld(sq + qb[j] + xk[kk]);
+        }
+      };
+      // Seed rows of accumulator block i are the 32 K rows of the half stage
+      // with 32 (2 ks + sh) == row0 + wm * WM + i * 32: Q row n holds
+      // X^T(n, m), and a lane's 4 rows m are one 8-byte piece of it.
+      auto seed_pull_ring = [&](int ks, int sh) {
+        if (!pp_late) return;
+        const T* sq = reinterpret_cast<const T*>(slot_q(ks));
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          if (ks * BK + 32 * sh != row0 + wm * WM + i * 32) continue;  // uniform per wave
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int nl = wn * WN + j * 32 + lcol;
+            const float mul = col0 + nl < seed_nlim ? seed_coef : 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x2_t w = *reinterpret_cast<const u32x2_t*>(sq + nl * BK + ((4 * sh + q) ^ swz(nl)) * VEC + lrow);
+              acc[i][j][4 * q + 0] = fmaf(mul, __uint_as_float(w[0] << 16), acc[i][j][4 * q + 0]);
+              acc[i][j][4 * q + 1] = fmaf(mul, __uint_as_float(w[0] & 0xffff0000u), acc[i][j][4 * q + 1]);
+              acc[i][j][4 * q + 2] = fmaf(mul, __uint_as_float(w[1] << 16), acc[i][j][4 * q + 2]);
+              acc[i][j][4 * q + 3] = fmaf(mul, __uint_as_float(w[1] & 0xffff0000u), acc[i][j][4 * q + 3]);
+            }
+          }
+        }
+      };
+      // the half stage's MFMAs with this wave's four loads of operand lh of
+      // stage lks in between (none for lks < 0)
+      constexpr int NMF = NKH * MI * NI, MPL = NMF / RPW;
+      static_assert(MPL * RPW == NMF, "loads spread evenly over the MFMAs");
+      auto mma_half = [&](int lks, int lh) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+          const int h = t / (MI * NI), i = (t / NI) % MI, j = t % NI;
+          acc[i][j] = M::mma(fa[h][i], fb[h][j], acc[i][j]);
+          if (t % MPL == MPL - 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (lks >= 0) dma_run(lks, lh, t / MPL);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto bar = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // before the loop: P and Q of stage 0 and P of stage 1; wait for stage 0
+#pragma unroll
+      for (int p = 0; p < RPW; ++p) {
+        dma_run(0, 0, p);
+        dma_run(0, 1, p);
+      }
+      if (nstage > 1) {
+#pragma unroll
+        for (int p = 0; p < RPW; ++p) dma_run(1, 0, p);
+        wait_vmcnt<RPW>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      bar();
+      // end of phase 4 ks + 3: all of stage ks + 1 has landed (only this
+      // wave's loads of P of stage ks + 2 may still be in flight)
+      auto wait_next = [&](int ks) {
+        if (ks + 2 < nstage) wait_vmcnt<RPW>();
+        else wait_vmcnt<0>();
+      };
+      if (grp == 0) {
+        for (int ks = 0; ks < nstage; ++ks) {
+          read_half(ks, 0);                                // phase 4 ks
+          seed_pull_ring(ks, 0);
+          wait_lgkmcnt0();
+          bar();
+          mma_half(ks + 1 < nstage ? ks + 1 : -1, 1);      // phase 4 ks + 1
+          bar();
+          read_half(ks, 1);                                // phase 4 ks + 2
+          seed_pull_ring(ks, 1);
+          wait_lgkmcnt0();
+          bar();
+          mma_half(ks + 2 < nstage ? ks + 2 : -1, 0);      // phase 4 ks + 3
+          wait_next(ks);
+          bar();
+        }
+      } else {
+        for (int ks = 0; ks < nstage; ++ks) {
+          if (ks > 0) {
+            mma_half(ks + 1 < nstage ? ks + 1 : -1, 1);    // phase 4 ks
+          } else if (nstage > 1) {
+#pragma unroll
+            for (int p = 0; p < RPW; ++p) dma_run(1, 1, p);
+          }
+          bar();
+          read_half(ks, 0);                                // phase 4 ks + 1
+          seed_pull_ring(ks, 0);
+          wait_lgkmcnt0();
+          bar();
+          mma_half(ks + 2 < nstage ? ks + 2 : -1, 0);      // phase 4 ks + 2
+          bar();
+          read_half(ks, 1);                                // phase 4 ks + 3
+          seed_pull_ring(ks, 1);
+          wait_lgkmcnt0();
+          wait_next(ks);
+          bar();
+        }
+        mma_half(-1, 0);
+      }
+    }
+  } else if constexpr (PP) {
     if (nstage > 0) {
       // Ping-pong: waves w and w + 4 share a SIMD.  Group 0 (waves 0-3) and
       // group 1 (waves 4-7) alternate between a memory phase (fragments of
@@ -962,7 +1148,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     }
   }
   if (PHASE == kG3) {
-    block_partial2<NT>(osq, 0.0, args.st, u.onorm_slot, u.onorm_part0 + job.tm * u.g3_cols + job.tn);
+    const int part = u.onorm_part0 + job.tm * u.g3_cols + job.tn;
+    if constexpr (RING5) {
+      // the static LDS of block_partial2 does not fit beside the slot ring:
+      // use bytes past the epilogue's slabs
+      static_assert(SLAB * BN * 4 + 2 * (NT / 64) * 8 <= kSmem, "reduction scratch");
+      block_partial2_at<NT>(osq, 0.0, args.st, u.onorm_slot, part,
+                            reinterpret_cast<double(*)[NT / 64]>(smem + SLAB * BN * 4));
+    } else {
+      block_partial2<NT>(osq, 0.0, args.st, u.onorm_slot, part);
+    }
   }
 }
 
