@@ -450,8 +450,9 @@ int hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 // Newton-Schulz iteration k of a chunk (K == 0: the single O = X0/||X0||
-// pass): G1, G2, G3 over every unit; the last one ends with the per-matrix
-// finalize of ||O||^2 (and, fused, of <W, O> and ||W||^2).
+// pass): G1, G2, G3 over every unit; the last one ends with the finalize of
+// the matrices' O-norm slots (||O||^2; for matrices run as resident tiles the
+// slot also carries <W, O>).
 int run_ns_iter(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r, const SlotTable& sl, hipStream_t s,
                 int k) {
   const float eps = r.o.ns_eps;
