@@ -108,6 +108,20 @@ def test_ns_coefficient_table_two_stage():
     assert rel(host(out), orc.newton_schulz(X, 10, coeffs=table)) <= TOL["f32"]
 
 
+def test_ns_coefficient_table_large_with_cubic_stage():
+    # 1100 x 1200 bf16 runs every product on 256-tiles; the textbook cubic
+    # stages (c = 0) leave G2 without a product: B = b A comes from the seed
+    # alone, added after the (empty) main loop.
+    banner("ns bf16 1100x1200, quintic then cubic stages")
+    table = [(3.4445, -4.7750, 2.0315)] * 4 + [(1.5, -0.5, 0.0)] * 2
+    G = gen.store(gen.spiked_grad(1100, 1200, 1e-3, seed=91), "bf16")
+    out = mm.ns_orthogonalize([dev(G, torch.bfloat16)], K=6, ns_dtype="bf16", coeffs=table)[0]
+    torch.cuda.synchronize()
+    err = rel(host(out), orc.newton_schulz(G, 6, coeffs=table))
+    print(f"  rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_ns_many_shapes_one_launch():
     banner("ns grouped launch, mixed shapes")
     shapes = [(64, 128), (128, 64), (200, 72), (33, 300), (256, 256)]
