@@ -121,9 +121,10 @@ typedef struct muonh_opts {
                                    formed from the updated M (Muon explainer, code section) */
   float        weight_decay;    /* MUONH_HOOK_NONE only: W <- W*(1 - eta*weight_decay) before
                                    the update (decoupled); finite, >= 0; default 0 */
-  int          lanes;           /* concurrent lanes, 1..4; 0 = automatic: 2, but 1 for
-                                   full-matrix Newton-Schulz when one iteration over the set
-                                   exceeds 2e12 flops (long products gain nothing from lanes).
+  int          lanes;           /* concurrent lanes, 1..4; 0 = automatic: 2, but 1 when every
+                                   matrix runs its Newton-Schulz as products of whole
+                                   matrices or of tiles above 128 and one iteration over the
+                                   set exceeds 2e12 flops (long products gain nothing from lanes).
                                    A call over
                                    two or more matrices that fit one workspace chunk is cut
                                    into that many runs of matrices, lane 0 on opts->stream and

@@ -43,9 +43,9 @@ struct MatPlan {
 };
 
 constexpr int kMaxLanes = 4;
-// Automatic lanes: two, except for full-matrix Newton-Schulz when one
-// iteration over the whole set exceeds this many flops (about 1.5 ms of
-// matrix-core work).
+// Automatic lanes: two, except for Newton-Schulz on the GEMM engine (full
+// matrices, or tiles above the resident size) when one iteration over the
+// whole set exceeds this many flops (about 1.5 ms of matrix-core work).
 constexpr double kAutoLaneIterFlops = 2e12;
 
 struct ChunkPlan {

@@ -106,12 +106,16 @@ def test_lanes_share_one_chunk_workspace():
 
 
 def test_automatic_lanes_follow_iteration_work():
-    # Two lanes, but one for full-matrix NS whose iteration exceeds 2e12 flops.
+    # Two lanes, but one for NS on the GEMM engine (full matrices, or tiles
+    # above the resident size 128) whose iteration exceeds 2e12 flops.
     small = [(1024, 1024)] * 4   # 4 * 6 * 1024^3 flops per iteration
     big = [(8192, 8192)] * 2     # 2 * 6 * 8192^3 > 2e12
     assert mm.plan_query(small, K=5)["lanes"] == 2
     assert mm.plan_query(big, K=5)["lanes"] == 1
-    assert mm.plan_query(big, K=5, tile_T=128)["lanes"] == 2
+    assert mm.plan_query(big, K=5, tile_T=128)["lanes"] == 2   # resident tiles
+    huge = [(16384, 16384)] * 8  # 8 * 4096 tiles of 256^2: 3.3e12 flops per iteration
+    assert mm.plan_query(huge, K=5, tile_T=256, workspace_limit=1 << 40)["lanes"] == 1
+    assert mm.plan_query(big, K=5, tile_T=256, workspace_limit=1 << 40)["lanes"] == 2  # 2.1e11
     assert mm.plan_query(big, K=5, lanes=2)["lanes"] == 2
     # a budget that forces sequential chunks leaves no room for lanes
     one = mm.plan_query(small[:1], K=5)["ws_bytes"]
