@@ -288,7 +288,12 @@ def main():
 
     dom = max(prof, key=lambda c: prof[c]["total_ms"])
     d = prof[dom]
-    if dom in NS_CLASSES:
+    # The resident-tile kernel also streams its tiles' state (read G, M and W,
+    # write M and O): it is bound by whichever floor is higher, matrix-core
+    # time or HBM time (HBM for T = 64 on bf16 state, about even at T = 128).
+    tile_hbm = (dom == "ns_tile_resident" and d["bytes"] > 0 and
+                d["bytes"] / (PEAK_HBM_GBS * 1e9) > d["flops"] / (PEAK_BF16_TFLOPS * 1e12))
+    if dom in NS_CLASSES and not tile_hbm:
         per_launch = d["flops"] / d["launches"]
         achieved = per_launch / (d["avg_ms"] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -308,6 +313,8 @@ def main():
     for c in NS_CLASSES:
         if c in prof and prof[c]["total_ms"] > 0:
             kernels[c]["tflops"] = round(prof[c]["flops"] / (prof[c]["total_ms"] * 1e-3) / 1e12, 2)
+            if prof[c]["bytes"] > 0:
+                kernels[c]["gbps"] = round(prof[c]["bytes"] / (prof[c]["total_ms"] * 1e-3) / 1e9, 1)
     for c in STREAM_CLASSES:
         if c in prof and prof[c]["total_ms"] > 0:
             kernels[c]["gbps"] = round(prof[c]["bytes"] / (prof[c]["total_ms"] * 1e-3) / 1e9, 1)

@@ -303,7 +303,8 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
           }
         t.nparts[s_onorm0 + mi] = m.nunits;
         const double numel = (double)m.H * m.W;
-        grp.bytes += cfg.kind == CALL_STEP ? numel * (3 * sb + es_op) : numel * 2 * sb;
+        // read G and M, write M and O; the hook's W read where it is fused
+        grp.bytes += cfg.kind == CALL_STEP ? numel * (3 * sb + es_op + (fused(m) ? 4 : 0)) : numel * 2 * sb;
       }
       grp.njobs = (int)t.tile_jobs.size() - grp.job0;
       t.flops_tile += grp.flops;
