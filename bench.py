@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 METRIC = "MuonH optimizer steps/sec + NS TFLOP/s (% bf16 MFMA peak), HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
@@ -87,16 +88,18 @@ def workload_shapes(name):
         return gen.dense_8b_shapes(), "8B-shaped dense matrix set: 32 x {4096x4096 q, 4096x1024 k, 4096x1024 v, 4096x4096 o, 4096x14336 gate, 4096x14336 up, 14336x4096 down}"
     if name == "single256":
         return [(256, 256)], "single 256x256 matrix"
+    if name == "single64x128":
+        return [(64, 128)], "single 64x128 matrix"
     raise SystemExit(f"unknown workload {name}")
 
 
-def make_device_inputs(shapes, nsets, seed, torch):
+def make_device_inputs(shapes, nsets, seed, torch, state_dtype=None):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     Ws, Ms, Gsets = [], [], []
     for H, W in shapes:
         Ws.append((torch.randn(H, W, generator=g, device="cuda") * 0.02).contiguous())
-        Ms.append(torch.zeros(H, W, device="cuda", dtype=torch.bfloat16))
+        Ms.append(torch.zeros(H, W, device="cuda", dtype=state_dtype or torch.bfloat16))
     sigma, rank, mag = 1e-3, 4, 10.0
     for _ in range(nsets):
         gs = []
@@ -105,7 +108,7 @@ def make_device_inputs(shapes, nsets, seed, torch):
             A = torch.randn(H, rank, generator=g, device="cuda")
             B = torch.randn(W, rank, generator=g, device="cuda")
             G = sigma * Z + (mag * sigma / math.sqrt(rank)) * (A @ B.t())
-            gs.append(G.to(torch.bfloat16).contiguous())
+            gs.append(G.to(state_dtype or torch.bfloat16).contiguous())
         Gsets.append(gs)
     rho = [float(torch.linalg.vector_norm(w.double())) for w in Ws]
     return Ws, Ms, Gsets, rho
@@ -200,6 +203,13 @@ def main():
                     help="concurrent lanes of a timed step (0: the library's automatic choice)")
     ap.add_argument("--profile-lanes", type=int, default=1, choices=[0, 1, 2, 3, 4],
                     help="lanes of the per-launch timing pass (1: every launch has the GPU to itself)")
+    ap.add_argument("--state", default="bf16", choices=["bf16", "f32"],
+                    help="gradient and momentum storage type (f32: the all-fp32 single-matrix setting)")
+    ap.add_argument("--ns-dtype", default="bf16", choices=["bf16", "f32"],
+                    help="Newton-Schulz operand type (f32 runs on fp32 MFMA)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of HIP graphs that captured one whole step per gradient set "
+                         "(after the warm-up has planned the call, so the captured launches allocate nothing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-sets", type=int, default=4)
     ap.add_argument("--ws-limit-mib", type=int, default=0,
@@ -222,12 +232,14 @@ def main():
 
     shapes, wdesc = workload_shapes(args.workload)
     K = args.K
-    Ws, Ms, Gsets, rho = make_device_inputs(shapes, args.grad_sets, 1234, torch)
+    Ws, Ms, Gsets, rho = make_device_inputs(shapes, args.grad_sets, 1234, torch,
+                                            torch.float32 if args.state == "f32" else torch.bfloat16)
+    ns_peak = PEAK_BF16_TFLOPS if args.ns_dtype == "bf16" else PEAK_F32_TFLOPS
     ws_limit = args.ws_limit_mib << 20
     q = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision, workspace_limit=ws_limit,
-                      lanes=args.lanes)
+                      ns_dtype=args.ns_dtype, lanes=args.lanes)
     qb = mm.plan_query(shapes, K=K, tile_T=args.tile, ns_precision=args.ns_precision, workspace_limit=ws_limit,
-                       lanes=args.profile_lanes)
+                       ns_dtype=args.ns_dtype, lanes=args.profile_lanes)
     if args.copy_calib_mib:
         # a plain copy kernel of known size: reads and writes copy_calib_mib MiB each
         n = args.copy_calib_mib * (1 << 20) // 4
@@ -250,17 +262,31 @@ def main():
                           workspace_limit=ws_limit)
             return
         mm.muonh_step(Ws, Gsets[i % len(Gsets)], Ms, eta=0.02, beta=0.95, K=K, rho=rho, tile_T=args.tile,
+                      ns_dtype=args.ns_dtype,
                       lanes=lanes,
                       ns_precision=args.ns_precision, workspace_limit=ws_limit, hook=args.hook)
 
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, len(Gsets) if args.graph else 0)):
         step(i)
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # one graph per gradient set, each the whole step on the same buffers
+        graphs = []
+        for k in range(len(Gsets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def run(i):
+            graphs[i % len(graphs)].replay()
 
     # pass A: headline, no events
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -292,12 +318,12 @@ def main():
     # write M and O): it is bound by whichever floor is higher, matrix-core
     # time or HBM time (HBM for T = 64 on bf16 state, about even at T = 128).
     tile_hbm = (dom == "ns_tile_resident" and d["bytes"] > 0 and
-                d["bytes"] / (PEAK_HBM_GBS * 1e9) > d["flops"] / (PEAK_BF16_TFLOPS * 1e12))
+                d["bytes"] / (PEAK_HBM_GBS * 1e9) > d["flops"] / (ns_peak * 1e12))
     if dom in NS_CLASSES and not tile_hbm:
         per_launch = d["flops"] / d["launches"]
         achieved = per_launch / (d["avg_ms"] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": ns_peak,
+                "unit": "TFLOP/s", "frac": round(achieved / ns_peak, 4),
                 "traffic": measured_traffic(dom, args),
                 "flops_per_launch": per_launch, "avg_launch_ms": d["avg_ms"], "timing_lanes": qb["lanes"]}
     else:
@@ -325,7 +351,7 @@ def main():
     else:
         opt_desc = (f"MuonH step, K={K} quintic NS "
                     f"{'tiled T=' + str(args.tile) if args.tile else 'full-matrix'}, "
-                    f"bf16 grads/momentum, fp32 master weights, " + HOOK_DESC[args.hook])
+                    f"{args.state} grads/momentum, {args.ns_dtype} NS operands, fp32 master weights, " + HOOK_DESC[args.hook])
     out = {
         "metric": METRIC if args.optimizer == "muonh" else "AdamH optimizer steps/sec, HBM GB/s",
         "value": round(1000.0 / ms_per_step, 3),
@@ -337,16 +363,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.optimizer == "muonh" else "f32",
+        "dtype": args.ns_dtype if args.optimizer == "muonh" else "f32",
         "data": "synthetic (seeded device RNG: W0 ~ N(0, 0.02^2); grads N(0, 1e-3^2) + rank-4 10x spike)",
         "config": {"workload": f"{wdesc}; {opt_desc}", "optimizer": args.optimizer,
                    "matrices": len(shapes), "K": K, "tile_T": args.tile, "ns_precision": args.ns_precision,
                    "hook": args.hook,
                    "elements": sum(h * w for h, w in shapes),
                    "chunks": q["chunks"] if args.optimizer == "muonh" else 1,
-                   "lanes": q["lanes"] if args.optimizer == "muonh" else 1},
+                   "lanes": q["lanes"] if args.optimizer == "muonh" else 1,
+                   "graph": bool(args.graph)},
         "ns_tflops": round(ns_tflops, 2) if ns_tflops else None,
-        "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
+        f"ns_frac_{args.ns_dtype}_peak": round(ns_tflops / ns_peak, 4) if ns_tflops else None,
         "ns_ms_per_step": round(ns_ms, 4),
         "stream_gbps": round(stream_gbs, 1) if stream_gbs else None,
         "stream_frac_hbm": round(stream_gbs / PEAK_HBM_GBS, 4) if stream_gbs else None,
