@@ -44,6 +44,13 @@
  *     opts->stream (opts->lanes = 1 keeps all work there).
  *     No entry point synchronizes the host except muonh_get_flags and
  *     muonh_profile_read.  GPU-side faults surface at the caller's next sync.
+ *   - Stream capture (HIP graphs): once a call with the same buffers, shapes
+ *     and options has run eagerly, a repeat of it queues only kernels and
+ *     event records / waits (no allocation, copy or memset) and can be
+ *     captured, side streams included.  The graph holds addresses of the
+ *     library's workspace and of that call's cached descriptor tables: it
+ *     stays valid until the workspace grows, muonh_release runs, or eight
+ *     other call signatures have pushed the call out of the plan cache.
  *   - Zero norms are not errors: they follow the rules above and bump the
  *     device flag counters (muonh_get_flags).
  *   - Thread-compatible: calls from several host threads must not overlap.
