@@ -34,23 +34,42 @@
  *     row-major buffers on the current HIP device.  The library never frees
  *     or retains them beyond the call.  Arrays of pointers, shapes, rho and
  *     coefficient tables are HOST memory, read during the call only.
- *   - Every argument is validated before any GPU work is queued; a call that
- *     returns an error has changed nothing.
+ *   - Every argument is validated before any GPU work is queued: a call that
+ *     returns MUONH_EINVAL, MUONH_ENOTIMPL or a planning MUONH_ENOMEM (the
+ *     workspace of one matrix exceeds the limit) has changed nothing.  A
+ *     failed allocation (MUONH_ENOMEM) also leaves the library's buffers as
+ *     they were.  MUONH_EHIP means a HIP call failed; if it failed after
+ *     some of the step's kernels were queued, those kernels still run, so
+ *     params and moms may hold a partly applied step.
  *   - Work is queued asynchronously on opts->stream (NULL: the null stream).
  *     A call over two or more matrices that fit one workspace chunk runs
  *     some of them on library-owned side streams (opts->lanes), which start
  *     after earlier work on opts->stream and which opts->stream waits for
  *     before its next work: ordering is as if everything ran on
  *     opts->stream (opts->lanes = 1 keeps all work there).
- *     No entry point synchronizes the host except muonh_get_flags and
- *     muonh_profile_read.  GPU-side faults surface at the caller's next sync.
+ *   - Host synchronization: muonh_get_flags, muonh_reset_flags,
+ *     muonh_profile_read and muonh_release synchronize.  A step, projection
+ *     or orthogonalization never waits for the device, with two
+ *     exceptions: the first call that needs a larger workspace (it frees
+ *     the old one, which waits for the device), and allocation itself.  A
+ *     call whose (buffers, shapes, options) are not in the plan cache builds
+ *     its descriptor tables on the host and uploads them with the
+ *     stream-ordered allocator and an asynchronous copy from pinned staging,
+ *     both on opts->stream; the host does not wait for earlier work.  The
+ *     cache holds the 32 most recently used call signatures; an evicted
+ *     plan's tables are released in stream order.
  *   - Stream capture (HIP graphs): once a call with the same buffers, shapes
  *     and options has run eagerly, a repeat of it queues only kernels and
  *     event records / waits (no allocation, copy or memset) and can be
  *     captured, side streams included.  The graph holds addresses of the
  *     library's workspace and of that call's cached descriptor tables: it
- *     stays valid until the workspace grows, muonh_release runs, or eight
+ *     stays valid until the workspace grows, muonh_release runs, or 32
  *     other call signatures have pushed the call out of the plan cache.
+ *     The reduction buffers a graph writes are never freed before
+ *     muonh_release (a larger one replaces them without freeing them).
+ *   - Determinism: every reduction is two-stage (one fp64 partial per block,
+ *     then a fixed-order sum), so a call is bitwise reproducible for the same
+ *     inputs, options and device, whatever opts->lanes and the chunking.
  *   - Zero norms are not errors: they follow the rules above and bump the
  *     device flag counters (muonh_get_flags).
  *   - Thread-compatible: calls from several host threads must not overlap.
@@ -89,8 +108,10 @@ enum { MUONH_F32 = 0, MUONH_BF16 = 1 };
  *                    shadow feeds the matrix cores (8 more bytes of traffic
  *                    per element and iteration).
  * Both fold the 1/(||M||+eps) pre-scale into the first iteration instead of
- * rounding the pre-scaled X0 to bf16.  Ignored when ns_dtype is MUONH_F32. */
-enum { MUONH_NS_X32 = 0, MUONH_NS_FOLD = 1 };
+ * rounding the pre-scaled X0 to bf16, and when the NS input is not itself a
+ * bf16 value (fp32 state, or the Nesterov blend) both seed the first a*X0
+ * term from an fp32 copy of X0.  Ignored when ns_dtype is MUONH_F32. */
+enum { MUONH_NS_FOLD = 0, MUONH_NS_X32 = 1 };
 
 /* weight-update hook */
 enum { MUONH_HOOK_HYPERBALL = 0, MUONH_HOOK_RADIAL_BRAKE = 1, MUONH_HOOK_NONE = 2, MUONH_HOOK_RELATIVE = 3 };
@@ -145,6 +166,10 @@ typedef struct muonh_opts {
                                    the tile_T rules), overriding tile_T -- per-layer tile
                                    sizes (Hierarchical Muon page, discussion of tile choice
                                    by aspect ratio).  NULL (default): tile_T for every matrix */
+  int          param_dtype;     /* dtype of params (master weights): MUONH_F32, the only one
+                                   supported (anything else: MUONH_EINVAL) */
+  int          deterministic;   /* 1 (default) or 0.  Every reduction is two-stage and bitwise
+                                   reproducible either way; 0 selects no faster path */
 } muonh_opts;
 
 /* Fill *o with the defaults listed above. */
@@ -213,20 +238,35 @@ int adamh_step(void* const params[], const void* const grads[], void* const exp_
                float beta2, float eps, int64_t step, const float rho[], const muonh_opts* opts);
 
 /*
- * ns_orthogonalize -- out[i] = NS_K(in[i]) (tile_T > 0: tiled), no momentum,
- * no hook.  in/out are device buffers of opts->state_dtype; out[i] may alias
- * in[i].  Same shape, K and tile_T rules as muonh_step.
+ * ns_orthogonalize -- out[i] = NS_K(in[i]), no momentum, no hook: the
+ * Newton-Schulz map of the Muon explainer (Newton-Schulz section, Equation 6,
+ * and the code section's newton_schulz5: divide by ||X||_F + eps, then K
+ * times A = X X^T, B = b A + c A A, X = a X + B X on the wide side); with
+ * tile_T > 0 the same map on every zero-padded tile_T x tile_T tile
+ * (Hierarchical Muon page, core claim and abstract).
+ *   in[i]   device, opts->state_dtype, shapes[2i] x shapes[2i+1], read only
+ *   out[i]  device, same dtype and shape, written; may alias in[i]
+ * Same shape, K, tile_T and opts rules (and errors) as muonh_step; a zero
+ * input gives a zero output (the eps).
  */
 int ns_orthogonalize(const void* const in[], void* const out[], const int64_t shapes[],
                      int n, int K, int tile_T, const muonh_opts* opts);
 
 /*
- * frob_project -- the Hyperball projection on its own:
+ * frob_project -- the Hyperball projection on its own (Hyperball show notes,
+ * §2 eq. 1 / Algorithm 1 and Method: U_hat = U / ||U||_F,
+ * W <- rho * Pi(W - eta * U_hat), Pi(x) = x / ||x||_F):
  *   W[i] <- rho[i] * Pi(W[i] - eta * U[i] / ||U[i]||)
  * (eta * rho[i] * U[i] / ||U[i]|| with opts->hyperball_step = RADIUS)
- * with the same zero rules as muonh_step.  W: device fp32, in place.
- * U: NULL (plain projection W <- rho * W / ||W||) or an array of n device
- * buffers of opts->state_dtype (a NULL entry is treated as a zero update).
+ * with the same zero rules as muonh_step (zero U: projection only; a
+ * numerically zero W' restores the radius along W; W = 0 is left and
+ * counted).
+ *   W[i]    device, fp32, shapes[2i] x shapes[2i+1], updated in place
+ *   U       NULL (plain projection W <- rho * W / ||W||) or an array of n
+ *           device buffers of opts->state_dtype, same shapes, read only (a
+ *           NULL entry is a zero update)
+ *   eta     finite, >= 0;  rho  host, n floats, finite, > 0
+ * Errors as muonh_step (MUONH_EINVAL for a bad pointer, shape or scalar).
  */
 int frob_project(void* const W[], const void* const U[], const int64_t shapes[], int n,
                  float eta, const float rho[], const muonh_opts* opts);

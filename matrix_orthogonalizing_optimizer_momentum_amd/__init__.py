@@ -34,7 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuonh.so
 
 MUONH_OK, MUONH_EINVAL, MUONH_ENOMEM, MUONH_EHIP, MUONH_ENOTIMPL = 0, -1, -2, -3, -4
 MUONH_F32, MUONH_BF16 = 0, 1
-MUONH_NS_X32, MUONH_NS_FOLD = 0, 1
+MUONH_NS_FOLD, MUONH_NS_X32 = 0, 1
 MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE, MUONH_HOOK_NONE, MUONH_HOOK_RELATIVE = 0, 1, 2, 3
 MUONH_HB_STEP_UNIT, MUONH_HB_STEP_RADIUS = 0, 1
 
@@ -78,6 +78,8 @@ class Opts(ctypes.Structure):
         ("lanes", c_int),
         ("hyperball_step", c_int),
         ("tile_sizes", POINTER(c_int)),
+        ("param_dtype", c_int),
+        ("deterministic", c_int),
     ]
 
 

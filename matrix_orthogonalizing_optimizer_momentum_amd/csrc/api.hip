@@ -41,7 +41,7 @@ hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblock
 hipError_t launch_finalize(const SlotTable& st, int slot0, int nslots, hipStream_t s);
 hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs, int njobs,
                           float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
-                          const SlotTable& st, hipStream_t s);
+                          int master32, int seed32, const SlotTable& st, hipStream_t s);
 hipError_t launch_tile_ns(int state_dt, int op_dt, const TileMat* mats, const TileJob* jobs, int njobs,
                           const TileArgs& args, hipStream_t s);
 
@@ -53,6 +53,7 @@ static_assert(kMaxK == kTileMaxK, "iteration tables");
 // ------------------------------------------------------------------ state
 struct DevTables {  // one chunk's tables on the device
   char* mem = nullptr;
+  bool mem_async = false;   // mem came from the stream-ordered allocator
   NsUnit* units = nullptr;
   GemmJob* g12[kGemmCfgs] = {};
   GemmJob* g3[kGemmCfgs] = {};
@@ -94,6 +95,16 @@ struct ProfRec {
   double flops, bytes;
 };
 
+// Pinned host staging for descriptor-table uploads.  A buffer is reusable
+// once the copy out of it has completed (its event); buffers are freed only
+// by muonh_release, so a cache miss never frees host memory the device may
+// still be reading.
+struct Staging {
+  char* p = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+};
+
 struct State {
   std::mutex mu;
   int device = -1;
@@ -103,6 +114,10 @@ struct State {
   int64_t partials_cap = 0;
   double* sums = nullptr;
   int slots_cap = 0;
+  // Meta buffers replaced by larger ones: kept until muonh_release, so that a
+  // captured graph holding their addresses never writes freed memory.
+  std::vector<void*> retired;
+  std::vector<Staging> staging;
   Flags* flags = nullptr;
   std::list<CachedPlan> plans;  // most recent first
   hipStream_t side[kMaxLanes] = {};  // lanes 1.. (created on first use; [0] unused)
@@ -122,37 +137,62 @@ const char* kClassNames[] = {"momentum_prep", "ns_gram_G1", "ns_poly_G2",       
 enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_FIN, PC_TILE, PC_AM, PC_AW, PC_N };
 
 // ------------------------------------------------------------------ helpers
-void free_plan(CachedPlan& p) {
-  for (auto& c : p.chunks)
-    if (c.mem) (void)hipFree(c.mem);
+// Frees a plan's device tables.  With a stream, stream-ordered allocations
+// are released after the work already queued on it (no host wait); without
+// one the device is synchronized first.
+void free_plan(CachedPlan& p, hipStream_t s = nullptr, bool ordered = false) {
+  for (auto& c : p.chunks) {
+    if (!c.mem) continue;
+    if (c.mem_async) {
+      (void)hipFreeAsync(c.mem, ordered ? s : nullptr);
+      if (!ordered) (void)hipStreamSynchronize(nullptr);
+    } else {
+      (void)hipFree(c.mem);
+    }
+    c.mem = nullptr;
+  }
   p.chunks.clear();
 }
 
+// Drops every cached plan (workspace growth, muonh_release): waits for the
+// device first, since queued work on any stream may still read the tables.
 void clear_plans(State& st) {
+  if (st.plans.empty()) return;
+  (void)hipDeviceSynchronize();
   for (auto& p : st.plans) free_plan(p);
   st.plans.clear();
 }
 
+// Plan cache capacity (call signatures); least recently used out first.
+constexpr size_t kPlanCacheSize = 32;
+
+// Grows the reduction buffers.  A larger buffer is allocated before the old
+// one is given up, so a failed allocation leaves the library as it was; the
+// old buffer is retired, not freed (see State::retired).
 int ensure_meta(State& st, int64_t parts, int slots) {
   if (!st.flags) {
-    if (hipMalloc(&st.flags, sizeof(Flags)) != hipSuccess) return MUONH_ENOMEM;
-    if (hipMemset(st.flags, 0, sizeof(Flags)) != hipSuccess) return MUONH_EHIP;
+    Flags* f = nullptr;
+    if (hipMalloc(&f, sizeof(Flags)) != hipSuccess) return MUONH_ENOMEM;
+    if (hipMemset(f, 0, sizeof(Flags)) != hipSuccess) {
+      (void)hipFree(f);
+      return MUONH_EHIP;
+    }
+    st.flags = f;
   }
   if (parts > st.partials_cap) {
-    if (st.partials) (void)hipFree(st.partials);
-    st.partials = nullptr;
-    const int64_t cap = std::max<int64_t>(parts, 4096);
-    if (hipMalloc(&st.partials, cap * 2 * sizeof(double)) != hipSuccess) {
-      st.partials_cap = 0;
-      return MUONH_ENOMEM;
-    }
+    const int64_t cap = std::max<int64_t>(parts, std::max<int64_t>(4096, 2 * st.partials_cap));
+    double* p = nullptr;
+    if (hipMalloc(&p, cap * 2 * sizeof(double)) != hipSuccess) return MUONH_ENOMEM;
+    if (st.partials) st.retired.push_back(st.partials);
+    st.partials = p;
     st.partials_cap = cap;
   }
   if (slots > st.slots_cap) {
-    if (st.sums) (void)hipFree(st.sums);
-    st.sums = nullptr;
-    const int cap = std::max(slots, 1024);
-    if (hipMalloc(&st.sums, cap * 2 * sizeof(double)) != hipSuccess) return MUONH_ENOMEM;
+    const int cap = std::max(slots, std::max(1024, 2 * st.slots_cap));
+    double* p = nullptr;
+    if (hipMalloc(&p, (size_t)cap * 2 * sizeof(double)) != hipSuccess) return MUONH_ENOMEM;
+    if (st.sums) st.retired.push_back(st.sums);
+    st.sums = p;
     st.slots_cap = cap;
   }
   return MUONH_OK;
@@ -182,6 +222,8 @@ int resolve(const muonh_opts* in, int K, Resolved& r) {
   muonh_default_opts(&r.o);
   if (in) r.o = *in;
   const muonh_opts& o = r.o;
+  if (o.param_dtype != MUONH_F32) return MUONH_EINVAL;  // fp32 master weights only
+  if (o.deterministic != 0 && o.deterministic != 1) return MUONH_EINVAL;
   if (o.state_dtype != MUONH_BF16 && o.state_dtype != MUONH_F32) return MUONH_EINVAL;
   if (o.ns_dtype != MUONH_BF16 && o.ns_dtype != MUONH_F32) return MUONH_EINVAL;
   if (o.ns_precision != MUONH_NS_X32 && o.ns_precision != MUONH_NS_FOLD) return MUONH_EINVAL;
@@ -243,6 +285,8 @@ Cfg make_cfg(int kind, int n, int K, int tile_T, const Resolved& r, size_t limit
   c.state_dt = r.o.state_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.op_dt = r.o.ns_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.x32 = (c.op_dt == DT_BF16 && r.o.ns_precision == MUONH_NS_X32) ? 1 : 0;
+  // bf16 operands, NS input not a bf16 value: fp32 state, or the Nesterov blend
+  c.seed32 = (c.op_dt == DT_BF16 && (c.state_dt == DT_F32 || (kind == CALL_STEP && r.o.nesterov))) ? 1 : 0;
   c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB
            : r.o.hook == MUONH_HOOK_NONE        ? kModeNone
            : r.o.hook == MUONH_HOOK_RELATIVE    ? kModeRel
@@ -262,7 +306,7 @@ void put(std::vector<char>& blob, const std::vector<T>& v, size_t& off) {
   if (!v.empty()) memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
 }
 
-int upload_chunk(const ChunkTables& t, DevTables& d) {
+int upload_chunk(State& st, const ChunkTables& t, DevTables& d, hipStream_t s) {
   std::vector<char> blob;
   size_t o_units, o_g12[kGemmCfgs], o_g3[kGemmCfgs], o_mm, o_mb, o_hm, o_hb, o_tm, o_tj, o_np, o_pb;
   put(blob, t.units, o_units);
@@ -281,9 +325,36 @@ int upload_chunk(const ChunkTables& t, DevTables& d) {
   put(blob, t.nparts, o_np);
   put(blob, t.part_base, o_pb);
   if (blob.empty()) blob.resize(256);
-  if (hipMalloc(&d.mem, blob.size()) != hipSuccess) return MUONH_ENOMEM;
-  // Synchronous copy: runs once per new (buffers, shapes, options) set.
-  if (hipMemcpy(d.mem, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess) return MUONH_EHIP;
+  // Once per new (buffers, shapes, options) set: device memory from the
+  // stream-ordered allocator and a copy from pinned staging, both queued on
+  // the caller's stream, so the host does not wait for earlier work.
+  Staging* sg = nullptr;
+  for (auto& c : st.staging)
+    if (c.cap >= blob.size() && hipEventQuery(c.done) == hipSuccess) {
+      sg = &c;
+      break;
+    }
+  if (!sg) {
+    Staging n;
+    n.cap = std::max<size_t>(blob.size(), (size_t)1 << 20);
+    if (hipHostMalloc((void**)&n.p, n.cap, hipHostMallocDefault) != hipSuccess) return MUONH_ENOMEM;
+    if (hipEventCreateWithFlags(&n.done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipHostFree(n.p);
+      return MUONH_EHIP;
+    }
+    st.staging.push_back(n);
+    sg = &st.staging.back();
+  }
+  memcpy(sg->p, blob.data(), blob.size());
+  if (hipMallocAsync((void**)&d.mem, blob.size(), s) == hipSuccess) {
+    d.mem_async = true;
+  } else {
+    (void)hipGetLastError();
+    d.mem = nullptr;
+    if (hipMalloc(&d.mem, blob.size()) != hipSuccess) return MUONH_ENOMEM;
+  }
+  if (hipMemcpyAsync(d.mem, sg->p, blob.size(), hipMemcpyHostToDevice, s) != hipSuccess) return MUONH_EHIP;
+  if (hipEventRecord(sg->done, s) != hipSuccess) return MUONH_EHIP;
   d.units = reinterpret_cast<NsUnit*>(d.mem + o_units);
   for (int g = 0; g < kGemmCfgs; ++g) {
     d.g12[g] = reinterpret_cast<GemmJob*>(d.mem + o_g12[g]);
@@ -327,7 +398,7 @@ void key_push_ptrs(std::vector<uint64_t>& k, const void* const* a, int n) {
 
 // Looks up or builds the device tables for this call.
 int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, const int64_t* shapes,
-             CachedPlan*& out) {
+             hipStream_t s, CachedPlan*& out) {
   std::vector<uint64_t> key;
   key.push_back((uint64_t)cfg.kind);
   key.push_back((uint64_t)cfg.n);
@@ -338,6 +409,7 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   key.push_back((uint64_t)cfg.state_dt);
   key.push_back((uint64_t)cfg.op_dt);
   key.push_back((uint64_t)cfg.x32);
+  key.push_back((uint64_t)cfg.seed32);
   key.push_back((uint64_t)cfg.hook);
   key.push_back((uint64_t)cfg.hb_radius);
   key.push_back((uint64_t)plan.chunks.size());
@@ -371,10 +443,10 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
     ChunkTables t;
     fill_chunk(plan, (int)c, cfg, p, st.ws, t);
     DevTables d;
-    const int rc = upload_chunk(t, d);
+    const int rc = upload_chunk(st, t, d, s);
     if (rc != MUONH_OK) {
-      if (d.mem) (void)hipFree(d.mem);
-      free_plan(cp);
+      cp.chunks.push_back(d);
+      free_plan(cp, s, true);
       return rc;
     }
     if (plan.lanes > 1) {  // concurrent chunks: disjoint reduction slots
@@ -390,12 +462,15 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   }
   const int rc = ensure_meta(st, cp.max_parts, cp.max_slots);
   if (rc != MUONH_OK) {
-    free_plan(cp);
+    free_plan(cp, s, true);
     return rc;
   }
   st.plans.push_front(std::move(cp));
-  while (st.plans.size() > 8) {  // bounded cache; hipFree waits for in-flight users
-    free_plan(st.plans.back());
+  while (st.plans.size() > kPlanCacheSize) {
+    // bounded cache: the evicted tables are released after the work queued
+    // so far on this stream (which, by the calling convention, includes every
+    // earlier call's work that may read them)
+    free_plan(st.plans.back(), s, true);
     st.plans.pop_back();
   }
   out = &st.plans.front();
@@ -460,7 +535,7 @@ int run_ns_iter(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r
     for (int g = 0; g < kGemmCfgs; ++g) {
       Prof pf(st, s, PC_G3, 0, 0);
       MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], 1.f, 0.f, 0.f, eps, 1, 1, 0, 1,
-                                   sl, s));
+                                   cfg.x32, cfg.seed32, sl, s));
     }
   } else {
     const float a = r.coeffs[3 * k], b = r.coeffs[3 * k + 1], c = r.coeffs[3 * k + 2];
@@ -469,19 +544,19 @@ int run_ns_iter(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r
       if (!d.n_g12[g]) continue;
       Prof pf(st, s, PC_G1, d.flops_g1[g], 0);
       MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 0, g, d.units, d.g12[g], d.n_g12[g], a, b, c, eps, first, 0, cur, 0,
-                                   sl, s));
+                                   cfg.x32, cfg.seed32, sl, s));
     }
     for (int g = 0; g < kGemmCfgs; ++g) {
       if (!d.n_g12[g]) continue;
       Prof pf(st, s, PC_G2, d.flops_g2[g], 0);
       MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 1, g, d.units, d.g12[g], d.n_g12[g], a, b, c, eps, first, 0, cur, 0,
-                                   sl, s));
+                                   cfg.x32, cfg.seed32, sl, s));
     }
     for (int g = 0; g < kGemmCfgs; ++g) {
       if (!d.n_g3[g]) continue;
       Prof pf(st, s, PC_G3, d.flops_g3[g], 0);
       MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], a, b, c, eps, first, last, cur, 0,
-                                   sl, s));
+                                   cfg.x32, cfg.seed32, sl, s));
     }
     if (!last) return MUONH_OK;
   }
@@ -608,10 +683,10 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
   if (rc != MUONH_OK) return rc;
   rc = ensure_ws(st, std::max<int64_t>(plan.ws_bytes, 256));
   if (rc != MUONH_OK) return rc;
-  CachedPlan* cp = nullptr;
-  rc = get_plan(st, plan, cfg, p, shapes, cp);
-  if (rc != MUONH_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(r.o.stream);
+  CachedPlan* cp = nullptr;
+  rc = get_plan(st, plan, cfg, p, shapes, s, cp);
+  if (rc != MUONH_OK) return rc;
   if (cp->lanes > 1) {
     // Lane 0 runs on the caller's stream, lane l on the library's side
     // stream l, started after lane l-1's opening pass (and so after all
@@ -695,6 +770,8 @@ void muonh_default_opts(muonh_opts* o) {
   o->lanes = 0;
   o->hyperball_step = MUONH_HB_STEP_UNIT;
   o->tile_sizes = nullptr;
+  o->param_dtype = MUONH_F32;
+  o->deterministic = 1;
 }
 
 int muonh_step(void* const params[], const void* const grads[], void* const moms[], const int64_t shapes[],
@@ -839,6 +916,13 @@ void muonh_release(void) {
   if (st.partials) (void)hipFree(st.partials);
   if (st.sums) (void)hipFree(st.sums);
   if (st.flags) (void)hipFree(st.flags);
+  for (void* q : st.retired) (void)hipFree(q);
+  st.retired.clear();
+  for (auto& g : st.staging) {
+    (void)hipEventDestroy(g.done);
+    (void)hipHostFree(g.p);
+  }
+  st.staging.clear();
   for (int l = 0; l < kMaxLanes; ++l) {
     if (st.side[l]) (void)hipStreamDestroy(st.side[l]);
     if (st.ev_gate[l]) (void)hipEventDestroy(st.ev_gate[l]);

@@ -42,7 +42,8 @@ struct NsUnit {
   int64_t o_ld;
   void* o_ptr;          // output base, already offset to the unit's origin
   void* xt[2];          // op-dtype X^T ping-pong (XT layout)
-  float* x32;           // fp32 master X^T (XT layout) or nullptr
+  float* x32;           // fp32 X^T (XT layout) or nullptr: the master copy (X32 mode)
+                        // and/or the fp32 X0 that seeds the first a X term
   void* a;              // op-dtype A = X X^T (r rows, ld_r)
   void* b;              // op-dtype B = b A + c A A (r rows, ld_r)
 };
@@ -65,6 +66,7 @@ struct MomMat {
   int32_t ntc;          // tiles per row (tile mode)
   int32_t nbc;          // 64-wide column blocks over the padded extent
   int32_t write_x;      // 1: write X0^T into the units' workspace
+  int32_t write_x32;    // 1: also write the fp32 X0^T into the units' x32 buffers
 };
 
 // One 64 x 64 block of a momentum / prep launch.

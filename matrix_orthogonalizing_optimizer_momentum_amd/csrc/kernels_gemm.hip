@@ -78,6 +78,8 @@ struct NsIterArgs {
   int last;           // final iteration: write O and its norm
   int cur;            // X^T ping-pong index read this iteration (G3 writes the other)
   int no_mma;         // K == 0: O = X0 / (||X0|| + eps) through the G3 epilogue
+  int master32;       // X32 mode: G3 keeps the fp32 master X^T in NsUnit::x32
+  int seed32;         // the first G3 seeds a X0 from NsUnit::x32 (fp32 X0^T)
   int njobs;
   SlotTable st;
 };
@@ -278,11 +280,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     zero_acc();
   } else if (PP) {
     zero_acc();
-    const bool m32 = PHASE == kG3 && !args.first && u.x32 != nullptr;
+    const bool m32 = PHASE == kG3 && u.x32 != nullptr && (args.first ? args.seed32 : args.master32);
     pp_late = nstage > 0 && !m32;
     pp_after = !pp_late;
   } else {
-    const bool m32 = PHASE == kG3 && !args.first && u.x32 != nullptr;  // fp32 master
+    // fp32 seed: the master X^T (X32 mode), or the fp32 X0^T on the first iteration
+    const bool m32 = PHASE == kG3 && u.x32 != nullptr && (args.first ? args.seed32 : args.master32);
     const T* src = seed_src;
     const float coef = seed_coef;
     late = kLateSeed && !m32;
@@ -924,7 +927,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     if (pp_after) {
       // fp32 master seeds (or no stages): from HBM, one accumulator row
       // block at a time
-      const bool m32 = PHASE == kG3 && !args.first && u.x32 != nullptr;
+      const bool m32 = PHASE == kG3 && u.x32 != nullptr && (args.first ? args.seed32 : args.master32);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -1021,7 +1024,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
             }
             if (ok) store8(reinterpret_cast<float*>(xo), o, vs);
           }
-          if (u.x32 != nullptr) {
+          if (args.master32 && u.x32 != nullptr) {
             float vs[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1169,9 +1172,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 // large units).
 hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs, int njobs,
                           float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
-                          const SlotTable& st, hipStream_t s) {
+                          int master32, int seed32, const SlotTable& st, hipStream_t s) {
   if (njobs <= 0) return hipSuccess;
-  NsIterArgs args{a, b, c, eps, first, last, cur, no_mma, njobs, st};
+  NsIterArgs args{a, b, c, eps, first, last, cur, no_mma, master32, seed32, njobs, st};
   dim3 grid(njobs);
 #define MUONH_LAUNCH(T, PH, B, K, GM, GN) \
   hipLaunchKernelGGL((k_ns_gemm<T, PH, B, B, K, GM, GN>), grid, dim3(64 * GM * GN), 0, s, units, jobs, args)

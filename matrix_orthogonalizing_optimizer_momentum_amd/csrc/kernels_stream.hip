@@ -120,6 +120,10 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
     // extent and its values outside the matrix are zero, so the padding is
     // written too.
     OT* const xt = reinterpret_cast<OT*>(u.xt[0]);
+    // fp32 X0^T beside it when the NS input is not a bf16 value (fp32 state or
+    // the Nesterov blend) and the operands are bf16: the first iteration's
+    // a X term is then seeded from it instead of the rounded operand copy
+    float* const x32 = mm.write_x32 ? u.x32 : nullptr;
     const int64_t ld = u.ld_r;
     if (mm.trans) {
       // X = M^T: X^T has M's layout; same element positions as loaded.
@@ -133,6 +137,7 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
 #pragma unroll
           for (int k = 0; k < 8; ++k) v[k] = tile[lr][cc * 8 + k];
           store8(xt, row * ld + col, v);
+          if (x32 != nullptr) store8(x32, row * ld + col, v);
         }
       }
     } else {
@@ -150,6 +155,7 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = tile[seg + 8 * h + k][lc];
             store8(xt, frow * ld + fcol + 8 * h, v);
+            if (x32 != nullptr) store8(x32, frow * ld + fcol + 8 * h, v);
           }
         }
       }

@@ -190,17 +190,17 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
   __syncthreads();
   if (tid == 0) ssig = (float)(1.0 / (sqrt(((sred[0] + sred[1]) + sred[2]) + sred[3]) + (double)args.eps));
   // Every thread takes its elements in the accumulator layout, which it owns
-  // from here to the final store.
+  // from here to the final store.  X0 is kept as formed (fp32): when it is
+  // not a bf16 value (fp32 state, or the Nesterov blend) the first a X term
+  // uses it unrounded; the operand copies below are rounded, and with fold
+  // every later X is rounded to bf16 after its update.
   float x32[MI][MI][16];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < MI; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float x = stg[(wr + i * 32 + acc_row(v, lane)) * SP + wc + j * 32 + lc];
-        x32[i][j][v] = args.fold ? bf2f(f2bf(x)) : x;  // fold: X itself is kept in bf16
-      }
+      for (int v = 0; v < 16; ++v) x32[i][j][v] = stg[(wr + i * 32 + acc_row(v, lane)) * SP + wc + j * 32 + lc];
   __syncthreads();  // staging is overwritten by the operand copies below
   // X0 into LDS (unscaled): sX row-major, and sT = X^T for bf16 operands.
   auto store_x = [&]() {

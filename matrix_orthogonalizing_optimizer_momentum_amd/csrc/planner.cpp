@@ -122,7 +122,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
       if (resident_tile(T)) {
         plan.jobs_per_iter += m.nunits;  // one workgroup per tile runs every iteration
       } else {
-        const UnitBytes ub = unit_bytes(T, T, cfg.op_dt, cfg.x32);
+        const UnitBytes ub = unit_bytes(T, T, cfg.op_dt, cfg.x32 || cfg.seed32);
         m.ws_bytes += (int64_t)m.nunits * ub.total();
         plan.jobs_per_iter += (int64_t)m.nunits * jobs_per_iter(T, T, cfg.op_dt);
       }
@@ -134,7 +134,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
       m.ntr = m.ntc = 1;
       // GEMM operand loads address a unit's X^T with 32-bit byte offsets.
       if ((pad_up(m.s, 256) * pad_up(m.r, kPad) + 256) * esize(cfg.op_dt) >= ((int64_t)1 << 32)) return MUONH_ENOTIMPL;
-      const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32);
+      const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32 || cfg.seed32);
       m.ws_bytes += ub.total();
       plan.ns_flops += ns_flops_true(m.H, m.W, cfg.K);
       plan.jobs_per_iter += jobs_per_iter(m.r, m.s, cfg.op_dt);
@@ -232,7 +232,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
       continue;
     }
-    const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32);
+    const UnitBytes ub = unit_bytes(m.r, m.s, cfg.op_dt, cfg.x32 || cfg.seed32);
     for (int k = 0; k < m.nunits; ++k) {
       NsUnit u{};
       u.r = m.r;
@@ -387,6 +387,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       mm.unit0 = unit0[mi];
       mm.ntc = m.ntc;
       mm.write_x = 1;
+      mm.write_x32 = cfg.seed32;
       int64_t rows_p, cols_p;
       if (T > 0) {
         rows_p = (int64_t)m.ntr * T;

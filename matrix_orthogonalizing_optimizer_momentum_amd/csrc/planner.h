@@ -24,6 +24,9 @@ struct Cfg {
   int tile_T;
   int state_dt, op_dt;
   int x32;        // fp32 master X (bf16 operands only)
+  int seed32;     // bf16 operands with an NS input that is not a bf16 value (fp32
+                  // state, or the Nesterov blend): the first a X term is seeded
+                  // from an fp32 copy of X0
   int hook;       // kModeHB / kModeRB / kModeNone / kModeRel
   int hb_radius;  // Hyperball: radius-sized step (eta * rho * U_hat)
   size_t ws_limit;
@@ -70,7 +73,7 @@ struct UnitBytes {
   int64_t xt, x32, a, b;
   int64_t total() const { return 2 * xt + x32 + a + b; }
 };
-UnitBytes unit_bytes(int r, int s, int op_dt, int x32);
+UnitBytes unit_bytes(int r, int s, int op_dt, int x32);  // x32: an fp32 X^T buffer (master or X0 seed)
 
 inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 inline int esize(int dt) { return dt == DT_F32 ? 4 : 2; }

@@ -77,7 +77,8 @@ def test_step_rejects_bad_options():
     for field, val in [("state_dtype", 7), ("ns_dtype", 3), ("ns_precision", 9), ("hook", 5),
                        ("outward", 1.5), ("inward", -0.1), ("ns_eps", float("nan")), ("momentum_ema", 2),
                        ("nesterov", -1), ("weight_decay", -0.5), ("weight_decay", float("inf")),
-                       ("lanes", -1), ("lanes", 5), ("hook", 4), ("hyperball_step", 2)]:
+                       ("lanes", -1), ("lanes", 5), ("hook", 4), ("hyperball_step", 2),
+                       ("param_dtype", 1), ("param_dtype", 7), ("deterministic", 2), ("deterministic", -1)]:
         o = _opts()
         setattr(o, field, val)
         assert _step(opts=o) == mm.MUONH_EINVAL, field
@@ -91,6 +92,16 @@ def test_default_options():
     assert o.hyperball_step == mm.MUONH_HB_STEP_UNIT
     assert abs(o.ns_eps - 1e-7) < 1e-12 and abs(o.zero_rel_eps - 1e-6) < 1e-11
     assert (o.outward, o.inward) == (0.5, 1.0)
+    assert (o.param_dtype, o.deterministic) == (mm.MUONH_F32, 1)
+
+
+def test_enums_follow_the_boundary_contract():
+    # MUONH_NS_FOLD = 0 (bf16 X, folded pre-scale), MUONH_NS_X32 = 1, as the
+    # header declares them
+    import re
+    hdr = open(HEADER).read()
+    m = re.search(r"enum\s*\{\s*MUONH_NS_FOLD\s*=\s*(\d+),\s*MUONH_NS_X32\s*=\s*(\d+)\s*\}", hdr)
+    assert m and (int(m.group(1)), int(m.group(2))) == (mm.MUONH_NS_FOLD, mm.MUONH_NS_X32) == (0, 1)
 
 
 def test_lanes_share_one_chunk_workspace():

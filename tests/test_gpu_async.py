@@ -1,0 +1,51 @@
+"""A call whose plan is not cached queues its table upload on the caller's
+stream and returns without waiting for the device (the header's
+host-synchronization contract)."""
+import time
+
+import numpy as np
+import pytest
+
+from oracle import muonh_oracle as orc
+from synth import gen
+
+torch = pytest.importorskip("torch")
+import matrix_orthogonalizing_optimizer_momentum_amd as mm  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def test_cache_miss_returns_before_queued_work_finishes():
+    print("[case] cache-miss call behind a busy stream", flush=True)
+    s = torch.cuda.current_stream()
+    a = torch.randn(8192, 8192, device="cuda")
+    torch.cuda.synchronize()
+    # a few hundred ms of matrix work queued ahead of the call
+    t0 = time.perf_counter()
+    for _ in range(3):
+        a = a @ a
+        a = a / a.norm()
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t0) / 3
+    reps = max(3, int(0.4 / max(per, 1e-4)))
+    x = gen.store(gen.spiked_grad(333, 517, 1e-3, 91), "bf16")
+    xt = torch.from_numpy(x).to("cuda").to(torch.bfloat16)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        a = a @ a
+        a = a / a.norm()
+    t1 = time.perf_counter()
+    # shape 333 x 517 and these buffers were never seen: the plan is built,
+    # its tables go up by an asynchronous copy on this stream
+    out = mm.ns_orthogonalize([xt], K=5, ns_dtype="bf16")[0]
+    t2 = time.perf_counter()
+    busy = not s.query()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    print(f"  queued work {reps * per * 1e3:.0f} ms; call returned after {(t2 - t1) * 1e3:.1f} ms, "
+          f"stream idle after {(t3 - t1) * 1e3:.0f} ms", flush=True)
+    assert busy, "the stream drained before the call returned"
+    assert (t2 - t1) < 0.5 * (t3 - t1)
+    ref = orc.newton_schulz(x, 5)
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 2e-2
