@@ -18,16 +18,24 @@ pytestmark = pytest.mark.gpu
 def test_cache_miss_returns_before_queued_work_finishes():
     print("[case] cache-miss call behind a busy stream", flush=True)
     s = torch.cuda.current_stream()
+    # one-time costs out of the way: the library's first call (code object
+    # load, symbol lookup) on another, larger signature -- so the workspace
+    # already fits the call below (growing it frees the old one, which is the
+    # header's one synchronizing exception) -- and the matmul library
+    w = torch.from_numpy(gen.store(gen.spiked_grad(1024, 1536, 1e-3, 90), "bf16")).to("cuda").to(torch.bfloat16)
+    mm.ns_orthogonalize([w], K=5, ns_dtype="bf16")
     a = torch.randn(8192, 8192, device="cuda")
-    torch.cuda.synchronize()
-    # a few hundred ms of matrix work queued ahead of the call
-    t0 = time.perf_counter()
     for _ in range(3):
         a = a @ a
         a = a / a.norm()
     torch.cuda.synchronize()
-    per = (time.perf_counter() - t0) / 3
-    reps = max(3, int(0.4 / max(per, 1e-4)))
+    t0 = time.perf_counter()
+    for _ in range(5):
+        a = a @ a
+        a = a / a.norm()
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t0) / 5
+    reps = max(5, int(1.0 / max(per, 1e-4)))  # about a second of queued work
     x = gen.store(gen.spiked_grad(333, 517, 1e-3, 91), "bf16")
     xt = torch.from_numpy(x).to("cuda").to(torch.bfloat16)
     torch.cuda.synchronize()
@@ -42,10 +50,10 @@ def test_cache_miss_returns_before_queued_work_finishes():
     busy = not s.query()
     torch.cuda.synchronize()
     t3 = time.perf_counter()
-    print(f"  queued work {reps * per * 1e3:.0f} ms; call returned after {(t2 - t1) * 1e3:.1f} ms, "
+    print(f"  queued work ~{reps * per * 1e3:.0f} ms; call returned after {(t2 - t1) * 1e3:.1f} ms, "
           f"stream idle after {(t3 - t1) * 1e3:.0f} ms", flush=True)
     assert busy, "the stream drained before the call returned"
-    assert (t2 - t1) < 0.5 * (t3 - t1)
+    assert (t2 - t1) < 0.25 * (t3 - t1)
     ref = orc.newton_schulz(x, 5)
     got = out.float().cpu().numpy().astype(np.float64)
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 2e-2
