@@ -205,6 +205,33 @@ int muonh_step(void* const params[], const void* const grads[], void* const moms
                const float rho[], int tile_T, const muonh_opts* opts);
 
 /*
+ * muonh_step_noalloc -- muonh_step for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, options and results as muonh_step (the
+ * same kernels; bitwise the same output), but the call allocates nothing:
+ * its workspace, descriptor tables and reduction partials live in a static
+ * device array of MUONH_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the
+ * library runs on holds until the process ends.
+ *   - Limit: the call's workspace may use 3/4 of the scratch (48 MiB), the
+ *     rest holds its tables and partials.  A call that needs more returns
+ *     MUONH_ENOMEM before queuing any work, and muonh_last_error() names the
+ *     sizes.  (Resident tiles, tile_T <= 128, need only the bf16 O buffer of
+ *     each matrix: 2 bytes per element; full-matrix Newton-Schulz needs the
+ *     X ping-pong, A, B and O buffers, about 13 MB for a 768 x 2304 matrix.)
+ *   - Every call on a GPU uses that GPU's one scratch and keeps the last
+ *     call's contents: calls queued on one stream are ordered, but calls that
+ *     overlap on one GPU (other streams, other threads, no ordering between
+ *     them) race and corrupt each other's results.
+ *   - All work is queued on opts->stream (opts->lanes is ignored: one lane).
+ *     Nothing is cached: each call plans on the host and uploads its tables
+ *     with one stream-ordered copy from host memory.
+ */
+#define MUONH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int muonh_step_noalloc(void* const params[], const void* const grads[], void* const moms[],
+                       const int64_t shapes[], int n, float eta, float beta, int K, const float rho[],
+                       int tile_T, const muonh_opts* opts);
+
+/*
  * adamh_step -- AdamH: the Hyperball wrapper around Adam's update (Hyperball
  * show notes, Method: any base step, Adam's preconditioned update first
  * among them; Key claims and Results report AdamH).  Adam itself (Muon
@@ -326,7 +353,8 @@ int muonh_profile_read(muonh_kernel_stat* out, int max, int* n_out);
 const char* muonh_version(void);
 
 /* Text of the last HIP failure behind a MUONH_EHIP return on this host
- * thread: the failing call and HIP's error string ("" if none). */
+ * thread (the failing call and HIP's error string), or of the sizes behind a
+ * muonh_step_noalloc MUONH_ENOMEM ("" if none). */
 const char* muonh_last_error(void);
 
 #ifdef __cplusplus

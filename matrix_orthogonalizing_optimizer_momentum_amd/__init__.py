@@ -8,7 +8,8 @@ point raises ``MuonhUnavailable``.
 
 Entry points mirror the C ABI in ``include/muonh.h``:
 
-* ``muonh_step(params, grads, moms, eta, beta, K, rho, tile_T=0, **opts)``
+* ``muonh_step(params, grads, moms, eta, beta, K, rho, tile_T=0, noalloc=False, **opts)``
+  (``noalloc=True``: ``muonh_step_noalloc``)
 * ``adamh_step(params, grads, exp_avg, exp_avg_sq, eta, step, beta1, beta2, eps, rho, **opts)``
 * ``ns_orthogonalize(inputs, outputs=None, K=5, tile_T=0, **opts)``
 * ``frob_project(W, U, eta, rho, **opts)``
@@ -39,7 +40,7 @@ MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE, MUONH_HOOK_NONE, MUONH_HOOK_RELAT
 MUONH_HB_STEP_UNIT, MUONH_HB_STEP_RADIUS = 0, 1
 
 EXPORTED = (
-    "muonh_default_opts", "muonh_step", "adamh_step", "ns_orthogonalize", "frob_project", "muonh_get_flags",
+    "muonh_default_opts", "muonh_step", "muonh_step_noalloc", "adamh_step", "ns_orthogonalize", "frob_project", "muonh_get_flags",
     "muonh_reset_flags", "muonh_strerror", "muonh_release", "muonh_plan_query",
     "muonh_profile_begin", "muonh_profile_read", "muonh_version", "muonh_last_error",
 )
@@ -121,6 +122,8 @@ def load(path: str = LIB_PATH):
     lib.muonh_step.argtypes = [pp, pp, pp, POINTER(c_int64), c_int, c_float, c_float, c_int,
                                POINTER(c_float), c_int, POINTER(Opts)]
     lib.muonh_step.restype = c_int
+    lib.muonh_step_noalloc.argtypes = lib.muonh_step.argtypes
+    lib.muonh_step_noalloc.restype = c_int
     lib.adamh_step.argtypes = [pp, pp, pp, pp, POINTER(c_int64), c_int, c_float, c_float, c_float, c_float,
                                c_int64, POINTER(c_float), POINTER(Opts)]
     lib.adamh_step.restype = c_int
@@ -268,8 +271,10 @@ def _check_dev(ts, what):
 # entry points
 # --------------------------------------------------------------------------
 
-def muonh_step(params, grads, moms, eta, beta, K, rho=None, tile_T=0, **opts):
-    """One MuonH step in place on ``params`` (fp32) and ``moms``."""
+def muonh_step(params, grads, moms, eta, beta, K, rho=None, tile_T=0, noalloc=False, **opts):
+    """One MuonH step in place on ``params`` (fp32) and ``moms``.  With
+    ``noalloc`` the call goes to ``muonh_step_noalloc`` (no device allocation:
+    the library's static scratch; see the header for its limit)."""
     import torch
     lib = load()
     n = len(params)
@@ -289,9 +294,10 @@ def muonh_step(params, grads, moms, eta, beta, K, rho=None, tile_T=0, **opts):
     _check_tile_sizes(opts, n)
     o, keep = make_opts(state_dtype=sd, K=K, **opts)
     rho_arr = (c_float * n)(*[float(r) for r in rho]) if rho is not None else None
-    rc = lib.muonh_step(_ptrs(params), _ptrs(grads), _ptrs(moms), _shapes(params), n, float(eta), float(beta),
-                        int(K), rho_arr, int(tile_T), ctypes.byref(o))
-    _check(rc, "muonh_step")
+    fn = lib.muonh_step_noalloc if noalloc else lib.muonh_step
+    rc = fn(_ptrs(params), _ptrs(grads), _ptrs(moms), _shapes(params), n, float(eta), float(beta),
+            int(K), rho_arr, int(tile_T), ctypes.byref(o))
+    _check(rc, "muonh_step_noalloc" if noalloc else "muonh_step")
 
 
 def adamh_step(params, grads, exp_avg, exp_avg_sq, eta, step, beta1=0.9, beta2=0.95, eps=1e-8, rho=None,

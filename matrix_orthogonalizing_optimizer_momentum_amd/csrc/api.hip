@@ -20,6 +20,15 @@
 #include "desc.h"
 #include "planner.h"
 
+// Device memory the library holds without allocating it: the flag counters of
+// every entry point, and the scratch of muonh_step_noalloc (its workspace,
+// descriptor tables and reduction partials), one copy per GPU for the life of
+// the process.  Host code never passes these names to a kernel: it takes each
+// GPU's addresses from hipGetSymbolAddress (device_symbols below).
+constexpr size_t kNoAllocScratchBytes = MUONH_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+static __device__ __align__(256) muonh::Flags g_flags;
+
 namespace muonh {
 
 // launchers (kernels_*.hip)
@@ -118,7 +127,7 @@ struct State {
   // captured graph holding their addresses never writes freed memory.
   std::vector<void*> retired;
   std::vector<Staging> staging;
-  Flags* flags = nullptr;
+  std::vector<char> noalloc_blob;  // host copy of muonh_step_noalloc's last tables
   std::list<CachedPlan> plans;  // most recent first
   hipStream_t side[kMaxLanes] = {};  // lanes 1.. (created on first use; [0] unused)
   hipEvent_t ev_gate[kMaxLanes] = {}, ev_join[kMaxLanes] = {};
@@ -170,15 +179,6 @@ constexpr size_t kPlanCacheSize = 32;
 // one is given up, so a failed allocation leaves the library as it was; the
 // old buffer is retired, not freed (see State::retired).
 int ensure_meta(State& st, int64_t parts, int slots) {
-  if (!st.flags) {
-    Flags* f = nullptr;
-    if (hipMalloc(&f, sizeof(Flags)) != hipSuccess) return MUONH_ENOMEM;
-    if (hipMemset(f, 0, sizeof(Flags)) != hipSuccess) {
-      (void)hipFree(f);
-      return MUONH_EHIP;
-    }
-    st.flags = f;
-  }
   if (parts > st.partials_cap) {
     const int64_t cap = std::max<int64_t>(parts, std::max<int64_t>(4096, 2 * st.partials_cap));
     double* p = nullptr;
@@ -306,55 +306,39 @@ void put(std::vector<char>& blob, const std::vector<T>& v, size_t& off) {
   if (!v.empty()) memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
 }
 
-int upload_chunk(State& st, const ChunkTables& t, DevTables& d, hipStream_t s) {
-  std::vector<char> blob;
-  size_t o_units, o_g12[kGemmCfgs], o_g3[kGemmCfgs], o_mm, o_mb, o_hm, o_hb, o_tm, o_tj, o_np, o_pb;
-  put(blob, t.units, o_units);
+// Byte offsets of one chunk's tables inside its serialized blob.
+struct BlobOffsets {
+  size_t units, g12[kGemmCfgs], g3[kGemmCfgs], mm, mb, hm, hb, hb1, tm, tj, np, pb;
+};
+
+// Appends chunk t's tables to blob (each array 256-byte aligned) and records
+// where each one starts.
+void serialize_chunk(const ChunkTables& t, std::vector<char>& blob, BlobOffsets& o) {
+  put(blob, t.units, o.units);
   for (int g = 0; g < kGemmCfgs; ++g) {
-    put(blob, t.g12_jobs[g], o_g12[g]);
-    put(blob, t.g3_jobs[g], o_g3[g]);
+    put(blob, t.g12_jobs[g], o.g12[g]);
+    put(blob, t.g3_jobs[g], o.g3[g]);
   }
-  put(blob, t.mom_mats, o_mm);
-  put(blob, t.mom_blocks, o_mb);
-  put(blob, t.hook_mats, o_hm);
-  put(blob, t.hook_blocks, o_hb);
-  size_t o_hb1;
-  put(blob, t.hook1_blocks, o_hb1);
-  put(blob, t.tile_mats, o_tm);
-  put(blob, t.tile_jobs, o_tj);
-  put(blob, t.nparts, o_np);
-  put(blob, t.part_base, o_pb);
-  if (blob.empty()) blob.resize(256);
-  // Once per new (buffers, shapes, options) set: device memory from the
-  // stream-ordered allocator and a copy from pinned staging, both queued on
-  // the caller's stream, so the host does not wait for earlier work.
-  Staging* sg = nullptr;
-  for (auto& c : st.staging)
-    if (c.cap >= blob.size() && hipEventQuery(c.done) == hipSuccess) {
-      sg = &c;
-      break;
-    }
-  if (!sg) {
-    Staging n;
-    n.cap = std::max<size_t>(blob.size(), (size_t)1 << 20);
-    if (hipHostMalloc((void**)&n.p, n.cap, hipHostMallocDefault) != hipSuccess) return MUONH_ENOMEM;
-    if (hipEventCreateWithFlags(&n.done, hipEventDisableTiming) != hipSuccess) {
-      (void)hipHostFree(n.p);
-      return MUONH_EHIP;
-    }
-    st.staging.push_back(n);
-    sg = &st.staging.back();
-  }
-  memcpy(sg->p, blob.data(), blob.size());
-  if (hipMallocAsync((void**)&d.mem, blob.size(), s) == hipSuccess) {
-    d.mem_async = true;
-  } else {
-    (void)hipGetLastError();
-    d.mem = nullptr;
-    if (hipMalloc(&d.mem, blob.size()) != hipSuccess) return MUONH_ENOMEM;
-  }
-  if (hipMemcpyAsync(d.mem, sg->p, blob.size(), hipMemcpyHostToDevice, s) != hipSuccess) return MUONH_EHIP;
-  if (hipEventRecord(sg->done, s) != hipSuccess) return MUONH_EHIP;
+  put(blob, t.mom_mats, o.mm);
+  put(blob, t.mom_blocks, o.mb);
+  put(blob, t.hook_mats, o.hm);
+  put(blob, t.hook_blocks, o.hb);
+  put(blob, t.hook1_blocks, o.hb1);
+  put(blob, t.tile_mats, o.tm);
+  put(blob, t.tile_jobs, o.tj);
+  put(blob, t.nparts, o.np);
+  put(blob, t.part_base, o.pb);
+  blob.resize((blob.size() + 255) / 256 * 256 + 256);
+}
+
+// Points d at the device copy of a blob (base = device address of the
+// blob's first byte) and copies the host-side launch parameters.
+void bind_chunk(const ChunkTables& t, const BlobOffsets& o, char* base, DevTables& d) {
+  d.mem = base;
+  const size_t o_units = o.units, o_mm = o.mm, o_mb = o.mb, o_hm = o.hm, o_hb = o.hb, o_hb1 = o.hb1, o_tm = o.tm,
+               o_tj = o.tj, o_np = o.np, o_pb = o.pb;
+  const size_t* o_g12 = o.g12;
+  const size_t* o_g3 = o.g3;
   d.units = reinterpret_cast<NsUnit*>(d.mem + o_units);
   for (int g = 0; g < kGemmCfgs; ++g) {
     d.g12[g] = reinterpret_cast<GemmJob*>(d.mem + o_g12[g]);
@@ -389,6 +373,46 @@ int upload_chunk(State& st, const ChunkTables& t, DevTables& d, hipStream_t s) {
   d.bytes_hook1 = t.bytes_hook1;
   d.bytes_hook2 = t.bytes_hook2;
   d.bytes_sumsq = t.bytes_sumsq;
+}
+
+
+int upload_chunk(State& st, const ChunkTables& t, DevTables& d, hipStream_t s) {
+  std::vector<char> blob;
+  BlobOffsets o;
+  serialize_chunk(t, blob, o);
+  // Once per new (buffers, shapes, options) set: device memory from the
+  // stream-ordered allocator and a copy from pinned staging, both queued on
+  // the caller's stream, so the host does not wait for earlier work.
+  Staging* sg = nullptr;
+  for (auto& c : st.staging)
+    if (c.cap >= blob.size() && hipEventQuery(c.done) == hipSuccess) {
+      sg = &c;
+      break;
+    }
+  if (!sg) {
+    Staging n;
+    n.cap = std::max<size_t>(blob.size(), (size_t)1 << 20);
+    if (hipHostMalloc((void**)&n.p, n.cap, hipHostMallocDefault) != hipSuccess) return MUONH_ENOMEM;
+    if (hipEventCreateWithFlags(&n.done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipHostFree(n.p);
+      return MUONH_EHIP;
+    }
+    st.staging.push_back(n);
+    sg = &st.staging.back();
+  }
+  memcpy(sg->p, blob.data(), blob.size());
+  char* mem = nullptr;
+  if (hipMallocAsync((void**)&mem, blob.size(), s) == hipSuccess) {
+    d.mem_async = true;
+  } else {
+    (void)hipGetLastError();
+    mem = nullptr;
+    if (hipMalloc(&mem, blob.size()) != hipSuccess) return MUONH_ENOMEM;
+  }
+  d.mem = mem;
+  if (hipMemcpyAsync(mem, sg->p, blob.size(), hipMemcpyHostToDevice, s) != hipSuccess) return MUONH_EHIP;
+  if (hipEventRecord(sg->done, s) != hipSuccess) return MUONH_EHIP;
+  bind_chunk(t, o, mem, d);
   return MUONH_OK;
 }
 
@@ -501,12 +525,20 @@ struct Prof {
   }
 };
 
-SlotTable slot_table(State& st, const DevTables& d) {
+// Where a call's reductions and flag counters live: the library's grown
+// buffers (regular calls) or the static scratch (muonh_step_noalloc).
+struct Meta {
+  double* partials;
+  double* sums;
+  Flags* flags;
+};
+
+SlotTable slot_table(const Meta& m, const DevTables& d) {
   SlotTable t;
-  t.partials = st.partials + 2 * d.part_off;
+  t.partials = m.partials + 2 * d.part_off;
   t.nparts = d.nparts;
   t.part_base = d.part_base;
-  t.sums = st.sums + 2 * (int64_t)d.slot_off;
+  t.sums = m.sums + 2 * (int64_t)d.slot_off;
   return t;
 }
 
@@ -523,6 +555,32 @@ int hip_fail(hipError_t e, const char* what) {
     const hipError_t e_ = (x);                            \
     if (e_ != hipSuccess) return hip_fail(e_, #x);        \
   } while (0)
+
+// Device addresses of the static symbols on one GPU, looked up once per
+// device with that device current.
+constexpr int kMaxDevices = 64;
+struct DevSyms {
+  char* scratch = nullptr;
+  Flags* flags = nullptr;
+};
+DevSyms g_syms[kMaxDevices];
+
+int device_symbols(int dev, DevSyms*& out) {
+  if (dev < 0 || dev >= kMaxDevices) return MUONH_EINVAL;
+  DevSyms& d = g_syms[dev];
+  if (d.flags == nullptr) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    void* f = nullptr;
+    e = hipGetSymbolAddress(&f, HIP_SYMBOL(g_flags));
+    if (e != hipSuccess || f == nullptr) return hip_fail(e, "hipGetSymbolAddress(g_flags)");
+    d.scratch = static_cast<char*>(p);
+    d.flags = static_cast<Flags*>(f);
+  }
+  out = &d;
+  return MUONH_OK;
+}
 
 // Newton-Schulz iteration k of a chunk (K == 0: the single O = X0/||X0||
 // pass): G1, G2, G3 over every unit; the last one ends with the finalize of
@@ -579,9 +637,9 @@ int chunk_stages(int kind, const Cfg& cfg, const DevTables& d) { return 2 + ns_s
 // rec_open is set it is recorded after the opening pass (momentum and its
 // norms, or the resident-tile kernel): the point where the next lane may
 // start.
-int run_chunk_stage(State& st, int kind, const Cfg& cfg, const DevTables& d, const Resolved& r, const CallPtrs& p,
-                    float beta, hipStream_t s, int stage, hipEvent_t rec_open) {
-  const SlotTable sl = slot_table(st, d);
+int run_chunk_stage(State& st, const Meta& meta, int kind, const Cfg& cfg, const DevTables& d, const Resolved& r,
+                    const CallPtrs& p, float beta, hipStream_t s, int stage, hipEvent_t rec_open) {
+  const SlotTable sl = slot_table(meta, d);
   const int nk = ns_stage_count(kind, cfg, d);
   if (stage >= 1 && stage <= nk) return run_ns_iter(st, cfg, d, r, sl, s, stage - 1);
   if (stage == 0) {
@@ -640,7 +698,7 @@ int run_chunk_stage(State& st, int kind, const Cfg& cfg, const DevTables& d, con
     Prof pf(st, s, PC_AW, 0, d.bytes_hook2);
     const float decay = cfg.hook == kModeNone ? 1.f - p.eta * r.o.weight_decay : 1.f;
     MUONH_TRY_HIP(launch_adam_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.adam, p.eta,
-                                    r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, st.flags, s));
+                                    r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, meta.flags, s));
     return MUONH_OK;
   }
   if (kind == CALL_PROJ && p.grads) {
@@ -661,7 +719,7 @@ int run_chunk_stage(State& st, int kind, const Cfg& cfg, const DevTables& d, con
       Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
       const float decay = cfg.hook == kModeNone ? 1.f - p.eta * r.o.weight_decay : 1.f;
       MUONH_TRY_HIP(launch_hook_write(cfg.hook, d.hook_mats, d.hook_blocks, d.n_hook, sl, p.eta,
-                                      r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, st.flags,
+                                      r.o.zero_rel_eps, r.o.outward, r.o.inward, r.o.rb_eps, decay, meta.flags,
                                       s));
     }
   }
@@ -676,6 +734,9 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
   MUONH_TRY_HIP(hipGetDevice(&dev));
   if (st.device != -1 && st.device != dev) return MUONH_EINVAL;  // one device per process
   st.device = dev;
+  DevSyms* syms = nullptr;
+  int rc0 = device_symbols(dev, syms);
+  if (rc0 != MUONH_OK) return rc0;
   const size_t limit = r.o.workspace_limit ? r.o.workspace_limit : default_limit();
   Cfg cfg = make_cfg(kind, n, K, tile_T, r, limit);
   Plan plan;
@@ -687,6 +748,7 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
   CachedPlan* cp = nullptr;
   rc = get_plan(st, plan, cfg, p, shapes, s, cp);
   if (rc != MUONH_OK) return rc;
+  const Meta meta{st.partials, st.sums, syms->flags};
   if (cp->lanes > 1) {
     // Lane 0 runs on the caller's stream, lane l on the library's side
     // stream l, started after lane l-1's opening pass (and so after all
@@ -710,7 +772,8 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
         if (stage >= chunk_stages(kind, cfg, d)) continue;
         hipStream_t ls = l == 0 ? s : st.side[l];
         if (stage == 0 && l > 0) MUONH_TRY_HIP(hipStreamWaitEvent(ls, st.ev_gate[l - 1], 0));
-        rc = run_chunk_stage(st, kind, cfg, d, r, p, beta, ls, stage, stage == 0 && l + 1 < L ? st.ev_gate[l] : nullptr);
+        rc = run_chunk_stage(st, meta, kind, cfg, d, r, p, beta, ls, stage,
+                             stage == 0 && l + 1 < L ? st.ev_gate[l] : nullptr);
         if (rc != MUONH_OK) return rc;
       }
     for (int l = 1; l < L; ++l) {
@@ -721,9 +784,78 @@ int run_call(int kind, const int64_t* shapes, int n, int K, int tile_T, const Re
   }
   for (const DevTables& d : cp->chunks)
     for (int stage = 0; stage < chunk_stages(kind, cfg, d); ++stage) {
-      rc = run_chunk_stage(st, kind, cfg, d, r, p, beta, s, stage, nullptr);
+      rc = run_chunk_stage(st, meta, kind, cfg, d, r, p, beta, s, stage, nullptr);
       if (rc != MUONH_OK) return rc;
     }
+  return MUONH_OK;
+}
+
+// muonh_step with every device byte in the static scratch: workspace,
+// descriptor tables and reduction partials are carved from this GPU's copy of
+// the array, the tables go up with one stream-ordered copy, and all work runs
+// on the caller's stream (one lane, no side streams or events).  Nothing is
+// cached: each call plans and uploads afresh.
+int run_step_noalloc(const int64_t* shapes, int n, int K, int tile_T, Resolved r, const CallPtrs& p, float beta) {
+  State& st = S();
+  std::lock_guard<std::mutex> lk(st.mu);
+  r.o.lanes = 1;
+  // a quarter of the scratch stays free for the tables and reductions
+  Cfg cfg = make_cfg(CALL_STEP, n, K, tile_T, r, kNoAllocScratchBytes / 4 * 3);
+  Plan plan;
+  int rc = make_plan(shapes, cfg, plan);
+  if (rc == MUONH_ENOMEM) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "muonh_step_noalloc: one matrix needs more workspace than the %zu bytes the static scratch "
+             "(%zu bytes) leaves for it", kNoAllocScratchBytes / 4 * 3, kNoAllocScratchBytes);
+    return rc;
+  }
+  if (rc != MUONH_OK) return rc;
+  const int64_t ws_bytes = align256(std::max<int64_t>(plan.ws_bytes, 256));
+  int dev = 0;
+  MUONH_TRY_HIP(hipGetDevice(&dev));
+  if (st.device != -1 && st.device != dev) return MUONH_EINVAL;  // one device per process
+  DevSyms* syms = nullptr;
+  rc = device_symbols(dev, syms);
+  if (rc != MUONH_OK) return rc;
+  st.device = dev;
+  char* const base = syms->scratch;
+  // layout: [workspace | tables of every chunk | slot sums | partials]
+  const size_t nch = plan.chunks.size();
+  std::vector<ChunkTables> tabs(nch);
+  std::vector<BlobOffsets> offs(nch);
+  std::vector<char>& blob = st.noalloc_blob;
+  blob.clear();
+  int64_t max_parts = 1;
+  int max_slots = 1;
+  for (size_t c = 0; c < nch; ++c) {
+    fill_chunk(plan, (int)c, cfg, p, base, tabs[c]);
+    serialize_chunk(tabs[c], blob, offs[c]);
+    max_parts = std::max(max_parts, tabs[c].parts_total);
+    max_slots = std::max(max_slots, (int)tabs[c].nparts.size());
+  }
+  const int64_t tables_off = ws_bytes;
+  const int64_t sums_off = tables_off + align256((int64_t)blob.size());
+  const int64_t parts_off = sums_off + align256((int64_t)max_slots * 2 * (int64_t)sizeof(double));
+  const int64_t total = parts_off + align256(max_parts * 2 * (int64_t)sizeof(double));
+  if (total > (int64_t)kNoAllocScratchBytes) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "muonh_step_noalloc: the call needs %lld bytes of scratch, the static scratch holds %zu",
+             (long long)total, kNoAllocScratchBytes);
+    return MUONH_ENOMEM;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(r.o.stream);
+  // stream-ordered: earlier work on s that still reads the scratch finishes first
+  MUONH_TRY_HIP(hipMemcpyAsync(base + tables_off, blob.data(), blob.size(), hipMemcpyHostToDevice, s));
+  const Meta meta{reinterpret_cast<double*>(base + parts_off), reinterpret_cast<double*>(base + sums_off),
+                  syms->flags};
+  for (size_t c = 0; c < nch; ++c) {
+    DevTables d;
+    bind_chunk(tabs[c], offs[c], base + tables_off, d);
+    for (int stage = 0; stage < chunk_stages(CALL_STEP, cfg, d); ++stage) {
+      rc = run_chunk_stage(st, meta, CALL_STEP, cfg, d, r, p, beta, s, stage, nullptr);
+      if (rc != MUONH_OK) return rc;
+    }
+  }
   return MUONH_OK;
 }
 
@@ -795,6 +927,30 @@ int muonh_step(void* const params[], const void* const grads[], void* const moms
     if (grads[i] == moms[i]) return MUONH_EINVAL;
   CallPtrs p{params, grads, moms, nullptr, r.o.hook == MUONH_HOOK_HYPERBALL ? rho : nullptr, eta};
   return run_call(CALL_STEP, shapes, n, K, tile_T, r, p, beta);
+}
+
+int muonh_step_noalloc(void* const params[], const void* const grads[], void* const moms[],
+                       const int64_t shapes[], int n, float eta, float beta, int K, const float rho[], int tile_T,
+                       const muonh_opts* opts) {
+  int rc = validate_common(shapes, n, K, tile_T);
+  if (rc != MUONH_OK) return rc;
+  if (bad_ptrs(params, n) || bad_ptrs(grads, n) || bad_ptrs((const void* const*)moms, n)) return MUONH_EINVAL;
+  if (!std::isfinite(eta) || eta < 0.f) return MUONH_EINVAL;
+  if (!std::isfinite(beta) || beta < 0.f || beta >= 1.f) return MUONH_EINVAL;
+  Resolved r;
+  rc = resolve(opts, K, r);
+  if (rc != MUONH_OK) return rc;
+  rc = check_tile_sizes(r.o.tile_sizes, n);
+  if (rc != MUONH_OK) return rc;
+  if (r.o.hook == MUONH_HOOK_HYPERBALL) {
+    if (!rho) return MUONH_EINVAL;
+    for (int i = 0; i < n; ++i)
+      if (!std::isfinite(rho[i]) || rho[i] <= 0.f) return MUONH_EINVAL;
+  }
+  for (int i = 0; i < n; ++i)
+    if (grads[i] == moms[i]) return MUONH_EINVAL;
+  CallPtrs p{params, grads, moms, nullptr, r.o.hook == MUONH_HOOK_HYPERBALL ? rho : nullptr, eta};
+  return run_step_noalloc(shapes, n, K, tile_T, r, p, beta);
 }
 
 int adamh_step(void* const params[], const void* const grads[], void* const exp_avg[], void* const exp_avg_sq[],
@@ -872,13 +1028,13 @@ int muonh_get_flags(uint64_t out[4]) {
   if (!out) return MUONH_EINVAL;
   State& st = S();
   std::lock_guard<std::mutex> lk(st.mu);
-  if (!st.flags) {
+  if (st.device < 0 || g_syms[st.device].flags == nullptr) {
     out[0] = out[1] = out[2] = out[3] = 0;
     return MUONH_OK;
   }
   Flags f;
   if (hipDeviceSynchronize() != hipSuccess) return MUONH_EHIP;
-  if (hipMemcpy(&f, st.flags, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return MUONH_EHIP;
+  if (hipMemcpy(&f, g_syms[st.device].flags, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return MUONH_EHIP;
   out[0] = f.zero_update;
   out[1] = f.restored;
   out[2] = f.unrestorable;
@@ -889,9 +1045,9 @@ int muonh_get_flags(uint64_t out[4]) {
 int muonh_reset_flags(void) {
   State& st = S();
   std::lock_guard<std::mutex> lk(st.mu);
-  if (!st.flags) return MUONH_OK;
+  if (st.device < 0 || g_syms[st.device].flags == nullptr) return MUONH_OK;
   if (hipDeviceSynchronize() != hipSuccess) return MUONH_EHIP;
-  if (hipMemset(st.flags, 0, sizeof(Flags)) != hipSuccess) return MUONH_EHIP;
+  if (hipMemset(g_syms[st.device].flags, 0, sizeof(Flags)) != hipSuccess) return MUONH_EHIP;
   return MUONH_OK;
 }
 
@@ -915,7 +1071,7 @@ void muonh_release(void) {
   if (st.ws) (void)hipFree(st.ws);
   if (st.partials) (void)hipFree(st.partials);
   if (st.sums) (void)hipFree(st.sums);
-  if (st.flags) (void)hipFree(st.flags);
+  if (g_syms[st.device].flags) (void)hipMemset(g_syms[st.device].flags, 0, sizeof(Flags));
   for (void* q : st.retired) (void)hipFree(q);
   st.retired.clear();
   for (auto& g : st.staging) {
@@ -942,7 +1098,6 @@ void muonh_release(void) {
   st.partials_cap = 0;
   st.sums = nullptr;
   st.slots_cap = 0;
-  st.flags = nullptr;
   st.device = -1;
 }
 

@@ -319,3 +319,20 @@ def test_plan_query_32bit_operand_offset_limit():
     # (which would fit) but to 65536 at 256
     with pytest.raises(mm.MuonhError):
         mm.plan_query([(32768, 65409)], K=5, workspace_limit=1 << 40)
+
+
+def test_noalloc_step_rejects_oversize_before_any_gpu_call():
+    # 8192 x 8192 full-matrix Newton-Schulz needs far more than the static
+    # scratch: rejected on the host, no HIP call (this machine has no GPU)
+    lib = mm.load()
+    P = ctypes.c_void_p * 1
+    ps, gs, ms = P(0x1000), P(0x2000), P(0x3000)
+    sh = (ctypes.c_int64 * 2)(8192, 8192)
+    rh = (ctypes.c_float * 1)(1.0)
+    o = _opts()
+    rc = lib.muonh_step_noalloc(ps, gs, ms, sh, 1, 0.02, 0.95, 5, rh, 0, ctypes.byref(o))
+    assert rc == mm.MUONH_ENOMEM
+    assert "scratch" in lib.muonh_last_error().decode()
+    # invalid arguments are rejected as by muonh_step
+    assert lib.muonh_step_noalloc(ps, gs, ms, sh, 0, 0.02, 0.95, 5, rh, 0, ctypes.byref(o)) == mm.MUONH_EINVAL
+    assert lib.muonh_step_noalloc(ps, gs, ms, sh, 1, 0.02, 1.5, 5, rh, 0, ctypes.byref(o)) == mm.MUONH_EINVAL
