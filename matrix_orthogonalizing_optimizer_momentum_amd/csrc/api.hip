@@ -142,8 +142,8 @@ State& S() {
 
 const char* kClassNames[] = {"momentum_prep", "ns_gram_G1", "ns_poly_G2",       "ns_update_G3",
                              "hook_reduce",   "hook_write", "sumsq",            "finalize",
-                             "ns_tile_resident", "adam_moments", "adam_write"};
-enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_FIN, PC_TILE, PC_AM, PC_AW, PC_N };
+                             "ns_tile_resident", "adam_moments", "adam_write", "ns_tile_fused"};
+enum { PC_MOM = 0, PC_G1, PC_G2, PC_G3, PC_HR, PC_HW, PC_SQ, PC_FIN, PC_TILE, PC_AM, PC_AW, PC_T256, PC_N };
 
 // ------------------------------------------------------------------ helpers
 // Frees a plan's device tables.  With a stream, stream-ordered allocations
@@ -660,7 +660,7 @@ int run_chunk_stage(State& st, const Meta& meta, int kind, const Cfg& cfg, const
         ta.st = sl;
         for (const TileGroup& g : d.tile_groups) {
           ta.T = g.T;
-          Prof pf(st, s, PC_TILE, g.flops, g.bytes);
+          Prof pf(st, s, g.T > kTileResidentMax ? PC_T256 : PC_TILE, g.flops, g.bytes);
           MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs + g.job0, g.njobs, ta, s));
         }
         if (!gemm) {

@@ -106,6 +106,9 @@ struct HookBlock {
 // Resident-tile Newton-Schulz (Hierarchical Muon with T <= kTileResidentMax):
 // one workgroup runs the whole step of one tile.
 constexpr int kTileResidentMax = 128;
+// Tiles of side kTileResidentMax < T <= kTileFusedMax run on the fused
+// 256-tile kernel (bf16 operands and state, X in bf16 between iterations).
+constexpr int kTileFusedMax = 256;
 constexpr int kTileMaxK = 64;
 
 struct TileMat {

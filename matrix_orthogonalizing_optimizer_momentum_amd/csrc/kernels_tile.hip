@@ -428,10 +428,17 @@ void launch_tile_t(int TP, dim3 grid, const TileMat* mats, const TileJob* jobs, 
 }
 }  // namespace
 
+hipError_t launch_tile256_ns(const TileMat* mats, const TileJob* jobs, int njobs, const TileArgs& args,
+                             hipStream_t s);
+
 hipError_t launch_tile_ns(int state_dt, int op_dt, const TileMat* mats, const TileJob* jobs, int njobs,
                           const TileArgs& args, hipStream_t s) {
   if (njobs <= 0) return hipSuccess;
-  if (args.T < 1 || args.T > kTileResidentMax || args.K < 0 || args.K > kTileMaxK) return hipErrorInvalidValue;
+  if (args.T > kTileResidentMax) {  // 128 < T <= 256: the fused 256-tile kernel (bf16 state and operands)
+    if (state_dt != DT_BF16 || op_dt != DT_BF16) return hipErrorInvalidValue;
+    return launch_tile256_ns(mats, jobs, njobs, args, s);
+  }
+  if (args.T < 1 || args.K < 0 || args.K > kTileMaxK) return hipErrorInvalidValue;
   const int TP = args.T <= 64 ? 64 : 128;
   const dim3 grid(njobs);
   if (state_dt == DT_BF16 && op_dt == DT_BF16) launch_tile_t<bf16_t, bf16_t>(TP, grid, mats, jobs, args, s);

@@ -1,0 +1,610 @@
+// Fused Newton-Schulz for Hierarchical-Muon tiles of side 128 < T <= 256
+// (gfx950).
+//
+// "Hierarchical Muon: Tiled Newton-Schulz Updates for Efficient Muon
+// Optimization" (core claim, abstract): every T x T tile of a momentum matrix
+// gets the same finite Newton-Schulz map on its own.  Here one workgroup of
+// four waves (one per SIMD) owns one tile, zero-padded to 256 x 256 (exact:
+// [[X, 0], [0, 0]] maps to [[NS(X), 0], [0, 0]]), for the whole step:
+//   - momentum M <- beta M + G (Muon explainer, momentum recap / Equation 1)
+//     on the tile's elements, M stored back, X0 = M and its Frobenius norm;
+//   - K iterations A = X X^T; B = b A + c A A; X = a X + B X (Muon explainer,
+//     Newton-Schulz section, Equation 6 and code section) with bf16 MFMA
+//     operands and fp32 accumulation, 1 / (||X0|| + eps) folded into the
+//     first iteration, X rounded to bf16 after every update (the FOLD
+//     precision), all of it on chip;
+//   - the cropped tile written once as O, with ||O||^2 and, for the weight
+//     update hook, <W, O> and ||W||^2 summed where O is stored.
+//
+// Registers.  Wave w owns the 128 x 128 quadrant (128 (w / 2), 128 (w % 2))
+// of every product: 4 x 4 accumulator blocks of 32 x 32 (256 fp32 values per
+// lane), and the same quadrant of X in bf16 pairs (128 registers per lane),
+// which carries X from one iteration to the next.
+//
+// LDS (160 KiB = one bf16 256 x 256 matrix + two 16 KiB pieces):
+//   - the matrix region holds A, then B (both symmetric, stored from the
+//     accumulators through the transposed path), and the staging of the input
+//     and output tiles; rows of 512 B, 16-byte granules XOR-swizzled by the
+//     row, so that the fragment reads of 32 rows at one k hit distinct banks;
+//   - G1 (A = X X^T) and G3 (B X) take X from the pieces: 32-deep slices of
+//     X^T written from the registers of the waves that hold them while every
+//     wave runs the previous slice's MFMAs (double buffered).  G1's slices
+//     are [n][m] rows read with the transposing LDS read (ds_read_b64_tr_b16);
+//     G3's are [n][k] rows of 64 B read directly.
+#include <type_traits>
+
+#include "common.h"
+
+namespace muonh {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+constexpr int kS = 256;                     // padded tile side
+constexpr int kNT = 256;                    // threads: 4 waves
+constexpr int kMatB = kS * kS * 2;          // bytes of the bf16 matrix region
+constexpr int kPieceB = 16384;              // bytes of one 32-deep X^T slice
+constexpr int kSmem = kMatB + 2 * kPieceB;  // 160 KiB
+
+// Byte offset of element (r, c) of the matrix region.
+__device__ __forceinline__ int mat_off(int r, int c) {
+  return r * 512 + ((((c >> 3) ^ (r & 15))) << 4) + ((c & 7) << 1);
+}
+// G3 slice: X^T(n, k0 + kk) for kk < 32, rows n of 64 B, granules swizzled by
+// n / 4 so that 16 consecutive rows read at one kk hit 16 distinct granules.
+__device__ __forceinline__ int g3_off(int n, int kk) {
+  return n * 64 + ((((kk >> 3) ^ ((n >> 2) & 3))) << 4) + ((kk & 7) << 1);
+}
+// X^T for G1 in the matrix region: element (n, m) in row n (512 B), column
+// (m + 32 (n % 4)) % 256, whose 16-byte granule is XORed with (n / 4) % 4.
+// The rotation puts the four rows one transposing read touches in different
+// banks; the XOR (the same for those four rows) spreads the 8-byte writes of
+// 32 consecutive rows.
+__device__ __forceinline__ int xt_off(int n, int m) {
+  const int rot = (m + 32 * (n & 3)) & 255;
+  return n * 512 + ((((rot >> 3) ^ ((n >> 2) & 3))) << 4) + ((rot & 7) << 1);
+}
+
+template <typename P>
+__device__ __forceinline__ __attribute__((address_space(3))) P* lds(void* p) {
+  return (__attribute__((address_space(3))) P*)p;
+}
+
+__device__ __forceinline__ bf16x8_t ld16(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+
+// Transposing read pair: one MFMA operand fragment (8 consecutive k of one
+// row m) from a [k][m] slice, as in the GEMM engine.
+__device__ __forceinline__ bf16x8_t ld_tr8(const char* p0, const char* p1) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds<i16x4_t>(const_cast<char*>(p0)));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds<i16x4_t>(const_cast<char*>(p1)));
+  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// The LDS addresses below depend only on the lane and compile-time offsets,
+// so the compiler would hoist every one of them out of the iteration loop and
+// spill them; passing the lane base through an empty asm per use keeps them
+// computed where they are used.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+}  // namespace
+
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ jobs, TileArgs args) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  char* const sM = smem;
+  char* const sP0 = smem + kMatB;
+  // reduction scratch in the second slice: it is first written by G1 after
+  // the barrier that follows every thread's read of the pre-scale sum
+  double* const sred = reinterpret_cast<double*>(smem + kMatB + kPieceB);
+
+  const TileJob job = jobs[blockIdx.x];
+  const TileMat mt = mats[job.mat];
+  const int T = args.T;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;  // quadrant origin
+  const int lc = lane & 31, lh = lane >> 5;
+  const int64_t r0 = (int64_t)job.ti * T, c0 = (int64_t)job.tj * T;
+  const int h = (int)min<int64_t>(T, mt.H - r0), w = (int)min<int64_t>(T, mt.W - c0);
+  const int64_t ldm = mt.W;
+  const bf16_t* const tg = mt.g ? reinterpret_cast<const bf16_t*>(mt.g) + r0 * ldm + c0 : nullptr;
+  bf16_t* const tm = reinterpret_cast<bf16_t*>(mt.m) + r0 * ldm + c0;
+
+  // ---- input: momentum on the tile (8-element row chunks, chunk t + 256 c
+  // for thread t), M stored back, X0 staged row-major in the matrix region.
+  float sq = 0.f;
+  if (mt.vec) {
+    // 16 chunks of M (and G) in flight per thread: with one workgroup per
+    // CU the loads must cover HBM latency on their own
+#pragma unroll
+    for (int cb = 0; cb < 32; cb += 16) {
+      u32x4_t mraw[16], graw[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int row = 8 * (cb + k) + (tid >> 5), col = (tid & 31) * 8;
+        const int64_t off = (row < h && col < w) ? (int64_t)row * ldm + col : 0;
+        mraw[k] = *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(tm + off));
+        if (tg) graw[k] = *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(tg + off));
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int row = 8 * (cb + k) + (tid >> 5), col = (tid & 31) * 8;
+        const bool ok = row < h && col < w;
+        u32x4_t pk = mraw[k];
+        if (tg) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = St<bf16_t>::round(fmaf(args.beta, lo_bf(mraw[k][e]), args.gcoef * lo_bf(graw[k][e])));
+            x[2 * e + 1] = St<bf16_t>::round(fmaf(args.beta, hi_bf(mraw[k][e]), args.gcoef * hi_bf(graw[k][e])));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+          if (ok) *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(tm + (int64_t)row * ldm + col)) = pk;
+        }
+        if (!ok) pk = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sq = fmaf(lo_bf(pk[e]), lo_bf(pk[e]), sq);
+          sq = fmaf(hi_bf(pk[e]), hi_bf(pk[e]), sq);
+        }
+        *reinterpret_cast<u32x4_t*>(sM + mat_off(row, col)) = pk;
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int c = 0; c < 32; ++c) {
+      const int row = 8 * c + (tid >> 5), col = (tid & 31) * 8;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = 0.f;
+        if (row < h && col + e < w) {
+          const int64_t o = (int64_t)row * ldm + col + e;
+          v = St<bf16_t>::ld(tm, o);
+          if (tg) {
+            v = St<bf16_t>::round(fmaf(args.beta, v, args.gcoef * St<bf16_t>::ld(tg, o)));
+            St<bf16_t>::st(tm, o, v);
+          }
+        }
+        x[e] = v;
+        sq = fmaf(v, v, sq);
+      }
+      u32x4_t pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+      *reinterpret_cast<u32x4_t*>(sM + mat_off(row, col)) = pk;
+    }
+  }
+  {
+    const double d = wave_sum((double)sq);
+    if (lane == 0) sred[wave] = d;
+  }
+  __syncthreads();
+  const double sig = 1.0 / (sqrt(((sred[0] + sred[1]) + sred[2]) + sred[3]) + (double)args.eps);
+
+  // X0 into registers in the accumulator layout: lane l of block (i, j),
+  // group q holds rows 8 q + 4 (l / 32) + 0..3 of column l % 32 -- one
+  // transposing read of the row-major staging per group (16-lane group g
+  // reads the 4 x 16 block at rows + 4 (g / 2), columns + 16 (g % 2)).
+  u32x2_t xr[4][4][4];  // bf16 pairs: rows (0, 1) and (2, 3) of a group
+  {
+    const int j16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int R = wr + i * 32 + 8 * q + 4 * (g >> 1) + (j16 >> 2);
+          const int C = wc + j * 32 + 16 * (g & 1) + 4 * (j16 & 3);
+          const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds<i16x4_t>(sM + mat_off(R, C)));
+          xr[i][j][q] = __builtin_bit_cast(u32x2_t, v);
+        }
+  }
+
+  // Accumulators are written only by MFMAs: the first k-step of a product
+  // takes a zero C operand, and the seed terms (b A, a X) are added in the
+  // epilogues, which only read them.  (Element writes into the accumulator
+  // tuples between products make the compiler move whole tuples through the
+  // arch VGPRs, which then spill.)
+  f32x16_t acc[4][4];
+  auto mma16 = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], auto zc) {
+    constexpr bool zero = decltype(zc)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], zero ? f32x16_t{} : acc[i][j], 0, 0, 0);
+  };
+  using Z = std::true_type;
+  using NZ = std::false_type;
+  auto bar = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // G3 slice p: X^T(n, 32 p + kk), written by the two waves whose row range
+  // holds rows 32 p .. 32 p + 31 of X (their block row p % 4).  The slice
+  // loop is unrolled, so p (and the register block) is a compile-time
+  // constant: indexing the register array at run time would move it to
+  // scratch memory.  Slice element (n, 8 q + 4 lh), n = wc + 32 j + lc, is
+  // at row n, granule q ^ (lc / 4 % 4); every lane base is derived from a
+  // fresh opaque copy of the lane id where it is used.
+  //
+  // G1 reads X^T whole from the matrix region (free at that point): every
+  // wave writes its quadrant, X(m..m+3, n) -> X^T(n, m..m+3).
+  auto put_xt = [&]() {
+    const int ln = opaque(lane), l31 = ln & 31, lhh = ln >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<u32x2_t*>(sM + xt_off(wc + 32 * j + l31, wr + 32 * i + 8 * q + 4 * lhh)) = xr[i][j][q];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  auto put_g3 = [&](auto pc, char* buf) {
+    constexpr int p = decltype(pc)::value, ib = p & 3;
+    if ((p >> 2) != (wave >> 1)) return;  // uniform per wave
+    const int ln = opaque(lane), l31 = ln & 31;
+    const int base = (wc + l31) * 64 + 8 * (ln >> 5), sw = (l31 >> 2) & 3;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      char* const bq = buf + base + ((q ^ sw) << 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x2_t*>(bq + 2048 * j) = xr[ib][j][q];
+    }
+  };
+
+  // G1 fragments (transposing reads of X^T, k = n): lane 16 g + j16 reads
+  // rows 16 ks + 8 (g / 2) + j16 / 4 and 4 rows further, elements
+  // 16 (g % 2) + 4 (j16 % 4) of its 32-wide block.  The layout depends on the
+  // row modulo 16 only, so a k-step adds 8 KiB; the two reads of a fragment
+  // differ in their granule XOR and get offsets of their own.
+  auto g1_offsets = [&](int (&g1p)[2][4], int (&g1q)[2][4]) {
+    const int ln = opaque(lane), j16 = ln & 15, g = ln >> 4;
+    const int krow = 8 * (g >> 1) + (j16 >> 2);
+    const int msub = 16 * (g & 1) + 4 * (j16 & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g1p[h][i] = xt_off(krow + 4 * h, wr + i * 32 + msub);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g1q[h][j] = xt_off(krow + 4 * h, wc + j * 32 + msub);
+    }
+  };
+
+  // Symmetric results go to the matrix region through the transposed path:
+  // the lane's rows m..m+3 of column n go to row n, elements m..m+3 (8
+  // bytes): mat_off(n, m) with n = wc + 32 j + lc, m = wr + 32 i + 8 q + 4 lh
+  // is row n (16 KiB per j), granule (wr / 8 + 4 i + q) ^ (lc % 16), byte
+  // 8 lh.  put_a stores A = sc * acc; put_b stores B = c * acc + b * A, with
+  // A read back from the very slot the lane then overwrites (c = 0: B = b A,
+  // acc unused).
+  auto sym_addr = [&](int row, int sw, int i, int j, int q) -> char* {
+    return sM + row + 16384 * j + ((((wr >> 3) + 4 * i + q) ^ sw) << 4);
+  };
+  // (scaled: times sc, the first iteration's sig^2 and 1 after it; a
+  // run-time branch between the two forms would join register states.)
+  auto put_a = [&](auto scaled, float sc) {
+    constexpr bool kScale = decltype(scaled)::value;
+    const int ln = opaque(lane), l31 = ln & 31;
+    const int row = (wc + l31) * 512 + 8 * (ln >> 5), sw = l31 & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = kScale ? acc[i][j][4 * q + e] * sc : acc[i][j][4 * q + e];
+          const uint32_t w0 = pack_bf16x2(v[0], v[1]);
+          const uint32_t w1 = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2_t*>(sym_addr(row, sw, i, j, q)) = u32x2_t{w0, w1};
+          // one block at a time: the scheduler would otherwise batch every
+          // accumulator read (register pressure)
+          if (q == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+  };
+  auto put_b = [&](float b, float c) {
+    const int ln = opaque(lane), l31 = ln & 31;
+    const int row = (wc + l31) * 512 + 8 * (ln >> 5), sw = l31 & 15;
+    // the next block's four A reads are in flight while this block is formed
+    u32x2_t av[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) av[0][q] = *reinterpret_cast<const u32x2_t*>(sym_addr(row, sw, 0, 0, q));
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3, cur = t & 1;
+      if (t + 1 < 16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          av[cur ^ 1][q] = *reinterpret_cast<const u32x2_t*>(sym_addr(row, sw, (t + 1) >> 2, (t + 1) & 3, q));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2_t a2 = av[cur][q];
+        float v[4] = {b * lo_bf(a2[0]), b * hi_bf(a2[0]), b * lo_bf(a2[1]), b * hi_bf(a2[1])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(c, acc[i][j][4 * q + e], v[e]);
+        *reinterpret_cast<u32x2_t*>(sym_addr(row, sw, i, j, q)) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int it = 0; it < args.K; ++it) {
+    const float a = args.abc[it][0], b = args.abc[it][1], c = args.abc[it][2];
+    const bool first = it == 0;
+
+    // ---------------- G1: A = X X^T (times sig^2 on the first iteration)
+    put_xt();
+    bar();
+    {
+      int g1p[2][4], g1q[2][4];
+      g1_offsets(g1p, g1q);
+      bf16x8_t fa[2][4], fb[2][4];
+      auto ld_x = [&](int buf, int ks) {
+        const int o = ks * 16 * 512;  // 16 rows further
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[buf][i] = ld_tr8(sM + g1p[0][i] + o, sM + g1p[1][i] + o);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[buf][j] = ld_tr8(sM + g1q[0][j] + o, sM + g1q[1][j] + o);
+      };
+      ld_x(0, 0);
+      static_for<8>([&](auto hc) {
+        constexpr int ks = 2 * decltype(hc)::value;
+        ld_x(1, ks + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma16(fa[0], fb[0], std::integral_constant<bool, ks == 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks + 2 < 16) ld_x(0, ks + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma16(fa[1], fb[1], NZ{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    bar();  // every wave is done reading X^T
+
+    // ---------------- A to LDS; G2: A A.  The product runs for c = 0 too
+    // (c * A A then adds nothing): a run-time branch around it would join two
+    // accumulator states, which the compiler resolves by copying all of them
+    // through the arch VGPRs.
+    put_a(std::true_type{}, first ? (float)(sig * sig) : 1.f);  // branch-free (see update below)
+    bar();
+    {
+      bf16x8_t fa[2][4], fb[2][4];
+      // rows wr + 32 i + lc (and wc + 32 j + lc): 16 KiB per block, granule
+      // (2 ks + lh) ^ (lc % 16)
+      auto ld_ab = [&](int buf, int ks) {
+        const int ln = opaque(lane), l31 = ln & 31;
+        const int g = ((2 * ks + (ln >> 5)) ^ (l31 & 15)) << 4;
+        const char* pa = sM + (wr + l31) * 512 + g;
+        const char* pb = sM + (wc + l31) * 512 + g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[buf][i] = ld16(pa + 16384 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[buf][j] = ld16(pb + 16384 * j);
+      };
+      ld_ab(0, 0);
+      static_for<8>([&](auto hc) {
+        constexpr int ks = 2 * decltype(hc)::value;
+        ld_ab(1, ks + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma16(fa[0], fb[0], std::integral_constant<bool, ks == 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks + 2 < 16) ld_ab(0, ks + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma16(fa[1], fb[1], NZ{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    bar();  // every wave is done reading A
+
+    // ---------------- B to LDS; G3: X <- a X + B X (times sig on the first)
+    put_b(b, c);
+    put_g3(std::integral_constant<int, 0>{}, sP0);
+    bar();
+    static_for<8>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      constexpr int so = (p & 1) * kPieceB;  // this slice's buffer
+      bf16x8_t fa[2][4], fb[2][4];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        // B rows wr + 32 i + lc at k = 32 p + 16 kk + 8 lh; slice rows
+        // wc + 32 j + lc at kk16 = 16 kk + 8 lh
+        const int ln = opaque(lane), l31 = ln & 31, lhh = ln >> 5;
+        const char* pa = sM + (wr + l31) * 512 + (((4 * p + 2 * kk + lhh) ^ (l31 & 15)) << 4);
+        const char* pb = smem + so + kMatB + (wc + l31) * 64 + (((2 * kk + lhh) ^ ((l31 >> 2) & 3)) << 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[kk][i] = ld16(pa + 16384 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[kk][j] = ld16(pb + 2048 * j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma16(fa[0], fb[0], std::integral_constant<bool, p == 0>{});
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (p + 1 < 8) put_g3(std::integral_constant<int, p + 1>{}, sP0 + ((p + 1) & 1) * kPieceB);
+      __builtin_amdgcn_sched_barrier(0);
+      mma16(fa[1], fb[1], NZ{});
+      bar();
+    });
+    // X <- a X + B X (times sig on the first iteration), rounded to bf16 and
+    // kept in registers for the next iteration
+    auto update = [&](auto scaled) {
+      constexpr bool kScale = decltype(scaled)::value;
+      const float xs = first ? (float)sig : 1.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x0 = xr[i][j][q][0], x1 = xr[i][j][q][1];
+            float v[4] = {fmaf(a, lo_bf(x0), acc[i][j][4 * q]), fmaf(a, hi_bf(x0), acc[i][j][4 * q + 1]),
+                          fmaf(a, lo_bf(x1), acc[i][j][4 * q + 2]), fmaf(a, hi_bf(x1), acc[i][j][4 * q + 3])};
+            if (kScale) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] *= xs;
+            }
+            xr[i][j][q] = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            if (q == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+    };
+    // branch-free: a run-time branch between the scaled and unscaled forms
+    // here joins two X register states, which the compiler copies and spills
+    update(std::true_type{});
+  }
+  if (args.K == 0) {  // O = X0 / (||X0|| + eps)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w0 = xr[i][j][q][0], w1 = xr[i][j][q][1];
+          xr[i][j][q] = u32x2_t{pack_bf16x2((float)((double)lo_bf(w0) * sig), (float)((double)hi_bf(w0) * sig)),
+                                pack_bf16x2((float)((double)lo_bf(w1) * sig), (float)((double)hi_bf(w1) * sig))};
+        }
+  }
+
+  // ---- output: O (bf16) staged row-major in the matrix region (behind a
+  // barrier: the last product's reads, or with K = 0 the X0 gather), then written as
+  // 8-element row chunks cropped to the matrix, with ||O||^2 and the hook's
+  // <W, O>, ||W||^2 at the same positions (fp64 per thread).
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = wr + i * 32 + 8 * q + 4 * lh, n = wc + j * 32 + lc;
+        const uint32_t w0 = xr[i][j][q][0], w1 = xr[i][j][q][1];
+        *reinterpret_cast<bf16_t*>(sM + mat_off(m + 0, n)) = (bf16_t)(w0 & 0xffffu);
+        *reinterpret_cast<bf16_t*>(sM + mat_off(m + 1, n)) = (bf16_t)(w0 >> 16);
+        *reinterpret_cast<bf16_t*>(sM + mat_off(m + 2, n)) = (bf16_t)(w1 & 0xffffu);
+        *reinterpret_cast<bf16_t*>(sM + mat_off(m + 3, n)) = (bf16_t)(w1 >> 16);
+      }
+  __syncthreads();
+  double osq = 0.0, swo = 0.0, sww = 0.0;
+  const float* const wp = mt.w;
+  const int64_t obase = r0 * ldm + c0;
+  if (mt.vec) {
+    // 8 chunks per batch: their W loads in flight together
+#pragma unroll
+    for (int cb = 0; cb < 32; cb += 8) {
+      f32x4_t wv[8][2];
+      if (wp != nullptr) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int row = 8 * (cb + k) + (tid >> 5), col = (tid & 31) * 8;
+          const int64_t o = (row < h && col < w) ? obase + (int64_t)row * ldm + col : obase;
+          typedef __attribute__((address_space(4))) const f32x4_t cf4;
+          wv[k][0] = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(wp + o));
+          wv[k][1] = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(wp + o + 4));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int row = 8 * (cb + k) + (tid >> 5), col = (tid & 31) * 8;
+        if (row >= h || col >= w) continue;
+        const u32x4_t pk = *reinterpret_cast<const u32x4_t*>(sM + mat_off(row, col));
+        const int64_t o = obase + (int64_t)row * ldm + col;
+        *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(reinterpret_cast<bf16_t*>(mt.out) + o)) = pk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double x = (double)((e & 1) ? hi_bf(pk[e >> 1]) : lo_bf(pk[e >> 1]));
+          osq = fma(x, x, osq);
+          if (wp != nullptr) {
+            const double wd = (double)wv[k][e >> 2][e & 3];
+            swo = fma(wd, x, swo);
+            sww = fma(wd, wd, sww);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int cch = 0; cch < 32; ++cch) {
+      const int row = 8 * cch + (tid >> 5), col = (tid & 31) * 8;
+      if (row >= h || col >= w) continue;
+      const u32x4_t pk = *reinterpret_cast<const u32x4_t*>(sM + mat_off(row, col));
+      const int64_t o = obase + (int64_t)row * ldm + col;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < w) {
+          const float x = (e & 1) ? hi_bf(pk[e >> 1]) : lo_bf(pk[e >> 1]);
+          store_dyn(mt.out, o + e, x, DT_BF16);
+          osq = fma((double)x, (double)x, osq);
+          if (wp != nullptr) {
+            const double wd = (double)load1_ro(wp, o + e);
+            swo = fma(wd, (double)x, swo);
+            sww = fma(wd, wd, sww);
+          }
+        }
+    }
+  }
+  // block sums: one fp64 partial per tile (the slices are idle: scratch)
+  osq = wave_sum(osq);
+  swo = wave_sum(swo);
+  sww = wave_sum(sww);
+  if (lane == 0) {
+    sred[wave] = osq;
+    sred[4 + wave] = swo;
+    sred[8 + wave] = sww;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double t0 = ((sred[0] + sred[1]) + sred[2]) + sred[3];
+    const double t1 = ((sred[4] + sred[5]) + sred[6]) + sred[7];
+    const double t2 = ((sred[8] + sred[9]) + sred[10]) + sred[11];
+    const SlotTable& st = args.st;
+    const int64_t pa = st.part_base[mt.onorm_slot] + job.part;
+    gmem(st.partials)[2 * pa] = t0;
+    gmem(st.partials)[2 * pa + 1] = wp != nullptr ? t1 : 0.0;
+    if (wp != nullptr) {
+      const int64_t pb = st.part_base[mt.hook_slot] + job.part;
+      gmem(st.partials)[2 * pb] = 0.0;
+      gmem(st.partials)[2 * pb + 1] = t2;
+    }
+  }
+}
+
+hipError_t launch_tile256_ns(const TileMat* mats, const TileJob* jobs, int njobs, const TileArgs& args,
+                             hipStream_t s) {
+  if (njobs <= 0) return hipSuccess;
+  if (args.T <= kTileResidentMax || args.T > kTileFusedMax || args.K < 0 || args.K > kTileMaxK || !args.fold)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tile256_ns, dim3(njobs), dim3(kNT), 0, s, mats, jobs, args);
+  return hipGetLastError();
+}
+
+}  // namespace muonh

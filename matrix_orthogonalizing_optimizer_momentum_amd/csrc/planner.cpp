@@ -48,6 +48,15 @@ UnitBytes unit_bytes(int r, int s, int op_dt, int x32) {
 // from r >= 512; smaller units keep 128-tiles, which fill the chip better.
 // MUONH_GEMM_BIG=0 / 2 forces 128 / 256 tiles (bf16) for tuning runs;
 // results do not depend on the choice beyond summation order.
+bool tile256_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = std::getenv("MUONH_TILE256");
+    on = (e && *e) ? (std::atoi(e) != 0) : 1;
+  }
+  return on != 0;
+}
+
 int unit_gemm_cfg(int r, int op_dt, bool phase12) {
   if (op_dt != DT_BF16) return 0;
   static int mode = -1;
@@ -89,7 +98,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
     MatPlan& m = plan.mats[i];
     const int T = mat_tile(cfg, i);
     m.T = no_ns(cfg.kind) ? 0 : T;
-    all_engine = all_engine && !resident_tile(m.T);
+    all_engine = all_engine && !resident_tile(cfg, m.T);
     m.H = shapes[2 * i];
     m.W = shapes[2 * i + 1];
     if (m.H < 1 || m.W < 1 || m.H > (int64_t)1 << 30 || m.W > (int64_t)1 << 30) return MUONH_EINVAL;
@@ -119,7 +128,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
           const int64_t w = std::min<int64_t>(T, m.W - (int64_t)b * T);
           plan.ns_flops += ns_flops_true(h, w, cfg.K);
         }
-      if (resident_tile(T)) {
+      if (resident_tile(cfg, T)) {
         plan.jobs_per_iter += m.nunits;  // one workgroup per tile runs every iteration
       } else {
         const UnitBytes ub = unit_bytes(T, T, cfg.op_dt, cfg.x32 || cfg.seed32);
@@ -147,7 +156,7 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
     // RelativeUpdate) and pass 2
     // hook pass 1: W and O (RelativeUpdate: W only); with resident tiles
     // the tile kernel reads W for the norms instead (4 bytes)
-    const bool fused_mat = cfg.kind == CALL_STEP && cfg.hook != kModeNone && resident_tile(T);
+    const bool fused_mat = cfg.kind == CALL_STEP && cfg.hook != kModeNone && resident_tile(cfg, T);
     const double hook1 = cfg.hook == kModeNone ? 0 : (cfg.hook == kModeRel || fused_mat) ? 4 : 4 + ob;
     if (cfg.kind == CALL_STEP) plan.stream_bytes += (double)numel * (3 * sb + hook1 + (4 + ob + 4));
     else plan.stream_bytes += (double)numel * (sb + sb);  // NS: read input, write output
@@ -228,7 +237,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
     const MatPlan& m = plan.mats[ch.m0 + mi];
     unit0[mi] = (int)t.units.size();
     if (no_ns(cfg.kind)) continue;
-    if (resident_tile(m.T)) {
+    if (resident_tile(cfg, m.T)) {
       if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
       continue;
     }
@@ -249,7 +258,7 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
     if (cfg.kind == CALL_STEP) obuf[mi] = carve(align256(m.H * m.W * es_op));
   }
   const int nunits = (int)t.units.size();
-  auto resident = [&](const MatPlan& m) { return !no_ns(cfg.kind) && resident_tile(m.T); };
+  auto resident = [&](const MatPlan& m) { return !no_ns(cfg.kind) && resident_tile(cfg, m.T); };
   // A step's hook norms (<W, O>, ||W||^2) are summed where O is stored for
   // matrices run as resident tiles: the tile kernel reads W at little cost,
   // while in the GEMM engine's last epilogue the extra read costs more than

@@ -93,8 +93,17 @@ int unit_gemm_cfg(int r, int op_dt, bool phase12);
 
 // Hierarchical Muon with T <= kTileResidentMax runs on the resident-tile
 // kernel (one workgroup per tile for the whole step, momentum fused, no
-// workspace but the step's O buffer); larger tiles go through the GEMM engine.
-inline bool resident_tile(int T) { return T > 0 && T <= kTileResidentMax; }
+// workspace but the step's O buffer).  Tiles of side 128 < T <= 256 do the
+// same on the 256-tile kernel when X stays bf16 between iterations and the NS
+// input is a bf16 value (bf16 operands and state, FOLD, no Nesterov blend);
+// otherwise, and for larger tiles, they go through the GEMM engine.
+bool tile256_enabled();  // MUONH_TILE256=0 routes such tiles to the GEMM engine (tuning runs)
+inline bool fused256_ok(const Cfg& c) {
+  return c.op_dt == DT_BF16 && c.state_dt == DT_BF16 && !c.x32 && !c.seed32 && tile256_enabled();
+}
+inline bool resident_tile(const Cfg& c, int T) {
+  return T > 0 && (T <= kTileResidentMax || (T <= kTileFusedMax && fused256_ok(c)));
+}
 inline int mat_tile(const Cfg& c, int i) { return c.tile_sizes ? c.tile_sizes[i] : c.tile_T; }
 
 // Resident-tile launches of one chunk: one per distinct tile side.

@@ -118,15 +118,18 @@ def test_lanes_share_one_chunk_workspace():
 
 def test_automatic_lanes_follow_iteration_work():
     # Two lanes, but one for NS on the GEMM engine (full matrices, or tiles
-    # above the resident size 128) whose iteration exceeds 2e12 flops.
+    # above the resident sizes) whose iteration exceeds 2e12 flops.
     small = [(1024, 1024)] * 4   # 4 * 6 * 1024^3 flops per iteration
     big = [(8192, 8192)] * 2     # 2 * 6 * 8192^3 > 2e12
     assert mm.plan_query(small, K=5)["lanes"] == 2
     assert mm.plan_query(big, K=5)["lanes"] == 1
     assert mm.plan_query(big, K=5, tile_T=128)["lanes"] == 2   # resident tiles
     huge = [(16384, 16384)] * 8  # 8 * 4096 tiles of 256^2: 3.3e12 flops per iteration
-    assert mm.plan_query(huge, K=5, tile_T=256, workspace_limit=1 << 40)["lanes"] == 1
-    assert mm.plan_query(big, K=5, tile_T=256, workspace_limit=1 << 40)["lanes"] == 2  # 2.1e11
+    # bf16 tiles of 256 run fused (resident): two lanes; with the fp32 master
+    # copy (X32) they go through the GEMM engine: one lane
+    assert mm.plan_query(huge, K=5, tile_T=256, workspace_limit=1 << 40)["lanes"] == 2
+    assert mm.plan_query(huge, K=5, tile_T=256, workspace_limit=1 << 40, ns_precision="x32")["lanes"] == 1
+    assert mm.plan_query(big, K=5, tile_T=256, workspace_limit=1 << 40, ns_precision="x32")["lanes"] == 2  # 2.1e11
     assert mm.plan_query(big, K=5, lanes=2)["lanes"] == 2
     # a budget that forces sequential chunks leaves no room for lanes
     one = mm.plan_query(small[:1], K=5)["ws_bytes"]
@@ -234,10 +237,24 @@ def test_plan_query_resident_tiles(T):
     assert q["chunks"] == 1
 
 
+def test_plan_query_fused_256_tiles_need_only_the_output():
+    # bf16 tiles of 129..256 run on the fused kernel: no Newton-Schulz
+    # workspace, only the step's bf16 O buffer; the fp32 master copy sends
+    # them to the GEMM engine, which needs per-tile workspace
+    shapes = [(768, 2304), (3072, 768)]
+    numel = sum(h * w for h, w in shapes)
+    for T in (192, 256):
+        assert mm.plan_query(shapes, K=5, tile_T=T, lanes=1)["ws_bytes"] <= 2 * numel + 2 * 256
+        assert mm.plan_query(shapes, K=5, tile_T=T, lanes=1, ns_precision="x32")["ws_bytes"] > 4 * numel
+
+
 def test_plan_query_gemm_engine_tiles_need_workspace():
-    # T > 128 (multiples of 64) runs through the GEMM engine with per-tile workspace.
+    # T > 256, or 128 < T <= 256 without the fused kernel's conditions (here
+    # the fp32 master copy), runs through the GEMM engine with per-tile workspace.
     shapes = [(768, 2304)]
-    assert mm.plan_query(shapes, K=5, tile_T=256)["ws_bytes"] > mm.plan_query(shapes, K=5, tile_T=128)["ws_bytes"]
+    assert mm.plan_query(shapes, K=5, tile_T=512)["ws_bytes"] > mm.plan_query(shapes, K=5, tile_T=128)["ws_bytes"]
+    assert (mm.plan_query(shapes, K=5, tile_T=256, ns_precision="x32")["ws_bytes"] >
+            mm.plan_query(shapes, K=5, tile_T=256)["ws_bytes"])
 
 
 def test_plan_query_chunking_under_a_budget():

@@ -258,6 +258,30 @@ def test_tiled_ns_bf16_ragged(T, prec):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T", [192, 256])
+@pytest.mark.parametrize("K", [0, 1, 5])
+@pytest.mark.parametrize("shape", [(300, 700), (512, 768), (1000, 260), (300, 701)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_tiled_ns_fused_tile_sides(shape, K, T):
+    # Tiles of side 128 < T <= 256 with bf16 operands and state run on the
+    # fused 256-tile kernel: ragged edges (T = 192 pads every tile), an odd
+    # width (no 16-byte rows), K = 0 / 1 / 5, against the tiled oracle.
+    banner(f"fused tiles {shape} T={T} K={K}")
+    X = gen.store(gen.spiked_grad(*shape, 1e-3, 31 + T + K), "bf16")
+    out = host(mm.ns_orthogonalize([dev(X, torch.bfloat16)], K=K, tile_T=T)[0])
+    err = rel(out, orc.tiled_newton_schulz(X, T, K))
+    print(f"  rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_tiled_ns_fused_coefficient_table_with_cubic_stage():
+    # per-iteration table with a c = 0 (textbook cubic) stage on the fused kernel
+    banner("fused tiles coefficient table")
+    X = gen.store(gen.spiked_grad(512, 512, 1e-3, 57), "bf16")
+    tab = [(3.4445, -4.7750, 2.0315)] * 3 + [(1.5, -0.5, 0.0)] * 2
+    out = host(mm.ns_orthogonalize([dev(X, torch.bfloat16)], K=5, tile_T=256, coeffs=tab)[0])
+    assert rel(out, orc.tiled_newton_schulz(X, 256, 5, coeffs=tab)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("T", [64, 128])
 def test_tiled_ns_f32_state_bf16_operands(T):
     # fp32 input, bf16 operands: the fp32 master keeps the unrounded input.
@@ -400,11 +424,11 @@ def test_step_gpt2_full_set_bf16(prec):
         assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("T", [64, 96, 128, 256])
+@pytest.mark.parametrize("T", [64, 96, 128, 192, 256])
 def test_step_himuon_bf16(T):
-    # T <= 128: resident-tile kernel with the momentum update fused in;
-    # T = 256: GEMM engine.  Momentum must match the oracle's bf16 rounding
-    # exactly either way.
+    # T <= 128: resident-tile kernel; 128 < T <= 256: the fused 256-tile
+    # kernel; both with the momentum update and the hook's norms fused in.
+    # Momentum must match the oracle's bf16 rounding exactly either way.
     banner(f"himuon step T={T}")
     shapes = [(768, 2304), (3072, 768), (300, 700)]
     Ws, Gs, Ms = _gpt2_like(shapes, cfg=4)
