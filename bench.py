@@ -523,6 +523,10 @@ def main():
     if cmp_run is not None:
         tkey = dict(prof_key, tile=args.compare_tile)
         tbusy = _profile_doc(f"{args.workload}_T{args.compare_tile}_mfma_busy.json", tkey)
+        ttraffic = _profile_doc(f"{args.workload}_T{args.compare_tile}_hbm_traffic.json", tkey)
+        cmp_run["roofline"] = dict(cmp_run["roofline"], traffic=None)
+        if ttraffic and cmp_run["roofline"]["kernel"] in ttraffic.get("kernels", {}):
+            cmp_run["roofline"]["traffic"] = ttraffic["kernels"][cmp_run["roofline"]["kernel"]]["hbm_bytes_per_launch"]
         out["himuon"] = dict(tile_T=args.compare_tile, **cmp_run,
                              mfma_busy=tbusy["kernels"] if tbusy else None)
     if not args.no_cpu_baseline:

@@ -419,14 +419,3 @@ def adamh_step(Ws, Gs, Ms, Vs, eta, beta1, beta2, eps, t, rhos=None, hook: str =
         Us.append(U)
         flags.append(f)
     return out_w, out_m, out_v, Us, flags
-
-
-# ---------------------------------------------------------------------------
-# work counts (used by the CPU baseline and tests, not by the method)
-# ---------------------------------------------------------------------------
-def ns_dense_flops(H: int, W: int, K: int) -> int:
-    """Dense flops of K full-matrix NS iterations on an H x W matrix:
-    K (4 r^2 s + 2 r^3) with r = min, s = max ([HIMUON] abstract counts the
-    full-matrix work as O(r^2 s K))."""
-    r, s = min(H, W), max(H, W)
-    return K * (4 * r * r * s + 2 * r * r * r)
