@@ -22,15 +22,15 @@
 // which carries X from one iteration to the next.
 //
 // LDS (160 KiB = one bf16 256 x 256 matrix + two 16 KiB pieces):
-//   - the matrix region holds A, then B (both symmetric, stored from the
-//     accumulators through the transposed path), and the staging of the input
-//     and output tiles; rows of 512 B, 16-byte granules XOR-swizzled by the
-//     row, so that the fragment reads of 32 rows at one k hit distinct banks;
-//   - G1 (A = X X^T) and G3 (B X) take X from the pieces: 32-deep slices of
-//     X^T written from the registers of the waves that hold them while every
-//     wave runs the previous slice's MFMAs (double buffered).  G1's slices
-//     are [n][m] rows read with the transposing LDS read (ds_read_b64_tr_b16);
-//     G3's are [n][k] rows of 64 B read directly.
+//   - the matrix region holds X^T for G1 (A = X X^T, read with the
+//     transposing LDS read ds_read_b64_tr_b16), then A, then B (both
+//     symmetric, stored from the accumulators through the transposed path),
+//     and the staging of the input and output tiles; rows of 512 B, 16-byte
+//     granules XOR-swizzled by the row, so that the fragment reads of 32 rows
+//     at one k hit distinct banks;
+//   - G3 (B X) takes X from the pieces: 32-deep slices of X^T ([n][k] rows of
+//     64 B) written from the registers of the waves that hold them while
+//     every wave runs the previous slice's MFMAs (double buffered).
 #include <type_traits>
 
 #include "common.h"
@@ -113,8 +113,8 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   char* const sM = smem;
   char* const sP0 = smem + kMatB;
-  // reduction scratch in the second slice: it is first written by G1 after
-  // the barrier that follows every thread's read of the pre-scale sum
+  // reduction scratch in the second slice: it is first written by G3 of the
+  // first iteration, long after every thread's read of the pre-scale sum
   double* const sred = reinterpret_cast<double*>(smem + kMatB + kPieceB);
 
   const TileJob job = jobs[blockIdx.x];
@@ -134,29 +134,35 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // for thread t), M stored back, X0 staged row-major in the matrix region.
   float sq = 0.f;
   if (mt.vec) {
-    // 16 chunks of M (and G) in flight per thread: with one workgroup per
-    // CU the loads must cover HBM latency on their own
+    // batches of 8 chunks of M (and G), three batches in flight: with one
+    // workgroup per CU the loads must cover HBM latency on their own, so the
+    // next batch is issued as soon as one has been consumed
+    u32x4_t mraw[3][8], graw[3][8];
+    auto load_in = [&](int cb, u32x4_t (&mr)[8], u32x4_t (&gr)[8]) {
 #pragma unroll
-    for (int cb = 0; cb < 32; cb += 16) {
-      u32x4_t mraw[16], graw[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < 8; ++k) {
         const int row = 8 * (cb + k) + (tid >> 5), col = (tid & 31) * 8;
         const int64_t off = (row < h && col < w) ? (int64_t)row * ldm + col : 0;
-        mraw[k] = *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(tm + off));
-        if (tg) graw[k] = *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(tg + off));
+        mr[k] = *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(tm + off));
+        if (tg) gr[k] = *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(tg + off));
       }
+    };
+    load_in(0, mraw[0], graw[0]);
+    load_in(8, mraw[1], graw[1]);
+    load_in(16, mraw[2], graw[2]);
+    static_for<4>([&](auto bc) {
+      constexpr int bi = decltype(bc)::value, cb = 8 * bi, sl = bi % 3;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < 8; ++k) {
         const int row = 8 * (cb + k) + (tid >> 5), col = (tid & 31) * 8;
         const bool ok = row < h && col < w;
-        u32x4_t pk = mraw[k];
+        u32x4_t pk = mraw[sl][k];
         if (tg) {
           float x[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[2 * e] = St<bf16_t>::round(fmaf(args.beta, lo_bf(mraw[k][e]), args.gcoef * lo_bf(graw[k][e])));
-            x[2 * e + 1] = St<bf16_t>::round(fmaf(args.beta, hi_bf(mraw[k][e]), args.gcoef * hi_bf(graw[k][e])));
+            x[2 * e] = St<bf16_t>::round(fmaf(args.beta, lo_bf(mraw[sl][k][e]), args.gcoef * lo_bf(graw[sl][k][e])));
+            x[2 * e + 1] = St<bf16_t>::round(fmaf(args.beta, hi_bf(mraw[sl][k][e]), args.gcoef * hi_bf(graw[sl][k][e])));
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
@@ -170,7 +176,8 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
         }
         *reinterpret_cast<u32x4_t*>(sM + mat_off(row, col)) = pk;
       }
-    }
+      if constexpr (bi == 0) load_in(24, mraw[0], graw[0]);
+    });
   } else {
 #pragma unroll 1
     for (int c = 0; c < 32; ++c) {
@@ -222,6 +229,9 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
           xr[i][j][q] = __builtin_bit_cast(u32x2_t, v);
         }
   }
+  // every wave has its X0 before the first iteration writes X^T over the
+  // staging (a wave's quadrant of X^T covers rows another wave gathers from)
+  __syncthreads();
 
   // Accumulators are written only by MFMAs: the first k-step of a product
   // takes a zero C operand, and the seed terms (b A, a X) are added in the
@@ -236,6 +246,18 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], zero ? f32x16_t{} : acc[i][j], 0, 0, 0);
+  };
+  // the same, calling next(i) after the four MFMAs that read fa[i] have
+  // issued (a load into fa[i] may follow them)
+  auto mma16_next = [&](bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], auto zc, auto next) {
+    constexpr bool zero = decltype(zc)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], zero ? f32x16_t{} : acc[i][j], 0, 0, 0);
+      next(i);
+    }
   };
   using Z = std::true_type;
   using NZ = std::false_type;
@@ -429,38 +451,54 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
     bar();  // every wave is done reading A
 
     // ---------------- B to LDS; G3: X <- a X + B X (times sig on the first)
-    put_b(b, c);
+    // (on the first iteration B is stored times sig, which with a * sig in
+    // the update gives sig (a X0 + B X0) without scaling the accumulators)
+    const float xs = first ? (float)sig : 1.f;
+    put_b(b * xs, c * xs);
     put_g3(std::integral_constant<int, 0>{}, sP0);
     bar();
-    static_for<8>([&](auto pc) {
-      constexpr int p = decltype(pc)::value;
-      constexpr int so = (p & 1) * kPieceB;  // this slice's buffer
+    {
+      // B rows wr + 32 i + lc at k = 32 p + 16 kk + 8 lh (the A operand) do
+      // not change during G3: each slice's are loaded during the previous
+      // slice's MFMAs, row block i as soon as the MFMAs that read the old
+      // fragment i have issued; after the barrier only the slice's own
+      // fragments (rows wc + 32 j + lc at kk16 = 16 kk + 8 lh) are read.
       bf16x8_t fa[2][4], fb[2][4];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // B rows wr + 32 i + lc at k = 32 p + 16 kk + 8 lh; slice rows
-        // wc + 32 j + lc at kk16 = 16 kk + 8 lh
+      auto ld_brow = [&](int p, int kk, int i) {
         const int ln = opaque(lane), l31 = ln & 31, lhh = ln >> 5;
-        const char* pa = sM + (wr + l31) * 512 + (((4 * p + 2 * kk + lhh) ^ (l31 & 15)) << 4);
-        const char* pb = smem + so + kMatB + (wc + l31) * 64 + (((2 * kk + lhh) ^ ((l31 >> 2) & 3)) << 4);
+        fa[kk][i] = ld16(sM + (wr + l31) * 512 + (((4 * p + 2 * kk + lhh) ^ (l31 & 15)) << 4) + 16384 * i);
+      };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[kk][i] = ld16(pa + 16384 * i);
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[kk][j] = ld16(pb + 2048 * j);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      mma16(fa[0], fb[0], std::integral_constant<bool, p == 0>{});
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (p + 1 < 8) put_g3(std::integral_constant<int, p + 1>{}, sP0 + ((p + 1) & 1) * kPieceB);
-      __builtin_amdgcn_sched_barrier(0);
-      mma16(fa[1], fb[1], NZ{});
-      bar();
-    });
-    // X <- a X + B X (times sig on the first iteration), rounded to bf16 and
-    // kept in registers for the next iteration
-    auto update = [&](auto scaled) {
-      constexpr bool kScale = decltype(scaled)::value;
-      const float xs = first ? (float)sig : 1.f;
+        for (int i = 0; i < 4; ++i) ld_brow(0, kk, i);
+      static_for<8>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int so = (p & 1) * kPieceB;  // this slice's buffer
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int ln = opaque(lane), l31 = ln & 31, lhh = ln >> 5;
+          const char* pb = smem + so + kMatB + (wc + l31) * 64 + (((2 * kk + lhh) ^ ((l31 >> 2) & 3)) << 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) fb[kk][j] = ld16(pb + 2048 * j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma16_next(fa[0], fb[0], std::integral_constant<bool, p == 0>{}, [&](int i) {
+          if constexpr (p + 1 < 8) ld_brow(p + 1, 0, i);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (p + 1 < 8) put_g3(std::integral_constant<int, p + 1>{}, sP0 + ((p + 1) & 1) * kPieceB);
+        __builtin_amdgcn_sched_barrier(0);
+        mma16_next(fa[1], fb[1], NZ{}, [&](int i) {
+          if constexpr (p + 1 < 8) ld_brow(p + 1, 1, i);
+        });
+        bar();
+      });
+    }
+    // X <- (a sig) X + (sig B) X on the first iteration, a X + B X after it,
+    // rounded to bf16 and kept in registers for the next iteration
+    {
+      const float ax = a * xs;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -468,19 +506,12 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t x0 = xr[i][j][q][0], x1 = xr[i][j][q][1];
-            float v[4] = {fmaf(a, lo_bf(x0), acc[i][j][4 * q]), fmaf(a, hi_bf(x0), acc[i][j][4 * q + 1]),
-                          fmaf(a, lo_bf(x1), acc[i][j][4 * q + 2]), fmaf(a, hi_bf(x1), acc[i][j][4 * q + 3])};
-            if (kScale) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] *= xs;
-            }
+            const float v[4] = {fmaf(ax, lo_bf(x0), acc[i][j][4 * q]), fmaf(ax, hi_bf(x0), acc[i][j][4 * q + 1]),
+                                fmaf(ax, lo_bf(x1), acc[i][j][4 * q + 2]), fmaf(ax, hi_bf(x1), acc[i][j][4 * q + 3])};
             xr[i][j][q] = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             if (q == 3) __builtin_amdgcn_sched_barrier(0);
           }
-    };
-    // branch-free: a run-time branch between the scaled and unscaled forms
-    // here joins two X register states, which the compiler copies and spills
-    update(std::true_type{});
+    }
   }
   if (args.K == 0) {  // O = X0 / (||X0|| + eps)
 #pragma unroll
@@ -498,7 +529,23 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // ---- output: O (bf16) staged row-major in the matrix region (behind a
   // barrier: the last product's reads, or with K = 0 the X0 gather), then written as
   // 8-element row chunks cropped to the matrix, with ||O||^2 and the hook's
-  // <W, O>, ||W||^2 at the same positions (fp64 per thread).
+  // <W, O>, ||W||^2 at the same positions (fp64 per thread).  The W rows do
+  // not depend on the result: the first batch is loaded before the staging,
+  // and each later one while the previous batch is consumed.
+  const float* const wp = mt.w;
+  const int64_t obase = r0 * ldm + c0;
+  typedef __attribute__((address_space(4))) const f32x4_t cf4;
+  f32x4_t wv[2][8][2];
+  auto load_w = [&](int cb, f32x4_t (&d)[8][2]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = 8 * (cb + k) + (tid >> 5), col = (tid & 31) * 8;
+      const int64_t o = (row < h && col < w) ? obase + (int64_t)row * ldm + col : obase;
+      d[k][0] = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(wp + o));
+      d[k][1] = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(wp + o + 4));
+    }
+  };
+  if (mt.vec && wp != nullptr) load_w(0, wv[0]);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -515,22 +562,11 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
       }
   __syncthreads();
   double osq = 0.0, swo = 0.0, sww = 0.0;
-  const float* const wp = mt.w;
-  const int64_t obase = r0 * ldm + c0;
   if (mt.vec) {
-    // 8 chunks per batch: their W loads in flight together
-#pragma unroll
-    for (int cb = 0; cb < 32; cb += 8) {
-      f32x4_t wv[8][2];
-      if (wp != nullptr) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int row = 8 * (cb + k) + (tid >> 5), col = (tid & 31) * 8;
-          const int64_t o = (row < h && col < w) ? obase + (int64_t)row * ldm + col : obase;
-          typedef __attribute__((address_space(4))) const f32x4_t cf4;
-          wv[k][0] = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(wp + o));
-          wv[k][1] = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(wp + o + 4));
-        }
+    static_for<4>([&](auto bc) {
+      constexpr int bi = decltype(bc)::value, cb = 8 * bi, sl = bi & 1;
+      if constexpr (bi < 3) {
+        if (wp != nullptr) load_w(cb + 8, wv[sl ^ 1]);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -544,13 +580,13 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
           const double x = (double)((e & 1) ? hi_bf(pk[e >> 1]) : lo_bf(pk[e >> 1]));
           osq = fma(x, x, osq);
           if (wp != nullptr) {
-            const double wd = (double)wv[k][e >> 2][e & 3];
+            const double wd = (double)wv[sl][k][e >> 2][e & 3];
             swo = fma(wd, x, swo);
             sww = fma(wd, wd, sww);
           }
         }
       }
-    }
+    });
   } else {
 #pragma unroll 1
     for (int cch = 0; cch < 32; ++cch) {
