@@ -30,7 +30,8 @@
 // (v_mfma_f32_32x32x2_f32), accumulation is fp32.  Two main loops:
 //   - 128 x 128 tiles (4 waves, two workgroups per CU): LDS stages double
 //     buffered behind a register prefetch ring of 16-byte global loads, MFMA
-//     fragments double buffered in registers;
+//     fragments double buffered in registers (the same loop on 64 x 64 tiles
+//     for fp32 units of side <= 256, whose products are latency-bound);
 //   - 256 x 256 tiles with bf16 operands (8 waves, one workgroup per CU): an
 //     8-wave ping-pong, waves w and w + 4 alternating between reading a half
 //     stage's fragments from LDS and running its MFMAs, with the operands
@@ -1188,7 +1189,8 @@ hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, co
     if (cfg == 1) MUONH_PHASES(bf16_t, 256, 64, 4, 2);
     else MUONH_PHASES(bf16_t, 128, 64, 2, 2);
   } else {
-    MUONH_PHASES(float, 128, 32, 2, 2);
+    if (cfg == 2) MUONH_PHASES(float, 64, 32, 2, 2);
+    else MUONH_PHASES(float, 128, 32, 2, 2);
   }
 #undef MUONH_PHASES
 #undef MUONH_LAUNCH

@@ -58,7 +58,9 @@ bool tile256_enabled() {
 }
 
 int unit_gemm_cfg(int r, int op_dt, bool phase12) {
-  if (op_dt != DT_BF16) return 0;
+  // fp32 units with r <= 256 (a product of at most a few 128-tiles) run on
+  // 64-tiles: four times the workgroups for the same latency-bound work
+  if (op_dt != DT_BF16) return r <= 256 ? 2 : 0;
   static int mode = -1;
   if (mode < 0) {
     const char* e = std::getenv("MUONH_GEMM_BIG");

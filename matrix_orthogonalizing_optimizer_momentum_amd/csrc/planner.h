@@ -86,8 +86,8 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan);
 // workgroups per CU); 1 = 256 x 256 (8 waves of 64 x 128, one workgroup per
 // CU, bf16 operands): a third less LDS traffic per MFMA, for units large
 // enough to fill the chip with them.
-constexpr int kGemmCfgs = 2;
-inline int gemm_tile_side(int cfg) { return cfg == 1 ? 256 : 128; }
+constexpr int kGemmCfgs = 3;
+inline int gemm_tile_side(int cfg) { return cfg == 1 ? 256 : cfg == 2 ? 64 : 128; }
 // Configuration of a unit's G1/G2 (phase12) or G3 products.
 int unit_gemm_cfg(int r, int op_dt, bool phase12);
 
