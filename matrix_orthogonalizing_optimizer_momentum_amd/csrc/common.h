@@ -68,6 +68,36 @@ __device__ __forceinline__ void load8(const float* p, int64_t i, float (&v)[8]) 
   v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
   v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
 }
+// 8 consecutive elements held in their storage form until unpacked.  A batch
+// of them can be in flight before any value is used; a conversion right next
+// to its load (above all inside a branch) makes the compiler wait for that
+// load there, one memory round trip per chunk.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4_t q;
+  __device__ __forceinline__ void load(const bf16_t* p, int64_t i) {
+    q = *reinterpret_cast<const MUONH_GLOBAL u32x4_t*>(gmem(p + i));
+  }
+  __device__ __forceinline__ void unpack(float (&v)[8]) const {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(q[k] << 16);
+      v[2 * k + 1] = __uint_as_float(q[k] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p, int64_t i) {
+    a = *reinterpret_cast<const MUONH_GLOBAL f32x4_t*>(gmem(p + i));
+    b = *reinterpret_cast<const MUONH_GLOBAL f32x4_t*>(gmem(p + i + 4));
+  }
+  __device__ __forceinline__ void unpack(float (&v)[8]) const {
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  }
+};
+
 // 8 floats from memory the running kernel does not write, read through the
 // constant address space so the loads may be issued ahead of the kernel's
 // own stores (p + i 16-byte aligned).

@@ -44,17 +44,24 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
   const ST* __restrict__ g = reinterpret_cast<const ST*>(mm.g);
   ST* __restrict__ m = reinterpret_cast<ST*>(mm.m);
 
-  // Issue both rows' loads before any store (m is read and written).
-  float gv[2][8], mv[2][8];
+  // Issue both rows' loads before any store (m is read and written), and
+  // before any value is converted (a conversion next to its load makes the
+  // compiler wait for it there).
+  Raw8<ST> gr[2], mr[2];
   bool fast[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int64_t row = (int64_t)blk.br * 64 + rr + 32 * p;
     const int64_t col0 = (int64_t)blk.bc * 64 + cc * 8;
     fast[p] = row < H && vec && col0 + 8 <= W;
-    if (fast[p]) {
-      load8(g, row * W + col0, gv[p]);
-      if (m != nullptr) load8(m, row * W + col0, mv[p]);
+    if (fast[p]) gr[p].load(g, row * W + col0);
+  }
+  if (m != nullptr) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int64_t row = (int64_t)blk.br * 64 + rr + 32 * p;
+      const int64_t col0 = (int64_t)blk.bc * 64 + cc * 8;
+      if (fast[p]) mr[p].load(m, row * W + col0);
     }
   }
   float sq = 0.f;
@@ -67,17 +74,21 @@ __global__ __launch_bounds__(kMomThreads) void k_momentum_prep(
     // gcoef*G + beta*v (Muon explainer, code section)
     float v[8];
     if (fast[p]) {
+      float gv[8];
+      gr[p].unpack(gv);
       if (m != nullptr) {
+        float mv[8];
+        mr[p].unpack(mv);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = St<ST>::round(fmaf(beta, mv[p][k], gcoef * gv[p][k]));
+        for (int k = 0; k < 8; ++k) v[k] = St<ST>::round(fmaf(beta, mv[k], gcoef * gv[k]));
         store8(m, row * W + col0, v);
         if (nesterov) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = fmaf(beta, v[k], gcoef * gv[p][k]);
+          for (int k = 0; k < 8; ++k) v[k] = fmaf(beta, v[k], gcoef * gv[k]);
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = gv[p][k];
+        for (int k = 0; k < 8; ++k) v[k] = gv[k];
       }
     } else {
 #pragma unroll
@@ -172,6 +183,42 @@ __device__ __forceinline__ void load8_dyn(const void* p, int64_t i, int dtype, f
   else load8(reinterpret_cast<const float*>(p), i, v);
 }
 
+// The kHookPerThread elements a thread of a whole hook block owns (chunks
+// base + (c * kHookThreads + t) * 8), W (fp32) and, when used, O (run-time
+// dtype), every load issued before any value is used.
+struct HookChunks {
+  static constexpr int NC = kHookPerThread / 8;
+  Raw8<float> w[NC], of[NC];
+  Raw8<bf16_t> ob[NC];
+  __device__ __forceinline__ static int64_t at(int64_t base, int c) {
+    return base + ((int64_t)c * kHookThreads + threadIdx.x) * 8;
+  }
+  __device__ __forceinline__ void load(const float* wp, const void* op, int o_dtype, int64_t base) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) w[c].load(wp, at(base, c));
+    if (op != nullptr) {
+      if (o_dtype == DT_BF16) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) ob[c].load(reinterpret_cast<const bf16_t*>(op), at(base, c));
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) of[c].load(reinterpret_cast<const float*>(op), at(base, c));
+      }
+    }
+  }
+  __device__ __forceinline__ void get(int c, bool use_o, int o_dtype, float (&wv)[8], float (&ov)[8]) const {
+    w[c].unpack(wv);
+    if (!use_o) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ov[k] = 0.f;
+    } else if (o_dtype == DT_BF16) {
+      ob[c].unpack(ov);
+    } else {
+      of[c].unpack(ov);
+    }
+  }
+};
+
 // Coefficient applied to O in W' = W - coef * O: eta times the shape scale
 // (RadialBrake, plain update), eta / ||O|| times the step scale (Hyperball:
 // 1 or rho), eta ||W|| / ||O|| (RelativeUpdate, from pass 1's ||W||^2).
@@ -228,27 +275,40 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_reduce(
   const void* const op = MODE == kModeRel ? nullptr : hm.o;
   double s0 = 0.0, s1 = 0.0;
   const int64_t base = (int64_t)hb.blk * kHookBlockElems;
-#pragma unroll
-  for (int it = 0; it < kHookPerThread / 8; ++it) {
-    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
-    if (i >= hm.numel) break;
-    float w[8], o[8];
-    if (i + 8 <= hm.numel) {
-      load8(hm.w, i, w);
-      if (op) load8_dyn(op, i, hm.o_dtype, o);
-      else for (int k = 0; k < 8; ++k) o[k] = 0.f;
-    } else {
-      for (int k = 0; k < 8; ++k) {
-        const bool ok = i + k < hm.numel;
-        w[k] = ok ? hm.w[i + k] : 0.f;
-        o[k] = (ok && op) ? load_dyn(op, i + k, hm.o_dtype) : 0.f;
-      }
-    }
+  auto add = [&](const float (&w)[8], const float (&o)[8]) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float wp = fmaf(-coef, o[k], w[k]);
       s0 = fma((double)wp, (double)wp, s0);
       s1 = fma((double)w[k], (double)w[k], s1);
+    }
+  };
+  if (base + kHookBlockElems <= hm.numel) {  // a whole block: all loads in flight together
+    HookChunks ch;
+    ch.load(hm.w, op, hm.o_dtype, base);
+#pragma unroll
+    for (int c = 0; c < HookChunks::NC; ++c) {
+      float w[8], o[8];
+      ch.get(c, op != nullptr, hm.o_dtype, w, o);
+      add(w, o);
+    }
+  } else {
+    for (int it = 0; it < kHookPerThread / 8; ++it) {
+      const int64_t i = HookChunks::at(base, it);
+      if (i >= hm.numel) break;
+      float w[8], o[8];
+      if (i + 8 <= hm.numel) {
+        load8(hm.w, i, w);
+        if (op) load8_dyn(op, i, hm.o_dtype, o);
+        else for (int k = 0; k < 8; ++k) o[k] = 0.f;
+      } else {
+        for (int k = 0; k < 8; ++k) {
+          const bool ok = i + k < hm.numel;
+          w[k] = ok ? hm.w[i + k] : 0.f;
+          o[k] = (ok && op) ? load_dyn(op, i + k, hm.o_dtype) : 0.f;
+        }
+      }
+      add(w, o);
     }
   }
   block_partial2<kHookThreads>(s0, s1, st, hm.slot, hb.blk);
@@ -284,24 +344,8 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
   if (hb.blk == 0 && threadIdx.x == 0) hook_flags(MODE, coef, hm.o != nullptr, branch, v0, v1, flags);
   if (branch == 2) return;
   const int64_t base = (int64_t)hb.blk * kHookBlockElems;
-#pragma unroll
-  for (int it = 0; it < kHookPerThread / 8; ++it) {
-    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
-    if (i >= hm.numel) break;
-    float w[8], o[8];
-    const bool full = i + 8 <= hm.numel;
-    if (full) {
-      load8(hm.w, i, w);
-      if (hm.o && branch == 0) load8_dyn(hm.o, i, hm.o_dtype, o);
-      else for (int k = 0; k < 8; ++k) o[k] = 0.f;
-    } else {
-      for (int k = 0; k < 8; ++k) {
-        const bool ok = i + k < hm.numel;
-        w[k] = ok ? hm.w[i + k] : 0.f;
-        o[k] = (ok && hm.o && branch == 0) ? load_dyn(hm.o, i + k, hm.o_dtype) : 0.f;
-      }
-    }
-    float r[8];
+  const bool use_o = hm.o != nullptr && branch == 0;
+  auto apply = [&](const float (&w)[8], const float (&o)[8], float (&r)[8]) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (MODE == kModeNone) {
@@ -314,6 +358,37 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
         r[k] = (float)((double)base_v * scale);
       }
     }
+  };
+  if (base + kHookBlockElems <= hm.numel) {  // a whole block: all loads in flight together
+    HookChunks ch;
+    ch.load(hm.w, use_o ? hm.o : nullptr, hm.o_dtype, base);
+#pragma unroll
+    for (int c = 0; c < HookChunks::NC; ++c) {
+      float w[8], o[8], r[8];
+      ch.get(c, use_o, hm.o_dtype, w, o);
+      apply(w, o, r);
+      store8(hm.w, HookChunks::at(base, c), r);
+    }
+    return;
+  }
+  for (int it = 0; it < kHookPerThread / 8; ++it) {
+    const int64_t i = HookChunks::at(base, it);
+    if (i >= hm.numel) break;
+    float w[8], o[8];
+    const bool full = i + 8 <= hm.numel;
+    if (full) {
+      load8(hm.w, i, w);
+      if (use_o) load8_dyn(hm.o, i, hm.o_dtype, o);
+      else for (int k = 0; k < 8; ++k) o[k] = 0.f;
+    } else {
+      for (int k = 0; k < 8; ++k) {
+        const bool ok = i + k < hm.numel;
+        w[k] = ok ? hm.w[i + k] : 0.f;
+        o[k] = (ok && use_o) ? load_dyn(hm.o, i + k, hm.o_dtype) : 0.f;
+      }
+    }
+    float r[8];
+    apply(w, o, r);
     if (full) {
       store8(hm.w, i, r);
     } else {

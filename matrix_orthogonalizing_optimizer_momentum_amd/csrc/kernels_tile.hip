@@ -131,26 +131,35 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
   if (mt.vec) {
     // Whole chunks are either inside the matrix or outside it (8-aligned
     // sides and origins); outside ones load the tile origin's chunk instead
-    // (always valid) and are zeroed.
-    float mv[NCH][8], gv[NCH][8];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    // (always valid) and are zeroed.  Every chunk's loads are issued before
+    // any is converted.
+    Raw8<ST> mr[NCH], gr[NCH];
+    auto chunk_off = [&](int c) -> int64_t {
       const int ch = tid + c * kTileThreads, row = ch / CPR, col = (ch % CPR) * 8;
-      const int64_t off = (row < h && col < w) ? (int64_t)row * ldm + col : 0;
-      load8(tm, off, mv[c]);
-      if (tg) load8(tg, off, gv[c]);
+      return (row < h && col < w) ? (int64_t)row * ldm + col : 0;
+    };
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) mr[c].load(tm, chunk_off(c));
+    if (tg) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) gr[c].load(tg, chunk_off(c));
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = tid + c * kTileThreads, row = ch / CPR, col = (ch % CPR) * 8;
       const bool ok = row < h && col < w;
       float x[8];
+      mr[c].unpack(x);
+      if (tg) {
+        float gv[8];
+        gr[c].unpack(gv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = tg ? St<ST>::round(fmaf(args.beta, mv[c][e], args.gcoef * gv[c][e])) : mv[c][e];
-      if (tg && ok) store8(tm, (int64_t)row * ldm + col, x);
-      if (tg && args.nesterov) {  // NS input: the Nesterov blend of G and the updated buffer
+        for (int e = 0; e < 8; ++e) x[e] = St<ST>::round(fmaf(args.beta, x[e], args.gcoef * gv[e]));
+        if (ok) store8(tm, (int64_t)row * ldm + col, x);
+        if (args.nesterov) {  // NS input: the Nesterov blend of G and the updated buffer
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = fmaf(args.beta, x[e], args.gcoef * gv[c][e]);
+          for (int e = 0; e < 8; ++e) x[e] = fmaf(args.beta, x[e], args.gcoef * gv[e]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -362,7 +371,23 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
 
   // ---- store phase: the result staged row-major in LDS (the last update's
   // operand reads are behind a barrier), then written as 8-element chunks,
-  // cropped to the matrix; sum of squares of the stored values.
+  // cropped to the matrix; sum of squares of the stored values.  The weight
+  // rows the hook's sums need do not depend on the result: their loads are
+  // issued first.
+  const float* const wp = mt.w;
+  const int64_t obase = r0 * ldm + c0;
+  typedef __attribute__((address_space(4))) const f32x4_t cf4;
+  f32x4_t wv[NCH][2];
+  const bool wvec = mt.vec && wp != nullptr;
+  if (wvec) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * kTileThreads, row = ch / CPR, col = (ch % CPR) * 8;
+      const int64_t o = (row < h && col < w) ? obase + (int64_t)row * ldm + col : obase;
+      wv[c][0] = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(wp + o));
+      wv[c][1] = *reinterpret_cast<cf4*>(reinterpret_cast<uintptr_t>(wp + o + 4));
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -374,8 +399,6 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
   // ||W||^2 at the same positions (fp64 per thread: the hook forms
   // ||W - c O||^2 from them, which must resolve an exactly cancelling step).
   double osq = 0.0, swo = 0.0, sww = 0.0;
-  const float* const wp = mt.w;
-  const int64_t obase = r0 * ldm + c0;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int ch = tid + c * kTileThreads, row = ch / CPR, col = (ch % CPR) * 8;
@@ -393,13 +416,12 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
       else store8(reinterpret_cast<float*>(mt.out), o, x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) osq = fma((double)x[e], (double)x[e], osq);
-      if (wp != nullptr) {
-        float wv[8];
-        load8_ro(wp, o, wv);
+      if (wvec) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          swo = fma((double)wv[e], (double)x[e], swo);
-          sww = fma((double)wv[e], (double)wv[e], sww);
+          const double wd = (double)wv[c][e >> 2][e & 3];
+          swo = fma(wd, (double)x[e], swo);
+          sww = fma(wd, wd, sww);
         }
       }
     } else {
