@@ -95,12 +95,14 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
   plan = Plan();
   const int n = cfg.n;
   plan.mats.resize(n);
-  bool all_engine = true;  // every matrix on the GEMM engine (full NS, or tiles above the resident size)
+  bool all_engine = true;    // every matrix on the GEMM engine (full NS, or tiles above the resident size)
+  bool all_resident = true;  // every matrix on a resident-tile kernel
   for (int i = 0; i < n; ++i) {
     MatPlan& m = plan.mats[i];
     const int T = mat_tile(cfg, i);
     m.T = no_ns(cfg.kind) ? 0 : T;
     all_engine = all_engine && !resident_tile(cfg, m.T);
+    all_resident = all_resident && resident_tile(cfg, m.T);
     m.H = shapes[2 * i];
     m.W = shapes[2 * i + 1];
     if (m.H < 1 || m.W < 1 || m.H > (int64_t)1 << 30 || m.W > (int64_t)1 << 30) return MUONH_EINVAL;
@@ -179,12 +181,17 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
   }
   plan.chunks.push_back({m0, n, acc, 0});
   for (auto& c : plan.chunks) plan.ws_bytes = std::max(plan.ws_bytes, c.ws_bytes);
-  // Automatic choice: two lanes, except for Newton-Schulz on the GEMM engine
-  // (full matrices, or tiles above the resident size) with a long iteration,
-  // where launch gaps are negligible and the lanes' large products only
-  // contend for the caches (measured slower: 1.2B set full, 8B set at T = 256).
+  // Automatic choice: two lanes, except (one lane) for Newton-Schulz on the
+  // GEMM engine (full matrices, or tiles above the resident size) with a long
+  // iteration, where launch gaps are negligible and the lanes' large products
+  // only contend for the caches (measured slower: 1.2B set full), and when
+  // every matrix runs on a resident-tile kernel: one launch per lane has no
+  // gaps to fill, and two concurrent tile launches each leave a partial last
+  // round (GPT-2-small set at T = 64 / 128 / 256: one lane 1% / 3% / 2%
+  // faster).
   const double iter_flops = plan.ns_flops / std::max(cfg.K, 1);
-  const int want = cfg.lanes > 0 ? cfg.lanes : (all_engine && iter_flops > kAutoLaneIterFlops ? 1 : 2);
+  const bool one = all_resident || (all_engine && iter_flops > kAutoLaneIterFlops);
+  const int want = cfg.lanes > 0 ? cfg.lanes : (one ? 1 : 2);
   const int L = std::min(want, n);
   if (plan.chunks.size() == 1 && L >= 2 && !no_ns(cfg.kind)) {
     // Lanes: cut the set into L runs of matrices whose Newton-Schulz work is

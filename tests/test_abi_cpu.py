@@ -118,16 +118,19 @@ def test_lanes_share_one_chunk_workspace():
 
 def test_automatic_lanes_follow_iteration_work():
     # Two lanes, but one for NS on the GEMM engine (full matrices, or tiles
-    # above the resident sizes) whose iteration exceeds 2e12 flops.
+    # above the resident sizes) whose iteration exceeds 2e12 flops, and one
+    # when every matrix runs as resident tiles.
     small = [(1024, 1024)] * 4   # 4 * 6 * 1024^3 flops per iteration
     big = [(8192, 8192)] * 2     # 2 * 6 * 8192^3 > 2e12
     assert mm.plan_query(small, K=5)["lanes"] == 2
     assert mm.plan_query(big, K=5)["lanes"] == 1
-    assert mm.plan_query(big, K=5, tile_T=128)["lanes"] == 2   # resident tiles
+    assert mm.plan_query(big, K=5, tile_T=128)["lanes"] == 1   # resident tiles
+    assert mm.plan_query(small, K=5, tile_T=64)["lanes"] == 1
     huge = [(16384, 16384)] * 8  # 8 * 4096 tiles of 256^2: 3.3e12 flops per iteration
-    # bf16 tiles of 256 run fused (resident): two lanes; with the fp32 master
-    # copy (X32) they go through the GEMM engine: one lane
-    assert mm.plan_query(huge, K=5, tile_T=256, workspace_limit=1 << 40)["lanes"] == 2
+    # bf16 tiles of 256 run fused (resident): one lane; with the fp32 master
+    # copy (X32) they go through the GEMM engine: one lane for this iteration
+    # size, two for a small one
+    assert mm.plan_query(huge, K=5, tile_T=256, workspace_limit=1 << 40)["lanes"] == 1
     assert mm.plan_query(huge, K=5, tile_T=256, workspace_limit=1 << 40, ns_precision="x32")["lanes"] == 1
     assert mm.plan_query(big, K=5, tile_T=256, workspace_limit=1 << 40, ns_precision="x32")["lanes"] == 2  # 2.1e11
     assert mm.plan_query(big, K=5, lanes=2)["lanes"] == 2
