@@ -419,26 +419,7 @@ __global__ __launch_bounds__(kHookThreads) void k_adam_moments(
   const float c1 = 1.f - a.b1, c2 = 1.f - a.b2;
   double s_uu = 0.0, s_wu = 0.0, s_ww = 0.0;
   const int64_t base = (int64_t)hb.blk * kHookBlockElems;
-#pragma unroll
-  for (int it = 0; it < kHookPerThread / 8; ++it) {
-    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
-    if (i >= hm.numel) break;
-    const bool full = i + 8 <= hm.numel;
-    float gv[8], m[8], v[8], w[8];
-    if (full) {
-      load8(g, i, gv);
-      load8(hm.am, i, m);
-      load8(hm.av, i, v);
-      if (SUMS) load8(hm.w, i, w);
-    } else {
-      for (int k = 0; k < 8; ++k) {
-        const bool ok = i + k < hm.numel;
-        gv[k] = ok ? load_dyn(g, i + k, hm.o_dtype) : 0.f;
-        m[k] = ok ? hm.am[i + k] : 0.f;
-        v[k] = ok ? hm.av[i + k] : 0.f;
-        w[k] = (ok && SUMS) ? hm.w[i + k] : 0.f;
-      }
-    }
+  auto update = [&](float (&gv)[8], float (&m)[8], float (&v)[8], const float (&w)[8]) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       m[k] = fmaf(a.b1, m[k], c1 * gv[k]);
@@ -450,12 +431,61 @@ __global__ __launch_bounds__(kHookThreads) void k_adam_moments(
         s_ww = fma(wd, wd, s_ww);
       }
     }
-    if (full) {
+  };
+  constexpr int NC = kHookPerThread / 8;
+  if (base + kHookBlockElems <= hm.numel) {  // a whole block: every chunk's loads in flight together
+    Raw8<GT> gr[NC];
+    Raw8<float> mr[NC], vr[NC], wr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int64_t i = HookChunks::at(base, c);
+      gr[c].load(g, i);
+      mr[c].load(hm.am, i);
+      vr[c].load(hm.av, i);
+      if (SUMS) wr[c].load(hm.w, i);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int64_t i = HookChunks::at(base, c);
+      float gv[8], m[8], v[8], w[8];
+      gr[c].unpack(gv);
+      mr[c].unpack(m);
+      vr[c].unpack(v);
+      if (SUMS) wr[c].unpack(w);
+      else for (int k = 0; k < 8; ++k) w[k] = 0.f;
+      update(gv, m, v, w);
       store8(hm.am, i, m);
       store8(hm.av, i, v);
-    } else {
-      for (int k = 0; k < 8; ++k)
-        if (i + k < hm.numel) { hm.am[i + k] = m[k]; hm.av[i + k] = v[k]; }
+    }
+  } else {
+    for (int it = 0; it < NC; ++it) {
+      const int64_t i = HookChunks::at(base, it);
+      if (i >= hm.numel) break;
+      const bool full = i + 8 <= hm.numel;
+      float gv[8], m[8], v[8], w[8];
+      if (full) {
+        load8(g, i, gv);
+        load8(hm.am, i, m);
+        load8(hm.av, i, v);
+        if (SUMS) load8(hm.w, i, w);
+        else for (int k = 0; k < 8; ++k) w[k] = 0.f;
+      } else {
+        for (int k = 0; k < 8; ++k) {
+          const bool ok = i + k < hm.numel;
+          gv[k] = ok ? load_dyn(g, i + k, hm.o_dtype) : 0.f;
+          m[k] = ok ? hm.am[i + k] : 0.f;
+          v[k] = ok ? hm.av[i + k] : 0.f;
+          w[k] = (ok && SUMS) ? hm.w[i + k] : 0.f;
+        }
+      }
+      update(gv, m, v, w);
+      if (full) {
+        store8(hm.am, i, m);
+        store8(hm.av, i, v);
+      } else {
+        for (int k = 0; k < 8; ++k)
+          if (i + k < hm.numel) { hm.am[i + k] = m[k]; hm.av[i + k] = v[k]; }
+      }
     }
   }
   if (!SUMS) return;
@@ -502,9 +532,43 @@ __global__ __launch_bounds__(kHookThreads) void k_adam_write(
   if (hb.blk == 0 && threadIdx.x == 0) hook_flags(MODE, coef, true, dec.branch, v0, v1, flags);
   if (dec.branch == 2) return;
   const int64_t base = (int64_t)hb.blk * kHookBlockElems;
+  auto apply = [&](const float (&w)[8], const float (&m)[8], const float (&v)[8], float (&r)[8]) {
 #pragma unroll
-  for (int it = 0; it < kHookPerThread / 8; ++it) {
-    const int64_t i = base + ((int64_t)it * kHookThreads + threadIdx.x) * 8;
+    for (int k = 0; k < 8; ++k) {
+      const float u = adam_u(m[k], v[k], a);
+      if (MODE == kModeNone) {
+        r[k] = fmaf(-coef, u, w[k] * decay);  // AdamW: decoupled decay, then W - eta U
+      } else if (MODE == kModeRel) {
+        r[k] = fmaf(-coef, u, w[k]);
+      } else {
+        const float base_v = (dec.branch == 0) ? fmaf(-coef, u, w[k]) : w[k];
+        r[k] = (float)((double)base_v * dec.scale);
+      }
+    }
+  };
+  constexpr int NC = kHookPerThread / 8;
+  if (base + kHookBlockElems <= hm.numel) {  // a whole block: every chunk's loads in flight together
+    Raw8<float> wr[NC], mr[NC], vr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int64_t i = HookChunks::at(base, c);
+      wr[c].load(hm.w, i);
+      mr[c].load(hm.am, i);
+      vr[c].load(hm.av, i);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float w[8], m[8], v[8], r[8];
+      wr[c].unpack(w);
+      mr[c].unpack(m);
+      vr[c].unpack(v);
+      apply(w, m, v, r);
+      store8(hm.w, HookChunks::at(base, c), r);
+    }
+    return;
+  }
+  for (int it = 0; it < NC; ++it) {
+    const int64_t i = HookChunks::at(base, it);
     if (i >= hm.numel) break;
     const bool full = i + 8 <= hm.numel;
     float w[8], m[8], v[8];
@@ -521,18 +585,7 @@ __global__ __launch_bounds__(kHookThreads) void k_adam_write(
       }
     }
     float r[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float u = adam_u(m[k], v[k], a);
-      if (MODE == kModeNone) {
-        r[k] = fmaf(-coef, u, w[k] * decay);  // AdamW: decoupled decay, then W - eta U
-      } else if (MODE == kModeRel) {
-        r[k] = fmaf(-coef, u, w[k]);
-      } else {
-        const float base_v = (dec.branch == 0) ? fmaf(-coef, u, w[k]) : w[k];
-        r[k] = (float)((double)base_v * dec.scale);
-      }
-    }
+    apply(w, m, v, r);
     if (full) {
       store8(hm.w, i, r);
     } else {
