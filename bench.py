@@ -438,9 +438,9 @@ def main():
         args.ws_limit_mib = DENSE8B_WS_MIB if big else 0
     if args.grad_sets is None:
         args.grad_sets = 2 if big else 4
-    if args.graph and args.grad_sets > 8:
-        raise SystemExit("--graph captures one step per gradient set and the library caches 8 call plans: "
-                         "use --grad-sets 8 or fewer")
+    if args.graph and args.grad_sets > 32:
+        raise SystemExit("--graph captures one step per gradient set and the library caches 32 call plans: "
+                         "use --grad-sets 32 or fewer")
     if args.graph and args.optimizer == "adamh":
         raise SystemExit("--graph with --optimizer adamh would replay one fixed Adam step count "
                          "(bias correction); not supported")
