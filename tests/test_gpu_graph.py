@@ -29,6 +29,8 @@ CASES = {
     # resident tiles (Hierarchical Muon, T = 64) with RadialBrake
     "tiles64-radial-brake": dict(shapes=[(300, 700), (256, 130)], state=torch.bfloat16,
                                  kw=dict(tile_T=64, hook="radial_brake")),
+    # the fused 256-tile kernel (T = 256, ragged tiles among them)
+    "tiles256-fused": dict(shapes=[(768, 768), (300, 700)], state=torch.bfloat16, kw=dict(tile_T=256)),
 }
 
 

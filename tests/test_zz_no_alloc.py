@@ -31,7 +31,7 @@ def _run(shapes, seed, noalloc, **kw):
     return [t.cpu() for t in w], [t.cpu() for t in m]
 
 
-@pytest.mark.parametrize("tile", [0, 64])
+@pytest.mark.parametrize("tile", [0, 64, 256])
 def test_noalloc_step_matches_muonh_step_twice(tile):
     # first call: three matrices (a ragged side among them); second call: a
     # smaller single matrix, reusing the scratch the first one left behind
