@@ -85,10 +85,11 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 }  // namespace
 
 // TP: padded tile side (64 or 128).  ST: momentum / input storage type,
-// OT: Newton-Schulz operand type.  With bf16 operands two workgroups fit one
+// OT: Newton-Schulz operand type; FOLD: X rounded to bf16 after every update
+// (bf16 operands without the fp32 master copy).  With bf16 operands two workgroups fit one
 // CU's LDS, so registers are capped for two waves per SIMD; a 128-side fp32
 // tile takes most of the LDS on its own.
-template <typename ST, typename OT, int TP>
+template <typename ST, typename OT, int TP, bool FOLD>
 __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(sizeof(OT) == 2 ? 2 : 1)))
 void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ jobs, TileArgs args) {
   using Op = TileOp<OT>;
@@ -240,6 +241,8 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
   constexpr int NK = TP / Op::KSTEP;
   static_assert(NK % 2 == 0, "k-steps come in pairs");
   using Frag = typename std::conditional<sizeof(OT) == 2, bf16x8_t, float>::type;
+  // The first k-step takes a zero C operand (the accumulators need no
+  // clearing), so a product starts from zero.
   auto product = [&](const OT* sp, const OT* sq_, bool q_kn) {
     const int kl = (lane >> 5) * (Op::KSTEP / 2);
     const OT* pa = sp + (wr + lc) * LD + kl;
@@ -259,34 +262,45 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
         else fb[buf][j] = q_kn ? pt[k * LD + j * 32] : pb[j * 32 * LD + k];
       }
     };
-    auto mma = [&](int buf) {
+    auto mma = [&](int buf, auto zc) {
+      constexpr bool zero = decltype(zc)::value;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < MI; ++j) {
+          const f32x16_t c_in = zero ? f32x16_t{} : acc[i][j];
           if constexpr (sizeof(OT) == 2)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], c_in, 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[buf][i], fb[buf][j], c_in, 0, 0, 0);
         }
     };
     load(0, 0);
+    load(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, min(2, NK - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1, std::false_type{});
+    __builtin_amdgcn_sched_barrier(0);
     constexpr int kUnroll = sizeof(OT) == 2 ? NK / 2 : 4;
 #pragma unroll kUnroll
-    for (int ks = 0; ks < NK; ks += 2) {
+    for (int ks = 2; ks < NK; ks += 2) {
       load(1, ks + 1);
       __builtin_amdgcn_sched_barrier(0);
-      mma(0);
+      mma(0, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       load(0, min(ks + 2, NK - 1));  // the last one re-reads a valid step, unused
       __builtin_amdgcn_sched_barrier(0);
-      mma(1);
+      mma(1, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Symmetric result (A or B) = acc * sc into sAB through the packed
+  // Symmetric result (A, times sc when scaled) into sAB through the packed
   // transposed path: sAB[col][row .. row+3].
-  auto store_sym = [&](float sc) {
+  auto store_a = [&](auto scaled, float sc) {
+    constexpr bool kScale = decltype(scaled)::value;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -294,53 +308,54 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = wr + i * 32 + acc_row(4 * q, lane), col = wc + j * 32 + lc;
-          Op::put4(&sAB[col * LD + row], acc[i][j][4 * q] * sc, acc[i][j][4 * q + 1] * sc,
-                   acc[i][j][4 * q + 2] * sc, acc[i][j][4 * q + 3] * sc);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = kScale ? acc[i][j][4 * q + e] * sc : acc[i][j][4 * q + e];
+          Op::put4(&sAB[col * LD + row], v[0], v[1], v[2], v[3]);
+        }
+  };
+  // B = c A A + b A in place of A: each lane reads back the A values at the
+  // very positions it then overwrites (c A A is in the accumulators).
+  auto store_b = [&](float b, float c) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < MI; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = wr + i * 32 + acc_row(4 * q, lane), col = wc + j * 32 + lc;
+          float av[4], v[4];
+          Op::get4(&sAB[col * LD + row], av);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = fmaf(c, acc[i][j][4 * q + e], b * av[e]);
+          Op::put4(&sAB[col * LD + row], v[0], v[1], v[2], v[3]);
         }
   };
 
-  for (int it = 0; it < args.K; ++it) {
+  // One iteration; the first (FIRST) folds the pre-scale: A = sig^2 X0 X0^T
+  // and X1 = sig (a X0 + B X0).  It is instantiated apart from the others, so
+  // the later iterations carry no scale factors or run-time selects.
+  auto iterate = [&](auto first_c, int it) {
+    constexpr bool FIRST = decltype(first_c)::value;
     const float a = args.abc[it][0], b = args.abc[it][1], c = args.abc[it][2];
-    const bool first = it == 0;
-    // G1: A = X X^T (times sig^2 on the first iteration: X0 is unscaled)
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < MI; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    // G1: A = X X^T
     product(sX, sX, false);
     __syncthreads();  // bf16: every wave is done reading X before A overwrites it
-    store_sym(first ? (float)(sig * sig) : 1.f);
+    store_a(std::integral_constant<bool, FIRST>{}, (float)(sig * sig));
     __syncthreads();
-    // G2: B = b A + c A A, as c (A A + (b/c) A) with the accumulator seeded
-    // from A; c == 0 leaves B = b A.
-    {
-      const float seed = c != 0.f ? b / c : b;
+    // G2: B = b A + c A A (c == 0: B = b A, no product)
+    if (c != 0.f) {
+      product(sAB, sAB, false);
+    } else {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < MI; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = wr + i * 32 + acc_row(4 * q, lane), col = wc + j * 32 + lc;
-            float av[4];
-            Op::get4(&sAB[col * LD + row], av);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = seed * av[e];
-          }
+        for (int j = 0; j < MI; ++j) acc[i][j] = f32x16_t{};
     }
-    if (c != 0.f) product(sAB, sAB, false);
     __syncthreads();  // every wave is done reading A
-    store_sym(c != 0.f ? c : 1.f);
+    store_b(b, c);
     __syncthreads();
-    // G3: X <- a X + B X, seeded with a X from the fp32 master
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < MI; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = a * x32[i][j][v];
+    // G3: B X; the update adds a X from the fp32 master
     if constexpr (kXT) product(sAB, sT, false);
     else product(sAB, sX, true);
     __syncthreads();  // every wave is done reading B, X and X^T
@@ -350,15 +365,19 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
       for (int j = 0; j < MI; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float t = acc[i][j][v];
-          if (first) t = (float)((double)t * sig);
-          if (args.fold) t = bf2f(f2bf(t));
+          float t = fmaf(a, x32[i][j][v], acc[i][j][v]);
+          if constexpr (FIRST) t = (float)((double)t * sig);
+          if constexpr (FOLD) t = bf2f(f2bf(t));
           x32[i][j][v] = t;
         }
     if (it + 1 < args.K) {
       store_x();
       __syncthreads();
     }
+  };
+  if (args.K > 0) {
+    iterate(std::true_type{}, 0);
+    for (int it = 1; it < args.K; ++it) iterate(std::false_type{}, it);
   }
   if (args.K == 0) {  // O = X0 / (||X0|| + eps)
 #pragma unroll
@@ -443,10 +462,16 @@ void k_tile_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ job
 }
 
 namespace {
+template <typename ST, typename OT, bool FOLD>
+void launch_tile_f(int TP, dim3 grid, const TileMat* mats, const TileJob* jobs, const TileArgs& args, hipStream_t s) {
+  if (TP == 64) hipLaunchKernelGGL((k_tile_ns<ST, OT, 64, FOLD>), grid, dim3(kTileThreads), 0, s, mats, jobs, args);
+  else hipLaunchKernelGGL((k_tile_ns<ST, OT, 128, FOLD>), grid, dim3(kTileThreads), 0, s, mats, jobs, args);
+}
 template <typename ST, typename OT>
 void launch_tile_t(int TP, dim3 grid, const TileMat* mats, const TileJob* jobs, const TileArgs& args, hipStream_t s) {
-  if (TP == 64) hipLaunchKernelGGL((k_tile_ns<ST, OT, 64>), grid, dim3(kTileThreads), 0, s, mats, jobs, args);
-  else hipLaunchKernelGGL((k_tile_ns<ST, OT, 128>), grid, dim3(kTileThreads), 0, s, mats, jobs, args);
+  // fp32 operands never fold (the master is the operand)
+  if (sizeof(OT) == 2 && args.fold) launch_tile_f<ST, OT, sizeof(OT) == 2>(TP, grid, mats, jobs, args, s);
+  else launch_tile_f<ST, OT, false>(TP, grid, mats, jobs, args, s);
 }
 }  // namespace
 
