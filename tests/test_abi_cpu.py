@@ -260,6 +260,16 @@ def test_plan_query_gemm_engine_tiles_need_workspace():
             mm.plan_query(shapes, K=5, tile_T=256)["ws_bytes"])
 
 
+def test_small_fp32_units_run_on_64_tiles():
+    # fp32 operands with r <= 256 take 64 x 64 output tiles: upper tiles of
+    # G1 and G2 (4 * 5 / 2 each) plus all 16 of G3 at 256 x 256; bf16 and
+    # larger fp32 units keep 128-tiles (3 + 3 + 4 at 256 x 256).
+    assert mm.plan_query([(256, 256)], K=5, ns_dtype="f32")["jobs_per_iter"] == 10 + 10 + 16
+    assert mm.plan_query([(256, 256)], K=5, ns_dtype="bf16")["jobs_per_iter"] == 3 + 3 + 4
+    assert mm.plan_query([(64, 128)], K=5, ns_dtype="f32")["jobs_per_iter"] == 1 + 1 + 2
+    assert mm.plan_query([(384, 384)], K=5, ns_dtype="f32")["jobs_per_iter"] == 6 + 6 + 9
+
+
 def test_plan_query_chunking_under_a_budget():
     shapes = gen.gpt2_small_shapes()
     one = mm.plan_query(shapes[:1], K=5)["ws_bytes"]
