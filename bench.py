@@ -428,7 +428,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the step: this build runs on a single GPU "
+        print("bench.py measures one GPU's share of the step: the library runs on a single GPU "
               "(no collectives); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     big = args.workload == "dense8b"

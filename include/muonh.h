@@ -93,7 +93,7 @@ enum {
   MUONH_EINVAL = -1,   /* invalid argument (null pointer, bad size, bad scalar, bad dtype) */
   MUONH_ENOMEM = -2,   /* workspace for one matrix exceeds workspace_limit, or allocation failed */
   MUONH_EHIP = -3,     /* a HIP runtime call or kernel launch failed */
-  MUONH_ENOTIMPL = -4  /* valid request this build does not implement */
+  MUONH_ENOTIMPL = -4  /* valid request the library does not implement */
 };
 
 /* element types */

@@ -1057,7 +1057,7 @@ const char* muonh_strerror(int code) {
     case MUONH_EINVAL: return "invalid argument";
     case MUONH_ENOMEM: return "workspace limit exceeded or device allocation failed";
     case MUONH_EHIP: return "HIP runtime or kernel launch error";
-    case MUONH_ENOTIMPL: return "not implemented in this build";
+    case MUONH_ENOTIMPL: return "not implemented by this library";
     default: return "unknown error";
   }
 }
