@@ -1013,6 +1013,51 @@ def test_ns_full_size_spiked_vs_oracle(shape):
     assert err <= TOL["bf16"]
 
 
+def test_step_full_size_8b_himuon_t256():
+    # The 8B-shaped HiMuon step as the benchmark times it (tile_T = 256, bf16
+    # state and operands: the fused 256-tile kernel), on an up/gate-shaped
+    # and a down-shaped matrix: the bf16 momentum bit for bit against the
+    # oracle's rounding; the orthogonalized update on sampled tiles against
+    # the oracle's Newton-Schulz of the same tile (all 1792 tiles through the
+    # oracle would take minutes); the Hyperball update recomputed in fp64 from
+    # the GPU's own O, and the radius.
+    banner("full-size HiMuon T=256 step 4096x14336 + 14336x4096")
+    shapes = [(4096, 14336), (14336, 4096)]
+    T, eta, beta = 256, 0.02, np.float32(0.95)
+    rng = np.random.default_rng(8)
+    for i, (H, W) in enumerate(shapes):
+        W0 = gen.gaussian((H, W), 0.02, 300 + i)
+        G = gen.store(gen.spiked_grad(H, W, 1e-3, 400 + i), "bf16")
+        M0 = gen.store(gen.gaussian((H, W), 1e-3, 500 + i), "bf16")
+        rho = np.float32(np.linalg.norm(W0.astype(np.float64)))
+        w, g, m = dev(W0), dev(G, torch.bfloat16), dev(M0, torch.bfloat16)
+        mm.muonh_step([w], [g], [m], eta=0.02, beta=float(beta), K=5, rho=[float(rho)], tile_T=T)
+        torch.cuda.synchronize()
+        M1 = orc.round_to_bf16(orc.momentum_update(M0, G, beta))
+        m_gpu = host(m)
+        assert np.array_equal(m_gpu, M1), "momentum differs from the oracle's bf16 rounding"
+        # O of the step's input (the new momentum) through the same kernel
+        O = host(mm.ns_orthogonalize([m], K=5, tile_T=T)[0])
+        worst = 0.0
+        for _ in range(6):
+            a, b = int(rng.integers(0, H // T)), int(rng.integers(0, W // T))
+            tile = m_gpu[a * T:(a + 1) * T, b * T:(b + 1) * T]
+            worst = max(worst, rel(O[a * T:(a + 1) * T, b * T:(b + 1) * T], orc.newton_schulz(tile, 5)))
+        print(f"  matrix {i} {(H, W)} worst sampled-tile NS rel err {worst:.3e}")
+        assert worst <= TOL["bf16"]
+        # Hyperball on the full matrix with that O, in fp64
+        W_ref, _ = orc.hyperball(W0, O, eta, rho)
+        w_gpu = host(w)
+        err = rel(w_gpu - W0, W_ref - W0)
+        print(f"  step rel err against fp64 Hyperball of the GPU's O {err:.3e}")
+        # fp32 master weights: two fp32 roundings of W (about 6e-8 of rho each)
+        # against a step of length eta
+        assert err <= 2e-3
+        assert abs(np.linalg.norm(w_gpu) / rho - 1) <= 1e-5
+        del w, g, m
+        torch.cuda.empty_cache()
+
+
 def test_step_full_size_8b_radius():
     # one 8B-shaped step through the 256-tile engine: the Hyperball invariant
     # holds at any size
