@@ -151,8 +151,10 @@ typedef struct muonh_opts {
                                    the update (decoupled); finite, >= 0; default 0 */
   int          lanes;           /* concurrent lanes, 1..4; 0 = automatic: 2, but 1 when every
                                    matrix runs its Newton-Schulz as products of whole
-                                   matrices or of tiles above 128 and one iteration over the
-                                   set exceeds 2e12 flops (long products gain nothing from lanes).
+                                   matrices or of tiles on the GEMM engine and one iteration
+                                   over the set exceeds 2e12 flops (long products gain
+                                   nothing from lanes), and 1 when every matrix runs on a
+                                   resident-tile kernel (one launch per lane, nothing to fill).
                                    A call over
                                    two or more matrices that fit one workspace chunk is cut
                                    into that many runs of matrices, lane 0 on opts->stream and
