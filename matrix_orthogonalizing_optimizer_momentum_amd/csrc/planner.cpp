@@ -378,8 +378,20 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
       // epilogue mirrors the off-diagonal ones.
       for (int tm = 0; tm < n12; ++tm)
         for (int tn = tm; tn < n12; ++tn) t.g12_jobs[gc12].push_back({uid, tm, tn, u.ld_r / 64});
-      for (int tn = 0; tn < g3c; ++tn)
-        for (int tm = 0; tm < g3r; ++tm) t.g3_jobs[gc3].push_back({uid, tm, tn, u.ld_r / 64});
+      // G3 jobs in column order while a column has at most 8 tiles; taller
+      // units go in blocks of 4 tile rows x 8 tile columns, so the 32
+      // workgroups one XCD runs together (its run of the job list) share
+      // 4 panels of B and 8 of X^T, against 16 + 2 in column order (r = 4096:
+      // 3% less G3 time; at 8 rows both orders touch 12 panels and column
+      // order measured no slower).
+      {
+        const int br = g3r <= 8 ? g3r : 4, bc = 32 / br;
+        for (int tn0 = 0; tn0 < g3c; tn0 += bc)
+          for (int tm0 = 0; tm0 < g3r; tm0 += br)
+            for (int tn = tn0; tn < std::min(tn0 + bc, g3c); ++tn)
+              for (int tm = tm0; tm < std::min(tm0 + br, g3r); ++tm)
+                t.g3_jobs[gc3].push_back({uid, tm, tn, u.ld_r / 64});
+      }
       const double r = (double)std::min(h, w), s = (double)std::max(h, w);
       t.flops_g1[gc12] += 2.0 * r * r * s;
       t.flops_g2[gc12] += 2.0 * r * r * r;
