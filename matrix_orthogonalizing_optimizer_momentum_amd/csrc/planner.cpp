@@ -165,21 +165,41 @@ int make_plan(const int64_t* shapes, const Cfg& cfg, Plan& plan) {
     if (cfg.kind == CALL_STEP) plan.stream_bytes += (double)numel * (3 * sb + hook1 + (4 + ob + 4));
     else plan.stream_bytes += (double)numel * (sb + sb);  // NS: read input, write output
   }
-  // chunks
+  // chunks: the fewest runs of consecutive matrices whose workspace fits the
+  // limit (greedy packing), then the same count re-cut at the smallest
+  // per-chunk cap that still packs into it, so chunks come out about equal
+  // (8B-shaped set, 16 GiB: four chunks of eight layers, not three of ten and
+  // a last one of two), each launch as full as the others.
   const int64_t limit = (int64_t)cfg.ws_limit;
-  int m0 = 0;
-  int64_t acc = 0;
+  int64_t biggest = 0;
   for (int i = 0; i < n; ++i) {
-    const int64_t b = plan.mats[i].ws_bytes;
-    if (b > limit) return MUONH_ENOMEM;
-    if (acc + b > limit && i > m0) {
-      plan.chunks.push_back({m0, i, acc, 0});
-      m0 = i;
-      acc = 0;
-    }
-    acc += b;
+    if (plan.mats[i].ws_bytes > limit) return MUONH_ENOMEM;
+    biggest = std::max(biggest, plan.mats[i].ws_bytes);
   }
-  plan.chunks.push_back({m0, n, acc, 0});
+  auto pack = [&](int64_t cap, bool emit) {
+    int m0 = 0, count = 1;
+    int64_t acc = 0;
+    for (int i = 0; i < n; ++i) {
+      const int64_t b = plan.mats[i].ws_bytes;
+      if (acc + b > cap && i > m0) {
+        if (emit) plan.chunks.push_back({m0, i, acc, 0});
+        m0 = i;
+        acc = 0;
+        ++count;
+      }
+      acc += b;
+    }
+    if (emit) plan.chunks.push_back({m0, n, acc, 0});
+    return count;
+  };
+  const int nchunks = pack(limit, false);
+  int64_t lo = biggest, hi = limit;  // pack(hi) <= nchunks always holds
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (pack(mid, false) <= nchunks) hi = mid;
+    else lo = mid + 1;
+  }
+  pack(hi, true);
   for (auto& c : plan.chunks) plan.ws_bytes = std::max(plan.ws_bytes, c.ws_bytes);
   // Automatic choice: two lanes, except (one lane) for Newton-Schulz on the
   // GEMM engine (full matrices, or tiles above the resident size) with a long

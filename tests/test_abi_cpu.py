@@ -280,6 +280,56 @@ def test_plan_query_chunking_under_a_budget():
     assert e.value.code == mm.MUONH_ENOMEM
 
 
+def _min_max_partition(b, parts):
+    """Smallest achievable largest sum when b is cut into `parts` runs (DP)."""
+    n = len(b)
+    pre = [0]
+    for v in b:
+        pre.append(pre[-1] + v)
+    INF = float("inf")
+    best = [[INF] * (n + 1) for _ in range(parts + 1)]
+    best[0][0] = 0
+    for k in range(1, parts + 1):
+        for j in range(1, n + 1):
+            for i in range(k - 1, j):
+                best[k][j] = min(best[k][j], max(best[k - 1][i], pre[j] - pre[i]))
+    return best[parts][n]
+
+
+def _greedy_count(b, limit):
+    count, acc = 1, 0
+    for v in b:
+        if acc + v > limit and acc > 0:
+            count, acc = count + 1, 0
+        acc += v
+    return count
+
+
+def test_chunks_are_fewest_and_balanced():
+    # The chunk count is the fewest that fit the budget, and the largest chunk
+    # is the smallest any cut into that many runs of consecutive matrices allows.
+    import random
+    rng = random.Random(7)
+    shapes = [(rng.choice([128, 384, 768, 1024, 2048]), rng.choice([256, 768, 3072])) for _ in range(14)]
+    b = [mm.plan_query([s], K=5)["ws_bytes"] for s in shapes]
+    total = mm.plan_query(shapes, K=5, lanes=1)["ws_bytes"]
+    assert total == sum(b)
+    for limit in (max(b), max(b) + 1, 2 * max(b), total // 3, total // 2, total - 1):
+        if limit < max(b):
+            continue
+        q = mm.plan_query(shapes, K=5, workspace_limit=limit)
+        want = _greedy_count(b, limit)
+        assert q["chunks"] == want, limit
+        if want > 1:
+            assert q["ws_bytes"] == _min_max_partition(b, want), limit
+    # Eight-layer chunks of the 8B-shaped set under a 16 GiB budget, not
+    # three chunks of ten layers and a short last one.
+    layer = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (4096, 14336), (4096, 14336), (14336, 4096)]
+    q16 = mm.plan_query(layer * 32, K=5, workspace_limit=16 << 30)
+    assert q16["chunks"] == 4
+    assert q16["ws_bytes"] == 8 * mm.plan_query(layer, K=5, lanes=1)["ws_bytes"]
+
+
 def test_x32_needs_more_workspace_than_fold():
     s = [(768, 3072)]
     assert mm.plan_query(s, ns_precision="x32")["ws_bytes"] > mm.plan_query(s, ns_precision="fold")["ws_bytes"]
