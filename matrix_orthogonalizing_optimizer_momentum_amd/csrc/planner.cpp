@@ -419,6 +419,25 @@ void fill_chunk(const Plan& plan, int c, const Cfg& cfg, const CallPtrs& p, char
     }
     t.nparts[s_onorm0 + mi] = part;
   }
+  // Within the run of the G1 / G2 job list that one XCD takes (the kernels'
+  // block -> job map gives XCD x the x-th of 8 near-equal contiguous runs),
+  // units with deeper Grams (G1 contracts over s) go first, so each run ends
+  // on its shortest jobs; a unit's own jobs keep their order.  GPT-2-small
+  // set (fc and proj Grams 4 times as deep as attn-out's): G1 7% faster; the
+  // 8B-shaped set (a run is one layer, gate / up / down 3.5 times as deep):
+  // G1 0.7% faster.  G3 keeps the unit order: its k / v jobs moved to the
+  // end of each layer measured 0.6% slower.
+  for (int g = 0; g < kGemmCfgs; ++g) {
+    std::vector<GemmJob>& v = t.g12_jobs[g];
+    const int nj = (int)v.size(), q = nj / 8, rem = nj % 8;
+    for (int x = 0, b = 0; x < 8; ++x) {
+      const int e = b + q + (x < rem ? 1 : 0);
+      std::stable_sort(v.begin() + b, v.begin() + e, [&](const GemmJob& l, const GemmJob& r) {
+        return t.units[l.unit].ld_s > t.units[r.unit].ld_s;
+      });
+      b = e;
+    }
+  }
 
   // --- momentum / prep blocks
   if (!no_ns(cfg.kind)) {
