@@ -985,59 +985,73 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   if (PHASE == kG3 && !args.last) {
     T* const xo = reinterpret_cast<T*>(args.cur ? u.xt[0] : u.xt[1]);
     const int hi = lane >> 5;
+    // Most waves' blocks lie inside the matrix, and all iterations but the
+    // first have no pre-scale: that case runs a copy of the store loop with
+    // neither the bounds tests nor the fp64 scaling (which the compiler
+    // would otherwise evaluate for every value and select away).
+    const bool inside = row0 + wm * WM + WM <= r && col0 + wn * WN + WN <= u.s;
+    auto store_x = [&](auto fast_c) {
+      constexpr bool fast = decltype(fast_c)::value;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int n = col0 + wn * WN + j * 32 + lcol;
+        for (int j = 0; j < NI; ++j) {
+          const int n = col0 + wn * WN + j * 32 + lcol;
 #pragma unroll
-        for (int pq = 0; pq < 2; ++pq) {
-          float v[2][4];  // groups q = 2pq, 2pq+1 of this lane's rows
+          for (int pq = 0; pq < 2; ++pq) {
+            float v[2][4];  // groups q = 2pq, 2pq+1 of this lane's rows
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int q = 2 * pq + h, m0 = row0 + wm * WM + i * 32 + 8 * q + lrow;
+            for (int h = 0; h < 2; ++h) {
+              const int q = 2 * pq + h, m0 = row0 + wm * WM + i * 32 + 8 * q + lrow;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float t = acc[i][j][4 * q + e];
-              if (args.first) t = (float)((double)t * sig);
-              v[h][e] = (m0 + e < r && n < u.s) ? t : 0.f;
+              for (int e = 0; e < 4; ++e) {
+                float t = acc[i][j][4 * q + e];
+                if constexpr (fast) {
+                  v[h][e] = t;
+                } else {
+                  if (args.first) t = (float)((double)t * sig);
+                  v[h][e] = (m0 + e < r && n < u.s) ? t : 0.f;
+                }
+              }
             }
-          }
-          // after the swaps: rows row0 + wm*WM + i*32 + 16*pq + 8*hi + 0..7
-          const int ms = row0 + wm * WM + i * 32 + 16 * pq + 8 * hi;
-          const bool ok = n < u.ld_s && ms < u.ld_r;
-          const int64_t o = (int64_t)(ok ? n : 0) * u.ld_r + (ok ? ms : 0);
-          if constexpr (sizeof(T) == 2) {
-            uint32_t w0 = pack_bf16x2(v[0][0], v[0][1]), w1 = pack_bf16x2(v[0][2], v[0][3]);
-            uint32_t w2 = pack_bf16x2(v[1][0], v[1][1]), w3 = pack_bf16x2(v[1][2], v[1][3]);
-            const auto s0 = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
-            const u32x4_t pk = {s0[0], s1[0], s0[1], s1[1]};
-            if (ok) *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(reinterpret_cast<bf16_t*>(xo) + o)) = pk;
-          } else {
-            float vs[8];
+            // after the swaps: rows row0 + wm*WM + i*32 + 16*pq + 8*hi + 0..7
+            const int ms = row0 + wm * WM + i * 32 + 16 * pq + 8 * hi;
+            const bool ok = fast || (n < u.ld_s && ms < u.ld_r);
+            const int64_t o = (int64_t)(ok ? n : 0) * u.ld_r + (ok ? ms : 0);
+            if constexpr (sizeof(T) == 2) {
+              uint32_t w0 = pack_bf16x2(v[0][0], v[0][1]), w1 = pack_bf16x2(v[0][2], v[0][3]);
+              uint32_t w2 = pack_bf16x2(v[1][0], v[1][1]), w3 = pack_bf16x2(v[1][2], v[1][3]);
+              const auto s0 = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+              const u32x4_t pk = {s0[0], s1[0], s0[1], s1[1]};
+              if (ok) *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(reinterpret_cast<bf16_t*>(xo) + o)) = pk;
+            } else {
+              float vs[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][e]), __float_as_uint(v[1][e]),
-                                                               false, false);
-              vs[e] = __uint_as_float(sw[0]);
-              vs[4 + e] = __uint_as_float(sw[1]);
+              for (int e = 0; e < 4; ++e) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][e]), __float_as_uint(v[1][e]),
+                                                                 false, false);
+                vs[e] = __uint_as_float(sw[0]);
+                vs[4 + e] = __uint_as_float(sw[1]);
+              }
+              if (ok) store8(reinterpret_cast<float*>(xo), o, vs);
             }
-            if (ok) store8(reinterpret_cast<float*>(xo), o, vs);
-          }
-          if (args.master32 && u.x32 != nullptr) {
-            float vs[8];
+            if (args.master32 && u.x32 != nullptr) {
+              float vs[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][e]), __float_as_uint(v[1][e]),
-                                                               false, false);
-              vs[e] = __uint_as_float(sw[0]);
-              vs[4 + e] = __uint_as_float(sw[1]);
+              for (int e = 0; e < 4; ++e) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][e]), __float_as_uint(v[1][e]),
+                                                                 false, false);
+                vs[e] = __uint_as_float(sw[0]);
+                vs[4 + e] = __uint_as_float(sw[1]);
+              }
+              if (ok) store8(u.x32, o, vs);
             }
-            if (ok) store8(u.x32, o, vs);
           }
         }
-      }
+    };
+    if (inside && !args.first) store_x(std::true_type{});
+    else store_x(std::false_type{});
     return;
   }
 
