@@ -239,16 +239,8 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // tuples between products make the compiler move whole tuples through the
   // arch VGPRs, which then spill.)
   f32x16_t acc[4][4];
-  auto mma16 = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], auto zc) {
-    constexpr bool zero = decltype(zc)::value;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], zero ? f32x16_t{} : acc[i][j], 0, 0, 0);
-  };
-  // the same, calling next(i) after the four MFMAs that read fa[i] have
-  // issued (a load into fa[i] may follow them)
+  // 16 MFMAs of the wave's quadrant, calling next(i) after the four that
+  // read fa[i] have issued (a load into fa[i] may follow them)
   auto mma16_next = [&](bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], auto zc, auto next) {
     constexpr bool zero = decltype(zc)::value;
 #pragma unroll
@@ -303,71 +295,143 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
     }
   };
 
-  // G1 fragments (transposing reads of X^T, k = n): lane 16 g + j16 reads
-  // rows 16 ks + 8 (g / 2) + j16 / 4 and 4 rows further, elements
-  // 16 (g % 2) + 4 (j16 % 4) of its 32-wide block.  The layout depends on the
-  // row modulo 16 only, so a k-step adds 8 KiB; the two reads of a fragment
-  // differ in their granule XOR and get offsets of their own.
-  auto g1_offsets = [&](int (&g1p)[2][4], int (&g1q)[2][4]) {
-    const int ln = opaque(lane), j16 = ln & 15, g = ln >> 4;
-    const int krow = 8 * (g >> 1) + (j16 >> 2);
-    const int msub = 16 * (g & 1) + 4 * (j16 & 3);
+  // ---- The symmetric products A = X X^T and A A on their distinct blocks
+  // only.  In 32-row blocks of the 256 x 256 matrix, waves 0 and 1 each take
+  // half of the upper right quadrant (blocks I = 0..3 by J = 4 + 2 w, 5 + 2 w:
+  // 8 blocks from fragments of 4 row blocks and 2 column blocks), and waves 2
+  // and 3 the blocks I <= J of the upper left / lower right quadrant (10
+  // blocks; P and Q are the same matrix, so the fragments of its 4 blocks
+  // serve every one of them): 36 of the 64 blocks, the busiest wave 10
+  // against 16.  A wave stores its blocks through the transposed path (block
+  // (I, J) lands at (J, I), in the lower triangle: for a symmetric result the
+  // cheap 8-byte writes of the accumulator layout) and then copies the
+  // off-diagonal ones into their upper positions with transposing reads, so
+  // the products after it read whole rows as before.
+  const int qb = 4 * (wave & 1);      // tri waves: first block of the quadrant
+  const int cbk = 4 + 2 * (wave & 1);  // rect waves: first column block
+  // the accumulator blocks of a wave: tri: acc[i][j], j >= i = block
+  // (qb + i, qb + j); rect: acc[i][j], j < 2 = block (i, cbk + j)
+  auto blk_i = [&](auto tri_c, int i) { return decltype(tri_c)::value ? qb + i : i; };
+  auto blk_j = [&](auto tri_c, int j) { return decltype(tri_c)::value ? qb + j : cbk + j; };
+  // fragment f of a wave: tri: block qb + f; rect: blocks 0..3, then cbk, cbk + 1
+  auto frag_blk = [&](auto tri_c, int f) { return decltype(tri_c)::value ? qb + f : (f < 4 ? f : cbk + f - 4); };
+
+  // G1 (g1 true: transposing reads of X^T, k = n) or G2 (plain reads of A
+  // rows) over the wave's blocks.  G1 fragments: lane 16 g + j16 reads rows
+  // 16 ks + 8 (g / 2) + j16 / 4 and 4 rows further, elements 16 (g % 2) +
+  // 4 (j16 % 4) of its 32-wide block (the layout repeats every 16 rows, so a
+  // k-step adds 8 KiB; the two reads differ in their granule XOR).  G2
+  // fragments: row 32 X + lc, granule (2 ks + lh) ^ (lc % 16).
+  auto sym_product = [&](auto tri_c, auto g1_c) {
+    constexpr bool TRI = decltype(tri_c)::value;
+    constexpr bool G1 = decltype(g1_c)::value;
+    constexpr int NF = TRI ? 4 : 6;
+    int off[2][NF];
+    {
+      const int ln = opaque(lane);
+      const int j16 = ln & 15, g = ln >> 4;
+      const int krow = 8 * (g >> 1) + (j16 >> 2), msub = 16 * (g & 1) + 4 * (j16 & 3);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) g1p[h][i] = xt_off(krow + 4 * h, wr + i * 32 + msub);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) g1q[h][j] = xt_off(krow + 4 * h, wc + j * 32 + msub);
+      for (int f = 0; f < NF; ++f) {
+        const int X = frag_blk(tri_c, f);
+        if constexpr (G1) {
+          off[0][f] = xt_off(krow, 32 * X + msub);
+          off[1][f] = xt_off(krow + 4, 32 * X + msub);
+        } else {
+          off[0][f] = (32 * X + (ln & 31)) * 512;
+          off[1][f] = 0;
+        }
+      }
     }
+    bf16x8_t fr[2][NF];
+    auto ld = [&](int buf, int ks) {
+      if constexpr (G1) {
+        const int o = ks * 16 * 512;  // 16 rows further
+#pragma unroll
+        for (int f = 0; f < NF; ++f) fr[buf][f] = ld_tr8(sM + off[0][f] + o, sM + off[1][f] + o);
+      } else {
+        const int ln = opaque(lane);
+        const int gofs = ((2 * ks + (ln >> 5)) ^ (ln & 15)) << 4;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) fr[buf][f] = ld16(sM + off[0][f] + gofs);
+      }
+    };
+    auto mm = [&](int buf, auto zc) {
+      constexpr bool zero = decltype(zc)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (TRI ? j < i : j >= 2) continue;
+          const bf16x8_t fq = TRI ? fr[buf][j] : fr[buf][4 + (j & 1)];
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][i], fq, zero ? f32x16_t{} : acc[i][j], 0, 0, 0);
+        }
+    };
+    ld(0, 0);
+    static_for<8>([&](auto hc) {
+      constexpr int ks = 2 * decltype(hc)::value;
+      ld(1, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mm(0, std::integral_constant<bool, ks == 0>{});
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ks + 2 < 16) ld(0, ks + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mm(1, NZ{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
-  // Symmetric results go to the matrix region through the transposed path:
-  // the lane's rows m..m+3 of column n go to row n, elements m..m+3 (8
-  // bytes): mat_off(n, m) with n = wc + 32 j + lc, m = wr + 32 i + 8 q + 4 lh
-  // is row n (16 KiB per j), granule (wr / 8 + 4 i + q) ^ (lc % 16), byte
-  // 8 lh.  put_a stores A = sc * acc; put_b stores B = c * acc + b * A, with
-  // A read back from the very slot the lane then overwrites (c = 0: B = b A,
-  // acc unused).
-  auto sym_addr = [&](int row, int sw, int i, int j, int q) -> char* {
-    return sM + row + 16384 * j + ((((wr >> 3) + 4 * i + q) ^ sw) << 4);
-  };
-  // (scaled: times sc, the first iteration's sig^2 and 1 after it; a
-  // run-time branch between the two forms would join register states.)
-  auto put_a = [&](auto scaled, float sc) {
-    constexpr bool kScale = decltype(scaled)::value;
+  // Element group q of the lane's value of block (I, J) -- rows 32 I + 8 q +
+  // 4 lh + 0..3 of column 32 J + lc -- goes to row 32 J + lc, elements
+  // 32 I + 8 q + 4 lh.. (mat_off: granule (4 I + q) ^ (lc % 16), byte 8 lh).
+  auto lo_addr = [&](int I, int J, int q) -> char* {
     const int ln = opaque(lane), l31 = ln & 31;
-    const int row = (wc + l31) * 512 + 8 * (ln >> 5), sw = l31 & 15;
+    return sM + (32 * J + l31) * 512 + 8 * (ln >> 5) + (((4 * I + q) ^ (l31 & 15)) << 4);
+  };
+  // A = sc * acc (scaled: times sc, the first iteration's sig^2 and 1 after
+  // it; a run-time branch between the two forms would join register states)
+  auto put_a = [&](auto tri_c, auto scaled, float sc) {
+    constexpr bool TRI = decltype(tri_c)::value;
+    constexpr bool kScale = decltype(scaled)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        if (TRI ? j < i : j >= 2) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = kScale ? acc[i][j][4 * q + e] * sc : acc[i][j][4 * q + e];
-          const uint32_t w0 = pack_bf16x2(v[0], v[1]);
-          const uint32_t w1 = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2_t*>(sym_addr(row, sw, i, j, q)) = u32x2_t{w0, w1};
-          // one block at a time: the scheduler would otherwise batch every
-          // accumulator read (register pressure)
-          if (q == 3) __builtin_amdgcn_sched_barrier(0);
+          *reinterpret_cast<u32x2_t*>(lo_addr(blk_i(tri_c, i), blk_j(tri_c, j), q)) =
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
+        // one block at a time: the scheduler would otherwise batch every
+        // accumulator read (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
-  auto put_b = [&](float b, float c) {
-    const int ln = opaque(lane), l31 = ln & 31;
-    const int row = (wc + l31) * 512 + 8 * (ln >> 5), sw = l31 & 15;
-    // the next block's four A reads are in flight while this block is formed
+  // B = c * acc + b * A, with A read back from the very slot the lane then
+  // overwrites (c = 0: B = b A, acc unused); the next block's four A reads
+  // are in flight while this block is formed
+  auto put_b = [&](auto tri_c, float b, float c) {
+    constexpr bool TRI = decltype(tri_c)::value;
+    constexpr int NB = TRI ? 10 : 8;
+    // block t of the wave in order
+    auto bi = [](int t) { return TRI ? (t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3) : t >> 1; };
+    auto bj = [](int t) { return TRI ? (t < 4 ? t : t < 7 ? t - 3 : t < 9 ? t - 5 : 3) : t & 1; };
     u32x2_t av[2][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) av[0][q] = *reinterpret_cast<const u32x2_t*>(sym_addr(row, sw, 0, 0, q));
+    for (int q = 0; q < 4; ++q)
+      av[0][q] = *reinterpret_cast<const u32x2_t*>(lo_addr(blk_i(tri_c, bi(0)), blk_j(tri_c, bj(0)), q));
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int i = t >> 2, j = t & 3, cur = t & 1;
-      if (t + 1 < 16) {
+    for (int t = 0; t < NB; ++t) {
+      const int i = bi(t), j = bj(t), cur = t & 1;
+      if (t + 1 < NB) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          av[cur ^ 1][q] = *reinterpret_cast<const u32x2_t*>(sym_addr(row, sw, (t + 1) >> 2, (t + 1) & 3, q));
+          av[cur ^ 1][q] =
+              *reinterpret_cast<const u32x2_t*>(lo_addr(blk_i(tri_c, bi(t + 1)), blk_j(tri_c, bj(t + 1)), q));
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -376,85 +440,92 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
         float v[4] = {b * lo_bf(a2[0]), b * hi_bf(a2[0]), b * lo_bf(a2[1]), b * hi_bf(a2[1])};
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = fmaf(c, acc[i][j][4 * q + e], v[e]);
-        *reinterpret_cast<u32x2_t*>(sym_addr(row, sw, i, j, q)) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2_t*>(lo_addr(blk_i(tri_c, i), blk_j(tri_c, j), q)) =
+            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // The wave's own blocks above the diagonal (I < J), each from its mirror
+  // (J, I) that the wave has just stored below it: a transposing read gives
+  // the lane rows 32 J + 8 q + 4 lh + 0..3 of column 32 I + lc, which are
+  // elements 32 J + 8 q + 4 lh.. of row 32 I + lc, one 8-byte write.  A
+  // wave's LDS accesses run in order, so it needs no barrier to read back its
+  // own stores; all reads are issued before the first write.
+  auto mirror = [&](auto tri_c) {
+    constexpr bool TRI = decltype(tri_c)::value;
+    constexpr int NM = TRI ? 6 : 8;
+    // block t of the wave off the diagonal: tri (i, j) with i < j, rect all
+    auto mi = [](int t) { return TRI ? (t < 3 ? 0 : t < 5 ? 1 : 2) : t >> 1; };
+    auto mj = [](int t) { return TRI ? (t < 3 ? t + 1 : t < 5 ? t - 1 : 3) : t & 1; };
+    const int ln = opaque(lane), j16 = ln & 15, g = ln >> 4;
+    u32x2_t v[NM][4];
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+      const int I = blk_i(tri_c, mi(t)), J = blk_j(tri_c, mj(t));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int R = 32 * J + 8 * q + 4 * (g >> 1) + (j16 >> 2);
+        const int C = 32 * I + 16 * (g & 1) + 4 * (j16 & 3);
+        v[t][q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds<i16x4_t>(sM + mat_off(R, C))));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+      const int I = blk_i(tri_c, mi(t)), J = blk_j(tri_c, mj(t));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x2_t*>(sM + mat_off(32 * I + (ln & 31), 32 * J + 8 * q + 4 * (ln >> 5))) = v[t][q];
+    }
+  };
+  const bool tri = (wave & 2) != 0;
+  using TRI_T = std::true_type;
+  using RECT_T = std::false_type;
 
   for (int it = 0; it < args.K; ++it) {
     const float a = args.abc[it][0], b = args.abc[it][1], c = args.abc[it][2];
     const bool first = it == 0;
 
-    // ---------------- G1: A = X X^T (times sig^2 on the first iteration)
+    // ---------------- G1: A = X X^T (times sig^2 on the first iteration),
+    // stored below the diagonal; the product and the store stay inside one
+    // wave-uniform branch, so no accumulator state is live where the two
+    // paths join.  G2 (A A) runs for c = 0 too (c * A A then adds nothing): a
+    // run-time branch around it would join two accumulator states, which the
+    // compiler resolves by copying all of them through the arch VGPRs.
     put_xt();
     bar();
-    {
-      int g1p[2][4], g1q[2][4];
-      g1_offsets(g1p, g1q);
-      bf16x8_t fa[2][4], fb[2][4];
-      auto ld_x = [&](int buf, int ks) {
-        const int o = ks * 16 * 512;  // 16 rows further
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[buf][i] = ld_tr8(sM + g1p[0][i] + o, sM + g1p[1][i] + o);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[buf][j] = ld_tr8(sM + g1q[0][j] + o, sM + g1q[1][j] + o);
-      };
-      ld_x(0, 0);
-      static_for<8>([&](auto hc) {
-        constexpr int ks = 2 * decltype(hc)::value;
-        ld_x(1, ks + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mma16(fa[0], fb[0], std::integral_constant<bool, ks == 0>{});
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (ks + 2 < 16) ld_x(0, ks + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        mma16(fa[1], fb[1], NZ{});
-        __builtin_amdgcn_sched_barrier(0);
-      });
+    const float asc = first ? (float)(sig * sig) : 1.f;  // branch-free (see update below)
+    if (tri) {
+      sym_product(TRI_T{}, std::true_type{});
+      bar();  // every wave is done reading X^T
+      put_a(TRI_T{}, std::true_type{}, asc);
+      mirror(TRI_T{});
+    } else {
+      sym_product(RECT_T{}, std::true_type{});
+      bar();
+      put_a(RECT_T{}, std::true_type{}, asc);
+      mirror(RECT_T{});
     }
-    bar();  // every wave is done reading X^T
-
-    // ---------------- A to LDS; G2: A A.  The product runs for c = 0 too
-    // (c * A A then adds nothing): a run-time branch around it would join two
-    // accumulator states, which the compiler resolves by copying all of them
-    // through the arch VGPRs.
-    put_a(std::true_type{}, first ? (float)(sig * sig) : 1.f);  // branch-free (see update below)
     bar();
-    {
-      bf16x8_t fa[2][4], fb[2][4];
-      // rows wr + 32 i + lc (and wc + 32 j + lc): 16 KiB per block, granule
-      // (2 ks + lh) ^ (lc % 16)
-      auto ld_ab = [&](int buf, int ks) {
-        const int ln = opaque(lane), l31 = ln & 31;
-        const int g = ((2 * ks + (ln >> 5)) ^ (l31 & 15)) << 4;
-        const char* pa = sM + (wr + l31) * 512 + g;
-        const char* pb = sM + (wc + l31) * 512 + g;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[buf][i] = ld16(pa + 16384 * i);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[buf][j] = ld16(pb + 16384 * j);
-      };
-      ld_ab(0, 0);
-      static_for<8>([&](auto hc) {
-        constexpr int ks = 2 * decltype(hc)::value;
-        ld_ab(1, ks + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mma16(fa[0], fb[0], std::integral_constant<bool, ks == 0>{});
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (ks + 2 < 16) ld_ab(0, ks + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        mma16(fa[1], fb[1], NZ{});
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    }
-    bar();  // every wave is done reading A
 
-    // ---------------- B to LDS; G3: X <- a X + B X (times sig on the first)
-    // (on the first iteration B is stored times sig, which with a * sig in
-    // the update gives sig (a X0 + B X0) without scaling the accumulators)
+    // ---------------- G2: B = b A + c A A, stored below the diagonal, then
+    // mirrored (on the first iteration B is stored times sig, which with
+    // a * sig in the update gives sig (a X0 + B X0) without scaling the
+    // accumulators)
     const float xs = first ? (float)sig : 1.f;
-    put_b(b * xs, c * xs);
+    if (tri) {
+      sym_product(TRI_T{}, std::false_type{});
+      bar();  // every wave is done reading A
+      put_b(TRI_T{}, b * xs, c * xs);
+      mirror(TRI_T{});
+    } else {
+      sym_product(RECT_T{}, std::false_type{});
+      bar();
+      put_b(RECT_T{}, b * xs, c * xs);
+      mirror(RECT_T{});
+    }
+
+    // ---------------- G3: X <- a X + B X (times sig on the first)
     put_g3(std::integral_constant<int, 0>{}, sP0);
     bar();
     {
