@@ -304,9 +304,10 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // serve every one of them): 36 of the 64 blocks, the busiest wave 10
   // against 16.  A wave stores its blocks through the transposed path (block
   // (I, J) lands at (J, I), in the lower triangle: for a symmetric result the
-  // cheap 8-byte writes of the accumulator layout) and then copies the
-  // off-diagonal ones into their upper positions with transposing reads, so
-  // the products after it read whole rows as before.
+  // cheap 8-byte writes of the accumulator layout).  G2 reads A from there,
+  // the part above the diagonal through transposing reads; B is copied into
+  // its upper positions as well (transposing reads again), so that G3 reads
+  // whole rows.
   const int qb = 4 * (wave & 1);      // tri waves: first block of the quadrant
   const int cbk = 4 + 2 * (wave & 1);  // rect waves: first column block
   // the accumulator blocks of a wave: tri: acc[i][j], j >= i = block
@@ -322,38 +323,57 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // 4 (j16 % 4) of its 32-wide block (the layout repeats every 16 rows, so a
   // k-step adds 8 KiB; the two reads differ in their granule XOR).  G2
   // fragments: row 32 X + lc, granule (2 ks + lh) ^ (lc % 16).
-  auto sym_product = [&](auto tri_c, auto g1_c) {
+  auto sym_product = [&](auto tri_c, auto g1_c, auto w1_c) __attribute__((always_inline)) {
     constexpr bool TRI = decltype(tri_c)::value;
     constexpr bool G1 = decltype(g1_c)::value;
+    // G2 of a wave whose blocks are known at compile time (w1_c: wave % 2)
+    // reads A from its lower triangle only: for k in a block K above the
+    // fragment's block X, A(32 X + lc, k) = A(k, 32 X + lc) comes from the
+    // stored block (K, X) through transposing reads (as G1 reads X^T)
+    constexpr int W1 = decltype(w1_c)::value;  // -1: not specialised
+    constexpr bool LOWER = !G1 && W1 >= 0;
     constexpr int NF = TRI ? 4 : 6;
-    int off[2][NF];
+    auto fblk_ct = [](int f) { return TRI ? 4 * W1 + f : (f < 4 ? f : 4 + 2 * W1 + f - 4); };
+    int off[2][NF], tro[2][NF];
     {
       const int ln = opaque(lane);
       const int j16 = ln & 15, g = ln >> 4;
       const int krow = 8 * (g >> 1) + (j16 >> 2), msub = 16 * (g & 1) + 4 * (j16 & 3);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const int X = frag_blk(tri_c, f);
+        const int X = LOWER ? fblk_ct(f) : frag_blk(tri_c, f);
         if constexpr (G1) {
           off[0][f] = xt_off(krow, 32 * X + msub);
           off[1][f] = xt_off(krow + 4, 32 * X + msub);
         } else {
           off[0][f] = (32 * X + (ln & 31)) * 512;
           off[1][f] = 0;
+          if constexpr (LOWER) {
+            // rows 16 ks + krow (+ 4): the granule XOR depends on the row
+            // modulo 16 only, so a k-step adds 8 KiB
+            tro[0][f] = mat_off(krow, 32 * X + msub);
+            tro[1][f] = mat_off(krow + 4, 32 * X + msub);
+          }
         }
       }
     }
     bf16x8_t fr[2][NF];
-    auto ld = [&](int buf, int ks) {
+    auto ld = [&](int buf, auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
       if constexpr (G1) {
-        const int o = ks * 16 * 512;  // 16 rows further
+        constexpr int o = ks * 16 * 512;  // 16 rows further
 #pragma unroll
         for (int f = 0; f < NF; ++f) fr[buf][f] = ld_tr8(sM + off[0][f] + o, sM + off[1][f] + o);
       } else {
         const int ln = opaque(lane);
         const int gofs = ((2 * ks + (ln >> 5)) ^ (ln & 15)) << 4;
 #pragma unroll
-        for (int f = 0; f < NF; ++f) fr[buf][f] = ld16(sM + off[0][f] + gofs);
+        for (int f = 0; f < NF; ++f) {
+          if (LOWER && ks / 2 > fblk_ct(f))
+            fr[buf][f] = ld_tr8(sM + tro[0][f] + ks * 8192, sM + tro[1][f] + ks * 8192);
+          else
+            fr[buf][f] = ld16(sM + off[0][f] + gofs);
+        }
       }
     };
     auto mm = [&](int buf, auto zc) {
@@ -367,14 +387,14 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][i], fq, zero ? f32x16_t{} : acc[i][j], 0, 0, 0);
         }
     };
-    ld(0, 0);
+    ld(0, std::integral_constant<int, 0>{});
     static_for<8>([&](auto hc) {
       constexpr int ks = 2 * decltype(hc)::value;
-      ld(1, ks + 1);
+      ld(1, std::integral_constant<int, ks + 1>{});
       __builtin_amdgcn_sched_barrier(0);
       mm(0, std::integral_constant<bool, ks == 0>{});
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (ks + 2 < 16) ld(0, ks + 2);
+      if constexpr (ks + 2 < 16) ld(0, std::integral_constant<int, ks + 2>{});
       __builtin_amdgcn_sched_barrier(0);
       mm(1, NZ{});
       __builtin_amdgcn_sched_barrier(0);
@@ -390,7 +410,7 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   };
   // A = sc * acc (scaled: times sc, the first iteration's sig^2 and 1 after
   // it; a run-time branch between the two forms would join register states)
-  auto put_a = [&](auto tri_c, auto scaled, float sc) {
+  auto put_a = [&](auto tri_c, auto scaled, float sc) __attribute__((always_inline)) {
     constexpr bool TRI = decltype(tri_c)::value;
     constexpr bool kScale = decltype(scaled)::value;
 #pragma unroll
@@ -414,7 +434,7 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // B = c * acc + b * A, with A read back from the very slot the lane then
   // overwrites (c = 0: B = b A, acc unused); the next block's four A reads
   // are in flight while this block is formed
-  auto put_b = [&](auto tri_c, float b, float c) {
+  auto put_b = [&](auto tri_c, float b, float c) __attribute__((always_inline)) {
     constexpr bool TRI = decltype(tri_c)::value;
     constexpr int NB = TRI ? 10 : 8;
     // block t of the wave in order
@@ -452,7 +472,7 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // elements 32 J + 8 q + 4 lh.. of row 32 I + lc, one 8-byte write.  A
   // wave's LDS accesses run in order, so it needs no barrier to read back its
   // own stores; all reads are issued before the first write.
-  auto mirror = [&](auto tri_c) {
+  auto mirror = [&](auto tri_c) __attribute__((always_inline)) {
     constexpr bool TRI = decltype(tri_c)::value;
     constexpr int NM = TRI ? 6 : 8;
     // block t of the wave off the diagonal: tri (i, j) with i < j, rect all
@@ -495,16 +515,15 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
     put_xt();
     bar();
     const float asc = first ? (float)(sig * sig) : 1.f;  // branch-free (see update below)
+    using ANY = std::integral_constant<int, -1>;
     if (tri) {
-      sym_product(TRI_T{}, std::true_type{});
+      sym_product(TRI_T{}, std::true_type{}, ANY{});
       bar();  // every wave is done reading X^T
       put_a(TRI_T{}, std::true_type{}, asc);
-      mirror(TRI_T{});
     } else {
-      sym_product(RECT_T{}, std::true_type{});
+      sym_product(RECT_T{}, std::true_type{}, ANY{});
       bar();
       put_a(RECT_T{}, std::true_type{}, asc);
-      mirror(RECT_T{});
     }
     bar();
 
@@ -513,17 +532,20 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
     // a * sig in the update gives sig (a X0 + B X0) without scaling the
     // accumulators)
     const float xs = first ? (float)sig : 1.f;
-    if (tri) {
-      sym_product(TRI_T{}, std::false_type{});
+    // (A is only below the diagonal: G2 reads the rest transposed, which
+    // needs the wave's blocks at compile time)
+    auto g2 = [&](auto tri_c, auto w1_c) __attribute__((always_inline)) {
+      sym_product(tri_c, std::false_type{}, w1_c);
       bar();  // every wave is done reading A
-      put_b(TRI_T{}, b * xs, c * xs);
-      mirror(TRI_T{});
-    } else {
-      sym_product(RECT_T{}, std::false_type{});
-      bar();
-      put_b(RECT_T{}, b * xs, c * xs);
-      mirror(RECT_T{});
-    }
+      put_b(tri_c, b * xs, c * xs);
+      mirror(tri_c);
+    };
+    using W0 = std::integral_constant<int, 0>;
+    using W1 = std::integral_constant<int, 1>;
+    if (wave == 3) g2(TRI_T{}, W1{});
+    else if (wave == 2) g2(TRI_T{}, W0{});
+    else if (wave == 1) g2(RECT_T{}, W1{});
+    else g2(RECT_T{}, W0{});
 
     // ---------------- G3: X <- a X + B X (times sig on the first)
     put_g3(std::integral_constant<int, 0>{}, sP0);
