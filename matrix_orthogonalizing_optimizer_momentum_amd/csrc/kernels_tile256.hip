@@ -297,12 +297,12 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
 
   // ---- The symmetric products A = X X^T and A A on their distinct blocks
   // only.  In 32-row blocks of the 256 x 256 matrix, waves 0 and 1 each take
-  // half of the upper right quadrant (blocks I = 0..3 by J = 4 + 2 w, 5 + 2 w:
-  // 8 blocks from fragments of 4 row blocks and 2 column blocks), and waves 2
-  // and 3 the blocks I <= J of the upper left / lower right quadrant (10
-  // blocks; P and Q are the same matrix, so the fragments of its 4 blocks
-  // serve every one of them): 36 of the 64 blocks, the busiest wave 10
-  // against 16.  A wave stores its blocks through the transposed path (block
+  // half of the upper right quadrant (blocks I = 0..3 by J = 4 + 2 w, 5 + 2 w,
+  // from fragments of 4 row blocks and 2 column blocks) plus one block those
+  // fragments also give, (4, 5) for wave 0 and (0, 1) for wave 1; waves 2 and
+  // 3 the other blocks I <= J of the upper left / lower right quadrant (P and
+  // Q are the same matrix, so the fragments of its 4 blocks serve every one
+  // of them): 36 of the 64 blocks, 9 per wave against 16.  A wave stores its blocks through the transposed path (block
   // (I, J) lands at (J, I), in the lower triangle: for a symmetric result the
   // cheap 8-byte writes of the accumulator layout).  G2 reads A from there,
   // the part above the diagonal through transposing reads; B is copied into
@@ -310,10 +310,19 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // whole rows.
   const int qb = 4 * (wave & 1);      // tri waves: first block of the quadrant
   const int cbk = 4 + 2 * (wave & 1);  // rect waves: first column block
-  // the accumulator blocks of a wave: tri: acc[i][j], j >= i = block
-  // (qb + i, qb + j); rect: acc[i][j], j < 2 = block (i, cbk + j)
-  auto blk_i = [&](auto tri_c, int i) { return decltype(tri_c)::value ? qb + i : i; };
-  auto blk_j = [&](auto tri_c, int j) { return decltype(tri_c)::value ? qb + j : cbk + j; };
+  // The accumulator slots of a wave, 9 each: tri: acc[i][j], j >= i, except
+  // (0, 1) = block (qb + i, qb + j); rect: acc[i][j], j < 2 = block
+  // (i, cbk + j), and acc[0][2] = the extra block, (cbk, cbk + 1) for wave 0
+  // and (0, 1) for wave 1.
+  auto slot_ok = [](bool TRI, int i, int j) {
+    return TRI ? (j >= i && !(i == 0 && j == 1)) : (j < 2 || (i == 0 && j == 2));
+  };
+  auto blk_i = [&](auto tri_c, int i, int j) {
+    return decltype(tri_c)::value ? qb + i : j < 2 ? i : (wave & 1) ? 0 : cbk;
+  };
+  auto blk_j = [&](auto tri_c, int i, int j) {
+    return decltype(tri_c)::value ? qb + j : j < 2 ? cbk + j : (wave & 1) ? 1 : cbk + 1;
+  };
   // fragment f of a wave: tri: block qb + f; rect: blocks 0..3, then cbk, cbk + 1
   auto frag_blk = [&](auto tri_c, int f) { return decltype(tri_c)::value ? qb + f : (f < 4 ? f : cbk + f - 4); };
 
@@ -382,9 +391,15 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (TRI ? j < i : j >= 2) continue;
-          const bf16x8_t fq = TRI ? fr[buf][j] : fr[buf][4 + (j & 1)];
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][i], fq, zero ? f32x16_t{} : acc[i][j], 0, 0, 0);
+          if (!slot_ok(TRI, i, j)) continue;
+          bf16x8_t fp = fr[buf][i], fq = TRI ? fr[buf][j] : fr[buf][4 + (j & 1)];
+          if (!TRI && j == 2) {
+            // the extra block: fragments 4, 5 (wave 0) or 0, 1 (wave 1)
+            const bool w1 = W1 >= 0 ? W1 == 1 : (wave & 1) != 0;
+            fp = w1 ? fr[buf][0] : fr[buf][4];
+            fq = w1 ? fr[buf][1] : fr[buf][5];
+          }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp, fq, zero ? f32x16_t{} : acc[i][j], 0, 0, 0);
         }
     };
     ld(0, std::integral_constant<int, 0>{});
@@ -417,13 +432,13 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (TRI ? j < i : j >= 2) continue;
+        if (!slot_ok(TRI, i, j)) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = kScale ? acc[i][j][4 * q + e] * sc : acc[i][j][4 * q + e];
-          *reinterpret_cast<u32x2_t*>(lo_addr(blk_i(tri_c, i), blk_j(tri_c, j), q)) =
+          *reinterpret_cast<u32x2_t*>(lo_addr(blk_i(tri_c, i, j), blk_j(tri_c, i, j), q)) =
               u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
         // one block at a time: the scheduler would otherwise batch every
@@ -436,22 +451,24 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // are in flight while this block is formed
   auto put_b = [&](auto tri_c, float b, float c) __attribute__((always_inline)) {
     constexpr bool TRI = decltype(tri_c)::value;
-    constexpr int NB = TRI ? 10 : 8;
-    // block t of the wave in order
-    auto bi = [](int t) { return TRI ? (t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3) : t >> 1; };
-    auto bj = [](int t) { return TRI ? (t < 4 ? t : t < 7 ? t - 3 : t < 9 ? t - 5 : 3) : t & 1; };
+    constexpr int NB = 9;
+    // slot t of the wave in order
+    constexpr int kTi[9] = {0, 0, 0, 1, 1, 1, 2, 2, 3}, kTj[9] = {0, 2, 3, 1, 2, 3, 2, 3, 3};
+    constexpr int kRi[9] = {0, 0, 1, 1, 2, 2, 3, 3, 0}, kRj[9] = {0, 1, 0, 1, 0, 1, 0, 1, 2};
+    auto bi = [&](int t) { return TRI ? kTi[t] : kRi[t]; };
+    auto bj = [&](int t) { return TRI ? kTj[t] : kRj[t]; };
     u32x2_t av[2][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      av[0][q] = *reinterpret_cast<const u32x2_t*>(lo_addr(blk_i(tri_c, bi(0)), blk_j(tri_c, bj(0)), q));
+      av[0][q] = *reinterpret_cast<const u32x2_t*>(lo_addr(blk_i(tri_c, bi(0), bj(0)), blk_j(tri_c, bi(0), bj(0)), q));
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int i = bi(t), j = bj(t), cur = t & 1;
       if (t + 1 < NB) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          av[cur ^ 1][q] =
-              *reinterpret_cast<const u32x2_t*>(lo_addr(blk_i(tri_c, bi(t + 1)), blk_j(tri_c, bj(t + 1)), q));
+          av[cur ^ 1][q] = *reinterpret_cast<const u32x2_t*>(
+              lo_addr(blk_i(tri_c, bi(t + 1), bj(t + 1)), blk_j(tri_c, bi(t + 1), bj(t + 1)), q));
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -460,7 +477,7 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
         float v[4] = {b * lo_bf(a2[0]), b * hi_bf(a2[0]), b * lo_bf(a2[1]), b * hi_bf(a2[1])};
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = fmaf(c, acc[i][j][4 * q + e], v[e]);
-        *reinterpret_cast<u32x2_t*>(lo_addr(blk_i(tri_c, i), blk_j(tri_c, j), q)) =
+        *reinterpret_cast<u32x2_t*>(lo_addr(blk_i(tri_c, i, j), blk_j(tri_c, i, j), q)) =
             u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -474,15 +491,18 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // own stores; all reads are issued before the first write.
   auto mirror = [&](auto tri_c) __attribute__((always_inline)) {
     constexpr bool TRI = decltype(tri_c)::value;
-    constexpr int NM = TRI ? 6 : 8;
-    // block t of the wave off the diagonal: tri (i, j) with i < j, rect all
-    auto mi = [](int t) { return TRI ? (t < 3 ? 0 : t < 5 ? 1 : 2) : t >> 1; };
-    auto mj = [](int t) { return TRI ? (t < 3 ? t + 1 : t < 5 ? t - 1 : 3) : t & 1; };
+    constexpr int NM = TRI ? 5 : 9;
+    // slot t of the wave off the diagonal: tri (i, j) with i < j but (0, 1),
+    // rect all
+    constexpr int kTi[5] = {0, 0, 1, 1, 2}, kTj[5] = {2, 3, 2, 3, 3};
+    constexpr int kRi[9] = {0, 0, 1, 1, 2, 2, 3, 3, 0}, kRj[9] = {0, 1, 0, 1, 0, 1, 0, 1, 2};
+    auto mi = [&](int t) { return TRI ? kTi[t] : kRi[t]; };
+    auto mj = [&](int t) { return TRI ? kTj[t] : kRj[t]; };
     const int ln = opaque(lane), j16 = ln & 15, g = ln >> 4;
     u32x2_t v[NM][4];
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
-      const int I = blk_i(tri_c, mi(t)), J = blk_j(tri_c, mj(t));
+      const int I = blk_i(tri_c, mi(t), mj(t)), J = blk_j(tri_c, mi(t), mj(t));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int R = 32 * J + 8 * q + 4 * (g >> 1) + (j16 >> 2);
@@ -492,7 +512,7 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
     }
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
-      const int I = blk_i(tri_c, mi(t)), J = blk_j(tri_c, mj(t));
+      const int I = blk_i(tri_c, mi(t), mj(t)), J = blk_j(tri_c, mi(t), mj(t));
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<u32x2_t*>(sM + mat_off(32 * I + (ln & 31), 32 * J + 8 * q + 4 * (ln >> 5))) = v[t][q];
