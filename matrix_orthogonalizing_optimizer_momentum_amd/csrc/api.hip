@@ -629,6 +629,13 @@ int ns_stage_count(int kind, const Cfg& cfg, const DevTables& d) {
   return (!no_ns(kind) && d.n_mom > 0) ? std::max(cfg.K, 1) : 0;
 }
 
+// A step whose matrices all run on the resident-tile kernels, which sum the
+// hook's norms where they store O: the hook sums are finalized together with
+// the O norms, right after the tile launch.
+bool hook_sums_with_tiles(int kind, const Cfg& cfg, const DevTables& d) {
+  return kind == CALL_STEP && cfg.hook != kModeNone && d.n_tile > 0 && d.n_mom == 0 && d.n_hook1 == 0;
+}
+
 // Stages of one chunk's step: 0 = the opening pass, 1..n = the Newton-Schulz
 // iterations through the GEMM engine, n + 1 = the closing passes.
 int chunk_stages(int kind, const Cfg& cfg, const DevTables& d) { return 2 + ns_stage_count(kind, cfg, d); }
@@ -664,8 +671,12 @@ int run_chunk_stage(State& st, const Meta& meta, int kind, const Cfg& cfg, const
           MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs + g.job0, g.njobs, ta, s));
         }
         if (!gemm) {
+          // ||O||^2 (and <W, O>) per matrix, and with them the hook's
+          // (0, ||W||^2) sums when every matrix summed its norms where O was
+          // stored (the next slots; the closing passes then have nothing to
+          // reduce): one launch
           Prof pf(st, s, PC_FIN, 0, 0);
-          MUONH_TRY_HIP(launch_finalize(sl, d.nunits, d.nmats, s));  // ||O||^2 (and <W, O>) per matrix
+          MUONH_TRY_HIP(launch_finalize(sl, d.nunits, hook_sums_with_tiles(kind, cfg, d) ? 2 * d.nmats : d.nmats, s));
         }
       }
       if (gemm) {
@@ -712,8 +723,10 @@ int run_chunk_stage(State& st, const Meta& meta, int kind, const Cfg& cfg, const
         Prof pf(st, s, PC_HR, 0, d.bytes_hook1);
         MUONH_TRY_HIP(launch_hook_reduce(cfg.hook, d.hook_mats, d.hook1_blocks, d.n_hook1, sl, p.eta, s));
       }
-      Prof pf(st, s, PC_FIN, 0, 0);
-      MUONH_TRY_HIP(launch_finalize(sl, d.nunits + d.nmats, d.nmats, s));  // hook sums per matrix
+      if (!hook_sums_with_tiles(kind, cfg, d)) {
+        Prof pf(st, s, PC_FIN, 0, 0);
+        MUONH_TRY_HIP(launch_finalize(sl, d.nunits + d.nmats, d.nmats, s));  // hook sums per matrix
+      }
     }
     {
       Prof pf(st, s, PC_HW, 0, d.bytes_hook2);
