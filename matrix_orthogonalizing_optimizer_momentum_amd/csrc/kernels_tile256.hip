@@ -419,15 +419,23 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   // Element group q of the lane's value of block (I, J) -- rows 32 I + 8 q +
   // 4 lh + 0..3 of column 32 J + lc -- goes to row 32 J + lc, elements
   // 32 I + 8 q + 4 lh.. (mat_off: granule (4 I + q) ^ (lc % 16), byte 8 lh).
-  auto lo_addr = [&](int I, int J, int q) -> char* {
+  // (lb: the lane's part, 512 lc + 8 lh and lc % 16, derived once per pass)
+  struct LaneBase {
+    int row, sw;
+  };
+  auto lane_base = [&]() {
     const int ln = opaque(lane), l31 = ln & 31;
-    return sM + (32 * J + l31) * 512 + 8 * (ln >> 5) + (((4 * I + q) ^ (l31 & 15)) << 4);
+    return LaneBase{l31 * 512 + 8 * (ln >> 5), l31 & 15};
+  };
+  auto lo_addr = [&](const LaneBase& lb, int I, int J, int q) -> char* {
+    return sM + lb.row + 16384 * J + (((4 * I + q) ^ lb.sw) << 4);
   };
   // A = sc * acc (scaled: times sc, the first iteration's sig^2 and 1 after
   // it; a run-time branch between the two forms would join register states)
   auto put_a = [&](auto tri_c, auto scaled, float sc) __attribute__((always_inline)) {
     constexpr bool TRI = decltype(tri_c)::value;
     constexpr bool kScale = decltype(scaled)::value;
+    const LaneBase lb = lane_base();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -438,7 +446,7 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = kScale ? acc[i][j][4 * q + e] * sc : acc[i][j][4 * q + e];
-          *reinterpret_cast<u32x2_t*>(lo_addr(blk_i(tri_c, i, j), blk_j(tri_c, i, j), q)) =
+          *reinterpret_cast<u32x2_t*>(lo_addr(lb, blk_i(tri_c, i, j), blk_j(tri_c, i, j), q)) =
               u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
         // one block at a time: the scheduler would otherwise batch every
@@ -457,10 +465,11 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
     constexpr int kRi[9] = {0, 0, 1, 1, 2, 2, 3, 3, 0}, kRj[9] = {0, 1, 0, 1, 0, 1, 0, 1, 2};
     auto bi = [&](int t) { return TRI ? kTi[t] : kRi[t]; };
     auto bj = [&](int t) { return TRI ? kTj[t] : kRj[t]; };
+    const LaneBase lb = lane_base();
     u32x2_t av[2][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      av[0][q] = *reinterpret_cast<const u32x2_t*>(lo_addr(blk_i(tri_c, bi(0), bj(0)), blk_j(tri_c, bi(0), bj(0)), q));
+      av[0][q] = *reinterpret_cast<const u32x2_t*>(lo_addr(lb, blk_i(tri_c, bi(0), bj(0)), blk_j(tri_c, bi(0), bj(0)), q));
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const int i = bi(t), j = bj(t), cur = t & 1;
@@ -468,7 +477,7 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           av[cur ^ 1][q] = *reinterpret_cast<const u32x2_t*>(
-              lo_addr(blk_i(tri_c, bi(t + 1), bj(t + 1)), blk_j(tri_c, bi(t + 1), bj(t + 1)), q));
+              lo_addr(lb, blk_i(tri_c, bi(t + 1), bj(t + 1)), blk_j(tri_c, bi(t + 1), bj(t + 1)), q));
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -477,7 +486,7 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
         float v[4] = {b * lo_bf(a2[0]), b * hi_bf(a2[0]), b * lo_bf(a2[1]), b * hi_bf(a2[1])};
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = fmaf(c, acc[i][j][4 * q + e], v[e]);
-        *reinterpret_cast<u32x2_t*>(lo_addr(blk_i(tri_c, i, j), blk_j(tri_c, i, j), q)) =
+        *reinterpret_cast<u32x2_t*>(lo_addr(lb, blk_i(tri_c, i, j), blk_j(tri_c, i, j), q)) =
             u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
       __builtin_amdgcn_sched_barrier(0);
