@@ -4,8 +4,9 @@
 // "Hierarchical Muon: Tiled Newton-Schulz Updates for Efficient Muon
 // Optimization" (core claim, abstract): every T x T tile of a momentum matrix
 // gets the same finite Newton-Schulz map on its own.  Here one workgroup of
-// four waves (one per SIMD) owns one tile, zero-padded to 256 x 256 (exact:
-// [[X, 0], [0, 0]] maps to [[NS(X), 0], [0, 0]]), for the whole step:
+// four waves (one per SIMD, one workgroup per CU, looping over tiles) owns
+// one tile at a time, zero-padded to 256 x 256 (exact: [[X, 0], [0, 0]] maps
+// to [[NS(X), 0], [0, 0]]), for the whole step:
 //   - momentum M <- beta M + G (Muon explainer, momentum recap / Equation 1)
 //     on the tile's elements, M stored back, X0 = M and its Frobenius norm;
 //   - K iterations A = X X^T; B = b A + c A A; X = a X + B X (Muon explainer,
@@ -31,6 +32,7 @@
 //   - G3 (B X) takes X from the pieces: 32-deep slices of X^T ([n][k] rows of
 //     64 B) written from the registers of the waves that hold them while
 //     every wave runs the previous slice's MFMAs (double buffered).
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -108,19 +110,19 @@ __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 
 
 }  // namespace
 
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ jobs, TileArgs args) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+// One tile, start to end (the caller's barrier separates it from the
+// workgroup's previous tile).
+__device__ __forceinline__ void tile256_one(char* const smem, const TileMat* __restrict__ mats, const TileJob job,
+                                            const TileArgs& args, const int tid) {
   char* const sM = smem;
   char* const sP0 = smem + kMatB;
   // reduction scratch in the second slice: it is first written by G3 of the
   // first iteration, long after every thread's read of the pre-scale sum
   double* const sred = reinterpret_cast<double*>(smem + kMatB + kPieceB);
 
-  const TileJob job = jobs[blockIdx.x];
   const TileMat mt = mats[job.mat];
   const int T = args.T;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;  // quadrant origin
   const int lc = lane & 31, lh = lane >> 5;
@@ -756,12 +758,61 @@ void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ 
   }
 }
 
+// Persistent: one workgroup per CU, workgroup b takes tiles b, b + grid, ...
+// (with a grid of all CUs, a multiple of 8, tile j stays on XCD j % 8, as
+// with one workgroup per tile).
+// Every tile costs the same, so workgroups that start together stay in step
+// and all of them load their inputs, and later store their outputs, at the
+// same moments, sharing HBM 256 ways while its bandwidth is idle the rest of
+// the tile.  With stagger > 0 the upper half of the grid first waits that
+// many ticks of the 100 MHz real-time counter (about half a tile), so that
+// one half's loads and stores fall into the other half's products.  The wait
+// ends after at most kMaxNaps naps whatever the counter reads.
+constexpr int kMaxNaps = 4096;
+
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_tile256_ns(const TileMat* __restrict__ mats, const TileJob* __restrict__ jobs, int njobs, TileArgs args,
+                  int stagger) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  if (stagger > 0 && 2 * (int)blockIdx.x >= (int)gridDim.x) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (int k = 0; k < kMaxNaps && __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)stagger; ++k)
+      __builtin_amdgcn_s_sleep(127);
+  }
+  for (int jb = blockIdx.x; jb < njobs; jb += gridDim.x) {
+    __syncthreads();  // the previous tile's last LDS reads are done
+    // (the thread id through an empty asm: nothing derived from it is loop
+    // invariant, so nothing is held in registers across the tiles)
+    tile256_one(smem, mats, jobs[jb], args, opaque((int)threadIdx.x));
+  }
+}
+
 hipError_t launch_tile256_ns(const TileMat* mats, const TileJob* jobs, int njobs, const TileArgs& args,
                              hipStream_t s) {
   if (njobs <= 0) return hipSuccess;
   if (args.T <= kTileResidentMax || args.T > kTileFusedMax || args.K < 0 || args.K > kTileMaxK || !args.fold)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_tile256_ns, dim3(njobs), dim3(kNT), 0, s, mats, jobs, args);
+  // one workgroup fills a CU (all of its LDS)
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int ncu = cus[dev].load(std::memory_order_relaxed);
+  if (ncu == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    ncu = n > 8 ? n / 8 * 8 : 8;
+    cus[dev].store(ncu, std::memory_order_relaxed);
+  }
+  const int grid = njobs < ncu ? njobs : ncu;
+  // Stagger only when every workgroup has two tiles or more; the extra tiles
+  // of a ragged count go to the lower half, which does not wait.  The wait is
+  // half a tile: about 28 us of loads and stores plus 21 us per iteration on
+  // MI355X.
+  const int stagger = njobs >= 2 * grid && njobs % grid <= grid / 2 ? (1400 + 1050 * args.K) : 0;
+  hipLaunchKernelGGL(k_tile256_ns, dim3(grid), dim3(kNT), 0, s, mats, jobs, njobs, args, stagger);
   return hipGetLastError();
 }
 
