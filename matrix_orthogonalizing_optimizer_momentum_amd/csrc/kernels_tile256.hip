@@ -105,6 +105,19 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// wave_sum with the lane id passed in (the same exchanges and additions, so
+// the same bits): the lane addresses are then not loop invariant either.
+__device__ __forceinline__ double wave_sum_at(double v, int lane) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int a = (lane ^ o) << 2;
+    const int lo = __builtin_amdgcn_ds_bpermute(a, __double2loint(v));
+    const int hi = __builtin_amdgcn_ds_bpermute(a, __double2hiint(v));
+    v += __hiloint2double(hi, lo);
+  }
+  return v;
+}
+
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -206,11 +219,13 @@ __device__ __forceinline__ void tile256_one(char* const smem, const TileMat* __r
     }
   }
   {
-    const double d = wave_sum((double)sq);
+    const double d = wave_sum_at((double)sq, lane);
     if (lane == 0) sred[wave] = d;
   }
   __syncthreads();
-  const double sig = 1.0 / (sqrt(((sred[0] + sred[1]) + sred[2]) + sred[3]) + (double)args.eps);
+  // (eps through the empty asm: its fp64 conversion is not held across tiles)
+  const double sig =
+      1.0 / (sqrt(((sred[0] + sred[1]) + sred[2]) + sred[3]) + (double)__int_as_float(opaque(__float_as_int(args.eps))));
 
   // X0 into registers in the accumulator layout: lane l of block (i, j),
   // group q holds rows 8 q + 4 (l / 32) + 0..3 of column l % 32 -- one
@@ -733,9 +748,12 @@ __device__ __forceinline__ void tile256_one(char* const smem, const TileMat* __r
     }
   }
   // block sums: one fp64 partial per tile (the slices are idle: scratch)
-  osq = wave_sum(osq);
-  swo = wave_sum(swo);
-  sww = wave_sum(sww);
+  {
+    const int ln = opaque(lane);  // (lane addresses derived here, not shared with the input's sum)
+    osq = wave_sum_at(osq, ln);
+    swo = wave_sum_at(swo, ln);
+    sww = wave_sum_at(sww, ln);
+  }
   if (lane == 0) {
     sred[wave] = osq;
     sred[4 + wave] = swo;
