@@ -258,6 +258,38 @@ def test_tiled_ns_bf16_ragged(T, prec):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("shape", [(4096, 8192), (4096, 7296)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_tiled_ns_fused_many_tiles_bitwise_vs_single_tile_calls(shape):
+    # The fused 256-tile kernel runs one workgroup per CU over a strided tile
+    # list; with two tiles or more per workgroup and a short ragged rest
+    # (512 tiles on 256 CUs) the upper half of the grid starts late, with a
+    # long rest (464 tiles) it does not.  A tile's result must not depend on
+    # which workgroup computed it or what that workgroup computed before:
+    # sampled tiles equal a call on the tile alone bit for bit, and two of
+    # them match the tiled oracle.
+    H, W = shape
+    T = 256
+    banner(f"fused tiles, many per workgroup: {H}x{W} T={T}")
+    X = gen.store(gen.spiked_grad(H, W, 1e-3, 77), "bf16")
+    out = host(mm.ns_orthogonalize([dev(X, torch.bfloat16)], K=5, tile_T=T)[0])
+    nr, nc = H // T, -(-W // T)
+    ntiles = nr * nc
+    rng = np.random.default_rng(5)
+    picks = {0, 1, 255, 256, 257, 383, 384, ntiles - 1} | {int(j) for j in rng.integers(0, ntiles, 16)}
+    for j in sorted(picks):
+        a, b = divmod(j, nc)
+        tile = np.ascontiguousarray(X[a * T:(a + 1) * T, b * T:(b + 1) * T])
+        one = host(mm.ns_orthogonalize([dev(tile, torch.bfloat16)], K=5, tile_T=T)[0])
+        got = out[a * T:(a + 1) * T, b * T:(b + 1) * T]
+        assert np.array_equal(got, one), f"tile {j} ({a}, {b}) differs from its own call"
+    for j in (257, ntiles - 1):
+        a, b = divmod(j, nc)
+        tile = X[a * T:(a + 1) * T, b * T:(b + 1) * T]
+        err = rel(out[a * T:(a + 1) * T, b * T:(b + 1) * T], orc.newton_schulz(tile, 5))
+        print(f"  tile {j}: rel err against the oracle {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("T", [192, 256])
 @pytest.mark.parametrize("K", [0, 1, 5])
 @pytest.mark.parametrize("shape", [(300, 700), (512, 768), (1000, 260), (300, 701)], ids=lambda s: f"{s[0]}x{s[1]}")
