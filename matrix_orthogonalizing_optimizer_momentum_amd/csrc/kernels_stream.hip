@@ -231,6 +231,12 @@ __device__ __forceinline__ float hook_coef(const HookMat& hm, const SlotTable& s
   return (float)((double)eta * (double)hm.oscale / sqrt(n2));
 }
 
+// ||W - c O||^2 formed as ||W||^2 - 2 c <W, O> + c^2 ||O||^2: rounding can take
+// it below zero, which is clamped; a NaN (a non-finite O or W) is kept, so the
+// matrix takes the same branch and is counted as non-finite exactly as when
+// pass 1 sums ||W - c O||^2 itself.
+__device__ __forceinline__ double clamp_expanded(double e) { return e < 0.0 ? 0.0 : e; }
+
 // Per-matrix decision of pass 2, identical in every block of the matrix,
 // from ||W'||^2 (v0) and ||W||^2 (v1).  branch 0: scale W', 1: scale W
 // (Hyperball restore), 2: leave W.
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(kHookThreads) void k_hook_write(
       const double c = (double)coef;
       const double uu = hm.onorm_slot >= 0 ? st.sums[2 * hm.onorm_slot] : 0.0;
       const double wo = hm.onorm_slot >= 0 ? st.sums[2 * hm.onorm_slot + 1] : 0.0;
-      v0 = fmax(v1 - 2.0 * c * wo + c * c * uu, 0.0);
+      v0 = clamp_expanded(v1 - 2.0 * c * wo + c * c * uu);
     } else {
       v0 = st.sums[2 * hm.slot];
     }
@@ -526,7 +532,7 @@ __global__ __launch_bounds__(kHookThreads) void k_adam_write(
     if (MODE == kModeHB) coef = uu > 0.0 ? (float)((double)eta * (double)hm.oscale / sqrt(uu)) : 0.f;
     else if (MODE == kModeRel) coef = uu > 0.0 ? (float)((double)eta * sqrt(v1) / sqrt(uu)) : 0.f;
     const double c = (double)coef;
-    v0 = fmax(v1 - 2.0 * c * wu + c * c * uu, 0.0);
+    v0 = clamp_expanded(v1 - 2.0 * c * wu + c * c * uu);
   }
   const HookDecision dec = hook_decide(MODE, v0, v1, hm.rho, zero_rel_eps, outward, inward, rb_eps);
   if (hb.blk == 0 && threadIdx.x == 0) hook_flags(MODE, coef, true, dec.branch, v0, v1, flags);

@@ -937,6 +937,67 @@ def test_adamh_zero_gradient_projects_only():
 
 
 # ---------------------------------------------------------------------------
+# non-finite gradients: counted per matrix on every path, other matrices untouched
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("tile,hook", [(0, "hyperball"), (64, "hyperball"), (256, "hyperball"),
+                                       (0, "radial_brake"), (128, "radial_brake")])
+def test_nonfinite_gradient_is_flagged(tile, hook):
+    # One gradient holds an Inf: its momentum, pre-scale and O become
+    # non-finite, so the matrix's post-update norm is not finite.  Whether the
+    # hook's norms come from a pass of their own (full-matrix NS) or were
+    # summed where O is stored (resident and fused tiles), the flag counts
+    # that matrix once; under Hyperball the step then restores the pre-update
+    # W to its radius (the norm test fails, W itself is finite); the other
+    # matrix gets exactly the bits of a call of its own.
+    banner(f"non-finite gradient tile={tile} hook={hook}")
+    shapes = [(300, 520), (256, 384)]
+    Ws, Gs, Ms = gen.model_set(shapes, 2, 5)
+    rho = [np.float32(np.linalg.norm(w.astype(np.float64))) for w in Ws]
+    Gbad = Gs[0].copy()
+    Gbad[7, 11] = np.inf
+    kw = dict(eta=0.02, beta=0.95, K=5, tile_T=tile, hook=hook)
+    if hook == "radial_brake":
+        kw.update(outward=0.5, inward=1.0)
+    w2 = [dev(w) for w in Ws]
+    m2 = [dev(m, torch.bfloat16) for m in Ms]
+    mm.reset_flags()
+    mm.muonh_step(w2, [dev(Gbad, torch.bfloat16), dev(Gs[1], torch.bfloat16)], m2, rho=rho, **kw)
+    torch.cuda.synchronize()
+    flags = mm.get_flags()
+    print(f"  flags {flags}")
+    assert flags[3] == 1
+    w1 = [dev(Ws[1])]
+    m1 = [dev(Ms[1], torch.bfloat16)]
+    mm.muonh_step(w1, [dev(Gs[1], torch.bfloat16)], m1, rho=rho[1:], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(w2[1], w1[0]) and torch.equal(m2[1], m1[0])
+    if hook == "hyperball":
+        got = host(w2[0])
+        assert np.isfinite(got).all() and flags[1] == 1
+        w64 = Ws[0].astype(np.float64)
+        assert np.allclose(got, float(rho[0]) * w64 / np.linalg.norm(w64), rtol=1e-5, atol=1e-7)
+
+
+def test_adamh_nonfinite_gradient_is_flagged():
+    # AdamH forms ||W - c U||^2 from sums taken in its moments pass: a NaN
+    # gradient is counted there too, and Hyperball restores W to its radius.
+    banner("adamh non-finite gradient")
+    W = gen.gaussian((64, 96), 0.5, 971)
+    G = gen.gaussian((64, 96), 0.02, 972)
+    G[3, 5] = np.nan
+    w_t = [dev(W)]
+    mm.reset_flags()
+    mm.adamh_step(w_t, [dev(G)], [torch.zeros(64, 96, device=DEV)], [torch.zeros(64, 96, device=DEV)], 0.1, 1,
+                  rho=[2.0])
+    torch.cuda.synchronize()
+    flags = mm.get_flags()
+    print(f"  flags {flags}")
+    assert flags[3] == 1 and flags[1] == 1
+    w64 = W.astype(np.float64)
+    assert np.allclose(host(w_t[0]), 2.0 * w64 / np.linalg.norm(w64), rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------------------
 # per-matrix tile sizes (Hierarchical Muon: a tile side per layer)
 # ---------------------------------------------------------------------------
 MIXED_SHAPES = [(768, 2304), (768, 768), (768, 3072), (3072, 768), (300, 700)]
