@@ -27,7 +27,7 @@ K (3 r^2 s + r^3), which counts the symmetric Gram and polynomial products
 (A = X X^T and A A) at half their dense work.
 
     python bench.py [--steps K] [--warmup W] [--workload dense8b|gpt2|qwen1p2b|single256|single64x128]
-                    [--tile T] [--compare-tile T] [--ns-precision fold|x32] [--lanes L]
+                    [--tile T] [--compare-tile T] [--ns-precision h16|fold|x32] [--lanes L]
                     [--profile-lanes L] [--ws-limit-mib MiB] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -401,7 +401,7 @@ def main():
     ap.add_argument("--compare-tile", type=int, default=None,
                     help="also time the Hierarchical-Muon step with this tile side in the same run "
                          "(default: 256 for the 8B-shaped set, else none; 0: none)")
-    ap.add_argument("--ns-precision", default="fold", choices=["fold", "x32"])
+    ap.add_argument("--ns-precision", default="h16", choices=["h16", "fold", "x32"])
     ap.add_argument("--hook", default="hyperball", choices=["hyperball", "radial_brake", "relative", "none"])
     ap.add_argument("--optimizer", default="muonh", choices=["muonh", "adamh"],
                     help="adamh: the Hyperball wrapper around Adam (streaming only, no Newton-Schulz)")
@@ -479,13 +479,18 @@ def main():
 
     chunk_desc = (f", memory-bounded chunking ({args.ws_limit_mib} MiB workspace budget, "
                   f"{head['chunks']} chunks)" if args.ws_limit_mib else "")
+    h16 = args.ns_dtype == "bf16" and args.ns_precision == "h16"
+    ns_desc = {"h16": "bf16 NS operands in the first iteration, fp16 iterates after it",
+               "fold": "bf16 NS operands and iterates", "x32": "bf16 NS operands, fp32 master X"}[args.ns_precision]
+    if args.ns_dtype != "bf16":
+        ns_desc = f"{args.ns_dtype} NS operands"
     if args.optimizer == "adamh":
         opt_desc = ("AdamH step (Adam betas 0.9/0.95, eps 1e-8, bias-corrected), bf16 grads, fp32 moments "
                     "and master weights, " + HOOK_DESC[args.hook])
     else:
         opt_desc = (f"MuonH step, K={K} quintic NS "
                     f"{'tiled T=' + str(args.tile) if args.tile else 'full-matrix'}{chunk_desc}, "
-                    f"{args.state} grads/momentum, {args.ns_dtype} NS operands, fp32 master weights, "
+                    f"{args.state} grads/momentum, {ns_desc}, fp32 master weights, "
                     + HOOK_DESC[args.hook])
     prof_key = {"workload": args.workload, "tile": args.tile, "K": K, "ns_precision": args.ns_precision,
                 "ws_limit_mib": args.ws_limit_mib, "hook": args.hook, "optimizer": args.optimizer}
@@ -505,7 +510,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": args.ns_dtype if args.optimizer == "muonh" else "f32",
+        # the arithmetic type of the Newton-Schulz products: with fp16 iterates
+        # 12 of the 15 products of a 5-step iteration run on fp16 operands
+        "dtype": ("fp16" if h16 else args.ns_dtype) if args.optimizer == "muonh" else "f32",
         "data": "synthetic (seeded device RNG: W0 ~ N(0, 0.02^2); grads N(0, 1e-3^2) + rank-4 10x spike)",
         "config": {"workload": f"{wdesc}; {opt_desc}", "optimizer": args.optimizer,
                    "matrices": len(shapes), "K": K, "tile_T": args.tile, "ns_precision": args.ns_precision,

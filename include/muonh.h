@@ -99,19 +99,31 @@ enum {
 /* element types */
 enum { MUONH_F32 = 0, MUONH_BF16 = 1 };
 
-/* How bf16 Newton-Schulz keeps X between iterations (MFMA operands are bf16
- * and accumulation is fp32 in both):
+/* How Newton-Schulz with bf16 operands keeps X (and the Gram side) between
+ * iterations; accumulation is fp32 in every mode:
  *   MUONH_NS_FOLD -- X itself is stored in bf16, as in the Muon explainer's
  *                    code section; a*X + B*X is formed in fp32 and rounded
- *                    once per iteration (default);
+ *                    once per iteration;
  *   MUONH_NS_X32  -- an fp32 master copy of X carries the a*X term, a bf16
  *                    shadow feeds the matrix cores (8 more bytes of traffic
- *                    per element and iteration).
- * Both fold the 1/(||M||+eps) pre-scale into the first iteration instead of
- * rounding the pre-scaled X0 to bf16, and when the NS input is not itself a
- * bf16 value (fp32 state, or the Nesterov blend) both seed the first a*X0
- * term from an fp32 copy of X0.  Ignored when ns_dtype is MUONH_F32. */
-enum { MUONH_NS_FOLD = 0, MUONH_NS_X32 = 1 };
+ *                    per element and iteration);
+ *   MUONH_NS_H16  -- the first iteration reads X0 and forms A0 = X0 X0^T and
+ *                    B0 in bf16, as FOLD does; from X1 on, X, A and B are
+ *                    stored in IEEE fp16 and the products after the first
+ *                    iteration's run on fp16 operands (the matrix cores'
+ *                    fp16 rate equals their bf16 rate).  Once the pre-scale
+ *                    has been applied every iterate is bounded (singular
+ *                    values below 1.25, |B| below 12), so fp16's range holds
+ *                    them and its 3 more mantissa bits shrink the rounding
+ *                    of X about 8x at FOLD's traffic (default).
+ * All fold the 1/(||M||+eps) pre-scale into the first iteration instead of
+ * rounding the pre-scaled X0, and when the NS input is not itself a bf16
+ * value (fp32 state, or the Nesterov blend) all seed the first a*X0 term from
+ * an fp32 copy of X0.  Resident tiles (tile sides <= 128) keep an fp32 master
+ * X in registers under X32 and H16; tiles of side 129..256 on the fused
+ * kernel hold X in bf16 under FOLD and H16.  Ignored when ns_dtype is
+ * MUONH_F32. */
+enum { MUONH_NS_FOLD = 0, MUONH_NS_X32 = 1, MUONH_NS_H16 = 2 };
 
 /* weight-update hook */
 enum { MUONH_HOOK_HYPERBALL = 0, MUONH_HOOK_RADIAL_BRAKE = 1, MUONH_HOOK_NONE = 2, MUONH_HOOK_RELATIVE = 3 };
@@ -127,7 +139,7 @@ typedef struct muonh_opts {
   int          state_dtype;     /* dtype of grads, momentum, ns_orthogonalize in/out and
                                    frob_project's U: MUONH_BF16 (default) or MUONH_F32 */
   int          ns_dtype;        /* Newton-Schulz operand dtype: MUONH_BF16 (default) or MUONH_F32 */
-  int          ns_precision;    /* MUONH_NS_FOLD (default) or MUONH_NS_X32 */
+  int          ns_precision;    /* MUONH_NS_H16 (default), MUONH_NS_FOLD or MUONH_NS_X32 */
   const float* coeffs;          /* host, 3*K floats: (a,b,c) for iteration k at [3k..3k+2];
                                    NULL = (3.4445, -4.7750, 2.0315) every iteration */
   float        ns_eps;          /* added to ||M||_F before dividing; default 1e-7 */

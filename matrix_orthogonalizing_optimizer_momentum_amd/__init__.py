@@ -17,7 +17,7 @@ Entry points mirror the C ABI in ``include/muonh.h``:
   ``profile_begin()``, ``profile_read()``, ``strerror(code)``, ``version()``
 
 ``opts`` keywords: ``ns_dtype`` ("bf16" | "f32"), ``ns_precision``
-("fold" | "x32"), ``coeffs`` (K rows of (a, b, c)), ``ns_eps``,
+("h16" | "fold" | "x32"; default "h16"), ``coeffs`` (K rows of (a, b, c)), ``ns_eps``,
 ``zero_rel_eps``, ``hook`` ("hyperball" | "radial_brake" | "relative" | "none"),
 ``hyperball_step`` ("unit" | "radius"), ``tile_sizes`` (per-matrix tile sides, 0 = full),
 ``outward``, ``inward``, ``rb_eps``, ``workspace_limit`` (bytes),
@@ -35,7 +35,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuonh.so
 
 MUONH_OK, MUONH_EINVAL, MUONH_ENOMEM, MUONH_EHIP, MUONH_ENOTIMPL = 0, -1, -2, -3, -4
 MUONH_F32, MUONH_BF16 = 0, 1
-MUONH_NS_FOLD, MUONH_NS_X32 = 0, 1
+MUONH_NS_FOLD, MUONH_NS_X32, MUONH_NS_H16 = 0, 1, 2
+_NS_PRECISION = {"fold": MUONH_NS_FOLD, "x32": MUONH_NS_X32, "h16": MUONH_NS_H16}
 MUONH_HOOK_HYPERBALL, MUONH_HOOK_RADIAL_BRAKE, MUONH_HOOK_NONE, MUONH_HOOK_RELATIVE = 0, 1, 2, 3
 MUONH_HB_STEP_UNIT, MUONH_HB_STEP_RADIUS = 0, 1
 
@@ -194,7 +195,7 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
 
 
-def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coeffs=None, ns_eps=None,
+def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="h16", coeffs=None, ns_eps=None,
               zero_rel_eps=None, hook="hyperball", outward=None, inward=None, rb_eps=None,
               workspace_limit=0, stream=None, K=None, momentum="sum", nesterov=False, weight_decay=None, lanes=0,
               hyperball_step="unit", tile_sizes=None):
@@ -205,7 +206,7 @@ def make_opts(state_dtype=MUONH_BF16, ns_dtype="bf16", ns_precision="fold", coef
     lib.muonh_default_opts(ctypes.byref(o))
     o.state_dtype = state_dtype
     o.ns_dtype = {"bf16": MUONH_BF16, "f32": MUONH_F32}[ns_dtype]
-    o.ns_precision = {"x32": MUONH_NS_X32, "fold": MUONH_NS_FOLD}[ns_precision]
+    o.ns_precision = _NS_PRECISION[ns_precision]
     keep = []
     if coeffs is not None:
         flat = [float(v) for row in coeffs for v in row]
@@ -396,7 +397,7 @@ def plan_query(shapes, K=5, tile_T=0, workspace_limit=0, **opts):
     if "ns_dtype" in opts:
         o.ns_dtype = {"bf16": MUONH_BF16, "f32": MUONH_F32}[opts["ns_dtype"]]
     if "ns_precision" in opts:
-        o.ns_precision = {"x32": MUONH_NS_X32, "fold": MUONH_NS_FOLD}[opts["ns_precision"]]
+        o.ns_precision = _NS_PRECISION[opts["ns_precision"]]
     if "lanes" in opts:
         o.lanes = int(opts["lanes"])
     keep = []

@@ -48,9 +48,9 @@ hipError_t launch_adam_write(int mode, const HookMat* mats, const HookBlock* blo
 hipError_t launch_sumsq(const HookMat* mats, const HookBlock* blocks, int nblocks, const SlotTable& st,
                         hipStream_t s);
 hipError_t launch_finalize(const SlotTable& st, int slot0, int nslots, hipStream_t s);
-hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs, int njobs,
-                          float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
-                          int master32, int seed32, const SlotTable& st, hipStream_t s);
+hipError_t launch_ns_gemm(int op_dt, int out_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs,
+                          int njobs, float a, float b, float c, float eps, int first, int last, int cur,
+                          int no_mma, int master32, int seed32, const SlotTable& st, hipStream_t s);
 hipError_t launch_tile_ns(int state_dt, int op_dt, const TileMat* mats, const TileJob* jobs, int njobs,
                           const TileArgs& args, hipStream_t s);
 
@@ -226,7 +226,8 @@ int resolve(const muonh_opts* in, int K, Resolved& r) {
   if (o.deterministic != 0 && o.deterministic != 1) return MUONH_EINVAL;
   if (o.state_dtype != MUONH_BF16 && o.state_dtype != MUONH_F32) return MUONH_EINVAL;
   if (o.ns_dtype != MUONH_BF16 && o.ns_dtype != MUONH_F32) return MUONH_EINVAL;
-  if (o.ns_precision != MUONH_NS_X32 && o.ns_precision != MUONH_NS_FOLD) return MUONH_EINVAL;
+  if (o.ns_precision != MUONH_NS_X32 && o.ns_precision != MUONH_NS_FOLD && o.ns_precision != MUONH_NS_H16)
+    return MUONH_EINVAL;
   if (o.hyperball_step != MUONH_HB_STEP_UNIT && o.hyperball_step != MUONH_HB_STEP_RADIUS) return MUONH_EINVAL;
   if (o.hook != MUONH_HOOK_HYPERBALL && o.hook != MUONH_HOOK_RADIAL_BRAKE && o.hook != MUONH_HOOK_NONE &&
       o.hook != MUONH_HOOK_RELATIVE)
@@ -285,6 +286,7 @@ Cfg make_cfg(int kind, int n, int K, int tile_T, const Resolved& r, size_t limit
   c.state_dt = r.o.state_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.op_dt = r.o.ns_dtype == MUONH_F32 ? DT_F32 : DT_BF16;
   c.x32 = (c.op_dt == DT_BF16 && r.o.ns_precision == MUONH_NS_X32) ? 1 : 0;
+  c.h16 = (c.op_dt == DT_BF16 && r.o.ns_precision == MUONH_NS_H16) ? 1 : 0;
   // bf16 operands, NS input not a bf16 value: fp32 state, or the Nesterov blend
   c.seed32 = (c.op_dt == DT_BF16 && (c.state_dt == DT_F32 || (kind == CALL_STEP && r.o.nesterov))) ? 1 : 0;
   c.hook = r.o.hook == MUONH_HOOK_RADIAL_BRAKE ? kModeRB
@@ -433,6 +435,7 @@ int get_plan(State& st, const Plan& plan, const Cfg& cfg, const CallPtrs& p, con
   key.push_back((uint64_t)cfg.state_dt);
   key.push_back((uint64_t)cfg.op_dt);
   key.push_back((uint64_t)cfg.x32);
+  key.push_back((uint64_t)cfg.h16);
   key.push_back((uint64_t)cfg.seed32);
   key.push_back((uint64_t)cfg.hook);
   key.push_back((uint64_t)cfg.hb_radius);
@@ -592,29 +595,34 @@ int run_ns_iter(State& st, const Cfg& cfg, const DevTables& d, const Resolved& r
   if (cfg.K == 0) {
     for (int g = 0; g < kGemmCfgs; ++g) {
       Prof pf(st, s, PC_G3, 0, 0);
-      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], 1.f, 0.f, 0.f, eps, 1, 1, 0, 1,
-                                   cfg.x32, cfg.seed32, sl, s));
+      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], 1.f, 0.f, 0.f, eps, 1,
+                                   1, 0, 1, cfg.x32, cfg.seed32, sl, s));
     }
   } else {
     const float a = r.coeffs[3 * k], b = r.coeffs[3 * k + 1], c = r.coeffs[3 * k + 2];
     const int first = k == 0, last = k == cfg.K - 1, cur = k & 1;
+    // Storage of this iteration's operands and products: with fp16 iterates
+    // (h16) the first iteration reads X0 and forms A0, B0 in bf16 and stores
+    // X1 in fp16; every later product reads and stores fp16.
+    const int in_dt = (cfg.h16 && !first) ? DT_F16 : cfg.op_dt;
+    const int x_dt = cfg.h16 ? DT_F16 : cfg.op_dt;
     for (int g = 0; g < kGemmCfgs; ++g) {
       if (!d.n_g12[g]) continue;
       Prof pf(st, s, PC_G1, d.flops_g1[g], 0);
-      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 0, g, d.units, d.g12[g], d.n_g12[g], a, b, c, eps, first, 0, cur, 0,
-                                   cfg.x32, cfg.seed32, sl, s));
+      MUONH_TRY_HIP(launch_ns_gemm(in_dt, in_dt, 0, g, d.units, d.g12[g], d.n_g12[g], a, b, c, eps, first, 0, cur,
+                                   0, cfg.x32, cfg.seed32, sl, s));
     }
     for (int g = 0; g < kGemmCfgs; ++g) {
       if (!d.n_g12[g]) continue;
       Prof pf(st, s, PC_G2, d.flops_g2[g], 0);
-      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 1, g, d.units, d.g12[g], d.n_g12[g], a, b, c, eps, first, 0, cur, 0,
-                                   cfg.x32, cfg.seed32, sl, s));
+      MUONH_TRY_HIP(launch_ns_gemm(in_dt, in_dt, 1, g, d.units, d.g12[g], d.n_g12[g], a, b, c, eps, first, 0, cur,
+                                   0, cfg.x32, cfg.seed32, sl, s));
     }
     for (int g = 0; g < kGemmCfgs; ++g) {
       if (!d.n_g3[g]) continue;
       Prof pf(st, s, PC_G3, d.flops_g3[g], 0);
-      MUONH_TRY_HIP(launch_ns_gemm(cfg.op_dt, 2, g, d.units, d.g3[g], d.n_g3[g], a, b, c, eps, first, last, cur, 0,
-                                   cfg.x32, cfg.seed32, sl, s));
+      MUONH_TRY_HIP(launch_ns_gemm(in_dt, last ? in_dt : x_dt, 2, g, d.units, d.g3[g], d.n_g3[g], a, b, c, eps,
+                                   first, last, cur, 0, cfg.x32, cfg.seed32, sl, s));
     }
     if (!last) return MUONH_OK;
   }
@@ -659,7 +667,10 @@ int run_chunk_stage(State& st, const Meta& meta, int kind, const Cfg& cfg, const
         for (int k = 0; k < cfg.K; ++k)
           for (int j = 0; j < 3; ++j) ta.abc[k][j] = r.coeffs[3 * k + j];
         ta.K = cfg.K;
-        ta.fold = (cfg.op_dt == DT_BF16 && !cfg.x32) ? 1 : 0;
+        // resident tiles keep X in registers: an fp32 master unless X is to be
+        // rounded to bf16 between iterations (FOLD); the fused 256-tile kernel
+        // always holds it as bf16 (it has no room for more)
+        const int fold_res = (cfg.op_dt == DT_BF16 && !cfg.x32 && !cfg.h16) ? 1 : 0;
         ta.beta = beta;
         ta.gcoef = (kind == CALL_STEP && r.o.momentum_ema) ? 1.f - beta : 1.f;
         ta.nesterov = (kind == CALL_STEP && r.o.nesterov) ? 1 : 0;
@@ -667,6 +678,7 @@ int run_chunk_stage(State& st, const Meta& meta, int kind, const Cfg& cfg, const
         ta.st = sl;
         for (const TileGroup& g : d.tile_groups) {
           ta.T = g.T;
+          ta.fold = g.T > kTileResidentMax ? 1 : fold_res;
           Prof pf(st, s, g.T > kTileResidentMax ? PC_T256 : PC_TILE, g.flops, g.bytes);
           MUONH_TRY_HIP(launch_tile_ns(cfg.state_dt, cfg.op_dt, d.tile_mats, d.tile_jobs + g.job0, g.njobs, ta, s));
         }
@@ -900,7 +912,7 @@ void muonh_default_opts(muonh_opts* o) {
   o->stream = nullptr;
   o->state_dtype = MUONH_BF16;
   o->ns_dtype = MUONH_BF16;
-  o->ns_precision = MUONH_NS_FOLD;
+  o->ns_precision = MUONH_NS_H16;
   o->coeffs = nullptr;
   o->ns_eps = 1e-7f;
   o->zero_rel_eps = 1e-6f;

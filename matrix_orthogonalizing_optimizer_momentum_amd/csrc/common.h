@@ -8,6 +8,7 @@
 namespace muonh {
 
 typedef uint16_t bf16_t;  // bfloat16 storage
+typedef _Float16 f16_t;   // IEEE half storage (Newton-Schulz iterates X, A, B in MUONH_NS_H16)
 
 // Pointers taken from descriptor tables are generic; accesses through them
 // compile to flat loads/stores, which count against both the vector-memory
@@ -30,6 +31,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
+
+// IEEE half <-> float: the conversion instructions round to nearest even.
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// The two 16-bit values of a packed pair as float (lo in bits 0..15), for
+// either 16-bit storage type.
+template <typename T> __device__ __forceinline__ float lo16(uint32_t w);
+template <typename T> __device__ __forceinline__ float hi16(uint32_t w);
+template <> __device__ __forceinline__ float lo16<bf16_t>(uint32_t w) { return __uint_as_float(w << 16); }
+template <> __device__ __forceinline__ float hi16<bf16_t>(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <> __device__ __forceinline__ float lo16<f16_t>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2_t, w)[0];
+}
+template <> __device__ __forceinline__ float hi16<f16_t>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2_t, w)[1];
+}
+template <typename T> __device__ __forceinline__ uint32_t pack16x2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack16x2<bf16_t>(float lo, float hi) { return pack_bf16x2(lo, hi); }
+template <> __device__ __forceinline__ uint32_t pack16x2<f16_t>(float lo, float hi) { return pack_f16x2(lo, hi); }
 
 // Storage traits: load / store one element of a storage type as float.
 template <typename T> struct St;
@@ -117,6 +140,12 @@ __device__ __forceinline__ void store8(bf16_t* p, int64_t i, const float (&v)[8]
   u32x4_t w;
 #pragma unroll
   for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+  *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(p + i)) = w;
+}
+__device__ __forceinline__ void store8(f16_t* p, int64_t i, const float (&v)[8]) {
+  u32x4_t w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = pack_f16x2(v[2 * k], v[2 * k + 1]);
   *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(p + i)) = w;
 }
 __device__ __forceinline__ void store8(float* p, int64_t i, const float (&v)[8]) {

@@ -6,7 +6,7 @@
 
 namespace muonh {
 
-enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+enum DType : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };  // DT_F16: Newton-Schulz storage only
 
 // Padding granule of every workspace leading dimension (elements).  Producers
 // write zeros into [valid, padded) so GEMM loaders can read whole vectors.

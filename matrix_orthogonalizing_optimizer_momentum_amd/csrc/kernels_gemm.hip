@@ -45,6 +45,7 @@
 namespace muonh {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
@@ -57,6 +58,16 @@ template <> struct Mf<bf16_t> {
   static __device__ __forceinline__ frag ld(const bf16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
   static __device__ __forceinline__ f32x16_t mma(frag a, frag b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mf<f16_t> {
+  static constexpr int KSTEP = 16;
+  static constexpr int VEC = 8;
+  static constexpr int PAD = 8;
+  using frag = f16x8_t;
+  static __device__ __forceinline__ frag ld(const f16_t* p) { return *reinterpret_cast<const f16x8_t*>(p); }
+  static __device__ __forceinline__ f32x16_t mma(frag a, frag b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
 };
 template <> struct Mf<float> {
@@ -98,19 +109,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // 4 consecutive elements as float.
-__device__ __forceinline__ void load4(const bf16_t* p, int64_t i, float (&v)[4]) {
+template <typename T16>
+__device__ __forceinline__ void load4_16(const T16* p, int64_t i, float (&v)[4]) {
   const u32x2_t q = *reinterpret_cast<const MUONH_GLOBAL u32x2_t*>(gmem(p + i));
-  v[0] = __uint_as_float(q[0] << 16);
-  v[1] = __uint_as_float(q[0] & 0xffff0000u);
-  v[2] = __uint_as_float(q[1] << 16);
-  v[3] = __uint_as_float(q[1] & 0xffff0000u);
+  v[0] = lo16<T16>(q[0]);
+  v[1] = hi16<T16>(q[0]);
+  v[2] = lo16<T16>(q[1]);
+  v[3] = hi16<T16>(q[1]);
 }
+__device__ __forceinline__ void load4(const bf16_t* p, int64_t i, float (&v)[4]) { load4_16(p, i, v); }
+__device__ __forceinline__ void load4(const f16_t* p, int64_t i, float (&v)[4]) { load4_16(p, i, v); }
 __device__ __forceinline__ void load4(const float* p, int64_t i, float (&v)[4]) {
   const f32x4_t a = *reinterpret_cast<const MUONH_GLOBAL f32x4_t*>(gmem(p + i));
   v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
 }
 __device__ __forceinline__ void store4(bf16_t* p, int64_t i, const float (&v)[4]) {
   const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  *reinterpret_cast<MUONH_GLOBAL u32x2_t*>(gmem(p + i)) = w;
+}
+__device__ __forceinline__ void store4(f16_t* p, int64_t i, const float (&v)[4]) {
+  const u32x2_t w = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
   *reinterpret_cast<MUONH_GLOBAL u32x2_t*>(gmem(p + i)) = w;
 }
 __device__ __forceinline__ void store4(float* p, int64_t i, const float (&v)[4]) {
@@ -147,22 +165,28 @@ __device__ __forceinline__ void store_out(void* p, int64_t i, const float (&v)[N
 // fragment: within each 16-lane group, lane j addresses row j / 4, elements
 // 4 (j % 4) .. + 3 of a [k][m] tile, and lane i receives element i of rows
 // 0..3 (4 consecutive k for one m); p1 covers the next 4 rows.
-__device__ __forceinline__ bf16x8_t ld_tr8(const bf16_t* p0, const bf16_t* p1) {
+template <typename F>
+__device__ __forceinline__ F ld_tr8(const uint16_t* p0, const uint16_t* p1) {
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p0);
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p1);
   const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8_t, v);
+  return __builtin_bit_cast(F, v);
 }
 
 // Block tile BM x BN (BM == BN) on WGM x WGN waves, each wave (BM/WGM) x
 // (BN/WGN) built from 32 x 32 MFMA tiles; BK elements of K per LDS stage.
 // Register budgets keep two waves per SIMD: 128-tiles run two workgroups of
 // 4 waves per CU, 256-tiles one workgroup of 8 waves.
-template <typename T, int PHASE, int BM, int BN, int BK, int WGM, int WGN>
+template <typename T, typename TO, int PHASE, int BM, int BN, int BK, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2))) void k_ns_gemm(
     const NsUnit* __restrict__ units, const GemmJob* __restrict__ jobs, NsIterArgs args) {
   using M = Mf<T>;
+  static_assert(sizeof(T) == sizeof(TO), "the output storage has the operand's width");
+  // 16-bit storage types of the operands and of the output (bf16 stand-ins
+  // for fp32 instances, whose 16-bit paths are compiled out)
+  using T16 = typename std::conditional<sizeof(T) == 2, T, bf16_t>::type;
+  using TO16 = typename std::conditional<sizeof(TO) == 2, TO, bf16_t>::type;
   constexpr int NT = 64 * WGM * WGN;  // threads
   constexpr bool TR = PHASE == kG1;   // operands are X^T tiles stored [k][m]
   constexpr int VEC = M::VEC, KSTEP = M::KSTEP;
@@ -436,8 +460,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     if constexpr (!TR) {
       return M::ld(stage + ofs + kk * KSTEP);
     } else if constexpr (sizeof(T) == 2) {
-      const bf16_t* p = reinterpret_cast<const bf16_t*>(stage) + ofs + kk * KSTEP * BM;
-      return ld_tr8(p, p + 4 * BM);
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(stage) + ofs + kk * KSTEP * BM;
+      return ld_tr8<typename M::frag>(p, p + 4 * BM);
     } else {
       return stage[ofs + kk * KSTEP * BM];
     }
@@ -592,10 +616,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const u32x2_t w = *reinterpret_cast<const u32x2_t*>(sq + nl * BK + ((4 * sh + q) ^ swz(nl)) * VEC + lrow);
-              acc[i][j][4 * q + 0] = fmaf(mul, __uint_as_float(w[0] << 16), acc[i][j][4 * q + 0]);
-              acc[i][j][4 * q + 1] = fmaf(mul, __uint_as_float(w[0] & 0xffff0000u), acc[i][j][4 * q + 1]);
-              acc[i][j][4 * q + 2] = fmaf(mul, __uint_as_float(w[1] << 16), acc[i][j][4 * q + 2]);
-              acc[i][j][4 * q + 3] = fmaf(mul, __uint_as_float(w[1] & 0xffff0000u), acc[i][j][4 * q + 3]);
+              acc[i][j][4 * q + 0] = fmaf(mul, lo16<T16>(w[0]), acc[i][j][4 * q + 0]);
+              acc[i][j][4 * q + 1] = fmaf(mul, hi16<T16>(w[0]), acc[i][j][4 * q + 1]);
+              acc[i][j][4 * q + 2] = fmaf(mul, lo16<T16>(w[1]), acc[i][j][4 * q + 2]);
+              acc[i][j][4 * q + 3] = fmaf(mul, hi16<T16>(w[1]), acc[i][j][4 * q + 3]);
             }
           }
         }
@@ -810,10 +834,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
               for (int q = 0; q < 4; ++q) {
                 const u32x2_t w =
                     *reinterpret_cast<const u32x2_t*>(sq + nl * BK + ((4 * sh + q) ^ swz(nl)) * VEC + lrow);
-                acc[i][j][4 * q + 0] = fmaf(mul, __uint_as_float(w[0] << 16), acc[i][j][4 * q + 0]);
-                acc[i][j][4 * q + 1] = fmaf(mul, __uint_as_float(w[0] & 0xffff0000u), acc[i][j][4 * q + 1]);
-                acc[i][j][4 * q + 2] = fmaf(mul, __uint_as_float(w[1] << 16), acc[i][j][4 * q + 2]);
-                acc[i][j][4 * q + 3] = fmaf(mul, __uint_as_float(w[1] & 0xffff0000u), acc[i][j][4 * q + 3]);
+                acc[i][j][4 * q + 0] = fmaf(mul, lo16<T16>(w[0]), acc[i][j][4 * q + 0]);
+                acc[i][j][4 * q + 1] = fmaf(mul, hi16<T16>(w[0]), acc[i][j][4 * q + 1]);
+                acc[i][j][4 * q + 2] = fmaf(mul, lo16<T16>(w[1]), acc[i][j][4 * q + 2]);
+                acc[i][j][4 * q + 3] = fmaf(mul, hi16<T16>(w[1]), acc[i][j][4 * q + 3]);
               }
             }
           }
@@ -964,10 +988,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
             (void)seed_off(i, j, q, ok);
             const float mul = ok ? seed_coef : 0.f;
             const u32x2_t w = seedv[i][j][q];
-            acc[i][j][4 * q + 0] = fmaf(mul, __uint_as_float(w[0] << 16), acc[i][j][4 * q + 0]);
-            acc[i][j][4 * q + 1] = fmaf(mul, __uint_as_float(w[0] & 0xffff0000u), acc[i][j][4 * q + 1]);
-            acc[i][j][4 * q + 2] = fmaf(mul, __uint_as_float(w[1] << 16), acc[i][j][4 * q + 2]);
-            acc[i][j][4 * q + 3] = fmaf(mul, __uint_as_float(w[1] & 0xffff0000u), acc[i][j][4 * q + 3]);
+            acc[i][j][4 * q + 0] = fmaf(mul, lo16<T16>(w[0]), acc[i][j][4 * q + 0]);
+            acc[i][j][4 * q + 1] = fmaf(mul, hi16<T16>(w[0]), acc[i][j][4 * q + 1]);
+            acc[i][j][4 * q + 2] = fmaf(mul, lo16<T16>(w[1]), acc[i][j][4 * q + 2]);
+            acc[i][j][4 * q + 3] = fmaf(mul, hi16<T16>(w[1]), acc[i][j][4 * q + 3]);
           }
     }
   }
@@ -983,7 +1007,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   // for the fp32 master).  The swaps run with every lane active; only the
   // stores are guarded.
   if (PHASE == kG3 && !args.last) {
-    T* const xo = reinterpret_cast<T*>(args.cur ? u.xt[0] : u.xt[1]);
+    TO* const xo = reinterpret_cast<TO*>(args.cur ? u.xt[0] : u.xt[1]);
     const int hi = lane >> 5;
     // Most waves' blocks lie inside the matrix, and all iterations but the
     // first have no pre-scale: that case runs a copy of the store loop with
@@ -1019,12 +1043,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
             const bool ok = fast || (n < u.ld_s && ms < u.ld_r);
             const int64_t o = (int64_t)(ok ? n : 0) * u.ld_r + (ok ? ms : 0);
             if constexpr (sizeof(T) == 2) {
-              uint32_t w0 = pack_bf16x2(v[0][0], v[0][1]), w1 = pack_bf16x2(v[0][2], v[0][3]);
-              uint32_t w2 = pack_bf16x2(v[1][0], v[1][1]), w3 = pack_bf16x2(v[1][2], v[1][3]);
+              uint32_t w0 = pack16x2<TO16>(v[0][0], v[0][1]), w1 = pack16x2<TO16>(v[0][2], v[0][3]);
+              uint32_t w2 = pack16x2<TO16>(v[1][0], v[1][1]), w3 = pack16x2<TO16>(v[1][2], v[1][3]);
               const auto s0 = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
               const auto s1 = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
               const u32x4_t pk = {s0[0], s1[0], s0[1], s1[1]};
-              if (ok) *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(reinterpret_cast<bf16_t*>(xo) + o)) = pk;
+              if (ok) *reinterpret_cast<MUONH_GLOBAL u32x4_t*>(gmem(reinterpret_cast<uint16_t*>(xo) + o)) = pk;
             } else {
               float vs[8];
 #pragma unroll
@@ -1080,7 +1104,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   const int q = tid % CPC, csub = tid / CPC;
   const bool o_vec = (u.o_dtype == DT_BF16) ? ((u.o_ld % 8) == 0 && ((uintptr_t)u.o_ptr % 16) == 0)
                                             : ((u.o_ld % 4) == 0 && ((uintptr_t)u.o_ptr % 16) == 0);
-  T* const out12 = reinterpret_cast<T*>(PHASE == kG1 ? u.a : u.b);
+  TO* const out12 = reinterpret_cast<TO*>(PHASE == kG1 ? u.a : u.b);
 
   constexpr int NCOL_IT = BN / COLS_PER_IT;
 #pragma unroll 1
@@ -1183,29 +1207,44 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 // host launcher
 // ---------------------------------------------------------------------------
 // Tile configurations (planner.h): 0 = 128 x 128 on 2 x 2 waves, K stages of
-// 64 (bf16) or 32 (fp32); 1 = 256 x 256 on 4 x 2 waves (bf16 operands,
-// large units).
-hipError_t launch_ns_gemm(int op_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs, int njobs,
-                          float a, float b, float c, float eps, int first, int last, int cur, int no_mma,
-                          int master32, int seed32, const SlotTable& st, hipStream_t s) {
+// 64 (bf16 / fp16) or 32 (fp32); 1 = 256 x 256 on 4 x 2 waves (16-bit
+// operands, large units); 2 = 64 x 64 on 2 x 2 waves (fp32 units of side
+// <= 256).  op_dt is the operands' storage, out_dt that of the product this
+// launch stores (A, B or the new X^T; the last update writes O in the
+// caller's dtype whatever out_dt says): (bf16, bf16), (bf16, fp16),
+// (fp16, fp16) and (fp32, fp32).
+hipError_t launch_ns_gemm(int op_dt, int out_dt, int phase, int cfg, const NsUnit* units, const GemmJob* jobs,
+                          int njobs, float a, float b, float c, float eps, int first, int last, int cur,
+                          int no_mma, int master32, int seed32, const SlotTable& st, hipStream_t s) {
   if (njobs <= 0) return hipSuccess;
   NsIterArgs args{a, b, c, eps, first, last, cur, no_mma, master32, seed32, njobs, st};
   dim3 grid(njobs);
-#define MUONH_LAUNCH(T, PH, B, K, GM, GN) \
-  hipLaunchKernelGGL((k_ns_gemm<T, PH, B, B, K, GM, GN>), grid, dim3(64 * GM * GN), 0, s, units, jobs, args)
-#define MUONH_PHASES(T, B, K, GM, GN)                          \
-  do {                                                         \
-    if (phase == kG1) MUONH_LAUNCH(T, kG1, B, K, GM, GN);      \
-    else if (phase == kG2) MUONH_LAUNCH(T, kG2, B, K, GM, GN); \
-    else MUONH_LAUNCH(T, kG3, B, K, GM, GN);                   \
+#define MUONH_LAUNCH(T, TO, PH, B, K, GM, GN) \
+  hipLaunchKernelGGL((k_ns_gemm<T, TO, PH, B, B, K, GM, GN>), grid, dim3(64 * GM * GN), 0, s, units, jobs, args)
+#define MUONH_PHASES(T, TO, B, K, GM, GN)                          \
+  do {                                                             \
+    if (phase == kG1) MUONH_LAUNCH(T, TO, kG1, B, K, GM, GN);      \
+    else if (phase == kG2) MUONH_LAUNCH(T, TO, kG2, B, K, GM, GN); \
+    else MUONH_LAUNCH(T, TO, kG3, B, K, GM, GN);                   \
   } while (0)
-  if (op_dt == DT_BF16) {
-    if (cfg == 1) MUONH_PHASES(bf16_t, 256, 64, 4, 2);
-    else MUONH_PHASES(bf16_t, 128, 64, 2, 2);
+#define MUONH_CFGS16(T, TO)                                 \
+  do {                                                      \
+    if (cfg == 1) MUONH_PHASES(T, TO, 256, 64, 4, 2);       \
+    else MUONH_PHASES(T, TO, 128, 64, 2, 2);                \
+  } while (0)
+  if (op_dt == DT_BF16 && out_dt == DT_BF16) {
+    MUONH_CFGS16(bf16_t, bf16_t);
+  } else if (op_dt == DT_BF16 && out_dt == DT_F16) {
+    MUONH_CFGS16(bf16_t, f16_t);
+  } else if (op_dt == DT_F16 && out_dt == DT_F16) {
+    MUONH_CFGS16(f16_t, f16_t);
+  } else if (op_dt == DT_F32 && out_dt == DT_F32) {
+    if (cfg == 2) MUONH_PHASES(float, float, 64, 32, 2, 2);
+    else MUONH_PHASES(float, float, 128, 32, 2, 2);
   } else {
-    if (cfg == 2) MUONH_PHASES(float, 64, 32, 2, 2);
-    else MUONH_PHASES(float, 128, 32, 2, 2);
+    return hipErrorInvalidValue;
   }
+#undef MUONH_CFGS16
 #undef MUONH_PHASES
 #undef MUONH_LAUNCH
   return hipGetLastError();

@@ -24,6 +24,7 @@ struct Cfg {
   int tile_T;
   int state_dt, op_dt;
   int x32;        // fp32 master X (bf16 operands only)
+  int h16;        // bf16 operands: X, A, B stored in fp16 after the first product (MUONH_NS_H16)
   int seed32;     // bf16 operands with an NS input that is not a bf16 value (fp32
                   // state, or the Nesterov blend): the first a X term is seeded
                   // from an fp32 copy of X0

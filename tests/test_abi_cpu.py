@@ -86,7 +86,7 @@ def test_step_rejects_bad_options():
 
 def test_default_options():
     o = _opts()
-    assert (o.state_dtype, o.ns_dtype, o.ns_precision, o.hook) == (mm.MUONH_BF16, mm.MUONH_BF16, mm.MUONH_NS_FOLD,
+    assert (o.state_dtype, o.ns_dtype, o.ns_precision, o.hook) == (mm.MUONH_BF16, mm.MUONH_BF16, mm.MUONH_NS_H16,
                                                                    mm.MUONH_HOOK_HYPERBALL)
     assert (o.momentum_ema, o.nesterov, o.weight_decay, o.workspace_limit, o.lanes) == (0, 0, 0.0, 0, 0)
     assert o.hyperball_step == mm.MUONH_HB_STEP_UNIT
@@ -97,11 +97,14 @@ def test_default_options():
 
 def test_enums_follow_the_boundary_contract():
     # MUONH_NS_FOLD = 0 (bf16 X, folded pre-scale), MUONH_NS_X32 = 1, as the
-    # header declares them
+    # boundary numbers them, and MUONH_NS_H16 = 2 after them, as the header
+    # declares them
     import re
     hdr = open(HEADER).read()
-    m = re.search(r"enum\s*\{\s*MUONH_NS_FOLD\s*=\s*(\d+),\s*MUONH_NS_X32\s*=\s*(\d+)\s*\}", hdr)
-    assert m and (int(m.group(1)), int(m.group(2))) == (mm.MUONH_NS_FOLD, mm.MUONH_NS_X32) == (0, 1)
+    m = re.search(r"enum\s*\{\s*MUONH_NS_FOLD\s*=\s*(\d+),\s*MUONH_NS_X32\s*=\s*(\d+),\s*MUONH_NS_H16\s*=\s*(\d+)\s*\}",
+                  hdr)
+    got = tuple(int(m.group(i)) for i in (1, 2, 3)) if m else None
+    assert got == (mm.MUONH_NS_FOLD, mm.MUONH_NS_X32, mm.MUONH_NS_H16) == (0, 1, 2)
 
 
 def test_lanes_share_one_chunk_workspace():
