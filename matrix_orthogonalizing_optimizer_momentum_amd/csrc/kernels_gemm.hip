@@ -10,8 +10,12 @@
 //                                       iteration; the last iteration writes O
 //                                       in the caller's layout and its sum of
 //                                       squares)
-// X lives only as X^T (s rows of r, both sides zero-padded to 64), in operand
-// precision, plus an fp32 master copy in the same layout when requested.
+// X lives only as X^T (s rows of r, both sides zero-padded to 64) in a 16-bit
+// storage type (bf16 X0^T from the momentum pass; with fp16 iterates every
+// later X^T, A and B in fp16) or fp32, plus an fp32 master copy in the same
+// layout when requested.  A launch reads its operands in one type and stores
+// its product in another (bf16 -> fp16 for the first update under fp16
+// iterates).
 // Every product is D[i][j] = sum_k P[i][k] Q[j][k]:
 //   G2 reads A twice and G3 reads B and X^T with K-contiguous rows;
 //   G1 reads X^T tiles [k][m] and forms K-contiguous MFMA fragments with
@@ -26,8 +30,9 @@
 // A launch covers every unit (matrix or HiMuon tile) of a chunk through a job
 // list of BM x BN output tiles; job order is remapped so that the jobs one XCD
 // runs are contiguous in the list (operand panels shared in its L2).
-// Operands are bf16 (v_mfma_f32_32x32x16_bf16) or fp32
-// (v_mfma_f32_32x32x2_f32), accumulation is fp32.  Two main loops:
+// Operands are bf16 (v_mfma_f32_32x32x16_bf16), fp16
+// (v_mfma_f32_32x32x16_f16, the same rate) or fp32 (v_mfma_f32_32x32x2_f32),
+// accumulation is fp32.  Two main loops:
 //   - 128 x 128 tiles (4 waves, two workgroups per CU): LDS stages double
 //     buffered behind a register prefetch ring of 16-byte global loads, MFMA
 //     fragments double buffered in registers (the same loop on 64 x 64 tiles

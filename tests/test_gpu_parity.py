@@ -1112,7 +1112,7 @@ def test_ns_full_size_closed_form_bf16_default(shape):
 @pytest.mark.parametrize("shape", [(4096, 14336), (14336, 4096), (2048, 6144), (4096, 4096)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_ns_full_size_spiked_vs_oracle(shape):
-    # Full-size bf16 parity on the default options (FOLD, 256-tile engine:
+    # Full-size bf16 parity on the default options (fp16 iterates, 256-tile engine:
     # the launch configuration the benchmark times) against the fp64 oracle
     # run on the same stored input: a spiked gradient of the workloads'
     # distribution (Gaussian + rank-4, 10x), stored in bf16.  The oracle
