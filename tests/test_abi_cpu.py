@@ -338,6 +338,26 @@ def test_x32_needs_more_workspace_than_fold():
     assert mm.plan_query(s, ns_precision="x32")["ws_bytes"] > mm.plan_query(s, ns_precision="fold")["ws_bytes"]
 
 
+def test_fp16_iterates_need_the_workspace_of_bf16_x():
+    # fp16 iterates take the place of the bf16 ones: same buffers, same bytes,
+    # the same chunks under a budget (the 8B-shaped set at 16 GiB: 4 chunks)
+    from synth import gen
+    for shapes, limit in (([(768, 3072), (3072, 768), (300, 700)], 0), (gen.dense_8b_shapes(), 16 << 30)):
+        h = mm.plan_query(shapes, ns_precision="h16", workspace_limit=limit)
+        f = mm.plan_query(shapes, ns_precision="fold", workspace_limit=limit)
+        assert h["ws_bytes"] == f["ws_bytes"] and h["chunks"] == f["chunks"]
+    assert mm.plan_query(gen.dense_8b_shapes(), workspace_limit=16 << 30)["chunks"] == 4
+
+
+def test_precision_option_is_validated():
+    o = _opts()
+    for bad in (3, -1):
+        o.ns_precision = bad
+        P = ctypes.c_void_p * 1
+        rc = mm.load().ns_orthogonalize(P(0x1000), P(0x2000), (ctypes.c_int64 * 2)(8, 8), 1, 5, 0, ctypes.byref(o))
+        assert rc == mm.MUONH_EINVAL
+
+
 def _adam(n=1, eta=0.01, b1=0.9, b2=0.95, eps=1e-8, step=1, null_rho=False, alias=None, opts=None):
     lib = mm.load()
     P = ctypes.c_void_p * max(n, 1)
